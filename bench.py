@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet token mixer on one MI355X.
+
+One step = the hot path over one batch of synthetic input:
+  prefill layer on the Qwen3.5-9B shape, T = 4096 tokens, bf16 io:
+      gdn_conv1d_fwd -> gdn_chunk_prefill -> gdn_gated_rmsnorm
+  decode step on the Qwen3.5-9B shape, 256 sequences, bf16 io, fp32 state:
+      gdn_recurrent_step (conv + state updated in place) -> gdn_gated_rmsnorm
+
+Reported ("value"): layer prefill tokens/s = 4096 / (conv + chunk + norm time),
+with the chunked core against the bf16 dense MFMA peak (roofline) and the decode
+step's algorithmic bytes against the HBM peak (roofline_decode).  Kernel times come
+from HIP events recorded on the stream the kernels run on (torch's current stream).
+Inputs are resident in HBM before timing starts.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+D = 128
+CHUNK = 64
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+
+
+def chunk_core_flops(n_tokens: int, hk: int, hv: int, seqlens=None) -> float:
+    """Algorithmic flops of the chunked core (triangles at their triangle, Gram
+    products once per key head), summed per chunk with partial chunks at their length:
+      per token  Hk (2 C d) + Hv (3 C d + C^2/3 + 6 d^2)."""
+    seqlens = seqlens or [n_tokens]
+    tot = 0.0
+    for L in seqlens:
+        full, tail = divmod(L, CHUNK)
+        for c, cnt in ((CHUNK, full), (tail, 1 if tail else 0)):
+            per_tok = hk * (2 * c * D) + hv * (3 * c * D + c * c / 3.0 + 6 * D * D)
+            tot += cnt * c * per_tok
+    return tot
+
+
+def decode_bytes(B: int, hk: int, hv: int, io_bytes: int = 2) -> float:
+    """Compulsory HBM bytes of one decode step: fp32 state read + write, conv state
+    read + write, x, a, b, conv weight, o."""
+    cq = 2 * hk * D + hv * D
+    state = 2.0 * B * hv * D * D * 4
+    conv_state = 2.0 * B * 3 * cq * io_bytes
+    x = B * cq * io_bytes
+    ab = 2.0 * B * hv * io_bytes
+    w = cq * 4 * 4 + 2 * hv * 4
+    o = B * hv * D * io_bytes
+    return state + conv_state + x + ab + w + o
+
+
+def _cpu_chain(task):
+    """Oracle work for one value head of the prefill layer (runs in a worker process)."""
+    import numpy as np
+    from oracle import gdn_oracle as G
+    x, w, a, b, A_log, dt_bias, z, norm_w, io = task
+    y, _ = G.conv1d_fwd(x, w)
+    y = G.to_io(y, io)
+    q, k, v = y[:, :D], y[:, D:2 * D], y[:, 2 * D:]
+    g, beta = G.gates(a[:, None], b[:, None], np.array([A_log]), np.array([dt_bias]))
+    o, S = G.delta_rule(G.l2_normalize(q), G.l2_normalize(k), v, g[:, 0], beta[:, 0],
+                        np.zeros((D, D)), 1.0 / np.sqrt(D))
+    o = G.to_io(o, io)
+    return G.to_io(G.gated_rmsnorm(o, z, norm_w), io).shape[0]
+
+
+def cpu_baseline(inp, budget_heads=None):
+    """Time the fp64 oracle on the prefill layer workload in a process pool over value
+    heads (one BLAS thread per worker).  Returns the cpu_baseline object."""
+    import multiprocessing as mp
+
+    import numpy as np
+    hk, hv, N = inp["Hk"], inp["Hv"], inp["N"]
+    r = hv // hk
+    heads = list(range(hv)) if budget_heads is None else list(range(budget_heads))
+    tasks = []
+    for h in heads:
+        kh = h // r
+        chans = np.concatenate([np.arange(kh * D, kh * D + D),
+                                hk * D + np.arange(kh * D, kh * D + D),
+                                2 * hk * D + np.arange(h * D, h * D + D)])
+        tasks.append((inp["x"][:, chans], inp["conv_w"][chans], inp["a"][:, h], inp["b"][:, h],
+                      float(inp["A_log"][h]), float(inp["dt_bias"][h]),
+                      inp["z"][:, h * D:(h + 1) * D], inp["norm_w"], inp["io"]))
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    procs = max(1, min(16, ncpu, len(tasks)))
+    env_keep = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                               "MKL_NUM_THREADS")}
+    for k in env_keep:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(procs) as pool:
+            pool.map(_cpu_chain, tasks[:procs])          # warm the workers (imports)
+            t0 = time.perf_counter()
+            pool.map(_cpu_chain, tasks, chunksize=1)
+            wall = time.perf_counter() - t0
+    finally:
+        for k, v in env_keep.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    tokens_per_s = N * (len(heads) / hv) / wall
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": procs, "kind": "oracle",
+            "wall_s": wall,
+            "sample": (f"fp64 NumPy oracle (token-by-token recurrence) of the Qwen3.5-9B prefill "
+                       f"layer, T={N}, {len(heads)} of {hv} value heads (conv+core+norm per head), "
+                       f"{procs} worker processes; tokens/s scaled by heads/{hv}")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=None,
+                    help="value heads in the CPU-oracle sample (default: all)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the mixer would shard by head groups or sequences with no exchange; "
+              "see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import hybrid_linear_attention_causal_amd as gdn
+    from hybrid_linear_attention_causal_amd import synth
+    from hybrid_linear_attention_causal_amd._lib import (gdn_chunk_prefill, gdn_conv1d_fwd,
+                                                         gdn_gated_rmsnorm, gdn_recurrent_step)
+    from hybrid_linear_attention_causal_amd.mixer import qkv_views
+
+    torch.cuda.set_device(0)
+    wl_p, wl_d = synth.workload(1), synth.workload(2)
+    pre = synth.make(wl_p)
+    dec = synth.make(wl_d)
+
+    def dev(a, f32=False):
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+        return (t if f32 else t.to(torch.bfloat16)).cuda()
+
+    hk, hv, N = pre["Hk"], pre["Hv"], pre["N"]
+    cq = pre["Cq"]
+    P = {name: dev(pre[name]) for name in ("x", "a", "b", "z")}
+    for name in ("conv_w", "A_log", "dt_bias", "norm_w"):
+        P[name] = dev(pre[name], True)
+    P["y"] = torch.empty_like(P["x"])
+    P["cs_out"] = torch.empty((1, 3, cq), dtype=torch.bfloat16, device="cuda")
+    P["o"] = torch.empty((N, hv, D), dtype=torch.bfloat16, device="cuda")
+    P["s_out"] = torch.empty((1, hv, D, D), dtype=torch.float32, device="cuda")
+    P["yn"] = torch.empty_like(P["o"])
+    q, k, v = qkv_views(P["y"], hk, hv)
+    zv = P["z"].view(N, hv, D)
+
+    B = dec["N"]
+    Dd = {name: dev(dec[name]) for name in ("x", "a", "b", "z", "conv_state_in")}
+    for name in ("conv_w", "A_log", "dt_bias", "norm_w", "state_in"):
+        Dd[name] = dev(dec[name], True)
+    Dd["o"] = torch.empty((B, hv, D), dtype=torch.bfloat16, device="cuda")
+    Dd["yn"] = torch.empty_like(Dd["o"])
+    zd = Dd["z"].view(B, hv, D)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        gdn_conv1d_fwd(P["x"], P["conv_w"], P["y"], None, None, P["cs_out"])
+        if ev:
+            ev[1].record()
+        gdn_chunk_prefill(q, k, v, P["a"], P["b"], P["A_log"], P["dt_bias"], P["o"], hk, hv,
+                          None, None, P["s_out"])
+        if ev:
+            ev[2].record()
+        gdn_gated_rmsnorm(P["o"], zv, P["norm_w"], P["yn"])
+        if ev:
+            ev[3].record()
+        gdn_recurrent_step(Dd["x"], Dd["conv_w"], Dd["conv_state_in"], Dd["a"], Dd["b"],
+                           Dd["A_log"], Dd["dt_bias"], Dd["state_in"], Dd["o"], hk, hv)
+        if ev:
+            ev[4].record()
+        gdn_gated_rmsnorm(Dd["o"], zd, Dd["norm_w"], Dd["yn"])
+        if ev:
+            ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["conv1d", "chunk_prefill", "prefill_norm", "recurrent_step", "decode_norm"]
+    ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    prefill_ms = ms["conv1d"] + ms["chunk_prefill"] + ms["prefill_norm"]
+    tokens_per_s = N / (prefill_ms * 1e-3)
+
+    flops = chunk_core_flops(N, hk, hv)
+    chunk_tflops = flops / (ms["chunk_prefill"] * 1e-3) / 1e12
+    dbytes = decode_bytes(B, hk, hv)
+    step_gbs = dbytes / (ms["recurrent_step"] * 1e-3) / 1e9
+
+    res = {
+        "metric": "GDN layer prefill tokens/s (%MFMA peak) + decode step state GB/s (%HBM peak)",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Qwen3.5-9B linear-attention layer shapes, random parameters)",
+        "config": {"workload": "Qwen3.5-9B GDN layer prefill T=4096 (B=1) + decode step B=256",
+                   "prefill_tokens": N, "decode_batch": B, "Hk": hk, "Hv": hv, "d": D,
+                   "conv_channels": cq, "chunk": CHUNK, "io": "bf16", "state": "fp32"},
+        "kernel_ms": ms,
+        "roofline": {"kernel": "gdn_chunk_prefill", "bound": "mfma", "achieved": chunk_tflops,
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": chunk_tflops * 1e12 / PEAK_BF16_FLOPS, "traffic": None,
+                     "algorithmic_per_launch": flops},
+        "roofline_decode": {"kernel": "gdn_recurrent_step", "bound": "hbm", "achieved": step_gbs,
+                            "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                            "frac": step_gbs * 1e9 / PEAK_HBM_BYTES, "traffic": None,
+                            "algorithmic_per_launch": dbytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(pre, args.cpu_heads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

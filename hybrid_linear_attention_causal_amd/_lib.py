@@ -1,0 +1,164 @@
+"""ctypes binding of libgdn (include/gdn.h), with the same call names.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libgdn.so.  Tensors are torch tensors on the GPU; their data
+pointers and torch's current HIP stream are handed to the C calls.  A missing
+library raises at first use -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "gdn.h")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+GDN_F32, GDN_BF16 = 0, 1
+_STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "gdn_last_error": ([], ctypes.c_char_p),
+    "gdn_version": ([], ctypes.c_char_p),
+    "gdn_conv1d_fwd": ([_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp], _i32),
+    "gdn_chunk_prefill_workspace_size": ([_i64, _i32, _i32, _i32, _i32], _sz),
+    "gdn_chunk_prefill": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
+                           _sz, _i32, _vp], _i32),
+    "gdn_recurrent_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                            _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp], _i32),
+    "gdn_gated_rmsnorm": ([_vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32, _vp], _i32),
+}
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, call: str, status: int, msg: str):
+        super().__init__(f"{call}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def declared_symbols(header: str = HEADER) -> list:
+    """Function names declared in include/gdn.h."""
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gdn_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "or python -m hybrid_linear_attention_causal_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(call: str, status: int):
+    if status != GDN_OK:
+        raise GdnError(call, status, lib().gdn_last_error().decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _io(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GDN_F32
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    raise TypeError(f"io tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libgdn takes device (GPU) tensors only")
+
+
+def version() -> str:
+    return lib().gdn_version().decode()
+
+
+def gdn_conv1d_fwd(x, w, y, cu_seqlens=None, conv_state_in=None, conv_state_out=None, K=4,
+                   stream=None):
+    """y = silu(causal depthwise conv1d(x)), per packed sequence; see gdn.h."""
+    _dev(x, w, y, cu_seqlens, conv_state_in, conv_state_out)
+    N, Cq = x.shape
+    Ns = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check("gdn_conv1d_fwd", lib().gdn_conv1d_fwd(
+        _p(x), _p(w), _p(y), _p(cu_seqlens), Ns, N, Cq, K, _p(conv_state_in), _p(conv_state_out),
+        _io(x), _stream(stream)))
+
+
+def gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, d=128) -> int:
+    return int(lib().gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, d))
+
+
+def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None, state_in=None,
+                      state_out=None, g_opt=None, beta_opt=None, scale=0.0, use_qk_l2norm=True,
+                      workspace=None, stream=None, dk=128, dv=128):
+    """Chunked gated delta rule; q, k, v are [N, *] row views (stride(0) may exceed the width)."""
+    _dev(q, k, v, a, b, A_log, dt_bias, o, cu_seqlens, state_in, state_out, g_opt, beta_opt,
+         workspace)
+    N = q.shape[0]
+    Ns = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    for t in (q, k, v):
+        if t.stride(-1) != 1:
+            raise ValueError("q, k, v rows must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("gdn_chunk_prefill", lib().gdn_chunk_prefill(
+        _p(q), _p(k), _p(v), q.stride(0), k.stride(0), v.stride(0), _p(a), _p(b), _p(A_log),
+        _p(dt_bias), _p(g_opt), _p(beta_opt), _p(state_in), _p(state_out), _p(o),
+        _p(cu_seqlens), Ns, N, Hk, Hv, dk, dv, float(scale), int(bool(use_qk_l2norm)),
+        _p(workspace), ws_bytes, _io(q), _stream(stream)))
+
+
+def gdn_recurrent_step(x, w, conv_state, a, b, A_log, dt_bias, state, o, Hk, Hv, g_opt=None,
+                       beta_opt=None, scale=0.0, use_qk_l2norm=True, K=4, stream=None,
+                       dk=128, dv=128):
+    """One decode token per sequence; conv_state and state are updated in place."""
+    _dev(x, w, conv_state, a, b, A_log, dt_bias, state, o, g_opt, beta_opt)
+    B = x.shape[0]
+    _check("gdn_recurrent_step", lib().gdn_recurrent_step(
+        _p(x), _p(w), _p(conv_state), _p(a), _p(b), _p(A_log), _p(dt_bias), _p(g_opt),
+        _p(beta_opt), _p(state), _p(o), B, Hk, Hv, dk, dv, K, float(scale),
+        int(bool(use_qk_l2norm)), _io(x), _stream(stream)))
+
+
+def gdn_gated_rmsnorm(o, z, w, y, eps=1e-6, stream=None):
+    """y = w * o / rms(o) * silu(z) over rows of 128 (o, z, y viewed as [rows, 128])."""
+    _dev(o, z, w, y)
+    D = o.shape[-1]
+    rows = o.numel() // D
+    _check("gdn_gated_rmsnorm", lib().gdn_gated_rmsnorm(
+        _p(o), _p(z), _p(w), _p(y), rows, D, float(eps), _io(o), _stream(stream)))

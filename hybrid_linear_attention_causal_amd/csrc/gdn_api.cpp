@@ -1,0 +1,200 @@
+// C ABI of libgdn (declared in include/gdn.h): argument checks on the host,
+// a one-time gfx950 check per device, then kernel launches on the caller's
+// stream.  Nothing here allocates device memory or synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "gdn.h"
+#include "gdn_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status_t fail(gdn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+gdn_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxDev = 64;
+std::mutex g_arch_mu;
+int g_arch_ok[kMaxDev];  // 0 unknown, 1 gfx950, -1 other
+
+// The kernels are written for gfx950 only: refuse any other device.
+gdn_status_t check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDev) return fail(GDN_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    g_arch_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    if (g_arch_ok[dev] < 0) {
+      return fail(GDN_ERR_UNSUPPORTED, "device %d is %s; libgdn is built for gfx950 only", dev,
+                  prop.gcnArchName);
+    }
+  }
+  if (g_arch_ok[dev] < 0) return fail(GDN_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return GDN_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool io_ok(gdn_dtype_t io) { return io == GDN_F32 || io == GDN_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return g_err; }
+
+const char* gdn_version(void) { return "0.1.0"; }
+
+gdn_status_t gdn_conv1d_fwd(const void* x, const float* w, void* y, const int32_t* cu_seqlens,
+                            int Ns, int64_t N, int Cq, int K, const void* conv_state_in,
+                            void* conv_state_out, gdn_dtype_t io, void* stream) {
+  g_err[0] = 0;
+  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "conv1d: unknown io dtype %d", (int)io);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "conv1d: kernel width %d (only 4)", K);
+  if (N < 0 || Ns < 1 || Cq < 1 || Cq % 8 != 0)
+    return fail(GDN_ERR_INVALID_ARG, "conv1d: bad sizes N=%lld Ns=%d Cq=%d (Cq %% 8 == 0)",
+                (long long)N, Ns, Cq);
+  if (!cu_seqlens && Ns != 1)
+    return fail(GDN_ERR_INVALID_ARG, "conv1d: cu_seqlens is NULL but Ns=%d", Ns);
+  if (N > 0 && (!x || !w || !y)) return fail(GDN_ERR_INVALID_ARG, "conv1d: NULL x, w or y");
+  if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)) || (w && !aligned(w, 16)) ||
+      (conv_state_in && !aligned(conv_state_in, 16)) ||
+      (conv_state_out && !aligned(conv_state_out, 16)))
+    return fail(GDN_ERR_INVALID_ARG, "conv1d: pointers must be 16-byte aligned");
+  if (x && y && x == y) return fail(GDN_ERR_INVALID_ARG, "conv1d: y must not alias x");
+  gdn_status_t st = check_device();
+  if (st != GDN_OK) return st;
+  gdn::ConvArgs a{x, w, y, cu_seqlens, Ns, N, Cq, conv_state_in, conv_state_out};
+  hipError_t e = gdn::launch_conv1d(a, io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? GDN_OK : hip_fail(e, "conv1d launch");
+}
+
+size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d) {
+  (void)N; (void)Ns; (void)Hk; (void)Hv; (void)d;
+  return 0;
+}
+
+gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int64_t stride_q,
+                               int64_t stride_k, int64_t stride_v, const void* a, const void* b,
+                               const float* A_log, const float* dt_bias, const float* g_opt,
+                               const float* beta_opt, const float* state_in, float* state_out,
+                               void* o, const int32_t* cu_seqlens, int Ns, int64_t N, int Hk,
+                               int Hv, int dk, int dv, float scale, int use_qk_l2norm,
+                               void* workspace, size_t ws_bytes, gdn_dtype_t io, void* stream) {
+  g_err[0] = 0;
+  (void)workspace;
+  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: unknown io dtype %d", (int)io);
+  if (dk != 128 || dv != 128)
+    return fail(GDN_ERR_UNSUPPORTED, "chunk_prefill: head widths %d/%d (only 128/128)", dk, dv);
+  if (Hk < 1 || Hv < 1 || Hv % Hk != 0)
+    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: Hv=%d must be a positive multiple of Hk=%d",
+                Hv, Hk);
+  if (Ns < 1 || N < 0) return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: Ns=%d N=%lld", Ns, (long long)N);
+  if (!cu_seqlens && Ns != 1)
+    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: cu_seqlens is NULL but Ns=%d", Ns);
+  if ((int64_t)Ns * Hv * 2 > 0x7fffffffLL)
+    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: too many (sequence, head) pairs");
+  if (stride_q < (int64_t)Hk * dk || stride_k < (int64_t)Hk * dk || stride_v < (int64_t)Hv * dv ||
+      stride_q % 8 || stride_k % 8 || stride_v % 8)
+    return fail(GDN_ERR_INVALID_ARG,
+                "chunk_prefill: strides must cover a row and be multiples of 8 (q %lld k %lld v %lld)",
+                (long long)stride_q, (long long)stride_k, (long long)stride_v);
+  const bool have_g = g_opt != nullptr, have_b = beta_opt != nullptr;
+  if (have_g != have_b)
+    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: give both g_opt and beta_opt or neither");
+  if (N > 0) {
+    if (!q || !k || !v || !o) return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: NULL q, k, v or o");
+    if (!have_g && (!a || !b || !A_log || !dt_bias))
+      return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: NULL a, b, A_log or dt_bias");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+      return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: q, k, v, o must be 16-byte aligned");
+  }
+  if (ws_bytes < gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk))
+    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: workspace too small");
+  if (scale <= 0.f) scale = 1.0f / sqrtf((float)dk);
+  gdn_status_t st = check_device();
+  if (st != GDN_OK) return st;
+  gdn::ChunkArgs args{q, k, v, stride_q, stride_k, stride_v, a, b, A_log, dt_bias, g_opt,
+                      beta_opt, state_in, state_out, o, cu_seqlens, Ns, N, Hk, Hv, scale,
+                      use_qk_l2norm ? 1 : 0};
+  hipError_t e = gdn::launch_chunk_prefill(args, io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? GDN_OK : hip_fail(e, "chunk_prefill launch");
+}
+
+gdn_status_t gdn_recurrent_step(const void* x, const float* w, void* conv_state, const void* a,
+                                const void* b, const float* A_log, const float* dt_bias,
+                                const float* g_opt, const float* beta_opt, float* state, void* o,
+                                int B, int Hk, int Hv, int dk, int dv, int K, float scale,
+                                int use_qk_l2norm, gdn_dtype_t io, void* stream) {
+  g_err[0] = 0;
+  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "recurrent_step: unknown io dtype %d", (int)io);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "recurrent_step: kernel width %d (only 4)", K);
+  if (dk != 128 || dv != 128)
+    return fail(GDN_ERR_UNSUPPORTED, "recurrent_step: head widths %d/%d (only 128/128)", dk, dv);
+  if (B < 0 || Hk < 1 || Hv < 1 || Hv % Hk != 0 || Hv / Hk > 128)
+    return fail(GDN_ERR_INVALID_ARG, "recurrent_step: B=%d Hk=%d Hv=%d", B, Hk, Hv);
+  if ((int64_t)B * Hk > 0x7fffffffLL)
+    return fail(GDN_ERR_INVALID_ARG, "recurrent_step: too many (sequence, key head) pairs");
+  const bool have_g = g_opt != nullptr, have_b = beta_opt != nullptr;
+  if (have_g != have_b)
+    return fail(GDN_ERR_INVALID_ARG, "recurrent_step: give both g_opt and beta_opt or neither");
+  if (B > 0) {
+    if (!x || !w || !conv_state || !state || !o)
+      return fail(GDN_ERR_INVALID_ARG, "recurrent_step: NULL x, w, conv_state, state or o");
+    if (!have_g && (!a || !b || !A_log || !dt_bias))
+      return fail(GDN_ERR_INVALID_ARG, "recurrent_step: NULL a, b, A_log or dt_bias");
+    if (!aligned(state, 16) || !aligned(w, 16))
+      return fail(GDN_ERR_INVALID_ARG, "recurrent_step: state and w must be 16-byte aligned");
+  }
+  if (scale <= 0.f) scale = 1.0f / sqrtf((float)dk);
+  gdn_status_t st = check_device();
+  if (st != GDN_OK) return st;
+  gdn::StepArgs args{x, w, conv_state, a, b, A_log, dt_bias, g_opt, beta_opt, state, o, B, Hk, Hv,
+                     scale, use_qk_l2norm ? 1 : 0};
+  hipError_t e = gdn::launch_recurrent_step(args, io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? GDN_OK : hip_fail(e, "recurrent_step launch");
+}
+
+gdn_status_t gdn_gated_rmsnorm(const void* o, const void* z, const float* w, void* y,
+                               int64_t rows, int D, float eps, gdn_dtype_t io, void* stream) {
+  g_err[0] = 0;
+  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "gated_rmsnorm: unknown io dtype %d", (int)io);
+  if (D != 128) return fail(GDN_ERR_UNSUPPORTED, "gated_rmsnorm: row width %d (only 128)", D);
+  if (rows < 0 || !(eps >= 0.f))
+    return fail(GDN_ERR_INVALID_ARG, "gated_rmsnorm: rows=%lld eps=%g", (long long)rows, (double)eps);
+  if (rows > 0) {
+    if (!o || !z || !w || !y) return fail(GDN_ERR_INVALID_ARG, "gated_rmsnorm: NULL pointer");
+    if (!aligned(o, 16) || !aligned(z, 16) || !aligned(w, 16) || !aligned(y, 16))
+      return fail(GDN_ERR_INVALID_ARG, "gated_rmsnorm: pointers must be 16-byte aligned");
+  }
+  gdn_status_t st = check_device();
+  if (st != GDN_OK) return st;
+  gdn::NormArgs args{o, z, w, y, rows, eps};
+  hipError_t e = gdn::launch_gated_rmsnorm(args, io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? GDN_OK : hip_fail(e, "gated_rmsnorm launch");
+}
+
+}  // extern "C"

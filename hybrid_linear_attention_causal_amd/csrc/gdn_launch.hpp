@@ -1,0 +1,76 @@
+// Internal launcher interface between the C ABI (gdn_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum IoType { IO_F32 = 0, IO_BF16 = 1 };
+
+struct ConvArgs {
+  const void* x;
+  const float* w;
+  void* y;
+  const int32_t* cu;     // may be null (one sequence)
+  int Ns;
+  int64_t N;
+  int Cq;
+  const void* state_in;  // may be null
+  void* state_out;       // may be null
+};
+
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t stride_q, stride_k, stride_v;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  const float* g_opt;     // both or neither
+  const float* beta_opt;
+  const float* state_in;  // may be null
+  float* state_out;       // may be null
+  void* o;
+  const int32_t* cu;      // may be null
+  int Ns;
+  int64_t N;
+  int Hk, Hv;
+  float scale;
+  int use_l2;
+};
+
+struct StepArgs {
+  const void* x;
+  const float* w;
+  void* conv_state;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  const float* g_opt;
+  const float* beta_opt;
+  float* state;
+  void* o;
+  int B, Hk, Hv;
+  float scale;
+  int use_l2;
+};
+
+struct NormArgs {
+  const void* o;
+  const void* z;
+  const float* w;
+  void* y;
+  int64_t rows;
+  float eps;
+};
+
+hipError_t launch_conv1d(const ConvArgs& a, int io, hipStream_t s);
+hipError_t launch_chunk_prefill(const ChunkArgs& a, int io, hipStream_t s);
+hipError_t launch_recurrent_step(const StepArgs& a, int io, hipStream_t s);
+hipError_t launch_gated_rmsnorm(const NormArgs& a, int io, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,212 @@
+// Single-token decode of the Gated DeltaNet mixer: conv window + SiLU, L2 norm,
+// gates and one gated delta-rule step per value head, with the conv state and
+// the fp32 recurrent state updated in place.
+//
+// Operation: KerasFormers Qwen page, "Generation" (decode carries the per-layer
+// conv state and the delta-rule recurrent state); HF Qwen3.5 docs page,
+// "Usage tips" (the single-token recurrence is memory-bandwidth-bound).
+//
+// Work split: one workgroup per (sequence, key head).  It owns the conv
+// channels of that key head's q and k and of its r = Hv/Hk value heads, so
+// every conv-state element is read and rewritten by exactly one thread, and it
+// runs the r value heads HPP (1 or 2) at a time with 256 threads per head.
+//
+// State traffic (the roofline): each head's 128 x 128 fp32 state is read once
+// and written once.  Thread (rg, cg) of a head holds rows 16*rg .. 16*rg+15 of
+// columns 4*cg .. 4*cg+3 in registers (16 float4 loads, each wave covering two
+// contiguous 512-byte rows per instruction).  S^T k and S^T q are column sums
+// over rows: reduced over the 8 row groups with one cross-lane shuffle and an
+// LDS exchange between the 4 waves of the head.
+#include "gdn_common.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+constexpr int SD = 128;  // head width (dk = dv)
+
+template <int IO, int HPP>
+__global__ void __launch_bounds__(256 * HPP)
+recurrent_step_kernel(StepArgs p) {
+  typedef Io<IO> io;
+  typedef typename io::T T;
+  extern __shared__ float smem[];
+  const int Hk = p.Hk, Hv = p.Hv;
+  const int r = Hv / Hk;
+  const int Cq = 2 * Hk * SD + Hv * SD;
+  const int bseq = blockIdx.x / Hk;
+  const int kh = blockIdx.x % Hk;
+  const int tid = threadIdx.x;
+  const int nthr = 256 * HPP;
+
+  // LDS: conv outputs [q | k | v of r heads], then reduction buffers and gates
+  float* yv = smem;                          // 256 + r*128
+  float* red1 = yv + 256 + r * SD;           // HPP * 4 waves * 128
+  float* red2 = red1 + HPP * 4 * SD;         // HPP * 4 * 128
+  float* gsh = red2 + HPP * 4 * SD;          // r: decay e^g
+  float* bsh = gsh + r;                      // r: beta
+  float* nsh = bsh + r;                      // 2: 1/|q|, 1/|k|
+
+  const int hl = tid >> 8;        // head slot inside a pass
+  const int t256 = tid & 255;
+  const int cg = t256 & 31;       // column group: columns 4cg .. 4cg+3
+  const int rg = t256 >> 5;       // row group: rows 16rg .. 16rg+15
+  const int wv = (t256 >> 6);     // wave within the head's 256 threads
+  const int hi_half = (t256 >> 5) & 1;
+
+  // issue the first pass's state loads before the conv so HBM latency overlaps it
+  float4 Sv[16];
+  {
+    const float* Sp = p.state + (((int64_t)bseq * Hv + kh * r + hl) * SD) * SD;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      Sv[i] = *reinterpret_cast<const float4*>(Sp + (rg * 16 + i) * SD + cg * 4);
+  }
+
+  // ---- conv window + SiLU for this group's channels; shift the conv state
+  const T* xb = (const T*)p.x + (int64_t)bseq * Cq;
+  T* cs = (T*)p.conv_state + (int64_t)bseq * 3 * Cq;
+  const int nch = 256 + r * SD;
+  for (int i = tid; i < nch; i += nthr) {
+    int c;
+    if (i < SD) c = kh * SD + i;                                   // q channel
+    else if (i < 2 * SD) c = Hk * SD + kh * SD + (i - SD);         // k channel
+    else c = 2 * Hk * SD + kh * r * SD + (i - 2 * SD);             // v channels
+    const float4 w4 = *reinterpret_cast<const float4*>(p.w + (int64_t)c * 4);
+    const T c0 = cs[c], c1 = cs[Cq + c], c2 = cs[2 * Cq + c], xc = xb[c];
+    const float f0 = io::ld(&c0, 0), f1 = io::ld(&c1, 0), f2 = io::ld(&c2, 0), fx = io::ld(&xc, 0);
+    float acc = w4.x * f0;
+    acc = fmaf(w4.y, f1, acc);
+    acc = fmaf(w4.z, f2, acc);
+    acc = fmaf(w4.w, fx, acc);
+    yv[i] = io::round(silu(acc));  // the conv output crosses the io boundary
+    cs[c] = c1;
+    cs[Cq + c] = c2;
+    cs[2 * Cq + c] = xc;
+  }
+  __syncthreads();
+
+  // ---- L2 norms of q and k, gates of the r value heads
+  if (tid < 64) {
+    const float q0 = yv[tid], q1 = yv[tid + 64], k0 = yv[SD + tid], k1 = yv[SD + tid + 64];
+    float sq = group_sum<64>(q0 * q0 + q1 * q1);
+    float sk = group_sum<64>(k0 * k0 + k1 * k1);
+    if (tid == 0) {
+      nsh[0] = p.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+      nsh[1] = p.use_l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+    }
+  } else if (tid >= 64 && tid < 64 + r) {
+    const int j = tid - 64;
+    const int h = kh * r + j;
+    float g, beta;
+    if (p.g_opt) {
+      g = p.g_opt[(int64_t)bseq * Hv + h];
+      beta = p.beta_opt[(int64_t)bseq * Hv + h];
+    } else {
+      const float av = io::ld((const T*)p.a, (int64_t)bseq * Hv + h);
+      const float bv = io::ld((const T*)p.b, (int64_t)bseq * Hv + h);
+      gate_pair(av, bv, p.A_log[h], p.dt_bias[h], g, beta);
+    }
+    gsh[j] = expf(g);
+    bsh[j] = beta;
+  }
+  __syncthreads();
+
+  const float rq = nsh[0], rk = nsh[1];
+
+  for (int h0 = 0; h0 < r; h0 += HPP) {
+    const int j = h0 + hl;        // value head inside the group
+    const int h = kh * r + j;
+    float* Sp = p.state + (((int64_t)bseq * Hv + h) * SD) * SD;
+    if (h0 > 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        Sv[i] = *reinterpret_cast<const float4*>(Sp + (rg * 16 + i) * SD + cg * 4);
+    }
+
+    // p = S^T k^ (undecayed)
+    float pk[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float kv = yv[SD + rg * 16 + i] * rk;
+      pk[0] = fmaf(Sv[i].x, kv, pk[0]);
+      pk[1] = fmaf(Sv[i].y, kv, pk[1]);
+      pk[2] = fmaf(Sv[i].z, kv, pk[2]);
+      pk[3] = fmaf(Sv[i].w, kv, pk[3]);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pk[c] += __shfl_xor(pk[c], 32, 64);
+    if (!hi_half) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) red1[(hl * 4 + wv) * SD + cg * 4 + c] = pk[c];
+    }
+    __syncthreads();
+    float u[4];
+    const float eg = gsh[j], beta = bsh[j];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) tot += red1[(hl * 4 + w4) * SD + cg * 4 + c];
+      const float vj = yv[2 * SD + j * SD + cg * 4 + c];
+      u[c] = beta * (vj - eg * tot);
+    }
+    // S <- e^g S + k^ u^T, and the output partials S^T q^
+    float po[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float kv = yv[SD + rg * 16 + i] * rk;
+      const float qv = yv[rg * 16 + i] * rq;
+      Sv[i].x = fmaf(eg, Sv[i].x, kv * u[0]);
+      Sv[i].y = fmaf(eg, Sv[i].y, kv * u[1]);
+      Sv[i].z = fmaf(eg, Sv[i].z, kv * u[2]);
+      Sv[i].w = fmaf(eg, Sv[i].w, kv * u[3]);
+      po[0] = fmaf(Sv[i].x, qv, po[0]);
+      po[1] = fmaf(Sv[i].y, qv, po[1]);
+      po[2] = fmaf(Sv[i].z, qv, po[2]);
+      po[3] = fmaf(Sv[i].w, qv, po[3]);
+      *reinterpret_cast<float4*>(Sp + (rg * 16 + i) * SD + cg * 4) = Sv[i];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) po[c] += __shfl_xor(po[c], 32, 64);
+    if (!hi_half) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) red2[(hl * 4 + wv) * SD + cg * 4 + c] = po[c];
+    }
+    __syncthreads();
+    if (t256 < 32) {
+      T* op = (T*)p.o + ((int64_t)bseq * Hv + h) * SD + cg * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) tot += red2[(hl * 4 + w4) * SD + cg * 4 + c];
+        io::st(op, c, p.scale * tot);
+      }
+    }
+    __syncthreads();  // red1/red2 are reused by the next pass
+  }
+}
+
+template <int IO, int HPP>
+static hipError_t step_launch(const StepArgs& a, hipStream_t s) {
+  const int r = a.Hv / a.Hk;
+  const size_t lds = sizeof(float) * (256 + r * SD + 2 * HPP * 4 * SD + 2 * r + 2);
+  hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP>), dim3((unsigned)(a.B * a.Hk)),
+                     dim3(256 * HPP), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int IO>
+static hipError_t step_impl(const StepArgs& a, hipStream_t s) {
+  const int r = a.Hv / a.Hk;
+  // two heads per pass at most: 512 threads leave 256 VGPRs per lane (no spills)
+  if (r % 2 == 0) return step_launch<IO, 2>(a, s);
+  return step_launch<IO, 1>(a, s);
+}
+
+hipError_t launch_recurrent_step(const StepArgs& a, int io, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  return io == IO_BF16 ? step_impl<IO_BF16>(a, s) : step_impl<IO_F32>(a, s);
+}
+
+}  // namespace gdn

@@ -1,0 +1,65 @@
+"""Thin helpers that allocate outputs with torch and chain the libgdn calls.
+
+prefill_layer:  conv1d+SiLU -> chunked delta rule -> z-gated RMSNorm
+decode_step:    recurrent step (conv + delta rule, in place) -> z-gated RMSNorm
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import gdn_chunk_prefill, gdn_conv1d_fwd, gdn_gated_rmsnorm, gdn_recurrent_step
+
+D = 128
+
+
+def qkv_views(y: torch.Tensor, Hk: int, Hv: int):
+    """Row views of the packed conv output: q | k | v, head-major inside each."""
+    return y[:, : Hk * D], y[:, Hk * D: 2 * Hk * D], y[:, 2 * Hk * D: 2 * Hk * D + Hv * D]
+
+
+def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens=None,
+                  conv_state_in=None, state_in=None, eps=1e-6, want_states=True, bufs=None,
+                  stream=None):
+    """x [N, Cq] io; z [N, Hv*128] io.  Returns a dict of device tensors."""
+    N, Cq = x.shape
+    Ns = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev, dt = x.device, x.dtype
+    bufs = {} if bufs is None else bufs
+    y = bufs.get("y_conv")
+    if y is None:
+        y = torch.empty_like(x)
+    cs_out = bufs.get("conv_state_out")
+    if cs_out is None and want_states:
+        cs_out = torch.empty((Ns, 3, Cq), dtype=dt, device=dev)
+    gdn_conv1d_fwd(x, conv_w, y, cu_seqlens, conv_state_in, cs_out, stream=stream)
+    q, k, v = qkv_views(y, Hk, Hv)
+    o = bufs.get("o")
+    if o is None:
+        o = torch.empty((N, Hv, D), dtype=dt, device=dev)
+    s_out = bufs.get("state_out")
+    if s_out is None and want_states:
+        s_out = torch.empty((Ns, Hv, D, D), dtype=torch.float32, device=dev)
+    gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens, state_in, s_out,
+                      stream=stream)
+    yn = bufs.get("y")
+    if yn is None:
+        yn = torch.empty_like(o)
+    gdn_gated_rmsnorm(o, z, norm_w, yn, eps, stream=stream)
+    return {"y_conv": y, "o": o, "y": yn, "conv_state_out": cs_out, "state_out": s_out}
+
+
+def decode_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w, Hk, Hv,
+                eps=1e-6, bufs=None, stream=None):
+    """One token per sequence.  conv_state [B,3,Cq] and state [B,Hv,128,128] update in place."""
+    B = x.shape[0]
+    bufs = {} if bufs is None else bufs
+    o = bufs.get("o")
+    if o is None:
+        o = torch.empty((B, Hv, D), dtype=x.dtype, device=x.device)
+    gdn_recurrent_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, o, Hk, Hv,
+                       stream=stream)
+    yn = bufs.get("y")
+    if yn is None:
+        yn = torch.empty_like(o)
+    gdn_gated_rmsnorm(o, z, norm_w, yn, eps, stream=stream)
+    return {"o": o, "y": yn}

@@ -116,10 +116,8 @@ def round_io(x32: np.ndarray, io: str) -> np.ndarray:
         return x32
     if io != "bf16":
         raise ValueError(io)
-    u = x32.view(np.uint32).astype(np.uint64)
-    # round-to-nearest-even on the upper 16 bits (inputs here are finite)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32)
+    import torch  # torch's fp32 -> bf16 cast rounds to nearest even
+    return torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy()
 
 
 def _normal(rng, shape, scale=1.0, offset=0.0):

@@ -1,0 +1,71 @@
+"""Shared helpers for the GPU parity tests: upload seeded inputs, compare to the oracle.
+
+Tolerances (stated once, used everywhere):
+* fp32 io: max |delta| <= 2e-3 on the core output o and the norm output y.
+* bf16 io: max_i (|delta_i| - 2^-8 max(|ref_i|, |gpu_i|))_+ <= 3e-2 * RMS(ref).  The
+  2^-8 term is the bf16 store itself (half an ulp is at most 2^-8 |x|), which the
+  fp64 oracle does not have; without it no bf16-output implementation passes.
+* final recurrent state: per sequence ||dS||_F / ||S_ref||_F <= 1e-3.
+* conv state: bit-exact (it is a copy of input rows).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+F32_ABS_TOL = 2e-3
+BF16_RMS_TOL = 3e-2
+STATE_REL_TOL = 1e-3
+BF16_HALF_ULP = 2.0 ** -8
+
+
+def to_dev(arr, io: str):
+    if arr is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    if io == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda()
+
+
+def f32_dev(arr):
+    return None if arr is None else torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def host(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def out_error(gpu, ref, io):
+    """Return (gated error, bound) for an io-dtype output."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), "non-finite GPU output"
+    d = np.abs(gpu - ref)
+    if io == "f32":
+        return float(d.max(initial=0.0)), F32_ABS_TOL
+    slack = BF16_HALF_ULP * np.maximum(np.abs(ref), np.abs(gpu))
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    return float(np.maximum(d - slack, 0.0).max(initial=0.0)), BF16_RMS_TOL * rms
+
+
+def assert_out(gpu, ref, io, what=""):
+    err, bound = out_error(gpu, ref, io)
+    assert err <= bound, f"{what}: error {err:.3e} > bound {bound:.3e} ({io})"
+    return err, bound
+
+
+def assert_state(gpu, ref, what=""):
+    """gpu, ref: [..., dk, dv] per (sequence, head); relative Frobenius per leading index 0."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(gpu)), "non-finite GPU state"
+    worst = 0.0
+    for s in range(ref.shape[0]):
+        den = np.linalg.norm(ref[s])
+        num = np.linalg.norm(gpu[s] - ref[s])
+        rel = num / den if den > 0 else num
+        worst = max(worst, rel)
+    assert worst <= STATE_REL_TOL, f"{what}: state rel err {worst:.3e} > {STATE_REL_TOL}"
+    return worst

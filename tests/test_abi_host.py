@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports every
+function include/gdn.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+
+import pytest
+
+from hybrid_linear_attention_causal_amd import _lib
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libgdn.so not built (run __graft_entry__.build())")
+
+EXPECTED = {"gdn_last_error", "gdn_version", "gdn_conv1d_fwd", "gdn_chunk_prefill_workspace_size",
+            "gdn_chunk_prefill", "gdn_recurrent_step", "gdn_gated_rmsnorm"}
+
+
+def test_header_declares_the_calls():
+    assert set(_lib.declared_symbols()) == EXPECTED
+
+
+def test_library_exports_every_declared_symbol():
+    handle = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _lib.declared_symbols():
+        assert hasattr(handle, name), name
+    assert _lib.version() == "0.1.0"
+
+
+def test_no_unexpected_exports():
+    # dynamic symbol table: the C ABI plus nothing named gdn_* that the header omits
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    assert {n for n in names if n.startswith("gdn_")} == EXPECTED
+
+
+L = None
+
+
+def _L():
+    global L
+    if L is None:
+        L = _lib.lib()
+    return L
+
+
+def _msg():
+    return _L().gdn_last_error().decode()
+
+
+P = ctypes.c_void_p(16)   # a non-null, aligned dummy address: never dereferenced on these paths
+
+
+def test_conv_rejects():
+    L = _L()
+    assert L.gdn_conv1d_fwd(P, P, P, None, 1, 10, 8, 3, None, None, 1, None) == _lib.GDN_ERR_UNSUPPORTED
+    assert "width" in _msg()
+    assert L.gdn_conv1d_fwd(None, P, P, None, 1, 10, 8, 4, None, None, 1, None) == _lib.GDN_ERR_INVALID_ARG
+    assert L.gdn_conv1d_fwd(P, P, P, None, 1, 10, 12, 4, None, None, 1, None) == _lib.GDN_ERR_INVALID_ARG
+    assert L.gdn_conv1d_fwd(P, P, P, None, 2, 10, 8, 4, None, None, 1, None) == _lib.GDN_ERR_INVALID_ARG
+    assert "cu_seqlens" in _msg()
+    assert L.gdn_conv1d_fwd(P, P, P, None, 1, -1, 8, 4, None, None, 1, None) == _lib.GDN_ERR_INVALID_ARG
+    assert L.gdn_conv1d_fwd(P, P, P, None, 1, 10, 8, 4, None, None, 7, None) == _lib.GDN_ERR_INVALID_ARG
+    assert L.gdn_conv1d_fwd(P, P, ctypes.c_void_p(18), None, 1, 10, 8, 4, None, None, 1, None) == _lib.GDN_ERR_INVALID_ARG
+    assert "aligned" in _msg()
+    assert L.gdn_conv1d_fwd(P, P, P, None, 1, 10, 8, 4, None, None, 1, None) == _lib.GDN_ERR_INVALID_ARG
+    assert "alias" in _msg()
+
+
+def _prefill(**kw):
+    args = dict(q=P, k=P, v=P, sq=4096, sk=4096, sv=4096, a=P, b=P, A_log=P, dt_bias=P, g=None,
+                beta=None, s_in=None, s_out=None, o=P, cu=None, Ns=1, N=64, Hk=16, Hv=32, dk=128,
+                dv=128, scale=0.0, l2=1, ws=None, ws_bytes=0, io=1)
+    args.update(kw)
+    return _L().gdn_chunk_prefill(*args.values(), None)
+
+
+def test_prefill_rejects():
+    assert _prefill(dk=64) == _lib.GDN_ERR_UNSUPPORTED
+    assert _prefill(Hv=24) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(Hk=0) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(Ns=3) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(sq=100) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(sv=4100) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(g=P) == _lib.GDN_ERR_INVALID_ARG
+    assert "both" in _msg()
+    assert _prefill(o=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(a=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(io=5) == _lib.GDN_ERR_INVALID_ARG
+    assert _lib.lib().gdn_chunk_prefill_workspace_size(4096, 1, 16, 32, 128) == 0
+
+
+def _step(**kw):
+    args = dict(x=P, w=P, cs=P, a=P, b=P, A_log=P, dt_bias=P, g=None, beta=None, st=P, o=P,
+                B=4, Hk=16, Hv=32, dk=128, dv=128, K=4, scale=0.0, l2=1, io=1)
+    args.update(kw)
+    return _L().gdn_recurrent_step(*args.values(), None)
+
+
+def test_step_rejects():
+    assert _step(K=2) == _lib.GDN_ERR_UNSUPPORTED
+    assert _step(dv=64) == _lib.GDN_ERR_UNSUPPORTED
+    assert _step(Hv=20) == _lib.GDN_ERR_INVALID_ARG
+    assert _step(B=-1) == _lib.GDN_ERR_INVALID_ARG
+    assert _step(st=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _step(beta=P) == _lib.GDN_ERR_INVALID_ARG
+    assert _step(st=ctypes.c_void_p(20)) == _lib.GDN_ERR_INVALID_ARG
+
+
+def test_norm_rejects():
+    L = _L()
+    assert L.gdn_gated_rmsnorm(P, P, P, P, 10, 64, 1e-6, 1, None) == _lib.GDN_ERR_UNSUPPORTED
+    assert L.gdn_gated_rmsnorm(P, P, P, P, -1, 128, 1e-6, 1, None) == _lib.GDN_ERR_INVALID_ARG
+    assert L.gdn_gated_rmsnorm(P, None, P, P, 10, 128, 1e-6, 1, None) == _lib.GDN_ERR_INVALID_ARG
+    assert L.gdn_gated_rmsnorm(P, P, P, P, 10, 128, -1.0, 1, None) == _lib.GDN_ERR_INVALID_ARG
