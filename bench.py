@@ -167,6 +167,8 @@ def main():
     P["o"] = torch.empty((N, hv, D), dtype=torch.bfloat16, device="cuda")
     P["s_out"] = torch.empty((1, hv, D, D), dtype=torch.float32, device="cuda")
     P["yn"] = torch.empty_like(P["o"])
+    P["ws"] = torch.empty(gdn.gdn_chunk_prefill_workspace_size(N, 1, hk, hv), dtype=torch.uint8,
+                          device="cuda")
     q, k, v = qkv_views(P["y"], hk, hv)
     zv = P["z"].view(N, hv, D)
 
@@ -186,7 +188,7 @@ def main():
         if ev:
             ev[1].record()
         gdn_chunk_prefill(q, k, v, P["a"], P["b"], P["A_log"], P["dt_bias"], P["o"], hk, hv,
-                          None, None, P["s_out"])
+                          None, None, P["s_out"], workspace=P["ws"])
         if ev:
             ev[2].record()
         gdn_gated_rmsnorm(P["o"], zv, P["norm_w"], P["yn"])

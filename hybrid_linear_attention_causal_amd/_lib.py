@@ -135,7 +135,10 @@ def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None,
     for t in (q, k, v):
         if t.stride(-1) != 1:
             raise ValueError("q, k, v rows must be contiguous")
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is None:
+        need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check("gdn_chunk_prefill", lib().gdn_chunk_prefill(
         _p(q), _p(k), _p(v), q.stride(0), k.stride(0), v.stride(0), _p(a), _p(b), _p(A_log),
         _p(dt_bias), _p(g_opt), _p(beta_opt), _p(state_in), _p(state_out), _p(o),

@@ -90,8 +90,9 @@ gdn_status_t gdn_conv1d_fwd(const void* x, const float* w, void* y, const int32_
 }
 
 size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d) {
-  (void)N; (void)Ns; (void)Hk; (void)Hv; (void)d;
-  return 0;
+  (void)Hk; (void)d;
+  if (N < 0 || Ns < 1 || Hv < 1) return 0;
+  return gdn::chunk_workspace_bytes(N, Ns, Hv);
 }
 
 gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int64_t stride_q,
@@ -102,7 +103,6 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
                                int Hv, int dk, int dv, float scale, int use_qk_l2norm,
                                void* workspace, size_t ws_bytes, gdn_dtype_t io, void* stream) {
   g_err[0] = 0;
-  (void)workspace;
   if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: unknown io dtype %d", (int)io);
   if (dk != 128 || dv != 128)
     return fail(GDN_ERR_UNSUPPORTED, "chunk_prefill: head widths %d/%d (only 128/128)", dk, dv);
@@ -129,15 +129,20 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
       return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: q, k, v, o must be 16-byte aligned");
   }
-  if (ws_bytes < gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk))
-    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: workspace too small");
+  const size_t need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+    return fail(GDN_ERR_INVALID_ARG,
+                "chunk_prefill: workspace must be a 256-byte aligned buffer of >= %zu bytes", need);
+  if ((N + 63) / 64 + Ns > 0x7fffffffLL)
+    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: too many chunks");
   if (scale <= 0.f) scale = 1.0f / sqrtf((float)dk);
   gdn_status_t st = check_device();
   if (st != GDN_OK) return st;
   gdn::ChunkArgs args{q, k, v, stride_q, stride_k, stride_v, a, b, A_log, dt_bias, g_opt,
                       beta_opt, state_in, state_out, o, cu_seqlens, Ns, N, Hk, Hv, scale,
                       use_qk_l2norm ? 1 : 0};
-  hipError_t e = gdn::launch_chunk_prefill(args, io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
+  hipError_t e = gdn::launch_chunk_prefill(args, workspace,
+                                           io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
                                            (hipStream_t)stream);
   return e == hipSuccess ? GDN_OK : hip_fail(e, "chunk_prefill launch");
 }

@@ -9,18 +9,22 @@
 // Chunk algebra (64 tokens, in-chunk cumulative log decay gamma_i, start state S):
 //   A_ij = beta_i e^{gamma_i - gamma_j} (k^_i . k^_j)  (j < i),  T = (I + A)^{-1}
 //   R    = V - diag(e^{gamma} / |k|) (K S)        (raw K; 1/|k| folds the L2 norm)
-//   U    = T diag(beta) R                          (= the WY/UT pseudo-values)
+//   U    = T diag(beta) R                          (the WY/UT pseudo-values)
 //   O    = scale (diag(e^{gamma} / |q|) (Q S) + P U),
 //          P_ij = e^{gamma_i - gamma_j} (q^_i . k^_j) (j <= i)
 //   S'   = e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U
 //
-// Work split: one 256-thread workgroup per (sequence, value head, 64-column
-// block of dv).  Each of its 4 waves keeps a 128 x 16 slice of the fp32 state
-// in registers for the whole sequence (MFMA accumulator layout) and walks the
-// chunks in order.  Per chunk the workgroup stages raw K and Q rows (bf16, or
-// bf16 hi/lo planes for fp32 io) in LDS, forms K K^T and Q K^T on MFMA,
-// inverts I + A with a blocked fp32 forward substitution, and then each wave
-// runs its column slice of the S-dependent products on MFMA.
+// Three launches:
+//   1. chunk map: chunk offsets of the packed sequences (one small workgroup).
+//   2. chunk prep: one workgroup per (chunk, value head), all in parallel.  Stages
+//      raw K and Q rows in LDS, forms K K^T and Q K^T on MFMA, inverts I + A by
+//      blocked fp32 forward substitution, and writes T' = T diag(beta) and P as
+//      bf16 hi/lo planes plus the per-token factors to the workspace.
+//   3. sweep: one workgroup per (sequence, value head, 64-column block of dv).
+//      Each of its 4 waves keeps a 128 x 16 slice of the fp32 state in MFMA
+//      accumulator registers for the whole sequence and walks the chunks in
+//      order; per chunk only the S-dependent products run (K S, T' R, Q S + P U,
+//      K^T U), on operands staged in LDS, while the next chunk's operands load.
 //
 // MFMA use: v_mfma_f32_16x16x32_bf16.  Operand fragments use a permuted
 // contraction index (lane group g, element e -> k = 4g + e for e < 4, 16 + 4g
@@ -29,10 +33,10 @@
 // any data movement.
 //
 // Precision (from an emulation of this exact scheme against the fp64
-// recurrence): raw bf16 K/Q/V enter MFMA exactly; every fp32 operand that
-// feeds the state or the output (S in K S and Q S, R and T in T R, P and U in
-// P U, U in the state update) is split into bf16 hi + lo, giving ~1e-5 of
-// the output RMS.
+// recurrence): raw bf16 K/Q/V enter MFMA exactly (fp32 io: split into bf16 hi
+// + lo); every fp32 operand that feeds the state or the output (S in K S and
+// Q S, R and T' in T' R, P and U in P U, U in the state update) is split into
+// bf16 hi + lo, which leaves ~1e-5 of the output RMS.
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
@@ -41,40 +45,48 @@ namespace gdn {
 constexpr int CH = 64;                 // chunk length
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int DVB = 64;                // dv columns per workgroup
+constexpr int DVB = 64;                // dv columns per sweep workgroup
 constexpr int NBLK = DV / DVB;
 constexpr int NTHR = 256;
 constexpr int KS_STRIDE = DK + 8;      // u16 per staged K/Q row
-constexpr int T_STRIDE = CH + 8;       // u16 per T'/P row
+constexpr int KT_STRIDE = CH + 8;      // u16 per staged K^T row
+constexpr int T_STRIDE = CH + 8;       // u16 per staged T'/P row
 constexpr int F_STRIDE = CH + 4;       // floats per A/T row
 
-template <int IO>
-struct ChunkSmem {
-  static constexpr int NLO = (IO == IO_F32) ? 1 : 0;
-  u16 kh[CH * KS_STRIDE];
-  u16 kl[NLO ? CH * KS_STRIDE : 2];
-  u16 qh[CH * KS_STRIDE];
-  u16 ql[NLO ? CH * KS_STRIDE : 2];
-  u16 th[CH * T_STRIDE];
-  u16 tl[CH * T_STRIDE];
-  u16 ph[CH * T_STRIDE];
-  u16 pl[CH * T_STRIDE];
-  float af[CH * F_STRIDE];
-  float tf[CH * F_STRIDE];
-  float msc[4][16 * 20];
-  float gam[CH];
-  float beta[CH];
-  float rnk[CH];
-  float rnq[CH];
-};
+// Workspace: chunk offsets (int32 [Ns + 1], padded to 256 bytes), then for every
+// (global chunk c, value head h) a record of T' hi, T' lo, P hi, P lo (row-major
+// 64 x 64 bf16 planes) and 4 x 64 fp32 factors: e^gamma/|k|, e^gamma/|q|,
+// e^{gamma_L - gamma}/|k|, and e^{gamma_L} (in slot 3 * 64).
+constexpr int64_t WS_PLANE = (int64_t)CH * CH;                       // u16 per plane
+constexpr int64_t WS_REC_BYTES = 4 * WS_PLANE * 2 + 4 * CH * 4;      // 33792
+constexpr int64_t WS_FAC_OFF = 4 * WS_PLANE * 2;                     // factors offset
+
+static int64_t ws_map_bytes(int Ns) { return (((int64_t)Ns + 1) * 4 + 255) / 256 * 256; }
+static int64_t ws_max_chunks(int64_t N, int Ns) { return (N + CH - 1) / CH + Ns; }
+
+size_t chunk_workspace_bytes(int64_t N, int Ns, int Hv) {
+  return (size_t)(ws_map_bytes(Ns) + ws_max_chunks(N, Ns) * Hv * WS_REC_BYTES);
+}
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair (hardware round-to-nearest-even)
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// hi = bf16(x), lo = bf16(x - hi) for a pair of values
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = cvt2(a, b);
+  lo = cvt2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
+
 __device__ __forceinline__ bf16x8 pack8(uint2 lo, uint2 hi) {
-  const uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
 // A-operand (or B-operand of a transposed matrix) from a row-major u16 tile:
@@ -84,36 +96,14 @@ __device__ __forceinline__ bf16x8 frag_rows(const u16* m, int stride, int row0, 
   return pack8(*reinterpret_cast<const uint2*>(p), *reinterpret_cast<const uint2*>(p + 16));
 }
 
-// A-operand of M^T from a row-major u16 tile: lane (g, r) gets M[k0 + perm(g, e)][col0 + r].
-__device__ __forceinline__ bf16x8 frag_cols(const u16* m, int stride, int k0, int col0, int lane) {
-  const int g = lane >> 4;
-  const u16* p = m + (k0 + 4 * g) * stride + col0 + (lane & 15);
-  uint32_t w[4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const u16* q = p + j * 16 * stride;
-    w[2 * j] = (uint32_t)q[0] | ((uint32_t)q[stride] << 16);
-    w[2 * j + 1] = (uint32_t)q[2 * stride] | ((uint32_t)q[3 * stride] << 16);
-  }
-  return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-}
-
 // B-operand from two stacked accumulator tiles (rows 0..15 and 16..31 of a
 // 32-row slab), split into bf16 hi and lo parts.
 __device__ __forceinline__ void frag_acc_split(f32x4 top, f32x4 bot, bf16x8& hi, bf16x8& lo) {
-  u16 h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = f2bf(top[e]);
-    l[e] = f2bf(top[e] - bf2f(h[e]));
-    h[e + 4] = f2bf(bot[e]);
-    l[e + 4] = f2bf(bot[e] - bf2f(h[e + 4]));
-  }
   uint4 vh, vl;
-  vh.x = h[0] | ((uint32_t)h[1] << 16); vh.y = h[2] | ((uint32_t)h[3] << 16);
-  vh.z = h[4] | ((uint32_t)h[5] << 16); vh.w = h[6] | ((uint32_t)h[7] << 16);
-  vl.x = l[0] | ((uint32_t)l[1] << 16); vl.y = l[2] | ((uint32_t)l[3] << 16);
-  vl.z = l[4] | ((uint32_t)l[5] << 16); vl.w = l[6] | ((uint32_t)l[7] << 16);
+  split2(top[0], top[1], vh.x, vl.x);
+  split2(top[2], top[3], vh.y, vl.y);
+  split2(bot[0], bot[1], vh.z, vl.z);
+  split2(bot[2], bot[3], vh.w, vl.w);
   hi = __builtin_bit_cast(bf16x8, vh);
   lo = __builtin_bit_cast(bf16x8, vl);
 }
@@ -123,21 +113,501 @@ __device__ __forceinline__ void tri_tile(int n, int& I, int& J) {
   I = (n >= 6) ? 3 : (n >= 3) ? 2 : (n >= 1) ? 1 : 0;
   J = n - I * (I + 1) / 2;
 }
-// strictly-upper tile list
-__device__ __forceinline__ void up_tile(int n, int& I, int& J) {
-  const int Is[6] = {0, 0, 0, 1, 1, 2};
-  const int Js[6] = {1, 2, 3, 2, 3, 3};
-  I = Is[n];
-  J = Js[n];
+
+// sequence bounds, clamped to [0, N] so inconsistent offsets cannot index outside
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int64_t N, int s, int64_t& b0,
+                                           int64_t& b1) {
+  b1 = cu ? min((int64_t)cu[s + 1], N) : N;
+  b0 = cu ? max((int64_t)0, min((int64_t)cu[s], b1)) : 0;
+}
+
+// Raw K/Q rows of one chunk for one thread: rows 4 rq .. 4 rq + 3, columns
+// 8 c8 .. 8 c8 + 7 (c8 = tid & 15 spans one 16-lane DPP row), as 16-byte words.
+template <int IO>
+struct RowBlock {
+  static constexpr int W = (IO == IO_F32) ? 2 : 1;  // uint4 words per 8 values
+  uint4 w[4][W];
+};
+
+template <int IO>
+__device__ __forceinline__ void load_rows(RowBlock<IO>& rb, const typename Io<IO>::T* base,
+                                          int64_t stride, int64_t t0, int L, int tid) {
+  const int c8 = tid & 15, rq = tid >> 4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 4 * rq + u;
+    const int64_t r = t0 + (row < L ? row : L - 1);   // in bounds; masked at use
+    const uint4* p = reinterpret_cast<const uint4*>(base + r * stride + c8 * 8);
+#pragma unroll
+    for (int w = 0; w < RowBlock<IO>::W; ++w) rb.w[u][w] = p[w];
+  }
+}
+
+// values of row u of a RowBlock as 8 floats (0 for rows past the chunk end)
+template <int IO>
+__device__ __forceinline__ void row_vals(const RowBlock<IO>& rb, int u, bool ok, float* v) {
+  if constexpr (IO == IO_F32) {
+    const float4 a = __builtin_bit_cast(float4, rb.w[u][0]);
+    const float4 b = __builtin_bit_cast(float4, rb.w[u][1]);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint32_t x[4] = {rb.w[u][0].x, rb.w[u][0].y, rb.w[u][0].z, rb.w[u][0].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(x[j] << 16);
+      v[2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = ok ? v[j] : 0.f;
+}
+
+// write 8 values of a staged row as bf16 (hi) and, for fp32 io, the lo residual
+template <int IO>
+__device__ __forceinline__ void put_row8(u16* hi, u16* lo, int off, const float* v, uint4& hw,
+                                         uint4& lw) {
+  if constexpr (IO == IO_F32) {
+    split2(v[0], v[1], hw.x, lw.x);
+    split2(v[2], v[3], hw.y, lw.y);
+    split2(v[4], v[5], hw.z, lw.z);
+    split2(v[6], v[7], hw.w, lw.w);
+    *reinterpret_cast<uint4*>(hi + off) = hw;
+    *reinterpret_cast<uint4*>(lo + off) = lw;
+  } else {
+    // bf16 inputs are exact bf16 values: repack without rounding
+    hw.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xFFFF0000u);
+    hw.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xFFFF0000u);
+    hw.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xFFFF0000u);
+    hw.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xFFFF0000u);
+    lw = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(hi + off) = hw;
+    (void)lo;
+  }
+}
+
+// ============================================================================ 1. chunk map
+// cmap[s] = number of 64-token chunks before sequence s; cmap[Ns] = total.
+__global__ void __launch_bounds__(256) chunk_map_kernel(const int32_t* cu, int Ns, int64_t N,
+                                                        int32_t* cmap) {
+  __shared__ int wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < Ns; base += 256) {
+    const int s = base + tid;
+    int n = 0;
+    if (s < Ns) {
+      int64_t b0, b1;
+      seq_bounds(cu, N, s, b0, b1);
+      n = (int)((b1 - b0 + CH - 1) / CH);
+    }
+    // inclusive scan inside the wave (exact in fp32 below 2^24 chunks)
+    const float incl = wave_prefix_sum((float)n);
+    if (lane == 63) wtot[wave] = (int)incl;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+    if (s < Ns) cmap[s] = before + (int)incl - n;
+    carry += wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    __syncthreads();
+  }
+  if (tid == 0) cmap[Ns] = carry;
+}
+
+// ============================================================================ 2. chunk prep
+template <int IO>
+struct PrepSmem {
+  static constexpr bool F32 = (IO == IO_F32);
+  u16 kh[CH * KS_STRIDE];                 // K rows (bf16 / hi part)
+  u16 kl[F32 ? CH * KS_STRIDE : 2];
+  u16 qh[CH * KS_STRIDE];
+  u16 ql[F32 ? CH * KS_STRIDE : 2];
+  float af[CH * F_STRIDE];                // strictly lower A (fp32)
+  float tf[CH * F_STRIDE];                // T (fp32); first holds the staged P planes
+  float msc[32 * 36];                     // block scratch of the solve
+  float gam[CH];                          // in-chunk cumulative log decay
+  float beta[CH];
+  float rnk[CH];                          // 1/|k_t| (1 without the L2 norm)
+  float rnq[CH];
+};
+
+template <int IO>
+__global__ void __launch_bounds__(NTHR, 2)
+chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __restrict__ recs) {
+  typedef Io<IO> io;
+  typedef typename io::T T;
+  constexpr bool F32 = (IO == IO_F32);
+  __shared__ PrepSmem<IO> sm;
+
+  const int c = blockIdx.x;               // global chunk
+  const int h = blockIdx.y;               // value head
+  const int Ns = p.Ns, Hv = p.Hv;
+  if (c >= cmap[Ns]) return;
+  int lo = 0, hi = Ns - 1;                // the sequence holding chunk c
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cmap[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo;
+  int64_t b0, b1;
+  seq_bounds(p.cu, p.N, s, b0, b1);
+  const int64_t t0 = b0 + (int64_t)(c - cmap[s]) * CH;
+  const int L = (int)min((int64_t)CH, b1 - t0);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int kh_ = h / (Hv / p.Hk);
+
+  // ---- stage K and Q rows, row norms (16 lanes of a DPP row share a token row)
+  {
+    RowBlock<IO> kb, qb;
+    load_rows<IO>(kb, (const T*)p.k + (int64_t)kh_ * DK, p.stride_k, t0, L, tid);
+    load_rows<IO>(qb, (const T*)p.q + (int64_t)kh_ * DK, p.stride_q, t0, L, tid);
+    float ga = 0.f, gb = 0.f;
+    if (tid < 64) {
+      const int64_t idx = (t0 + (lane < L ? lane : L - 1)) * Hv + h;
+      if (p.g_opt) {
+        ga = p.g_opt[idx];
+        gb = p.beta_opt[idx];
+      } else {
+        ga = io::ld((const T*)p.a, idx);
+        gb = io::ld((const T*)p.b, idx);
+      }
+    }
+    const int c8 = tid & 15, rq = tid >> 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = 4 * rq + u;
+      const bool ok = row < L;
+      float kv[8], qv[8];
+      row_vals<IO>(kb, u, ok, kv);
+      row_vals<IO>(qb, u, ok, qv);
+      uint4 hw, lw;
+      put_row8<IO>(sm.kh, sm.kl, row * KS_STRIDE + c8 * 8, kv, hw, lw);
+      put_row8<IO>(sm.qh, sm.ql, row * KS_STRIDE + c8 * 8, qv, hw, lw);
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sk = fmaf(kv[j], kv[j], sk);
+        sq = fmaf(qv[j], qv[j], sq);
+      }
+      sk = row16_sum(sk);
+      sq = row16_sum(sq);
+      if (c8 == 0) {
+        sm.rnk[row] = p.use_l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+        sm.rnq[row] = p.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+      }
+    }
+    if (wave == 0) {
+      float g = 0.f, beta = 0.f;
+      if (lane < L) {
+        if (p.g_opt) {
+          g = ga;
+          beta = gb;
+        } else {
+          gate_pair(ga, gb, p.A_log[h], p.dt_bias[h], g, beta);
+        }
+      }
+      g = wave_prefix_sum(g);       // in-chunk cumulative log decay (padding adds 0)
+      sm.gam[lane] = g;
+      sm.beta[lane] = beta;
+    }
+  }
+  __syncthreads();
+
+  uint8_t* rec = recs + ((int64_t)c * Hv + h) * WS_REC_BYTES;
+  // ---- per-token factors for the sweep
+  if (tid < 64) {
+    const float gl = sm.gam[CH - 1];
+    const float gt = sm.gam[tid];
+    const float eg = __expf(gt);
+    float* fac = reinterpret_cast<float*>(rec + WS_FAC_OFF);
+    fac[tid] = eg * sm.rnk[tid];
+    fac[CH + tid] = eg * sm.rnq[tid];
+    fac[2 * CH + tid] = __expf(gl - gt) * sm.rnk[tid];
+    fac[3 * CH + tid] = __expf(gl);
+  }
+
+  // ---- Gram tiles: 10 lower (I >= J) tile pairs A (from K K^T) and P (from Q K^T)
+  // share the K_J fragments; P's strictly-upper tiles are zero.  P is staged as
+  // two row-major 64 x 64 bf16 planes in the (not yet used) T buffer.
+  u16* pst = reinterpret_cast<u16*>(sm.tf);
+  for (int n = wave; n < 16; n += 4) {
+    int I, J;
+    if (n < 10) {
+      tri_tile(n, I, J);
+      bf16x8 bk[4], ak[4], aq[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        bk[m] = frag_rows(sm.kh, KS_STRIDE, 16 * J, 32 * m, lane);
+        ak[m] = frag_rows(sm.kh, KS_STRIDE, 16 * I, 32 * m, lane);
+        aq[m] = frag_rows(sm.qh, KS_STRIDE, 16 * I, 32 * m, lane);
+      }
+      f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        gk = mma(ak[m], bk[m], gk);
+        gq = mma(aq[m], bk[m], gq);
+      }
+      if constexpr (F32) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x8 bl = frag_rows(sm.kl, KS_STRIDE, 16 * J, 32 * m, lane);
+          gk = mma(frag_rows(sm.kl, KS_STRIDE, 16 * I, 32 * m, lane), bk[m], gk);
+          gk = mma(ak[m], bl, gk);
+          gq = mma(frag_rows(sm.ql, KS_STRIDE, 16 * I, 32 * m, lane), bk[m], gq);
+          gq = mma(aq[m], bl, gq);
+        }
+      }
+      const int j = 16 * J + c16;
+      const int i0 = 16 * I + 4 * g4;
+      const float gj = sm.gam[j], rkj = sm.rnk[j];
+      const float4 gi4 = *reinterpret_cast<const float4*>(&sm.gam[i0]);
+      const float4 bi4 = *reinterpret_cast<const float4*>(&sm.beta[i0]);
+      const float4 ki4 = *reinterpret_cast<const float4*>(&sm.rnk[i0]);
+      const float4 qi4 = *reinterpret_cast<const float4*>(&sm.rnq[i0]);
+      const float gi[4] = {gi4.x, gi4.y, gi4.z, gi4.w};
+      const float bi[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
+      const float ki[4] = {ki4.x, ki4.y, ki4.z, ki4.w};
+      const float qi[4] = {qi4.x, qi4.y, qi4.z, qi4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        const float d = (i >= j) ? __expf(gi[e] - gj) * rkj : 0.f;   // exponent <= 0
+        sm.af[i * F_STRIDE + j] = (i > j) ? bi[e] * ki[e] * d * gk[e] : 0.f;
+        uint32_t ph, pl;
+        split2(qi[e] * d * gq[e], 0.f, ph, pl);
+        pst[i * CH + j] = (u16)ph;
+        pst[WS_PLANE + i * CH + j] = (u16)pl;
+      }
+    } else {
+      const int Is[6] = {0, 0, 0, 1, 1, 2};
+      const int Js[6] = {1, 2, 3, 2, 3, 3};
+      I = Is[n - 10];
+      J = Js[n - 10];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * I + 4 * g4 + e, j = 16 * J + c16;
+        pst[i * CH + j] = 0;
+        pst[WS_PLANE + i * CH + j] = 0;
+      }
+    }
+  }
+  __syncthreads();
+  // P planes to the workspace (16 KB: four 16-byte words per thread)
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(pst);
+    uint4* dst = reinterpret_cast<uint4*>(rec + 2 * WS_PLANE * 2);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) dst[tid + NTHR * it] = src[tid + NTHR * it];
+  }
+  __syncthreads();   // the T buffer is reused below
+
+  // ---- T = (I + A)^{-1}, blocked: 16 x 16 diagonal blocks by forward substitution
+  // (one column per lane); then T_10, T_32 = -T_ii A_ij T_jj; then the lower
+  // 32 x 32 block T[32:64, 0:32] = -T[32:64, 32:64] A[32:64, 0:32] T[0:32, 0:32]
+  if (g4 == 0) {
+    const int b = wave;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float* arow = &sm.af[(16 * b + i) * F_STRIDE + 16 * b];
+      float a[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(arow + 4 * q4);
+        a[4 * q4] = t4.x; a[4 * q4 + 1] = t4.y; a[4 * q4 + 2] = t4.z; a[4 * q4 + 3] = t4.w;
+      }
+      float sacc = (i == c16) ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) sacc = fmaf(-a[j], x[j], sacc);
+      x[i] = sacc;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.tf[(16 * b + i) * F_STRIDE + 16 * b + c16] = x[i];
+  } else if (g4 == 1 && (wave & 1) == 0) {
+    // the strictly-upper blocks T_01 and T_23 enter the 32 x 32 products below: zero
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.tf[(16 * wave + i) * F_STRIDE + 16 * wave + 16 + c16] = 0.f;
+  }
+  __syncthreads();
+  {
+    // blocks (1,0) (waves 0,1) and (3,2) (waves 2,3): 2 outputs per lane
+    const int bb = wave >> 1;
+    const int I = 2 * bb + 1, J = 2 * bb;
+    const int li = ((wave & 1) << 6) | lane;   // 0..127
+    const int ri = li >> 3;                    // row 0..15
+    const int cj = 2 * (li & 7);               // columns cj, cj+1
+    float* msc = sm.msc + bb * (16 * 20);
+    {
+      const float* arow = &sm.af[(16 * I + ri) * F_STRIDE + 16 * J];
+      float a[16];
+      float2 tv[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(arow + 4 * q4);
+        a[4 * q4] = t4.x; a[4 * q4 + 1] = t4.y; a[4 * q4 + 2] = t4.z; a[4 * q4 + 3] = t4.w;
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        tv[k] = *reinterpret_cast<const float2*>(&sm.tf[(16 * J + k) * F_STRIDE + 16 * J + cj]);
+      float2 m2 = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        m2.x = fmaf(a[k], tv[k].x, m2.x);
+        m2.y = fmaf(a[k], tv[k].y, m2.y);
+      }
+      *reinterpret_cast<float2*>(&msc[ri * 20 + cj]) = m2;
+    }
+    __syncthreads();
+    {
+      const float* trow = &sm.tf[(16 * I + ri) * F_STRIDE + 16 * I];
+      float tr[16];
+      float2 mv[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(trow + 4 * q4);
+        tr[4 * q4] = t4.x; tr[4 * q4 + 1] = t4.y; tr[4 * q4 + 2] = t4.z; tr[4 * q4 + 3] = t4.w;
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) mv[k] = *reinterpret_cast<const float2*>(&msc[k * 20 + cj]);
+      float2 t2 = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        t2.x = fmaf(-tr[k], mv[k].x, t2.x);
+        t2.y = fmaf(-tr[k], mv[k].y, t2.y);
+      }
+      *reinterpret_cast<float2*>(&sm.tf[(16 * I + ri) * F_STRIDE + 16 * J + cj]) = t2;
+    }
+    __syncthreads();
+  }
+  {
+    const int ri = tid >> 3;                   // row 0..31 of the block
+    const int cj = 4 * (tid & 7);              // columns cj .. cj+3
+    {
+      const float* arow = &sm.af[(32 + ri) * F_STRIDE];
+      float a[32];
+#pragma unroll
+      for (int q4 = 0; q4 < 8; ++q4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(arow + 4 * q4);
+        a[4 * q4] = t4.x; a[4 * q4 + 1] = t4.y; a[4 * q4 + 2] = t4.z; a[4 * q4 + 3] = t4.w;
+      }
+      float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const float4 tv = *reinterpret_cast<const float4*>(&sm.tf[k * F_STRIDE + cj]);
+        m4.x = fmaf(a[k], tv.x, m4.x);
+        m4.y = fmaf(a[k], tv.y, m4.y);
+        m4.z = fmaf(a[k], tv.z, m4.z);
+        m4.w = fmaf(a[k], tv.w, m4.w);
+      }
+      *reinterpret_cast<float4*>(&sm.msc[ri * 36 + cj]) = m4;
+    }
+    __syncthreads();
+    {
+      const float* trow = &sm.tf[(32 + ri) * F_STRIDE + 32];
+      float tr[32];
+#pragma unroll
+      for (int q4 = 0; q4 < 8; ++q4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(trow + 4 * q4);
+        tr[4 * q4] = t4.x; tr[4 * q4 + 1] = t4.y; tr[4 * q4 + 2] = t4.z; tr[4 * q4 + 3] = t4.w;
+      }
+      float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const float4 mv = *reinterpret_cast<const float4*>(&sm.msc[k * 36 + cj]);
+        t4.x = fmaf(-tr[k], mv.x, t4.x);
+        t4.y = fmaf(-tr[k], mv.y, t4.y);
+        t4.z = fmaf(-tr[k], mv.z, t4.z);
+        t4.w = fmaf(-tr[k], mv.w, t4.w);
+      }
+      *reinterpret_cast<float4*>(&sm.tf[(32 + ri) * F_STRIDE + cj]) = t4;
+    }
+    __syncthreads();
+  }
+  // ---- T' = T diag(beta), lower triangle, as bf16 hi/lo planes straight to the
+  // workspace (4 consecutive columns per thread per step: 8-byte stores)
+  {
+    u16* tph = reinterpret_cast<u16*>(rec);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = tid + NTHR * it;          // row i, column group j0
+      const int i = idx >> 4, j0 = (idx & 15) * 4;
+      const float4 t4 = *reinterpret_cast<const float4*>(&sm.tf[i * F_STRIDE + j0]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[j0]);
+      const float v0 = (j0 <= i) ? t4.x * b4.x : 0.f;
+      const float v1 = (j0 + 1 <= i) ? t4.y * b4.y : 0.f;
+      const float v2 = (j0 + 2 <= i) ? t4.z * b4.z : 0.f;
+      const float v3 = (j0 + 3 <= i) ? t4.w * b4.w : 0.f;
+      uint32_t h0, l0, h1, l1;
+      split2(v0, v1, h0, l0);
+      split2(v2, v3, h1, l1);
+      *reinterpret_cast<uint2*>(tph + i * CH + j0) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(tph + WS_PLANE + i * CH + j0) = make_uint2(l0, l1);
+    }
+  }
+}
+
+// ============================================================================ 3. sweep
+template <int IO>
+struct SweepSmem {
+  static constexpr bool F32 = (IO == IO_F32);
+  u16 kh[CH * KS_STRIDE];                 // K rows (bf16 / hi part)
+  u16 kl[F32 ? CH * KS_STRIDE : 2];
+  u16 qh[CH * KS_STRIDE];
+  u16 ql[F32 ? CH * KS_STRIDE : 2];
+  u16 kth[DK * KT_STRIDE];                // K^T
+  u16 ktl[F32 ? DK * KT_STRIDE : 2];
+  u16 th[CH * T_STRIDE];                  // T' hi/lo
+  u16 tl[CH * T_STRIDE];
+  u16 ph[CH * T_STRIDE];                  // P hi/lo
+  u16 pl[CH * T_STRIDE];
+  float fac[4 * CH];                      // e^g/|k|, e^g/|q|, e^{gL-g}/|k|, e^{gL}
+};
+
+// Registers holding one chunk's operands between their global loads and the LDS commit.
+template <int IO>
+struct SweepPrefetch {
+  RowBlock<IO> k, q;
+  uint4 tp[4];                            // T' hi/lo planes (16 KB per workgroup)
+  uint4 pp[4];                            // P hi/lo planes
+  uint4 fc;                               // 16 bytes of the factor block (tid < 64)
+  float v[4][4];                          // V slice in accumulator layout
+};
+
+template <int IO>
+__device__ __forceinline__ void sweep_prefetch(const ChunkArgs& p, SweepPrefetch<IO>& pf,
+                                               const uint8_t* rec, const typename Io<IO>::T* qg,
+                                               const typename Io<IO>::T* kg,
+                                               const typename Io<IO>::T* vg, int64_t t0, int L,
+                                               int tid) {
+  typedef Io<IO> io;
+  load_rows<IO>(pf.k, kg, p.stride_k, t0, L, tid);
+  load_rows<IO>(pf.q, qg, p.stride_q, t0, L, tid);
+  const uint4* tsrc = reinterpret_cast<const uint4*>(rec);
+  const uint4* psrc = reinterpret_cast<const uint4*>(rec + 2 * WS_PLANE * 2);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    pf.tp[it] = tsrc[tid + NTHR * it];
+    pf.pp[it] = psrc[tid + NTHR * it];
+  }
+  if (tid < 64) pf.fc = reinterpret_cast<const uint4*>(rec + WS_FAC_OFF)[tid];
+  const int g4 = (tid & 63) >> 4;
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * I + 4 * g4 + e;
+      pf.v[I][e] = io::ld(vg, (t0 + (t < L ? t : L - 1)) * p.stride_v);
+    }
 }
 
 template <int IO>
 __global__ void __launch_bounds__(NTHR)
-chunk_prefill_kernel(ChunkArgs p) {
+chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
   typedef Io<IO> io;
   typedef typename io::T T;
   constexpr bool F32 = (IO == IO_F32);
-  __shared__ ChunkSmem<IO> sm;
+  __shared__ SweepSmem<IO> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,9 +622,9 @@ chunk_prefill_kernel(ChunkArgs p) {
   const int h = bid % Hv;
   const int s = bid / Hv;
   const int kh = h / (Hv / p.Hk);
-  // sequence bounds, clamped to [0, N] so inconsistent offsets cannot index outside q/k/v/o
-  const int64_t b1 = p.cu ? min((int64_t)p.cu[s + 1], p.N) : p.N;
-  const int64_t b0 = p.cu ? max((int64_t)0, min((int64_t)p.cu[s], b1)) : 0;
+  int64_t b0, b1;
+  seq_bounds(p.cu, p.N, s, b0, b1);
+  const int c0 = cmap[s];
   const int col = blk * DVB + wave * 16 + c16;      // this lane's dv column
 
   const T* qg = (const T*)p.q + (int64_t)kh * DK;
@@ -165,288 +635,109 @@ chunk_prefill_kernel(ChunkArgs p) {
 
   // ---- recurrent state slice: S[i] holds rows 16 i + 4 g4 + e of column col
   f32x4 S[8];
-  {
-    const float* sp = p.state_in ? p.state_in + ((int64_t)s * Hv + h) * DK * DV + col : nullptr;
+  if (p.state_in) {
+    const float* sp = p.state_in + ((int64_t)s * Hv + h) * DK * DV + col;
+    float tmp[32];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int k = 0; k < 32; ++k) tmp[k] = sp[(16 * (k >> 2) + 4 * g4 + (k & 3)) * DV];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[i][e] = sp ? sp[(16 * i + 4 * g4 + e) * DV] : 0.f;
+    for (int k = 0; k < 32; ++k) S[k >> 2][k & 3] = tmp[k];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  float A_log = 0.f, dt_bias = 0.f;
-  if (!p.g_opt) {
-    A_log = p.A_log[h];
-    dt_bias = p.dt_bias[h];
-  }
+  SweepPrefetch<IO> pf;
+  if (b0 < b1)
+    sweep_prefetch<IO>(p, pf, recs + ((int64_t)c0 * Hv + h) * WS_REC_BYTES, qg, kg, vg, b0,
+                       (int)min((int64_t)CH, b1 - b0), tid);
 
-  for (int64_t t0 = b0; t0 < b1; t0 += CH) {
+  int c = c0;
+  for (int64_t t0 = b0; t0 < b1; t0 += CH, ++c) {
     const int L = (b1 - t0) < CH ? (int)(b1 - t0) : CH;
 
-    // ---------------- (1) loads: V slice into registers, K/Q rows into LDS, gates
+    // ---------------- commit the prefetched operands to LDS
+    {
+      const int c8 = tid & 15, rq = tid >> 4;
+      uint32_t kt_h[8][2], kt_l[8][2];          // K^T words: 4 consecutive rows per column
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = 4 * rq + u;
+        const bool ok = row < L;
+        float kv[8], qv[8];
+        row_vals<IO>(pf.k, u, ok, kv);
+        row_vals<IO>(pf.q, u, ok, qv);
+        uint4 hw, lw, qhw, qlw;
+        put_row8<IO>(sm.kh, sm.kl, row * KS_STRIDE + c8 * 8, kv, hw, lw);
+        put_row8<IO>(sm.qh, sm.ql, row * KS_STRIDE + c8 * 8, qv, qhw, qlw);
+        const uint32_t hs[4] = {hw.x, hw.y, hw.z, hw.w};
+        const uint32_t ls[4] = {lw.x, lw.y, lw.z, lw.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t hv = (j & 1) ? (hs[j >> 1] >> 16) : (hs[j >> 1] & 0xFFFFu);
+          const uint32_t lv = (j & 1) ? (ls[j >> 1] >> 16) : (ls[j >> 1] & 0xFFFFu);
+          if (u & 1) {
+            kt_h[j][u >> 1] |= hv << 16;
+            kt_l[j][u >> 1] |= lv << 16;
+          } else {
+            kt_h[j][u >> 1] = hv;
+            kt_l[j][u >> 1] = lv;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int off = (c8 * 8 + j) * KT_STRIDE + 4 * rq;
+        *reinterpret_cast<uint2*>(&sm.kth[off]) = make_uint2(kt_h[j][0], kt_h[j][1]);
+        if constexpr (F32) *reinterpret_cast<uint2*>(&sm.ktl[off]) = make_uint2(kt_l[j][0], kt_l[j][1]);
+      }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int idx = tid + NTHR * it;        // 16-byte word of the hi|lo planes
+        const int plane = idx >> 9, w = idx & 511;
+        const int off = (w >> 3) * T_STRIDE + (w & 7) * 8;
+        *reinterpret_cast<uint4*>((plane ? sm.tl : sm.th) + off) = pf.tp[it];
+        *reinterpret_cast<uint4*>((plane ? sm.pl : sm.ph) + off) = pf.pp[it];
+      }
+      if (tid < 64) *reinterpret_cast<uint4*>(&sm.fac[4 * tid]) = pf.fc;
+    }
     float vr[4][4];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * I + 4 * g4 + e;
-        vr[I][e] = (t < L) ? io::ld(vg, (t0 + t) * p.stride_v) : 0.f;
-      }
-
-    if constexpr (!F32) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = (tid >> 4) + 16 * j;
-        const int c8 = tid & 15;
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-        if (row < L) {
-          kv = *reinterpret_cast<const uint4*>(kg + (t0 + row) * p.stride_k + c8 * 8);
-          qv = *reinterpret_cast<const uint4*>(qg + (t0 + row) * p.stride_q + c8 * 8);
-        }
-        *reinterpret_cast<uint4*>(&sm.kh[row * KS_STRIDE + c8 * 8]) = kv;
-        *reinterpret_cast<uint4*>(&sm.qh[row * KS_STRIDE + c8 * 8]) = qv;
-        float sk = 0.f, sq = 0.f;
-        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float k0 = __uint_as_float(kw[u] << 16), k1 = __uint_as_float(kw[u] & 0xFFFF0000u);
-          const float q0 = __uint_as_float(qw[u] << 16), q1 = __uint_as_float(qw[u] & 0xFFFF0000u);
-          sk = fmaf(k0, k0, fmaf(k1, k1, sk));
-          sq = fmaf(q0, q0, fmaf(q1, q1, sq));
-        }
-        sk = group_sum<16>(sk);
-        sq = group_sum<16>(sq);
-        if (c8 == 0) {
-          sm.rnk[row] = p.use_l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
-          sm.rnq[row] = p.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = (tid >> 5) + 8 * j;
-        const int c4 = tid & 31;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-        if (row < L) {
-          kv = *reinterpret_cast<const float4*>((const float*)kg + (t0 + row) * p.stride_k + c4 * 4);
-          qv = *reinterpret_cast<const float4*>((const float*)qg + (t0 + row) * p.stride_q + c4 * 4);
-        }
-        const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
-        const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
-        u16 khi[4], klo[4], qhi[4], qlo[4];
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          khi[u] = f2bf(kk[u]);
-          klo[u] = f2bf(kk[u] - bf2f(khi[u]));
-          qhi[u] = f2bf(qq[u]);
-          qlo[u] = f2bf(qq[u] - bf2f(qhi[u]));
-          sk = fmaf(kk[u], kk[u], sk);
-          sq = fmaf(qq[u], qq[u], sq);
-        }
-        const int off = row * KS_STRIDE + c4 * 4;
-        *reinterpret_cast<uint2*>(&sm.kh[off]) =
-            make_uint2(khi[0] | ((uint32_t)khi[1] << 16), khi[2] | ((uint32_t)khi[3] << 16));
-        *reinterpret_cast<uint2*>(&sm.kl[off]) =
-            make_uint2(klo[0] | ((uint32_t)klo[1] << 16), klo[2] | ((uint32_t)klo[3] << 16));
-        *reinterpret_cast<uint2*>(&sm.qh[off]) =
-            make_uint2(qhi[0] | ((uint32_t)qhi[1] << 16), qhi[2] | ((uint32_t)qhi[3] << 16));
-        *reinterpret_cast<uint2*>(&sm.ql[off]) =
-            make_uint2(qlo[0] | ((uint32_t)qlo[1] << 16), qlo[2] | ((uint32_t)qlo[3] << 16));
-        sk = group_sum<32>(sk);
-        sq = group_sum<32>(sq);
-        if (c4 == 0) {
-          sm.rnk[row] = p.use_l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
-          sm.rnq[row] = p.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-        }
-      }
-    }
-
-    if (wave == 0) {
-      const int t = lane;
-      float g = 0.f, beta = 0.f;
-      if (t < L) {
-        const int64_t idx = (t0 + t) * Hv + h;
-        if (p.g_opt) {
-          g = p.g_opt[idx];
-          beta = p.beta_opt[idx];
-        } else {
-          gate_pair(io::ld((const T*)p.a, idx), io::ld((const T*)p.b, idx), A_log, dt_bias, g,
-                    beta);
-        }
-      }
-      // inclusive prefix sum of g over the chunk (padding tokens add 0)
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float up = __shfl_up(g, off, 64);
-        if (lane >= off) g += up;
-      }
-      sm.gam[t] = g;
-      sm.beta[t] = beta;
-    }
+      for (int e = 0; e < 4; ++e) vr[I][e] = (16 * I + 4 * g4 + e < L) ? pf.v[I][e] : 0.f;
     __syncthreads();
 
-    // ---------------- (2) Gram tiles: A (strictly lower, fp32) and P (lower, hi/lo)
-    for (int n = wave; n < 26; n += 4) {
-      int I, J;
-      if (n < 20) {
-        tri_tile(n < 10 ? n : n - 10, I, J);
-        const bool isK = n < 10;
-        const u16* ah = isK ? sm.kh : sm.qh;
-        const u16* al = isK ? sm.kl : sm.ql;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const bf16x8 a = frag_rows(ah, KS_STRIDE, 16 * I, 32 * m, lane);
-          const bf16x8 b = frag_rows(sm.kh, KS_STRIDE, 16 * J, 32 * m, lane);
-          acc = mma(a, b, acc);
-          if constexpr (F32) {
-            acc = mma(frag_rows(al, KS_STRIDE, 16 * I, 32 * m, lane), b, acc);
-            acc = mma(a, frag_rows(sm.kl, KS_STRIDE, 16 * J, 32 * m, lane), acc);
-          }
-        }
-        const int j = 16 * J + c16;
-        const float gj = sm.gam[j], rkj = sm.rnk[j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * I + 4 * g4 + e;
-          if (isK) {
-            float v = 0.f;
-            if (i > j) v = sm.beta[i] * expf(sm.gam[i] - gj) * sm.rnk[i] * rkj * acc[e];
-            sm.af[i * F_STRIDE + j] = v;
-          } else {
-            float v = 0.f;
-            if (i >= j) v = expf(sm.gam[i] - gj) * sm.rnq[i] * rkj * acc[e];
-            const u16 hv = f2bf(v);
-            sm.ph[i * T_STRIDE + j] = hv;
-            sm.pl[i * T_STRIDE + j] = f2bf(v - bf2f(hv));
-          }
-        }
-      } else {
-        up_tile(n - 20, I, J);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * I + 4 * g4 + e, j = 16 * J + c16;
-          sm.ph[i * T_STRIDE + j] = 0;
-          sm.pl[i * T_STRIDE + j] = 0;
-        }
-      }
-    }
-    __syncthreads();
+    // the next chunk's operands load while this chunk's products run
+    if (t0 + CH < b1)
+      sweep_prefetch<IO>(p, pf, recs + ((int64_t)(c + 1) * Hv + h) * WS_REC_BYTES, qg, kg, vg,
+                         t0 + CH, (int)min((int64_t)CH, b1 - t0 - CH), tid);
 
-    // ---------------- (3) T = (I + A)^{-1}: 16 x 16 diagonal blocks by forward
-    // substitution (one column per lane), then off-diagonal blocks by levels:
-    //   T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
-    if (g4 == 0) {
-      const int b = wave;
-      float x[16];
+    // ---------------- S-dependent products for this wave's 16 columns
+    bf16x8 sh[4], sl[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float sacc = (i == c16) ? 1.f : 0.f;
-        const float* arow = &sm.af[(16 * b + i) * F_STRIDE + 16 * b];
-#pragma unroll
-        for (int j = 0; j < i; ++j) sacc = fmaf(-arow[j], x[j], sacc);
-        x[i] = sacc;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.tf[(16 * b + i) * F_STRIDE + 16 * b + c16] = x[i];
-    }
-    __syncthreads();
-    {
-      const int ri = lane >> 2;          // row inside the 16 x 16 block
-      const int cj = 4 * (lane & 3);     // 4 columns
-      float* msc = sm.msc[wave];
-#pragma unroll
-      for (int lev = 1; lev <= 3; ++lev) {
-        const bool active = wave < 4 - lev;
-        const int J = wave, I = wave + lev;
-        if (active) {
-          float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f);
-          for (int K = J; K < I; ++K) {
-            const float* arow = &sm.af[(16 * I + ri) * F_STRIDE + 16 * K];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-              const float av = arow[k];
-              const float4 tv = *reinterpret_cast<const float4*>(&sm.tf[(16 * K + k) * F_STRIDE + 16 * J + cj]);
-              m4.x = fmaf(av, tv.x, m4.x);
-              m4.y = fmaf(av, tv.y, m4.y);
-              m4.z = fmaf(av, tv.z, m4.z);
-              m4.w = fmaf(av, tv.w, m4.w);
-            }
-          }
-          *reinterpret_cast<float4*>(&msc[ri * 20 + cj]) = m4;
-        }
-        __syncthreads();
-        if (active) {
-          float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
-          const float* trow = &sm.tf[(16 * I + ri) * F_STRIDE + 16 * I];
-#pragma unroll
-          for (int k = 0; k <= 15; ++k) {
-            const float tv = trow[k];
-            const float4 mv = *reinterpret_cast<const float4*>(&msc[k * 20 + cj]);
-            t4.x = fmaf(-tv, mv.x, t4.x);
-            t4.y = fmaf(-tv, mv.y, t4.y);
-            t4.z = fmaf(-tv, mv.z, t4.z);
-            t4.w = fmaf(-tv, mv.w, t4.w);
-          }
-          *reinterpret_cast<float4*>(&sm.tf[(16 * I + ri) * F_STRIDE + 16 * J + cj]) = t4;
-        }
-        __syncthreads();
-      }
-    }
-    // T' = T diag(beta), lower triangle, split into bf16 hi/lo planes
-    for (int idx = tid; idx < CH * CH; idx += NTHR) {
-      const int i = idx >> 6, j = idx & 63;
-      const float v = (j <= i) ? sm.tf[i * F_STRIDE + j] * sm.beta[j] : 0.f;
-      const u16 hv = f2bf(v);
-      sm.th[i * T_STRIDE + j] = hv;
-      sm.tl[i * T_STRIDE + j] = f2bf(v - bf2f(hv));
-    }
-    __syncthreads();
-
-    // ---------------- (4) S-dependent products for this wave's 16 columns
-    float eg[4][4], rkt[4][4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * I + 4 * g4 + e;
-        eg[I][e] = expf(sm.gam[t]);
-        rkt[I][e] = sm.rnk[t];
-      }
-
-    // K S and Q S with S split hi/lo (S rows are the contraction index)
-    f32x4 KS[4], QS[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      KS[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-      QS[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      bf16x8 sh, sl;
-      frag_acc_split(S[2 * m], S[2 * m + 1], sh, sl);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const bf16x8 ak = frag_rows(sm.kh, KS_STRIDE, 16 * I, 32 * m, lane);
-        const bf16x8 aq = frag_rows(sm.qh, KS_STRIDE, 16 * I, 32 * m, lane);
-        KS[I] = mma(ak, sh, KS[I]);
-        KS[I] = mma(ak, sl, KS[I]);
-        QS[I] = mma(aq, sh, QS[I]);
-        QS[I] = mma(aq, sl, QS[I]);
-        if constexpr (F32) {
-          KS[I] = mma(frag_rows(sm.kl, KS_STRIDE, 16 * I, 32 * m, lane), sh, KS[I]);
-          QS[I] = mma(frag_rows(sm.ql, KS_STRIDE, 16 * I, 32 * m, lane), sh, QS[I]);
-        }
-      }
-    }
+    for (int m = 0; m < 4; ++m) frag_acc_split(S[2 * m], S[2 * m + 1], sh[m], sl[m]);
 
     // R = V - diag(e^gamma / |k|) K S
     f32x4 R[4];
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
+    for (int I = 0; I < 4; ++I) {
+      bf16x8 ak[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) R[I][e] = vr[I][e] - eg[I][e] * rkt[I][e] * KS[I][e];
+      for (int m = 0; m < 4; ++m) ak[m] = frag_rows(sm.kh, KS_STRIDE, 16 * I, 32 * m, lane);
+      f32x4 ks = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        ks = mma(ak[m], sh[m], ks);
+        ks = mma(ak[m], sl[m], ks);
+        if constexpr (F32) ks = mma(frag_rows(sm.kl, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], ks);
+      }
+      const float4 c4 = *reinterpret_cast<const float4*>(&sm.fac[16 * I + 4 * g4]);
+      R[I][0] = vr[I][0] - c4.x * ks[0];
+      R[I][1] = vr[I][1] - c4.y * ks[1];
+      R[I][2] = vr[I][2] - c4.z * ks[2];
+      R[I][3] = vr[I][3] - c4.w * ks[3];
+    }
 
     // U = T' R   (T' lower triangular: row tile I needs token slabs 0 .. I/2)
     f32x4 U[4];
@@ -475,51 +766,62 @@ chunk_prefill_kernel(ChunkArgs p) {
       frag_acc_split(U[2], U[3], uh[1], ul[1]);
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        f32x4 PU = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 aq[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) aq[m] = frag_rows(sm.qh, KS_STRIDE, 16 * I, 32 * m, lane);
+        f32x4 qs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          qs = mma(aq[m], sh[m], qs);
+          qs = mma(aq[m], sl[m], qs);
+          if constexpr (F32) qs = mma(frag_rows(sm.ql, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], qs);
+        }
+        f32x4 pu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m <= I / 2; ++m) {
           const bf16x8 ah = frag_rows(sm.ph, T_STRIDE, 16 * I, 32 * m, lane);
           const bf16x8 al = frag_rows(sm.pl, T_STRIDE, 16 * I, 32 * m, lane);
-          PU = mma(ah, uh[m], PU);
-          PU = mma(al, uh[m], PU);
-          PU = mma(ah, ul[m], PU);
+          pu = mma(ah, uh[m], pu);
+          pu = mma(al, uh[m], pu);
+          pu = mma(ah, ul[m], pu);
         }
+        const float4 c4 = *reinterpret_cast<const float4*>(&sm.fac[CH + 16 * I + 4 * g4]);
+        const float cqv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * I + 4 * g4 + e;
-          if (t < L) {
-            const float ov = p.scale * (eg[I][e] * sm.rnq[t] * QS[I][e] + PU[e]);
-            io::st(og, (t0 + t) * o_stride, ov);
-          }
+          if (t < L) io::st(og, (t0 + t) * o_stride, p.scale * (cqv[e] * qs[e] + pu[e]));
         }
       }
     }
 
     // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U
     {
-      const float gl = sm.gam[CH - 1];
-      const float egl = expf(gl);
       f32x4 Us[4];
 #pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * I + 4 * g4 + e;
-          Us[I][e] = expf(gl - sm.gam[t]) * rkt[I][e] * U[I][e];
-        }
+      for (int I = 0; I < 4; ++I) {
+        const float4 c4 = *reinterpret_cast<const float4*>(&sm.fac[2 * CH + 16 * I + 4 * g4]);
+        Us[I][0] = c4.x * U[I][0];
+        Us[I][1] = c4.y * U[I][1];
+        Us[I][2] = c4.z * U[I][2];
+        Us[I][3] = c4.w * U[I][3];
+      }
       bf16x8 uh[2], ul[2];
       frag_acc_split(Us[0], Us[1], uh[0], ul[0]);
       frag_acc_split(Us[2], Us[3], uh[1], ul[1]);
+      const float egl = sm.fac[3 * CH];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        bf16x8 ak[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) ak[m] = frag_rows(sm.kth, KT_STRIDE, 16 * i, 32 * m, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[i][e] *= egl;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const bf16x8 ak = frag_cols(sm.kh, KS_STRIDE, 32 * m, 16 * i, lane);
-          S[i] = mma(ak, uh[m], S[i]);
-          S[i] = mma(ak, ul[m], S[i]);
-          if constexpr (F32) S[i] = mma(frag_cols(sm.kl, KS_STRIDE, 32 * m, 16 * i, lane), uh[m], S[i]);
+          S[i] = mma(ak[m], uh[m], S[i]);
+          S[i] = mma(ak[m], ul[m], S[i]);
+          if constexpr (F32) S[i] = mma(frag_rows(sm.ktl, KT_STRIDE, 16 * i, 32 * m, lane), uh[m], S[i]);
         }
       }
     }
@@ -536,14 +838,27 @@ chunk_prefill_kernel(ChunkArgs p) {
 }
 
 template <int IO>
-static hipError_t chunk_impl(const ChunkArgs& a, hipStream_t s) {
+static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
+  int32_t* cmap = reinterpret_cast<int32_t*>(ws);
+  uint8_t* recs = reinterpret_cast<uint8_t*>(ws) + ws_map_bytes(a.Ns);
+  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, st, a.cu, a.Ns, a.N, cmap);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t cmax = ws_max_chunks(a.N, a.Ns);
+  if (a.N > 0) {
+    hipLaunchKernelGGL(chunk_prep_kernel<IO>, dim3((unsigned)cmax, (unsigned)a.Hv), dim3(NTHR), 0,
+                       st, a, (const int32_t*)cmap, recs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t blocks = (int64_t)a.Ns * a.Hv * NBLK;
-  hipLaunchKernelGGL(chunk_prefill_kernel<IO>, dim3((unsigned)blocks), dim3(NTHR), 0, s, a);
+  hipLaunchKernelGGL(chunk_sweep_kernel<IO>, dim3((unsigned)blocks), dim3(NTHR), 0, st, a,
+                     (const int32_t*)cmap, (const uint8_t*)recs);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_prefill(const ChunkArgs& a, int io, hipStream_t s) {
-  return io == IO_BF16 ? chunk_impl<IO_BF16>(a, s) : chunk_impl<IO_F32>(a, s);
+hipError_t launch_chunk_prefill(const ChunkArgs& a, void* ws, int io, hipStream_t s) {
+  return io == IO_BF16 ? chunk_impl<IO_BF16>(a, ws, s) : chunk_impl<IO_F32>(a, ws, s);
 }
 
 }  // namespace gdn

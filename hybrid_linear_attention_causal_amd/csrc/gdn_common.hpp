@@ -85,6 +85,34 @@ __device__ __forceinline__ void gate_pair(float a, float b, float A_log, float d
   beta = sigmoid(b);
 }
 
+// ---------------------------------------------------------------- DPP cross-lane ops
+// (VALU data-parallel primitives: no LDS round trip)
+template <int CTRL, int ROW_MASK = 0xf, bool BOUND_ZERO = true>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf,
+                                                    BOUND_ZERO));
+}
+
+// sum over each DPP row of 16 lanes; every lane receives its row's total
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: pairs
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: quads
+  v += dpp<0x141>(v);   // row_half_mirror: the two quads of each half row
+  v += dpp<0x140>(v);   // row_mirror: the two halves of the row
+  return v;
+}
+
+// inclusive prefix sum over the 64 lanes of a wavefront
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp<0x111>(v);            // row_shr:1  (lanes shifted in from outside the row read 0)
+  v += dpp<0x112>(v);            // row_shr:2
+  v += dpp<0x114>(v);            // row_shr:4
+  v += dpp<0x118>(v);            // row_shr:8   -> inclusive scan inside each row of 16
+  v += dpp<0x142, 0xa, false>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp<0x143, 0xc, false>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // ---------------------------------------------------------------- reductions
 // sum over groups of W consecutive lanes (W a power of two <= 64)
 template <int W>

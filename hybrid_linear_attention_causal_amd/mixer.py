@@ -7,7 +7,8 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import gdn_chunk_prefill, gdn_conv1d_fwd, gdn_gated_rmsnorm, gdn_recurrent_step
+from ._lib import (gdn_chunk_prefill, gdn_chunk_prefill_workspace_size, gdn_conv1d_fwd,
+                   gdn_gated_rmsnorm, gdn_recurrent_step)
 
 D = 128
 
@@ -39,8 +40,13 @@ def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens
     s_out = bufs.get("state_out")
     if s_out is None and want_states:
         s_out = torch.empty((Ns, Hv, D, D), dtype=torch.float32, device=dev)
+    ws = bufs.get("workspace")
+    need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        bufs["workspace"] = ws
     gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens, state_in, s_out,
-                      stream=stream)
+                      workspace=ws, stream=stream)
     yn = bufs.get("y")
     if yn is None:
         yn = torch.empty_like(o)

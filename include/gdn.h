@@ -96,7 +96,12 @@ gdn_status_t gdn_conv1d_fwd(const void* x, const float* w, void* y, const int32_
 
 /*
  * gdn_chunk_prefill_workspace_size -- bytes of device workspace that
- * gdn_chunk_prefill needs for these sizes (0 for the current kernels).
+ * gdn_chunk_prefill needs for N packed tokens in Ns sequences with Hv value heads
+ * (Hk and d are accepted for symmetry and do not change the size).  The
+ * workspace holds the chunk map of the packed sequences and, per (64-token
+ * chunk, value head), the chunk's 64 x 64 T' and P matrices as bf16 hi/lo
+ * planes plus per-token factors: 33792 bytes per (chunk, head), for at most
+ * ceil(N/64) + Ns chunks.  Returns 0 for invalid sizes.
  */
 size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d);
 
@@ -130,11 +135,12 @@ size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d
  *   o               [N, Hv, dv]            io   (must not alias the inputs)
  *   cu_seqlens      [Ns + 1]               int32 or NULL
  *   scale           <= 0 selects 1/sqrt(dk)
- *   workspace       device buffer of gdn_chunk_prefill_workspace_size() bytes
- *                   (may be NULL when that size is 0)
+ *   workspace       device buffer (256-byte aligned) of at least
+ *                   gdn_chunk_prefill_workspace_size() bytes, owned by the caller;
+ *                   its contents need no initialisation and are scratch
  * Errors: dk != 128 or dv != 128 -> UNSUPPORTED; Hk < 1, Hv % Hk != 0, Ns < 1,
  * N < 0, a stride below its row width or not a multiple of 8, NULL required
- * pointers, ws_bytes below the required size -> INVALID_ARG.
+ * pointers, a missing, unaligned or too small workspace -> INVALID_ARG.
  */
 gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int64_t stride_q,
                                int64_t stride_k, int64_t stride_v, const void* a, const void* b,

@@ -87,7 +87,12 @@ def test_prefill_rejects():
     assert _prefill(o=None) == _lib.GDN_ERR_INVALID_ARG
     assert _prefill(a=None) == _lib.GDN_ERR_INVALID_ARG
     assert _prefill(io=5) == _lib.GDN_ERR_INVALID_ARG
-    assert _lib.lib().gdn_chunk_prefill_workspace_size(4096, 1, 16, 32, 128) == 0
+    assert _prefill(ws=P, ws_bytes=1024) == _lib.GDN_ERR_INVALID_ARG
+    assert "workspace" in _msg()
+    # chunk map (padded to 256 B) + (ceil(N/64) + Ns) chunks x Hv heads x 33792 B
+    assert _lib.lib().gdn_chunk_prefill_workspace_size(4096, 1, 16, 32, 128) == 256 + 65 * 32 * 33792
+    assert _lib.lib().gdn_chunk_prefill_workspace_size(100, 3, 1, 2, 128) == 256 + 5 * 2 * 33792
+    assert _lib.lib().gdn_chunk_prefill_workspace_size(-1, 1, 16, 32, 128) == 0
 
 
 def _step(**kw):
