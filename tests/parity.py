@@ -2,9 +2,16 @@
 
 Tolerances (stated once, used everywhere):
 * fp32 io: max |delta| <= 2e-3 on the core output o and the norm output y.
-* bf16 io: max_i (|delta_i| - 2^-8 max(|ref_i|, |gpu_i|))_+ <= 3e-2 * RMS(ref).  The
-  2^-8 term is the bf16 store itself (half an ulp is at most 2^-8 |x|), which the
-  fp64 oracle does not have; without it no bf16-output implementation passes.
+* bf16 io: max_i (|delta_i| - s * max(|ref_i|, |gpu_i|))_+ <= 3e-2 * RMS(ref) with
+  s = 2^-8 for a call's own output: the bf16 store itself (half an ulp is at most
+  2^-8 |x|), which the fp64 oracle does not have; without it no bf16-output
+  implementation passes.  A value computed from another bf16 call output (the
+  gated norm of the core output o inside a whole-layer check) also carries that
+  input's rounding: fp32 and fp64 values of o that straddle a bf16 rounding
+  boundary round to neighbours one ulp (<= 2^-7 |o|) apart, which the norm
+  passes on element by element, so there s = 2^-8 + 2^-7 = 3 * 2^-8.  (Measured
+  with the oracle alone: 1-ulp flips of 1% of o give a gated error of 8e-2 RMS
+  at s = 2^-8 and 7e-3 RMS at s = 3 * 2^-8.)
 * final recurrent state: per sequence ||dS||_F / ||S_ref||_F <= 1e-3.
 * conv state: bit-exact (it is a copy of input rows).
 """
@@ -36,8 +43,9 @@ def host(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def out_error(gpu, ref, io):
-    """Return (gated error, bound) for an io-dtype output."""
+def out_error(gpu, ref, io, upstream_bf16=0):
+    """Return (gated error, bound) for an io-dtype output; upstream_bf16 = number of
+    bf16 call outputs between the shared inputs and this value (0 or 1)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
@@ -45,13 +53,13 @@ def out_error(gpu, ref, io):
     d = np.abs(gpu - ref)
     if io == "f32":
         return float(d.max(initial=0.0)), F32_ABS_TOL
-    slack = BF16_HALF_ULP * np.maximum(np.abs(ref), np.abs(gpu))
+    slack = BF16_HALF_ULP * (1 + 2 * upstream_bf16) * np.maximum(np.abs(ref), np.abs(gpu))
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
     return float(np.maximum(d - slack, 0.0).max(initial=0.0)), BF16_RMS_TOL * rms
 
 
-def assert_out(gpu, ref, io, what=""):
-    err, bound = out_error(gpu, ref, io)
+def assert_out(gpu, ref, io, what="", upstream_bf16=0):
+    err, bound = out_error(gpu, ref, io, upstream_bf16)
     assert err <= bound, f"{what}: error {err:.3e} > bound {bound:.3e} ({io})"
     return err, bound
 
