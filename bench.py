@@ -167,7 +167,7 @@ def main():
     P["o"] = torch.empty((N, hv, D), dtype=torch.bfloat16, device="cuda")
     P["s_out"] = torch.empty((1, hv, D, D), dtype=torch.float32, device="cuda")
     P["yn"] = torch.empty_like(P["o"])
-    P["ws"] = torch.empty(gdn.gdn_chunk_prefill_workspace_size(N, 1, hk, hv), dtype=torch.uint8,
+    P["ws"] = torch.empty(gdn.gdn_chunk_prefill_workspace_size(N, 1, hk, hv, io=torch.bfloat16), dtype=torch.uint8,
                           device="cuda")
     q, k, v = qkv_views(P["y"], hk, hv)
     zv = P["z"].view(N, hv, D)

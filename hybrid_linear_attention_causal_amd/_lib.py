@@ -32,7 +32,7 @@ _SIGS = {
     "gdn_last_error": ([], ctypes.c_char_p),
     "gdn_version": ([], ctypes.c_char_p),
     "gdn_conv1d_fwd": ([_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp], _i32),
-    "gdn_chunk_prefill_workspace_size": ([_i64, _i32, _i32, _i32, _i32], _sz),
+    "gdn_chunk_prefill_workspace_size": ([_i64, _i32, _i32, _i32, _i32, _i32], _sz),
     "gdn_chunk_prefill": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                            _sz, _i32, _vp], _i32),
@@ -120,8 +120,11 @@ def gdn_conv1d_fwd(x, w, y, cu_seqlens=None, conv_state_in=None, conv_state_out=
         _io(x), _stream(stream)))
 
 
-def gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, d=128) -> int:
-    return int(lib().gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, d))
+def gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, d=128, io=GDN_BF16) -> int:
+    """Workspace bytes for gdn_chunk_prefill (io: GDN_BF16, GDN_F32 or a torch dtype)."""
+    if isinstance(io, torch.dtype):
+        io = GDN_F32 if io == torch.float32 else GDN_BF16
+    return int(lib().gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, d, io))
 
 
 def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None, state_in=None,
@@ -136,7 +139,7 @@ def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None,
         if t.stride(-1) != 1:
             raise ValueError("q, k, v rows must be contiguous")
     if workspace is None:
-        need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk)
+        need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk, _io(q))
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("gdn_chunk_prefill", lib().gdn_chunk_prefill(

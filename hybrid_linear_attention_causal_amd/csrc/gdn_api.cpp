@@ -89,10 +89,9 @@ gdn_status_t gdn_conv1d_fwd(const void* x, const float* w, void* y, const int32_
   return e == hipSuccess ? GDN_OK : hip_fail(e, "conv1d launch");
 }
 
-size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d) {
-  (void)Hk; (void)d;
-  if (N < 0 || Ns < 1 || Hv < 1) return 0;
-  return gdn::chunk_workspace_bytes(N, Ns, Hv);
+size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d, gdn_dtype_t io) {
+  if (N < 0 || Ns < 1 || Hk < 1 || Hv < 1 || d != 128 || !io_ok(io)) return 0;
+  return gdn::chunk_workspace_bytes(N, Ns, Hk, Hv, io == GDN_F32);
 }
 
 gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int64_t stride_q,
@@ -129,7 +128,7 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
       return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: q, k, v, o must be 16-byte aligned");
   }
-  const size_t need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk);
+  const size_t need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk, io);
   if (!workspace || ws_bytes < need || !aligned(workspace, 256))
     return fail(GDN_ERR_INVALID_ARG,
                 "chunk_prefill: workspace must be a 256-byte aligned buffer of >= %zu bytes", need);

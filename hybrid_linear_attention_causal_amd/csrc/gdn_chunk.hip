@@ -52,20 +52,30 @@ constexpr int KS_STRIDE = DK + 8;      // u16 per staged K/Q row
 constexpr int KT_STRIDE = CH + 8;      // u16 per staged K^T row
 constexpr int T_STRIDE = CH + 8;       // u16 per staged T'/P row
 constexpr int F_STRIDE = CH + 4;       // floats per A/T row
+constexpr int O_STRIDE = DVB + 8;      // u16 per staged output row (bf16 io)
 
-// Workspace: chunk offsets (int32 [Ns + 1], padded to 256 bytes), then for every
-// (global chunk c, value head h) a record of T' hi, T' lo, P hi, P lo (row-major
-// 64 x 64 bf16 planes) and 4 x 64 fp32 factors: e^gamma/|k|, e^gamma/|q|,
-// e^{gamma_L - gamma}/|k|, and e^{gamma_L} (in slot 3 * 64).
-constexpr int64_t WS_PLANE = (int64_t)CH * CH;                       // u16 per plane
-constexpr int64_t WS_REC_BYTES = 4 * WS_PLANE * 2 + 4 * CH * 4;      // 33792
-constexpr int64_t WS_FAC_OFF = 4 * WS_PLANE * 2;                     // factors offset
+// Workspace (all LDS-ready, so the sweep stages operands with plain DMA copies):
+//   chunk offsets: int32 [Ns + 1], padded to 256 bytes;
+//   per (global chunk c, value head h), 37888 bytes: T' hi, T' lo, P hi, P lo as
+//     row-major 64 x 72 (padded) bf16 planes, then 4 x 64 fp32 factors
+//     e^gamma/|k|, e^gamma/|q|, e^{gamma_L - gamma}/|k|, e^{gamma_L};
+//   per (global chunk c, key head kh): bf16 io: K^T as 128 x 72 bf16 (18432 bytes);
+//     fp32 io: K hi, K lo, Q hi, Q lo rows (64 x 136 bf16 each) then K^T hi, K^T lo.
+constexpr int64_t WS_PL_BYTES = (int64_t)CH * T_STRIDE * 2;          // 9216 per plane
+constexpr int64_t WS_FAC_OFF = 4 * WS_PL_BYTES;                       // 36864
+constexpr int64_t WS_REC_BYTES = WS_FAC_OFF + 4 * CH * 4;             // 37888
+constexpr int64_t WS_ROWS_BYTES = (int64_t)CH * KS_STRIDE * 2;       // 17408 per row plane
+constexpr int64_t WS_KT_BYTES = (int64_t)DK * KT_STRIDE * 2;          // 18432 per K^T plane
 
 static int64_t ws_map_bytes(int Ns) { return (((int64_t)Ns + 1) * 4 + 255) / 256 * 256; }
 static int64_t ws_max_chunks(int64_t N, int Ns) { return (N + CH - 1) / CH + Ns; }
+__host__ __device__ constexpr int64_t ws_krec_bytes(bool f32) {
+  return f32 ? 4 * WS_ROWS_BYTES + 2 * WS_KT_BYTES : WS_KT_BYTES;
+}
 
-size_t chunk_workspace_bytes(int64_t N, int Ns, int Hv) {
-  return (size_t)(ws_map_bytes(Ns) + ws_max_chunks(N, Ns) * Hv * WS_REC_BYTES);
+size_t chunk_workspace_bytes(int64_t N, int Ns, int Hk, int Hv, bool f32) {
+  const int64_t cmax = ws_max_chunks(N, Ns);
+  return (size_t)(ws_map_bytes(Ns) + cmax * Hv * WS_REC_BYTES + cmax * Hk * ws_krec_bytes(f32));
 }
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -231,8 +241,9 @@ struct PrepSmem {
 };
 
 template <int IO>
-__global__ void __launch_bounds__(NTHR, 2)
-chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __restrict__ recs) {
+__global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? 2 : 1)
+chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __restrict__ recs,
+                  uint8_t* __restrict__ krecs) {
   typedef Io<IO> io;
   typedef typename io::T T;
   constexpr bool F32 = (IO == IO_F32);
@@ -377,7 +388,7 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
         uint32_t ph, pl;
         split2(qi[e] * d * gq[e], 0.f, ph, pl);
         pst[i * CH + j] = (u16)ph;
-        pst[WS_PLANE + i * CH + j] = (u16)pl;
+        pst[CH * CH + i * CH + j] = (u16)pl;
       }
     } else {
       const int Is[6] = {0, 0, 0, 1, 1, 2};
@@ -388,17 +399,52 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * I + 4 * g4 + e, j = 16 * J + c16;
         pst[i * CH + j] = 0;
-        pst[WS_PLANE + i * CH + j] = 0;
+        pst[CH * CH + i * CH + j] = 0;
       }
     }
   }
   __syncthreads();
-  // P planes to the workspace (16 KB: four 16-byte words per thread)
+  // P planes to the workspace record, rows padded to 72 (four 16-byte words per thread)
   {
     const uint4* src = reinterpret_cast<const uint4*>(pst);
-    uint4* dst = reinterpret_cast<uint4*>(rec + 2 * WS_PLANE * 2);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) dst[tid + NTHR * it] = src[tid + NTHR * it];
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + NTHR * it;            // plane i >> 9, row (i & 511) >> 3, word i & 7
+      const int plane = i >> 9, row = (i & 511) >> 3, w = i & 7;
+      *reinterpret_cast<uint4*>(rec + (2 + plane) * WS_PL_BYTES + row * (T_STRIDE * 2) + w * 16) =
+          src[i];
+    }
+  }
+  // K record of this (chunk, key head), written once by its first value head: K^T (from the
+  // staged rows, 8 tokens per 16-byte word) and, for fp32 io, the hi/lo K and Q rows
+  if (h % (Hv / p.Hk) == 0) {
+    uint8_t* krec = krecs + ((int64_t)c * p.Hk + kh_) * ws_krec_bytes(F32);
+    uint8_t* kt_dst = krec + (F32 ? 4 * WS_ROWS_BYTES : 0);
+#pragma unroll
+    for (int pl = 0; pl < (F32 ? 2 : 1); ++pl) {
+      const u16* srcp = pl ? sm.kl : sm.kh;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int i = tid + NTHR * it;          // K^T row d = i >> 3, tokens 8j .. 8j+7
+        const int d = i >> 3, j = i & 7;
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          w[u] = (uint32_t)srcp[(8 * j + 2 * u) * KS_STRIDE + d] |
+                 ((uint32_t)srcp[(8 * j + 2 * u + 1) * KS_STRIDE + d] << 16);
+        *reinterpret_cast<uint4*>(kt_dst + pl * WS_KT_BYTES + d * (KT_STRIDE * 2) + j * 16) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    if constexpr (F32) {
+      const u16* planes[4] = {sm.kh, sm.kl, sm.qh, sm.ql};
+#pragma unroll
+      for (int pl = 0; pl < 4; ++pl) {
+        const uint4* src = reinterpret_cast<const uint4*>(planes[pl]);
+        uint4* dst = reinterpret_cast<uint4*>(krec + pl * WS_ROWS_BYTES);
+        for (int i = tid; i < (int)(WS_ROWS_BYTES / 16); i += NTHR) dst[i] = src[i];
+      }
+    }
   }
   __syncthreads();   // the T buffer is reused below
 
@@ -541,73 +587,79 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
       uint32_t h0, l0, h1, l1;
       split2(v0, v1, h0, l0);
       split2(v2, v3, h1, l1);
-      *reinterpret_cast<uint2*>(tph + i * CH + j0) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(tph + WS_PLANE + i * CH + j0) = make_uint2(l0, l1);
+      *reinterpret_cast<uint2*>(tph + i * T_STRIDE + j0) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(tph + CH * T_STRIDE + i * T_STRIDE + j0) = make_uint2(l0, l1);
     }
   }
 }
 
 // ============================================================================ 3. sweep
-template <int IO>
-struct SweepSmem {
-  static constexpr bool F32 = (IO == IO_F32);
-  u16 kh[CH * KS_STRIDE];                 // K rows (bf16 / hi part)
-  u16 kl[F32 ? CH * KS_STRIDE : 2];
-  u16 qh[CH * KS_STRIDE];
-  u16 ql[F32 ? CH * KS_STRIDE : 2];
-  u16 kth[DK * KT_STRIDE];                // K^T
-  u16 ktl[F32 ? DK * KT_STRIDE : 2];
-  u16 th[CH * T_STRIDE];                  // T' hi/lo
-  u16 tl[CH * T_STRIDE];
-  u16 ph[CH * T_STRIDE];                  // P hi/lo
-  u16 pl[CH * T_STRIDE];
-  float fac[4 * CH];                      // e^g/|k|, e^g/|q|, e^{gL-g}/|k|, e^{gL}
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Registers holding one chunk's operands between their global loads and the LDS commit.
-template <int IO>
-struct SweepPrefetch {
-  RowBlock<IO> k, q;
-  uint4 tp[4];                            // T' hi/lo planes (16 KB per workgroup)
-  uint4 pp[4];                            // P hi/lo planes
-  uint4 fc;                               // 16 bytes of the factor block (tid < 64)
-  float v[4][4];                          // V slice in accumulator layout
-};
-
-template <int IO>
-__device__ __forceinline__ void sweep_prefetch(const ChunkArgs& p, SweepPrefetch<IO>& pf,
-                                               const uint8_t* rec, const typename Io<IO>::T* qg,
-                                               const typename Io<IO>::T* kg,
-                                               const typename Io<IO>::T* vg, int64_t t0, int L,
-                                               int tid) {
-  typedef Io<IO> io;
-  load_rows<IO>(pf.k, kg, p.stride_k, t0, L, tid);
-  load_rows<IO>(pf.q, qg, p.stride_q, t0, L, tid);
-  const uint4* tsrc = reinterpret_cast<const uint4*>(rec);
-  const uint4* psrc = reinterpret_cast<const uint4*>(rec + 2 * WS_PLANE * 2);
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    pf.tp[it] = tsrc[tid + NTHR * it];
-    pf.pp[it] = psrc[tid + NTHR * it];
+// Copy nslots 16-byte words from a linear global source into linear LDS with the
+// LDS DMA path (global_load_lds_dwordx4: lane l's word lands at dst + 16 l); the
+// workgroup's waves take turns by instruction.
+__device__ __forceinline__ void dma_linear(const uint8_t* src, void* dst, int nslots, int wave,
+                                           int lane) {
+  for (int ins = wave; ins * 64 < nslots; ins += NTHR / 64) {
+    const int sl = ins * 64 + lane;
+    if (sl < nslots)
+      __builtin_amdgcn_global_load_lds(src + (int64_t)sl * 16,
+                                       (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
   }
-  if (tid < 64) pf.fc = reinterpret_cast<const uint4*>(rec + WS_FAC_OFF)[tid];
-  const int g4 = (tid & 63) >> 4;
-#pragma unroll
-  for (int I = 0; I < 4; ++I)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * I + 4 * g4 + e;
-      pf.v[I][e] = io::ld(vg, (t0 + (t < L ? t : L - 1)) * p.stride_v);
-    }
 }
+
+// K or Q rows of one chunk from the packed input into LDS rows padded to KS_STRIDE:
+// 17 words per row (word 16 is padding); rows past the chunk end repeat the last
+// valid row, which the chunk algebra multiplies by zero.
+template <typename T>
+__device__ __forceinline__ void dma_rows(const T* base, int64_t stride, int64_t t0, int L,
+                                         u16* dst, int wave, int lane) {
+  constexpr int WPR = KS_STRIDE * 2 / 16;      // 17 words per staged row
+  constexpr int NSL = CH * WPR;                // 1088
+  for (int ins = wave; ins * 64 < NSL; ins += NTHR / 64) {
+    const int sl = ins * 64 + lane;
+    const int row = sl / WPR, w = sl - row * WPR;
+    const int64_t r = t0 + (row < L ? row : L - 1);
+    const T* src = base + r * stride + (w < 16 ? w : 15) * 8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
+  }
+}
+
+// wait for all of this wave's outstanding vector-memory operations (incl. LDS DMA)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS buffers of the sweep, one __shared__ object each so that the compiler can tell
+// the DMA destinations of one phase from the buffers the other phase reads.
+template <int IO>
+struct SweepSizes {
+  static constexpr bool F32 = (IO == IO_F32);
+  static constexpr int ROWS = CH * KS_STRIDE;          // K or Q rows (u16)
+  static constexpr int ROWS_LO = F32 ? ROWS : 8;
+  static constexpr int KT = DK * KT_STRIDE;            // K^T (u16)
+  static constexpr int KT_LO = F32 ? KT : 8;
+  static constexpr int PL2 = 2 * CH * T_STRIDE;        // a hi|lo plane pair (u16)
+  static constexpr int OST = F32 ? 8 : CH * O_STRIDE;
+};
 
 template <int IO>
 __global__ void __launch_bounds__(NTHR)
-chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
+chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs,
+                   const uint8_t* __restrict__ krecs) {
   typedef Io<IO> io;
   typedef typename io::T T;
   constexpr bool F32 = (IO == IO_F32);
-  __shared__ SweepSmem<IO> sm;
+  typedef SweepSizes<IO> Z;
+  __shared__ __attribute__((aligned(16))) u16 s_kh[Z::ROWS];    // K rows (bf16 / hi)  phase A
+  __shared__ __attribute__((aligned(16))) u16 s_kl[Z::ROWS_LO];
+  __shared__ __attribute__((aligned(16))) u16 s_qh[Z::ROWS];    // Q rows              phase A
+  __shared__ __attribute__((aligned(16))) u16 s_ql[Z::ROWS_LO];
+  __shared__ __attribute__((aligned(16))) u16 s_tp[Z::PL2];     // T' hi | lo          phase A
+  __shared__ __attribute__((aligned(16))) u16 s_pp[Z::PL2];     // P hi | lo           phase B
+  __shared__ __attribute__((aligned(16))) u16 s_kth[Z::KT];     // K^T                 phase B
+  __shared__ __attribute__((aligned(16))) u16 s_ktl[Z::KT_LO];
+  __shared__ __attribute__((aligned(16))) float s_fac[4 * CH];  // per-token factors    phase A
+  __shared__ __attribute__((aligned(16))) u16 s_ost[Z::OST];    // output tiles (bf16 io)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -625,13 +677,16 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   int64_t b0, b1;
   seq_bounds(p.cu, p.N, s, b0, b1);
   const int c0 = cmap[s];
+  const int nch = (int)((b1 - b0 + CH - 1) / CH);
   const int col = blk * DVB + wave * 16 + c16;      // this lane's dv column
 
   const T* qg = (const T*)p.q + (int64_t)kh * DK;
   const T* kg = (const T*)p.k + (int64_t)kh * DK;
   const T* vg = (const T*)p.v + (int64_t)h * DV + col;
   T* og = (T*)p.o + (int64_t)h * DV + col;
+  T* og0 = (T*)p.o + (int64_t)h * DV + blk * DVB;   // this workgroup's output columns
   const int64_t o_stride = (int64_t)Hv * DV;
+  const int64_t krec_bytes = ws_krec_bytes(F32);
 
   // ---- recurrent state slice: S[i] holds rows 16 i + 4 g4 + e of column col
   f32x4 S[8];
@@ -647,185 +702,236 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     for (int i = 0; i < 8; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  SweepPrefetch<IO> pf;
-  if (b0 < b1)
-    sweep_prefetch<IO>(p, pf, recs + ((int64_t)c0 * Hv + h) * WS_REC_BYTES, qg, kg, vg, b0,
-                       (int)min((int64_t)CH, b1 - b0), tid);
+  // phase-A operands of chunk n (K, Q rows, T' planes, factors) and its V slice
+  T vraw[4][4];
+  auto stage_a = [&](int n) {
+    const int64_t t0 = b0 + (int64_t)n * CH;
+    const int L = (int)min((int64_t)CH, b1 - t0);
+    const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * WS_REC_BYTES;
+    if constexpr (F32) {
+      const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
+      dma_linear(krec, s_kh, (int)(WS_ROWS_BYTES / 16), wave, lane);
+      dma_linear(krec + WS_ROWS_BYTES, s_kl, (int)(WS_ROWS_BYTES / 16), wave, lane);
+      dma_linear(krec + 2 * WS_ROWS_BYTES, s_qh, (int)(WS_ROWS_BYTES / 16), wave, lane);
+      dma_linear(krec + 3 * WS_ROWS_BYTES, s_ql, (int)(WS_ROWS_BYTES / 16), wave, lane);
+    } else {
+      dma_rows(kg, p.stride_k, t0, L, s_kh, wave, lane);
+      dma_rows(qg, p.stride_q, t0, L, s_qh, wave, lane);
+    }
+    dma_linear(rec, s_tp, (int)(2 * WS_PL_BYTES / 16), wave, lane);
+    dma_linear(rec + WS_FAC_OFF, s_fac, 4 * CH * 4 / 16, wave, lane);
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * g4 + e;
+        vraw[I][e] = vg[(t0 + (t < L ? t : L - 1)) * p.stride_v];
+      }
+  };
+  // phase-B operands of chunk n (P planes, K^T)
+  auto stage_b = [&](int n) {
+    const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * WS_REC_BYTES;
+    const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
+    dma_linear(rec + 2 * WS_PL_BYTES, s_pp, (int)(2 * WS_PL_BYTES / 16), wave, lane);
+    if constexpr (F32) {
+      dma_linear(krec + 4 * WS_ROWS_BYTES, s_kth, (int)(WS_KT_BYTES / 16), wave, lane);
+      dma_linear(krec + 4 * WS_ROWS_BYTES + WS_KT_BYTES, s_ktl, (int)(WS_KT_BYTES / 16), wave,
+                 lane);
+    } else {
+      dma_linear(krec, s_kth, (int)(WS_KT_BYTES / 16), wave, lane);
+    }
+  };
+  // bf16 io: a chunk's output stays in registers (packed pairs of rows) through the
+  // next chunk boundary, is written to the LDS tile there while no DMA is in flight
+  // (the compiler makes LDS stores wait for every pending DMA), and leaves as
+  // coalesced 16-byte rows after the next barrier.
+  uint32_t opk[4][2];
+  auto write_ost = [&]() {
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * g4 + e;
+        const uint32_t w = opk[I][e >> 1];
+        s_ost[t * O_STRIDE + wave * 16 + c16] = (u16)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+      }
+  };
+  auto store_o = [&](int n) {
+    const int64_t t0 = b0 + (int64_t)n * CH;
+    const int L = (int)min((int64_t)CH, b1 - t0);
+    const u16* ot = s_ost;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + NTHR * it;
+      const int row = idx >> 3, c8 = idx & 7;
+      if (row < L)
+        *reinterpret_cast<uint4*>(og0 + (t0 + row) * o_stride + c8 * 8) =
+            *reinterpret_cast<const uint4*>(&ot[row * O_STRIDE + c8 * 8]);
+    }
+  };
 
-  int c = c0;
-  for (int64_t t0 = b0; t0 < b1; t0 += CH, ++c) {
+  if (nch > 0) stage_a(0);
+
+  for (int n = 0; n < nch; ++n) {
+    const int64_t t0 = b0 + (int64_t)n * CH;
     const int L = (b1 - t0) < CH ? (int)(b1 - t0) : CH;
 
-    // ---------------- commit the prefetched operands to LDS
-    {
-      const int c8 = tid & 15, rq = tid >> 4;
-      uint32_t kt_h[8][2], kt_l[8][2];          // K^T words: 4 consecutive rows per column
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = 4 * rq + u;
-        const bool ok = row < L;
-        float kv[8], qv[8];
-        row_vals<IO>(pf.k, u, ok, kv);
-        row_vals<IO>(pf.q, u, ok, qv);
-        uint4 hw, lw, qhw, qlw;
-        put_row8<IO>(sm.kh, sm.kl, row * KS_STRIDE + c8 * 8, kv, hw, lw);
-        put_row8<IO>(sm.qh, sm.ql, row * KS_STRIDE + c8 * 8, qv, qhw, qlw);
-        const uint32_t hs[4] = {hw.x, hw.y, hw.z, hw.w};
-        const uint32_t ls[4] = {lw.x, lw.y, lw.z, lw.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t hv = (j & 1) ? (hs[j >> 1] >> 16) : (hs[j >> 1] & 0xFFFFu);
-          const uint32_t lv = (j & 1) ? (ls[j >> 1] >> 16) : (ls[j >> 1] & 0xFFFFu);
-          if (u & 1) {
-            kt_h[j][u >> 1] |= hv << 16;
-            kt_l[j][u >> 1] |= lv << 16;
-          } else {
-            kt_h[j][u >> 1] = hv;
-            kt_l[j][u >> 1] = lv;
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int off = (c8 * 8 + j) * KT_STRIDE + 4 * rq;
-        *reinterpret_cast<uint2*>(&sm.kth[off]) = make_uint2(kt_h[j][0], kt_h[j][1]);
-        if constexpr (F32) *reinterpret_cast<uint2*>(&sm.ktl[off]) = make_uint2(kt_l[j][0], kt_l[j][1]);
-      }
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int idx = tid + NTHR * it;        // 16-byte word of the hi|lo planes
-        const int plane = idx >> 9, w = idx & 511;
-        const int off = (w >> 3) * T_STRIDE + (w & 7) * 8;
-        *reinterpret_cast<uint4*>((plane ? sm.tl : sm.th) + off) = pf.tp[it];
-        *reinterpret_cast<uint4*>((plane ? sm.pl : sm.ph) + off) = pf.pp[it];
-      }
-      if (tid < 64) *reinterpret_cast<uint4*>(&sm.fac[4 * tid]) = pf.fc;
+    wait_vmem();
+    __syncthreads();       // phase-A operands of chunk n are in LDS; phase B of n-1 is done
+    if constexpr (!F32) {
+      if (n > 0) write_ost();
     }
+    stage_b(n);
+
+    // ================= phase A: K S and Q S (S hi/lo), R, U = T' R
     float vr[4][4];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vr[I][e] = (16 * I + 4 * g4 + e < L) ? pf.v[I][e] : 0.f;
-    __syncthreads();
+      for (int e = 0; e < 4; ++e)
+        vr[I][e] = (16 * I + 4 * g4 + e < L) ? io::ld(&vraw[I][e], 0) : 0.f;
 
-    // the next chunk's operands load while this chunk's products run
-    if (t0 + CH < b1)
-      sweep_prefetch<IO>(p, pf, recs + ((int64_t)(c + 1) * Hv + h) * WS_REC_BYTES, qg, kg, vg,
-                         t0 + CH, (int)min((int64_t)CH, b1 - t0 - CH), tid);
-
-    // ---------------- S-dependent products for this wave's 16 columns
-    bf16x8 sh[4], sl[4];
+    f32x4 R[4], QS[4];
+    {
+      bf16x8 sh[4], sl[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) frag_acc_split(S[2 * m], S[2 * m + 1], sh[m], sl[m]);
-
-    // R = V - diag(e^gamma / |k|) K S
-    f32x4 R[4];
+      for (int m = 0; m < 4; ++m) frag_acc_split(S[2 * m], S[2 * m + 1], sh[m], sl[m]);
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      bf16x8 ak[4];
+      for (int I = 0; I < 4; ++I) {
+        bf16x8 ak[4], aq[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) ak[m] = frag_rows(sm.kh, KS_STRIDE, 16 * I, 32 * m, lane);
-      f32x4 ks = {0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 4; ++m) {
+          ak[m] = frag_rows(s_kh, KS_STRIDE, 16 * I, 32 * m, lane);
+          aq[m] = frag_rows(s_qh, KS_STRIDE, 16 * I, 32 * m, lane);
+        }
+        f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        ks = mma(ak[m], sh[m], ks);
-        ks = mma(ak[m], sl[m], ks);
-        if constexpr (F32) ks = mma(frag_rows(sm.kl, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], ks);
+        for (int m = 0; m < 4; ++m) {
+          ks = mma(ak[m], sh[m], ks);
+          qs = mma(aq[m], sh[m], qs);
+          ks = mma(ak[m], sl[m], ks);
+          qs = mma(aq[m], sl[m], qs);
+          if constexpr (F32) {
+            ks = mma(frag_rows(s_kl, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], ks);
+            qs = mma(frag_rows(s_ql, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], qs);
+          }
+        }
+        const float4 cq = *reinterpret_cast<const float4*>(&s_fac[CH + 16 * I + 4 * g4]);
+        QS[I][0] = cq.x * qs[0];
+        QS[I][1] = cq.y * qs[1];
+        QS[I][2] = cq.z * qs[2];
+        QS[I][3] = cq.w * qs[3];
+        const float4 c4 = *reinterpret_cast<const float4*>(&s_fac[16 * I + 4 * g4]);
+        R[I][0] = vr[I][0] - c4.x * ks[0];
+        R[I][1] = vr[I][1] - c4.y * ks[1];
+        R[I][2] = vr[I][2] - c4.z * ks[2];
+        R[I][3] = vr[I][3] - c4.w * ks[3];
       }
-      const float4 c4 = *reinterpret_cast<const float4*>(&sm.fac[16 * I + 4 * g4]);
-      R[I][0] = vr[I][0] - c4.x * ks[0];
-      R[I][1] = vr[I][1] - c4.y * ks[1];
-      R[I][2] = vr[I][2] - c4.z * ks[2];
-      R[I][3] = vr[I][3] - c4.w * ks[3];
     }
-
     // U = T' R   (T' lower triangular: row tile I needs token slabs 0 .. I/2)
     f32x4 U[4];
     {
       bf16x8 rh[2], rl[2];
       frag_acc_split(R[0], R[1], rh[0], rl[0]);
       frag_acc_split(R[2], R[3], rh[1], rl[1]);
+      const u16* th = s_tp;
+      const u16* tl = s_tp + CH * T_STRIDE;
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         U[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m <= I / 2; ++m) {
-          const bf16x8 ah = frag_rows(sm.th, T_STRIDE, 16 * I, 32 * m, lane);
-          const bf16x8 al = frag_rows(sm.tl, T_STRIDE, 16 * I, 32 * m, lane);
+          const bf16x8 ah = frag_rows(th, T_STRIDE, 16 * I, 32 * m, lane);
+          const bf16x8 al = frag_rows(tl, T_STRIDE, 16 * I, 32 * m, lane);
           U[I] = mma(ah, rh[m], U[I]);
           U[I] = mma(al, rh[m], U[I]);
           U[I] = mma(ah, rl[m], U[I]);
         }
       }
     }
-
-    // O = scale (diag(e^gamma / |q|) Q S + P U)
-    {
-      bf16x8 uh[2], ul[2];
-      frag_acc_split(U[0], U[1], uh[0], ul[0]);
-      frag_acc_split(U[2], U[3], uh[1], ul[1]);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        bf16x8 aq[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) aq[m] = frag_rows(sm.qh, KS_STRIDE, 16 * I, 32 * m, lane);
-        f32x4 qs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          qs = mma(aq[m], sh[m], qs);
-          qs = mma(aq[m], sl[m], qs);
-          if constexpr (F32) qs = mma(frag_rows(sm.ql, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], qs);
-        }
-        f32x4 pu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m <= I / 2; ++m) {
-          const bf16x8 ah = frag_rows(sm.ph, T_STRIDE, 16 * I, 32 * m, lane);
-          const bf16x8 al = frag_rows(sm.pl, T_STRIDE, 16 * I, 32 * m, lane);
-          pu = mma(ah, uh[m], pu);
-          pu = mma(al, uh[m], pu);
-          pu = mma(ah, ul[m], pu);
-        }
-        const float4 c4 = *reinterpret_cast<const float4*>(&sm.fac[CH + 16 * I + 4 * g4]);
-        const float cqv[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * I + 4 * g4 + e;
-          if (t < L) io::st(og, (t0 + t) * o_stride, p.scale * (cqv[e] * qs[e] + pu[e]));
-        }
-      }
-    }
-
-    // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U
+    // the state update's right operand diag(e^{gamma_L - gamma} / |k|) U, and e^{gamma_L}:
+    // every factor is read in phase A, since the next chunk's factors land in phase B
+    bf16x8 wh[2], wl[2];
+    const float egl = s_fac[3 * CH];
     {
       f32x4 Us[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        const float4 c4 = *reinterpret_cast<const float4*>(&sm.fac[2 * CH + 16 * I + 4 * g4]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&s_fac[2 * CH + 16 * I + 4 * g4]);
         Us[I][0] = c4.x * U[I][0];
         Us[I][1] = c4.y * U[I][1];
         Us[I][2] = c4.z * U[I][2];
         Us[I][3] = c4.w * U[I][3];
       }
+      frag_acc_split(Us[0], Us[1], wh[0], wl[0]);
+      frag_acc_split(Us[2], Us[3], wh[1], wl[1]);
+    }
+
+    wait_vmem();
+    __syncthreads();       // phase-B operands of chunk n are in LDS; phase A of n is done
+    if (n + 1 < nch) stage_a(n + 1);
+    if constexpr (!F32) {
+      if (n > 0) store_o(n - 1);
+    }
+
+    // ================= phase B: O = scale (diag(e^g/|q|) Q S + P U); state update
+    {
       bf16x8 uh[2], ul[2];
-      frag_acc_split(Us[0], Us[1], uh[0], ul[0]);
-      frag_acc_split(Us[2], Us[3], uh[1], ul[1]);
-      const float egl = sm.fac[3 * CH];
+      frag_acc_split(U[0], U[1], uh[0], ul[0]);
+      frag_acc_split(U[2], U[3], uh[1], ul[1]);
+      const u16* ph = s_pp;
+      const u16* pl = s_pp + CH * T_STRIDE;
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m <= I / 2; ++m) {
+          const bf16x8 ah = frag_rows(ph, T_STRIDE, 16 * I, 32 * m, lane);
+          const bf16x8 al = frag_rows(pl, T_STRIDE, 16 * I, 32 * m, lane);
+          pu = mma(ah, uh[m], pu);
+          pu = mma(al, uh[m], pu);
+          pu = mma(ah, ul[m], pu);
+        }
+        float ov[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = p.scale * (QS[I][e] + pu[e]);
+        if constexpr (F32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * I + 4 * g4 + e;
+            if (t < L) io::st(og, (t0 + t) * o_stride, ov[e]);
+          }
+        } else {
+          opk[I][0] = cvt2(ov[0], ov[1]);
+          opk[I][1] = cvt2(ov[2], ov[3]);
+        }
+      }
+    }
+    // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U
+    {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         bf16x8 ak[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) ak[m] = frag_rows(sm.kth, KT_STRIDE, 16 * i, 32 * m, lane);
+        for (int m = 0; m < 2; ++m) ak[m] = frag_rows(s_kth, KT_STRIDE, 16 * i, 32 * m, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[i][e] *= egl;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          S[i] = mma(ak[m], uh[m], S[i]);
-          S[i] = mma(ak[m], ul[m], S[i]);
-          if constexpr (F32) S[i] = mma(frag_rows(sm.ktl, KT_STRIDE, 16 * i, 32 * m, lane), uh[m], S[i]);
+          S[i] = mma(ak[m], wh[m], S[i]);
+          S[i] = mma(ak[m], wl[m], S[i]);
+          if constexpr (F32) S[i] = mma(frag_rows(s_ktl, KT_STRIDE, 16 * i, 32 * m, lane), wh[m], S[i]);
         }
       }
     }
-    __syncthreads();  // the next chunk overwrites the LDS tiles
+  }
+  if constexpr (!F32) {
+    if (nch > 0) {
+      __syncthreads();     // every wave has read the tile of chunk nch-2
+      write_ost();
+      __syncthreads();
+      store_o(nch - 1);
+    }
   }
 
   if (p.state_out) {
@@ -839,21 +945,22 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 
 template <int IO>
 static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
+  const int64_t cmax = ws_max_chunks(a.N, a.Ns);
   int32_t* cmap = reinterpret_cast<int32_t*>(ws);
   uint8_t* recs = reinterpret_cast<uint8_t*>(ws) + ws_map_bytes(a.Ns);
+  uint8_t* krecs = recs + cmax * a.Hv * WS_REC_BYTES;
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, st, a.cu, a.Ns, a.N, cmap);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t cmax = ws_max_chunks(a.N, a.Ns);
   if (a.N > 0) {
     hipLaunchKernelGGL(chunk_prep_kernel<IO>, dim3((unsigned)cmax, (unsigned)a.Hv), dim3(NTHR), 0,
-                       st, a, (const int32_t*)cmap, recs);
+                       st, a, (const int32_t*)cmap, recs, krecs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t blocks = (int64_t)a.Ns * a.Hv * NBLK;
   hipLaunchKernelGGL(chunk_sweep_kernel<IO>, dim3((unsigned)blocks), dim3(NTHR), 0, st, a,
-                     (const int32_t*)cmap, (const uint8_t*)recs);
+                     (const int32_t*)cmap, (const uint8_t*)recs, (const uint8_t*)krecs);
   return hipGetLastError();
 }
 

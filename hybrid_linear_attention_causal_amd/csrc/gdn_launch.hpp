@@ -70,7 +70,7 @@ struct NormArgs {
 
 hipError_t launch_conv1d(const ConvArgs& a, int io, hipStream_t s);
 // device workspace of the chunked prefill (chunk map + per (chunk, head) records)
-size_t chunk_workspace_bytes(int64_t N, int Ns, int Hv);
+size_t chunk_workspace_bytes(int64_t N, int Ns, int Hk, int Hv, bool f32);
 hipError_t launch_chunk_prefill(const ChunkArgs& a, void* ws, int io, hipStream_t s);
 hipError_t launch_recurrent_step(const StepArgs& a, int io, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, int io, hipStream_t s);

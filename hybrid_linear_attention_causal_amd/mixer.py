@@ -41,7 +41,7 @@ def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens
     if s_out is None and want_states:
         s_out = torch.empty((Ns, Hv, D, D), dtype=torch.float32, device=dev)
     ws = bufs.get("workspace")
-    need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv)
+    need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, io=dt)
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         bufs["workspace"] = ws
