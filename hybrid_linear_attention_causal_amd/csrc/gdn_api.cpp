@@ -114,9 +114,11 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
   if ((int64_t)Ns * Hv * 2 > 0x7fffffffLL)
     return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: too many (sequence, head) pairs");
   if (stride_q < (int64_t)Hk * dk || stride_k < (int64_t)Hk * dk || stride_v < (int64_t)Hv * dv ||
-      stride_q % 8 || stride_k % 8 || stride_v % 8)
+      stride_q % 8 || stride_k % 8 || stride_v % 8 || stride_q > GDN_MAX_ROW_STRIDE ||
+      stride_k > GDN_MAX_ROW_STRIDE || stride_v > GDN_MAX_ROW_STRIDE)
     return fail(GDN_ERR_INVALID_ARG,
-                "chunk_prefill: strides must cover a row and be multiples of 8 (q %lld k %lld v %lld)",
+                "chunk_prefill: strides must cover a row, be multiples of 8 and at most 2^20 "
+                "(q %lld k %lld v %lld)",
                 (long long)stride_q, (long long)stride_k, (long long)stride_v);
   const bool have_g = g_opt != nullptr, have_b = beta_opt != nullptr;
   if (have_g != have_b)

@@ -53,6 +53,7 @@ constexpr int KT_STRIDE = CH + 8;      // u16 per staged K^T row
 constexpr int T_STRIDE = CH + 8;       // u16 per staged T'/P row
 constexpr int F_STRIDE = CH + 4;       // floats per A/T row
 constexpr int O_STRIDE = DVB + 8;      // u16 per staged output row (bf16 io)
+constexpr int V_STRIDE = DVB + 8;      // u16 per staged V row (bf16 io)
 
 // Workspace (all LDS-ready, so the sweep stages operands with plain DMA copies):
 //   chunk offsets: int32 [Ns + 1], padded to 256 bytes;
@@ -597,32 +598,56 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Copy nslots 16-byte words from a linear global source into linear LDS with the
-// LDS DMA path (global_load_lds_dwordx4: lane l's word lands at dst + 16 l); the
-// workgroup's waves take turns by instruction.
-__device__ __forceinline__ void dma_linear(const uint8_t* src, void* dst, int nslots, int wave,
-                                           int lane) {
-  for (int ins = wave; ins * 64 < nslots; ins += NTHR / 64) {
-    const int sl = ins * 64 + lane;
-    if (sl < nslots)
-      __builtin_amdgcn_global_load_lds(src + (int64_t)sl * 16,
-                                       (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
+// LDS DMA path (global_load_lds_dwordx4: lane l's word lands at dst + 16 l).  Sources
+// are a wave-uniform base plus a 32-bit per-lane offset, the LDS destination (M0) is
+// scalar, and the workgroup's four waves take turns by instruction.  Every wave issues
+// the same number of copies (a wave past the last instruction repeats it, writing the
+// same bytes again), so a piece is straight-line code that stays where it is placed.
+template <int NS>   // 16-byte slots, a multiple of 64
+__device__ __forceinline__ void dma_linear(const uint8_t* src, void* dst, int wave, int lane) {
+  static_assert(NS % 64 == 0, "whole instructions only");
+  constexpr int INS = NS / 64;
+#pragma unroll
+  for (int j = 0; j < (INS + 3) / 4; ++j) {
+    const int ins = min(wave + 4 * j, INS - 1);
+    __builtin_amdgcn_global_load_lds(src + ins * 1024 + lane * 16,
+                                     (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
   }
 }
 
-// K or Q rows of one chunk from the packed input into LDS rows padded to KS_STRIDE:
-// 17 words per row (word 16 is padding); rows past the chunk end repeat the last
-// valid row, which the chunk algebra multiplies by zero.
-template <typename T>
-__device__ __forceinline__ void dma_rows(const T* base, int64_t stride, int64_t t0, int L,
-                                         u16* dst, int wave, int lane) {
-  constexpr int WPR = KS_STRIDE * 2 / 16;      // 17 words per staged row
-  constexpr int NSL = CH * WPR;                // 1088
-  for (int ins = wave; ins * 64 < NSL; ins += NTHR / 64) {
-    const int sl = ins * 64 + lane;
-    const int row = sl / WPR, w = sl - row * WPR;
-    const int64_t r = t0 + (row < L ? row : L - 1);
-    const T* src = base + r * stride + (w < 16 ? w : 15) * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
+// Staged-row DMA: a chunk's 64 rows of DW 16-byte words each land in LDS rows of
+// DW + 1 words (the extra word pads the row against bank conflicts and re-reads the
+// last data word); slot = 64 ins + lane with ins = min(wave + 4 j, INS - 1).  The table
+// packs each slot's row (bits 0..7) and the source byte offset of its word (bits 8..).
+template <int DW>
+struct RowDma {
+  static constexpr int INS = CH * (DW + 1) / 64;               // instructions per block
+  static constexpr int J = (INS + NTHR / 64 - 1) / (NTHR / 64);  // per wave, rounded up
+};
+
+template <int DW>
+__device__ __forceinline__ void rows_table(int wave, int lane, uint32_t (&tab)[RowDma<DW>::J]) {
+#pragma unroll
+  for (int j = 0; j < RowDma<DW>::J; ++j) {
+    const int sl = min(wave + 4 * j, RowDma<DW>::INS - 1) * 64 + lane;
+    const int row = sl / (DW + 1), w = sl - row * (DW + 1);
+    tab[j] = (uint32_t)row | ((uint32_t)((w < DW ? w : DW - 1) * 16) << 8);
+  }
+}
+
+// rows t0 .. t0+63 of one chunk into LDS; rows past the chunk end (L valid rows) repeat
+// the last valid row, which the chunk algebra multiplies by zero.  base = the chunk's
+// first row (wave-uniform), row_bytes < 2^24.
+template <int DW>
+__device__ __forceinline__ void dma_rows(const uint8_t* base, uint32_t row_bytes, int L,
+                                         const uint32_t (&tab)[RowDma<DW>::J], void* dst,
+                                         int wave) {
+#pragma unroll
+  for (int j = 0; j < RowDma<DW>::J; ++j) {
+    const int ins = min(wave + 4 * j, RowDma<DW>::INS - 1);
+    const uint32_t row = min(tab[j] & 0xFFu, (uint32_t)(L - 1));
+    const uint32_t off = __umul24(row, row_bytes) + (tab[j] >> 8);
+    __builtin_amdgcn_global_load_lds(base + off, (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
   }
 }
 
@@ -640,6 +665,7 @@ struct SweepSizes {
   static constexpr int KT_LO = F32 ? KT : 8;
   static constexpr int PL2 = 2 * CH * T_STRIDE;        // a hi|lo plane pair (u16)
   static constexpr int OST = F32 ? 8 : CH * O_STRIDE;
+  static constexpr int VST = F32 ? 8 : CH * V_STRIDE;
 };
 
 template <int IO>
@@ -659,7 +685,8 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   __shared__ __attribute__((aligned(16))) u16 s_kth[Z::KT];     // K^T                 phase B
   __shared__ __attribute__((aligned(16))) u16 s_ktl[Z::KT_LO];
   __shared__ __attribute__((aligned(16))) float s_fac[4 * CH];  // per-token factors    phase A
-  __shared__ __attribute__((aligned(16))) u16 s_ost[Z::OST];    // output tiles (bf16 io)
+  __shared__ __attribute__((aligned(16))) u16 s_ost[Z::OST];    // output tile (bf16 io)
+  __shared__ __attribute__((aligned(16))) u16 s_v[Z::VST];      // V slice (bf16 io)   phase A
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -682,7 +709,6 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 
   const T* qg = (const T*)p.q + (int64_t)kh * DK;
   const T* kg = (const T*)p.k + (int64_t)kh * DK;
-  const T* vg = (const T*)p.v + (int64_t)h * DV + col;
   T* og = (T*)p.o + (int64_t)h * DV + col;
   T* og0 = (T*)p.o + (int64_t)h * DV + blk * DVB;   // this workgroup's output columns
   const int64_t o_stride = (int64_t)Hv * DV;
@@ -702,44 +728,74 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     for (int i = 0; i < 8; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // phase-A operands of chunk n (K, Q rows, T' planes, factors) and its V slice
-  T vraw[4][4];
-  auto stage_a = [&](int n) {
+  // Operands of chunk n, copied in pieces so that the copies issue between the
+  // matrix products of the other phase.  Phase A (K, Q rows, T' planes, factors, the
+  // V slice) lands while the previous chunk's phase B runs, phase B (P planes, K^T)
+  // while chunk n's phase A runs.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t ktab[RowDma<16>::J], vtab[RowDma<8>::J];
+  rows_table<16>(wave_u, lane, ktab);
+  rows_table<8>(wave_u, lane, vtab);
+  const uint32_t qrow_bytes = (uint32_t)(p.stride_q * (int64_t)sizeof(T));
+  const uint32_t krow_bytes = (uint32_t)(p.stride_k * (int64_t)sizeof(T));
+  const uint32_t vrow_bytes = (uint32_t)(p.stride_v * (int64_t)sizeof(T));
+  const uint8_t* vg0 = (const uint8_t*)p.v + ((int64_t)h * DV + blk * DVB) * sizeof(T);
+  const uint32_t vcol = (uint32_t)((wave * 16 + c16) * sizeof(T));
+  T vraw[4][4];   // fp32 io: the V slice goes through registers
+  // (sched_barrier keeps the instruction scheduler from sinking a piece past the
+  // products it is meant to overlap)
+  auto stage_a = [&](int n, int part) {
+    __builtin_amdgcn_sched_barrier(0);
     const int64_t t0 = b0 + (int64_t)n * CH;
     const int L = (int)min((int64_t)CH, b1 - t0);
     const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * WS_REC_BYTES;
-    if constexpr (F32) {
-      const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
-      dma_linear(krec, s_kh, (int)(WS_ROWS_BYTES / 16), wave, lane);
-      dma_linear(krec + WS_ROWS_BYTES, s_kl, (int)(WS_ROWS_BYTES / 16), wave, lane);
-      dma_linear(krec + 2 * WS_ROWS_BYTES, s_qh, (int)(WS_ROWS_BYTES / 16), wave, lane);
-      dma_linear(krec + 3 * WS_ROWS_BYTES, s_ql, (int)(WS_ROWS_BYTES / 16), wave, lane);
-    } else {
-      dma_rows(kg, p.stride_k, t0, L, s_kh, wave, lane);
-      dma_rows(qg, p.stride_q, t0, L, s_qh, wave, lane);
-    }
-    dma_linear(rec, s_tp, (int)(2 * WS_PL_BYTES / 16), wave, lane);
-    dma_linear(rec + WS_FAC_OFF, s_fac, 4 * CH * 4 / 16, wave, lane);
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * I + 4 * g4 + e;
-        vraw[I][e] = vg[(t0 + (t < L ? t : L - 1)) * p.stride_v];
+    const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
+    if (part == 0) {
+      if constexpr (F32) {
+        dma_linear<(WS_ROWS_BYTES) / 16>(krec, s_kh, wave_u, lane);
+        dma_linear<(WS_ROWS_BYTES) / 16>(krec + WS_ROWS_BYTES, s_kl, wave_u, lane);
+      } else {
+        dma_rows<16>((const uint8_t*)kg + t0 * krow_bytes, krow_bytes, L, ktab, s_kh, wave_u);
       }
+    } else if (part == 1) {
+      if constexpr (F32) {
+        dma_linear<(WS_ROWS_BYTES) / 16>(krec + 2 * WS_ROWS_BYTES, s_qh, wave_u, lane);
+        dma_linear<(WS_ROWS_BYTES) / 16>(krec + 3 * WS_ROWS_BYTES, s_ql, wave_u, lane);
+      } else {
+        dma_rows<16>((const uint8_t*)qg + t0 * qrow_bytes, qrow_bytes, L, ktab, s_qh, wave_u);
+      }
+    } else if (part == 2) {
+      dma_linear<(2 * WS_PL_BYTES) / 16>(rec, s_tp, wave_u, lane);
+      dma_linear<4 * CH * 4 / 16>(rec + WS_FAC_OFF, s_fac, wave_u, lane);
+    } else {
+      const uint8_t* vb = vg0 + t0 * vrow_bytes;
+      if constexpr (F32) {
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t t = (uint32_t)min(16 * I + 4 * g4 + e, L - 1);
+            vraw[I][e] = *(const T*)(vb + (__umul24(t, vrow_bytes) + vcol));
+          }
+      } else {
+        dma_rows<8>(vb, vrow_bytes, L, vtab, s_v, wave_u);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // phase-B operands of chunk n (P planes, K^T)
-  auto stage_b = [&](int n) {
+  auto stage_b = [&](int n, int part) {
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * WS_REC_BYTES;
     const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
-    dma_linear(rec + 2 * WS_PL_BYTES, s_pp, (int)(2 * WS_PL_BYTES / 16), wave, lane);
-    if constexpr (F32) {
-      dma_linear(krec + 4 * WS_ROWS_BYTES, s_kth, (int)(WS_KT_BYTES / 16), wave, lane);
-      dma_linear(krec + 4 * WS_ROWS_BYTES + WS_KT_BYTES, s_ktl, (int)(WS_KT_BYTES / 16), wave,
-                 lane);
+    if (part == 0) {
+      dma_linear<(2 * WS_PL_BYTES) / 16>(rec + 2 * WS_PL_BYTES, s_pp, wave_u, lane);
+    } else if constexpr (F32) {
+      dma_linear<(WS_KT_BYTES) / 16>(krec + 4 * WS_ROWS_BYTES, s_kth, wave_u, lane);
+      dma_linear<(WS_KT_BYTES) / 16>(krec + 4 * WS_ROWS_BYTES + WS_KT_BYTES, s_ktl, wave_u, lane);
     } else {
-      dma_linear(krec, s_kth, (int)(WS_KT_BYTES / 16), wave, lane);
+      dma_linear<(WS_KT_BYTES) / 16>(krec, s_kth, wave_u, lane);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   // bf16 io: a chunk's output stays in registers (packed pairs of rows) through the
   // next chunk boundary, is written to the LDS tile there while no DMA is in flight
@@ -770,7 +826,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     }
   };
 
-  if (nch > 0) stage_a(0);
+  if (nch > 0) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) stage_a(0, part);
+  }
 
   for (int n = 0; n < nch; ++n) {
     const int64_t t0 = b0 + (int64_t)n * CH;
@@ -781,15 +840,19 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     if constexpr (!F32) {
       if (n > 0) write_ost();
     }
-    stage_b(n);
+    stage_b(n, 0);
 
     // ================= phase A: K S and Q S (S hi/lo), R, U = T' R
     float vr[4][4];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vr[I][e] = (16 * I + 4 * g4 + e < L) ? io::ld(&vraw[I][e], 0) : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * g4 + e;
+        // rows past the chunk end hold copies of its last row: read, then zero
+        const float x = F32 ? (float)vraw[I][e] : bf2f(s_v[t * V_STRIDE + wave * 16 + c16]);
+        vr[I][e] = t < L ? x : 0.f;
+      }
 
     f32x4 R[4], QS[4];
     {
@@ -826,6 +889,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
         R[I][1] = vr[I][1] - c4.y * ks[1];
         R[I][2] = vr[I][2] - c4.z * ks[2];
         R[I][3] = vr[I][3] - c4.w * ks[3];
+        if (I == 1) stage_b(n, 1);
       }
     }
     // U = T' R   (T' lower triangular: row tile I needs token slabs 0 .. I/2)
@@ -869,7 +933,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 
     wait_vmem();
     __syncthreads();       // phase-B operands of chunk n are in LDS; phase A of n is done
-    if (n + 1 < nch) stage_a(n + 1);
+    // the last chunk reloads its own phase-A operands (unread in phase B) so that the
+    // copies stay unconditional and keep their places between the products
+    const int na = n + 1 < nch ? n + 1 : n;
+    stage_a(na, 0);
     if constexpr (!F32) {
       if (n > 0) store_o(n - 1);
     }
@@ -905,8 +972,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
           opk[I][0] = cvt2(ov[0], ov[1]);
           opk[I][1] = cvt2(ov[2], ov[3]);
         }
+        if (I == 1) stage_a(na, 1);
       }
     }
+    stage_a(na, 2);
     // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U
     {
 #pragma unroll
@@ -922,6 +991,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
           S[i] = mma(ak[m], wl[m], S[i]);
           if constexpr (F32) S[i] = mma(frag_rows(s_ktl, KT_STRIDE, 16 * i, 32 * m, lane), wh[m], S[i]);
         }
+        if (i == 3) stage_a(na, 3);
       }
     }
   }

@@ -64,6 +64,10 @@ typedef enum {
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
 
+/* Largest row stride, in elements, that gdn_chunk_prefill accepts for q, k, v
+ * (the kernels address a chunk's rows with 24-bit row offsets). */
+#define GDN_MAX_ROW_STRIDE (1LL << 20)
+
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char* gdn_last_error(void);
 
@@ -126,8 +130,8 @@ size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d
  *                   head-major (head kh at offset kh*dk)                  io
  *   v               row t at v + t*stride_v: Hv*dv values, head-major      io
  *                   (q, k, v are normally views into gdn_conv1d_fwd's y with
- *                   stride Cq; strides are in elements, >= the row width, and
- *                   multiples of 8)
+ *                   stride Cq; strides are in elements, >= the row width,
+ *                   multiples of 8 and at most GDN_MAX_ROW_STRIDE)
  *   a, b            [N, Hv]                io   (ignored when g_opt, beta_opt given)
  *   A_log, dt_bias  [Hv]                   fp32 (ignored when g_opt, beta_opt given)
  *   g_opt, beta_opt [N, Hv]                fp32 log-decay and write strength, or NULL
@@ -140,7 +144,8 @@ size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d
  *                   gdn_chunk_prefill_workspace_size() bytes, owned by the caller;
  *                   its contents need no initialisation and are scratch
  * Errors: dk != 128 or dv != 128 -> UNSUPPORTED; Hk < 1, Hv % Hk != 0, Ns < 1,
- * N < 0, a stride below its row width or not a multiple of 8, NULL required
+ * N < 0, a stride below its row width, above GDN_MAX_ROW_STRIDE or not a
+ * multiple of 8, NULL required
  * pointers, a missing, unaligned or too small workspace -> INVALID_ARG.
  */
 gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int64_t stride_q,

@@ -82,6 +82,7 @@ def test_prefill_rejects():
     assert _prefill(Ns=3) == _lib.GDN_ERR_INVALID_ARG
     assert _prefill(sq=100) == _lib.GDN_ERR_INVALID_ARG
     assert _prefill(sv=4100) == _lib.GDN_ERR_INVALID_ARG
+    assert _prefill(sk=(1 << 20) + 8) == _lib.GDN_ERR_INVALID_ARG
     assert _prefill(g=P) == _lib.GDN_ERR_INVALID_ARG
     assert "both" in _msg()
     assert _prefill(o=None) == _lib.GDN_ERR_INVALID_ARG
