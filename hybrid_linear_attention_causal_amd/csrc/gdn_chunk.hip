@@ -83,6 +83,25 @@ __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16 x 16 fp32 tile X Y (X: 16 x K, Y: K x 16, both row-major fp32 in LDS) on the fp32
+// MFMA: step s takes lane l's X[l % 16][4 s + l / 16] and Y[4 s + l / 16][l % 16]; the
+// result is in accumulator layout (lane l: rows 4 (l / 16) + e, column l % 16).
+template <int K>
+__device__ __forceinline__ f32x4 tile_mma_f32(const float* x, int sx, const float* y, int sy,
+                                              int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  float xa[K / 4], yb[K / 4];
+#pragma unroll
+  for (int st = 0; st < K / 4; ++st) {
+    xa[st] = x[r * sx + 4 * st + g];
+    yb[st] = y[(4 * st + g) * sy + r];
+  }
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < K / 4; ++st) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[st], yb[st], c, 0, 0, 0);
+  return c;
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // two fp32 -> packed bf16 pair (hardware round-to-nearest-even)
@@ -228,17 +247,18 @@ __global__ void __launch_bounds__(256) chunk_map_kernel(const int32_t* cu, int N
 template <int IO>
 struct PrepSmem {
   static constexpr bool F32 = (IO == IO_F32);
-  u16 kh[CH * KS_STRIDE];                 // K rows (bf16 / hi part)
-  u16 kl[F32 ? CH * KS_STRIDE : 2];
-  u16 qh[CH * KS_STRIDE];
-  u16 ql[F32 ? CH * KS_STRIDE : 2];
-  float af[CH * F_STRIDE];                // strictly lower A (fp32)
-  float tf[CH * F_STRIDE];                // T (fp32); first holds the staged P planes
-  float msc[32 * 36];                     // block scratch of the solve
-  float gam[CH];                          // in-chunk cumulative log decay
-  float beta[CH];
-  float rnk[CH];                          // 1/|k_t| (1 without the L2 norm)
-  float rnq[CH];
+  // every member a multiple of 16 bytes, so that vector LDS accesses stay aligned
+  alignas(16) u16 kh[CH * KS_STRIDE];                 // K rows (bf16 / hi part)
+  alignas(16) u16 kl[F32 ? CH * KS_STRIDE : 8];
+  alignas(16) u16 qh[CH * KS_STRIDE];
+  alignas(16) u16 ql[F32 ? CH * KS_STRIDE : 8];
+  alignas(16) float af[CH * F_STRIDE];                // strictly lower A (fp32)
+  alignas(16) float tf[CH * F_STRIDE];                // T (fp32); first holds the staged P planes
+  alignas(16) float msc[32 * 36];                     // block products of the solve
+  alignas(16) float gam[CH];                          // in-chunk cumulative log decay
+  alignas(16) float beta[CH];
+  alignas(16) float rnk[CH];                          // 1/|k_t| (1 without the L2 norm)
+  alignas(16) float rnq[CH];
 };
 
 template <int IO>
@@ -392,10 +412,10 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
         pst[CH * CH + i * CH + j] = (u16)pl;
       }
     } else {
-      const int Is[6] = {0, 0, 0, 1, 1, 2};
-      const int Js[6] = {1, 2, 3, 2, 3, 3};
-      I = Is[n - 10];
-      J = Js[n - 10];
+      // strictly-upper tiles (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+      const int m = n - 10;
+      I = (m >= 5) ? 2 : (m >= 3) ? 1 : 0;
+      J = m - (I == 0 ? 0 : I == 1 ? 3 : 5) + I + 1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * I + 4 * g4 + e, j = 16 * J + c16;
@@ -477,98 +497,34 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
     for (int i = 0; i < 16; ++i) sm.tf[(16 * wave + i) * F_STRIDE + 16 * wave + 16 + c16] = 0.f;
   }
   __syncthreads();
-  {
-    // blocks (1,0) (waves 0,1) and (3,2) (waves 2,3): 2 outputs per lane
-    const int bb = wave >> 1;
-    const int I = 2 * bb + 1, J = 2 * bb;
-    const int li = ((wave & 1) << 6) | lane;   // 0..127
-    const int ri = li >> 3;                    // row 0..15
-    const int cj = 2 * (li & 7);               // columns cj, cj+1
-    float* msc = sm.msc + bb * (16 * 20);
-    {
-      const float* arow = &sm.af[(16 * I + ri) * F_STRIDE + 16 * J];
-      float a[16];
-      float2 tv[16];
+  // blocks (1,0) (wave 0) and (3,2) (wave 1): T_IJ = -T_II (A_IJ T_JJ), 16 x 16 fp32
+  // MFMA products; the intermediate goes through a wave-private LDS tile
+  if (wave < 2) {
+    const int I = 2 * wave + 1, J = 2 * wave;
+    float* mt = sm.msc + wave * (16 * 20);
+    f32x4 m = tile_mma_f32<16>(&sm.af[16 * I * F_STRIDE + 16 * J], F_STRIDE,
+                               &sm.tf[16 * J * F_STRIDE + 16 * J], F_STRIDE, lane);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(arow + 4 * q4);
-        a[4 * q4] = t4.x; a[4 * q4 + 1] = t4.y; a[4 * q4 + 2] = t4.z; a[4 * q4 + 3] = t4.w;
-      }
+    for (int e = 0; e < 4; ++e) mt[(4 * g4 + e) * 20 + c16] = m[e];
+    const f32x4 t = tile_mma_f32<16>(&sm.tf[16 * I * F_STRIDE + 16 * I], F_STRIDE, mt, 20, lane);
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        tv[k] = *reinterpret_cast<const float2*>(&sm.tf[(16 * J + k) * F_STRIDE + 16 * J + cj]);
-      float2 m2 = make_float2(0.f, 0.f);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        m2.x = fmaf(a[k], tv[k].x, m2.x);
-        m2.y = fmaf(a[k], tv[k].y, m2.y);
-      }
-      *reinterpret_cast<float2*>(&msc[ri * 20 + cj]) = m2;
-    }
-    __syncthreads();
-    {
-      const float* trow = &sm.tf[(16 * I + ri) * F_STRIDE + 16 * I];
-      float tr[16];
-      float2 mv[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(trow + 4 * q4);
-        tr[4 * q4] = t4.x; tr[4 * q4 + 1] = t4.y; tr[4 * q4 + 2] = t4.z; tr[4 * q4 + 3] = t4.w;
-      }
-#pragma unroll
-      for (int k = 0; k < 16; ++k) mv[k] = *reinterpret_cast<const float2*>(&msc[k * 20 + cj]);
-      float2 t2 = make_float2(0.f, 0.f);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        t2.x = fmaf(-tr[k], mv[k].x, t2.x);
-        t2.y = fmaf(-tr[k], mv[k].y, t2.y);
-      }
-      *reinterpret_cast<float2*>(&sm.tf[(16 * I + ri) * F_STRIDE + 16 * J + cj]) = t2;
-    }
-    __syncthreads();
+    for (int e = 0; e < 4; ++e) sm.tf[(16 * I + 4 * g4 + e) * F_STRIDE + 16 * J + c16] = -t[e];
   }
+  __syncthreads();
+  // lower 32 x 32 block: T[32:64, 0:32] = -T[32:64, 32:64] (A[32:64, 0:32] T[0:32, 0:32]),
+  // one 16 x 16 output tile per wave
   {
-    const int ri = tid >> 3;                   // row 0..31 of the block
-    const int cj = 4 * (tid & 7);              // columns cj .. cj+3
-    {
-      const float* arow = &sm.af[(32 + ri) * F_STRIDE];
-      float a[32];
+    const int ti = wave >> 1, tj = wave & 1;
+    const f32x4 m = tile_mma_f32<32>(&sm.af[(32 + 16 * ti) * F_STRIDE], F_STRIDE,
+                                     &sm.tf[16 * tj], F_STRIDE, lane);
 #pragma unroll
-      for (int q4 = 0; q4 < 8; ++q4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(arow + 4 * q4);
-        a[4 * q4] = t4.x; a[4 * q4 + 1] = t4.y; a[4 * q4 + 2] = t4.z; a[4 * q4 + 3] = t4.w;
-      }
-      float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const float4 tv = *reinterpret_cast<const float4*>(&sm.tf[k * F_STRIDE + cj]);
-        m4.x = fmaf(a[k], tv.x, m4.x);
-        m4.y = fmaf(a[k], tv.y, m4.y);
-        m4.z = fmaf(a[k], tv.z, m4.z);
-        m4.w = fmaf(a[k], tv.w, m4.w);
-      }
-      *reinterpret_cast<float4*>(&sm.msc[ri * 36 + cj]) = m4;
-    }
+    for (int e = 0; e < 4; ++e) sm.msc[(16 * ti + 4 * g4 + e) * 36 + 16 * tj + c16] = m[e];
     __syncthreads();
-    {
-      const float* trow = &sm.tf[(32 + ri) * F_STRIDE + 32];
-      float tr[32];
+    const f32x4 t = tile_mma_f32<32>(&sm.tf[(32 + 16 * ti) * F_STRIDE + 32], F_STRIDE,
+                                     &sm.msc[16 * tj], 36, lane);
 #pragma unroll
-      for (int q4 = 0; q4 < 8; ++q4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(trow + 4 * q4);
-        tr[4 * q4] = t4.x; tr[4 * q4 + 1] = t4.y; tr[4 * q4 + 2] = t4.z; tr[4 * q4 + 3] = t4.w;
-      }
-      float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const float4 mv = *reinterpret_cast<const float4*>(&sm.msc[k * 36 + cj]);
-        t4.x = fmaf(-tr[k], mv.x, t4.x);
-        t4.y = fmaf(-tr[k], mv.y, t4.y);
-        t4.z = fmaf(-tr[k], mv.z, t4.z);
-        t4.w = fmaf(-tr[k], mv.w, t4.w);
-      }
-      *reinterpret_cast<float4*>(&sm.tf[(32 + ri) * F_STRIDE + cj]) = t4;
-    }
+    for (int e = 0; e < 4; ++e)
+      sm.tf[(32 + 16 * ti + 4 * g4 + e) * F_STRIDE + 16 * tj + c16] = -t[e];
     __syncthreads();
   }
   // ---- T' = T diag(beta), lower triangle, as bf16 hi/lo planes straight to the
