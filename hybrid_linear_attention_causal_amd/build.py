@@ -27,7 +27,10 @@ def flags():
     return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
             "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
             # no packed-fp32 instructions (v_pk_*_f32) in device code
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in ordinary VGPRs: the kernels post-process every product
+            # with vector ALU work, which AGPR results would first have to copy out
+            "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def build(verbose: bool = False) -> str:

@@ -30,9 +30,11 @@ gdn_status_t hip_fail(hipError_t e, const char* what) {
 constexpr int kMaxDev = 64;
 std::mutex g_arch_mu;
 int g_arch_ok[kMaxDev];  // 0 unknown, 1 gfx950, -1 other
+int g_cus[kMaxDev];      // compute units of each checked device
 
-// The kernels are written for gfx950 only: refuse any other device.
-gdn_status_t check_device() {
+// The kernels are written for gfx950 only: refuse any other device.  cus (optional)
+// receives the current device's compute-unit count.
+gdn_status_t check_device(int* cus = nullptr) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -43,12 +45,14 @@ gdn_status_t check_device() {
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
     g_arch_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_cus[dev] = prop.multiProcessorCount;
     if (g_arch_ok[dev] < 0) {
       return fail(GDN_ERR_UNSUPPORTED, "device %d is %s; libgdn is built for gfx950 only", dev,
                   prop.gcnArchName);
     }
   }
   if (g_arch_ok[dev] < 0) return fail(GDN_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  if (cus) *cus = g_cus[dev];
   return GDN_OK;
 }
 
@@ -137,11 +141,12 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
   if ((N + 63) / 64 + Ns > 0x7fffffffLL)
     return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: too many chunks");
   if (scale <= 0.f) scale = 1.0f / sqrtf((float)dk);
-  gdn_status_t st = check_device();
+  int cus = 0;
+  gdn_status_t st = check_device(&cus);
   if (st != GDN_OK) return st;
   gdn::ChunkArgs args{q, k, v, stride_q, stride_k, stride_v, a, b, A_log, dt_bias, g_opt,
                       beta_opt, state_in, state_out, o, cu_seqlens, Ns, N, Hk, Hv, scale,
-                      use_qk_l2norm ? 1 : 0};
+                      use_qk_l2norm ? 1 : 0, cus};
   hipError_t e = gdn::launch_chunk_prefill(args, workspace,
                                            io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
                                            (hipStream_t)stream);

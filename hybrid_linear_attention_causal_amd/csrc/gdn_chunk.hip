@@ -45,15 +45,11 @@ namespace gdn {
 constexpr int CH = 64;                 // chunk length
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int DVB = 64;                // dv columns per sweep workgroup
-constexpr int NBLK = DV / DVB;
-constexpr int NTHR = 256;
+constexpr int NTHR = 256;              // prep workgroup
 constexpr int KS_STRIDE = DK + 8;      // u16 per staged K/Q row
 constexpr int KT_STRIDE = CH + 8;      // u16 per staged K^T row
 constexpr int T_STRIDE = CH + 8;       // u16 per staged T'/P row
 constexpr int F_STRIDE = CH + 4;       // floats per A/T row
-constexpr int O_STRIDE = DVB + 8;      // u16 per staged output row (bf16 io)
-constexpr int V_STRIDE = DVB + 8;      // u16 per staged V row (bf16 io)
 
 // Workspace (all LDS-ready, so the sweep stages operands with plain DMA copies):
 //   chunk offsets: int32 [Ns + 1], padded to 256 bytes;
@@ -556,16 +552,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Copy nslots 16-byte words from a linear global source into linear LDS with the
 // LDS DMA path (global_load_lds_dwordx4: lane l's word lands at dst + 16 l).  Sources
 // are a wave-uniform base plus a 32-bit per-lane offset, the LDS destination (M0) is
-// scalar, and the workgroup's four waves take turns by instruction.  Every wave issues
+// scalar, and the sweep workgroup's waves take turns by instruction.  Every wave issues
 // the same number of copies (a wave past the last instruction repeats it, writing the
 // same bytes again), so a piece is straight-line code that stays where it is placed.
-template <int NS>   // 16-byte slots, a multiple of 64
+template <int NS, int NW>   // 16-byte slots (a multiple of 64), waves taking turns
 __device__ __forceinline__ void dma_linear(const uint8_t* src, void* dst, int wave, int lane) {
   static_assert(NS % 64 == 0, "whole instructions only");
   constexpr int INS = NS / 64;
 #pragma unroll
-  for (int j = 0; j < (INS + 3) / 4; ++j) {
-    const int ins = min(wave + 4 * j, INS - 1);
+  for (int j = 0; j < (INS + NW - 1) / NW; ++j) {
+    const int ins = min(wave + NW * j, INS - 1);
     __builtin_amdgcn_global_load_lds(src + ins * 1024 + lane * 16,
                                      (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
   }
@@ -573,19 +569,20 @@ __device__ __forceinline__ void dma_linear(const uint8_t* src, void* dst, int wa
 
 // Staged-row DMA: a chunk's 64 rows of DW 16-byte words each land in LDS rows of
 // DW + 1 words (the extra word pads the row against bank conflicts and re-reads the
-// last data word); slot = 64 ins + lane with ins = min(wave + 4 j, INS - 1).  The table
+// last data word); slot = 64 ins + lane with ins = min(wave + NW j, INS - 1).  The table
 // packs each slot's row (bits 0..7) and the source byte offset of its word (bits 8..).
-template <int DW>
+template <int DW, int NW>
 struct RowDma {
-  static constexpr int INS = CH * (DW + 1) / 64;               // instructions per block
-  static constexpr int J = (INS + NTHR / 64 - 1) / (NTHR / 64);  // per wave, rounded up
+  static constexpr int INS = CH * (DW + 1) / 64;   // instructions per block
+  static constexpr int J = (INS + NW - 1) / NW;    // per wave, rounded up
 };
 
-template <int DW>
-__device__ __forceinline__ void rows_table(int wave, int lane, uint32_t (&tab)[RowDma<DW>::J]) {
+template <int DW, int NW>
+__device__ __forceinline__ void rows_table(int wave, int lane, uint32_t (&tab)[RowDma<DW, NW>::J]) {
+  typedef RowDma<DW, NW> R;
 #pragma unroll
-  for (int j = 0; j < RowDma<DW>::J; ++j) {
-    const int sl = min(wave + 4 * j, RowDma<DW>::INS - 1) * 64 + lane;
+  for (int j = 0; j < R::J; ++j) {
+    const int sl = min(wave + NW * j, R::INS - 1) * 64 + lane;
     const int row = sl / (DW + 1), w = sl - row * (DW + 1);
     tab[j] = (uint32_t)row | ((uint32_t)((w < DW ? w : DW - 1) * 16) << 8);
   }
@@ -594,13 +591,14 @@ __device__ __forceinline__ void rows_table(int wave, int lane, uint32_t (&tab)[R
 // rows t0 .. t0+63 of one chunk into LDS; rows past the chunk end (L valid rows) repeat
 // the last valid row, which the chunk algebra multiplies by zero.  base = the chunk's
 // first row (wave-uniform), row_bytes < 2^24.
-template <int DW>
+template <int DW, int NW>
 __device__ __forceinline__ void dma_rows(const uint8_t* base, uint32_t row_bytes, int L,
-                                         const uint32_t (&tab)[RowDma<DW>::J], void* dst,
+                                         const uint32_t (&tab)[RowDma<DW, NW>::J], void* dst,
                                          int wave) {
+  typedef RowDma<DW, NW> R;
 #pragma unroll
-  for (int j = 0; j < RowDma<DW>::J; ++j) {
-    const int ins = min(wave + 4 * j, RowDma<DW>::INS - 1);
+  for (int j = 0; j < R::J; ++j) {
+    const int ins = min(wave + NW * j, R::INS - 1);
     const uint32_t row = min(tab[j] & 0xFFu, (uint32_t)(L - 1));
     const uint32_t off = __umul24(row, row_bytes) + (tab[j] >> 8);
     __builtin_amdgcn_global_load_lds(base + off, (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
@@ -612,9 +610,14 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 // LDS buffers of the sweep, one __shared__ object each so that the compiler can tell
 // the DMA destinations of one phase from the buffers the other phase reads.
-template <int IO>
+template <int IO, int NW>
 struct SweepSizes {
   static constexpr bool F32 = (IO == IO_F32);
+  static constexpr int THR = 64 * NW;
+  static constexpr int DVB = 16 * NW;                  // dv columns per workgroup
+  static constexpr int NBLK = DV / DVB;
+  static constexpr int O_STRIDE = DVB + 8;             // u16 per staged output row
+  static constexpr int V_STRIDE = DVB + 8;             // u16 per staged V row
   static constexpr int ROWS = CH * KS_STRIDE;          // K or Q rows (u16)
   static constexpr int ROWS_LO = F32 ? ROWS : 8;
   static constexpr int KT = DK * KT_STRIDE;            // K^T (u16)
@@ -622,16 +625,19 @@ struct SweepSizes {
   static constexpr int PL2 = 2 * CH * T_STRIDE;        // a hi|lo plane pair (u16)
   static constexpr int OST = F32 ? 8 : CH * O_STRIDE;
   static constexpr int VST = F32 ? 8 : CH * V_STRIDE;
+  static constexpr int VW = DVB * 2 / 16;              // 16-byte words per bf16 V row slice
+  static constexpr int OW = DVB / 8;                   // 16-byte words per bf16 output row
 };
 
-template <int IO>
-__global__ void __launch_bounds__(NTHR)
+template <int IO, int NW>
+__global__ void __launch_bounds__(64 * NW)
 chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs,
                    const uint8_t* __restrict__ krecs) {
   typedef Io<IO> io;
   typedef typename io::T T;
   constexpr bool F32 = (IO == IO_F32);
-  typedef SweepSizes<IO> Z;
+  typedef SweepSizes<IO, NW> Z;
+  constexpr int DVB = Z::DVB, NBLK = Z::NBLK, O_STRIDE = Z::O_STRIDE, V_STRIDE = Z::V_STRIDE;
   __shared__ __attribute__((aligned(16))) u16 s_kh[Z::ROWS];    // K rows (bf16 / hi)  phase A
   __shared__ __attribute__((aligned(16))) u16 s_kl[Z::ROWS_LO];
   __shared__ __attribute__((aligned(16))) u16 s_qh[Z::ROWS];    // Q rows              phase A
@@ -689,9 +695,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   // V slice) lands while the previous chunk's phase B runs, phase B (P planes, K^T)
   // while chunk n's phase A runs.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t ktab[RowDma<16>::J], vtab[RowDma<8>::J];
-  rows_table<16>(wave_u, lane, ktab);
-  rows_table<8>(wave_u, lane, vtab);
+  constexpr int VW = Z::VW;
+  uint32_t ktab[RowDma<16, NW>::J], vtab[RowDma<VW, NW>::J];
+  rows_table<16, NW>(wave_u, lane, ktab);
+  rows_table<VW, NW>(wave_u, lane, vtab);
   const uint32_t qrow_bytes = (uint32_t)(p.stride_q * (int64_t)sizeof(T));
   const uint32_t krow_bytes = (uint32_t)(p.stride_k * (int64_t)sizeof(T));
   const uint32_t vrow_bytes = (uint32_t)(p.stride_v * (int64_t)sizeof(T));
@@ -708,21 +715,21 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
     if (part == 0) {
       if constexpr (F32) {
-        dma_linear<(WS_ROWS_BYTES) / 16>(krec, s_kh, wave_u, lane);
-        dma_linear<(WS_ROWS_BYTES) / 16>(krec + WS_ROWS_BYTES, s_kl, wave_u, lane);
+        dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec, s_kh, wave_u, lane);
+        dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec + WS_ROWS_BYTES, s_kl, wave_u, lane);
       } else {
-        dma_rows<16>((const uint8_t*)kg + t0 * krow_bytes, krow_bytes, L, ktab, s_kh, wave_u);
+        dma_rows<16, NW>((const uint8_t*)kg + t0 * krow_bytes, krow_bytes, L, ktab, s_kh, wave_u);
       }
     } else if (part == 1) {
       if constexpr (F32) {
-        dma_linear<(WS_ROWS_BYTES) / 16>(krec + 2 * WS_ROWS_BYTES, s_qh, wave_u, lane);
-        dma_linear<(WS_ROWS_BYTES) / 16>(krec + 3 * WS_ROWS_BYTES, s_ql, wave_u, lane);
+        dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec + 2 * WS_ROWS_BYTES, s_qh, wave_u, lane);
+        dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec + 3 * WS_ROWS_BYTES, s_ql, wave_u, lane);
       } else {
-        dma_rows<16>((const uint8_t*)qg + t0 * qrow_bytes, qrow_bytes, L, ktab, s_qh, wave_u);
+        dma_rows<16, NW>((const uint8_t*)qg + t0 * qrow_bytes, qrow_bytes, L, ktab, s_qh, wave_u);
       }
     } else if (part == 2) {
-      dma_linear<(2 * WS_PL_BYTES) / 16>(rec, s_tp, wave_u, lane);
-      dma_linear<4 * CH * 4 / 16>(rec + WS_FAC_OFF, s_fac, wave_u, lane);
+      dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec, s_tp, wave_u, lane);
+      dma_linear<4 * CH * 4 / 16, NW>(rec + WS_FAC_OFF, s_fac, wave_u, lane);
     } else {
       const uint8_t* vb = vg0 + t0 * vrow_bytes;
       if constexpr (F32) {
@@ -734,7 +741,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
             vraw[I][e] = *(const T*)(vb + (__umul24(t, vrow_bytes) + vcol));
           }
       } else {
-        dma_rows<8>(vb, vrow_bytes, L, vtab, s_v, wave_u);
+        dma_rows<VW, NW>(vb, vrow_bytes, L, vtab, s_v, wave_u);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -744,12 +751,12 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * WS_REC_BYTES;
     const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
     if (part == 0) {
-      dma_linear<(2 * WS_PL_BYTES) / 16>(rec + 2 * WS_PL_BYTES, s_pp, wave_u, lane);
+      dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec + 2 * WS_PL_BYTES, s_pp, wave_u, lane);
     } else if constexpr (F32) {
-      dma_linear<(WS_KT_BYTES) / 16>(krec + 4 * WS_ROWS_BYTES, s_kth, wave_u, lane);
-      dma_linear<(WS_KT_BYTES) / 16>(krec + 4 * WS_ROWS_BYTES + WS_KT_BYTES, s_ktl, wave_u, lane);
+      dma_linear<(WS_KT_BYTES) / 16, NW>(krec + 4 * WS_ROWS_BYTES, s_kth, wave_u, lane);
+      dma_linear<(WS_KT_BYTES) / 16, NW>(krec + 4 * WS_ROWS_BYTES + WS_KT_BYTES, s_ktl, wave_u, lane);
     } else {
-      dma_linear<(WS_KT_BYTES) / 16>(krec, s_kth, wave_u, lane);
+      dma_linear<(WS_KT_BYTES) / 16, NW>(krec, s_kth, wave_u, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -772,10 +779,12 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     const int64_t t0 = b0 + (int64_t)n * CH;
     const int L = (int)min((int64_t)CH, b1 - t0);
     const u16* ot = s_ost;
+    constexpr int WPR = Z::OW;
+    static_assert((CH * WPR) % Z::THR == 0, "whole output tile per pass");
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int idx = tid + NTHR * it;
-      const int row = idx >> 3, c8 = idx & 7;
+    for (int it = 0; it < CH * WPR / Z::THR; ++it) {
+      const int idx = tid + Z::THR * it;
+      const int row = idx / WPR, c8 = idx % WPR;
       if (row < L)
         *reinterpret_cast<uint4*>(og0 + (t0 + row) * o_stride + c8 * 8) =
             *reinterpret_cast<const uint4*>(&ot[row * O_STRIDE + c8 * 8]);
@@ -984,9 +993,21 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t blocks = (int64_t)a.Ns * a.Hv * NBLK;
-  hipLaunchKernelGGL(chunk_sweep_kernel<IO>, dim3((unsigned)blocks), dim3(NTHR), 0, st, a,
-                     (const int32_t*)cmap, (const uint8_t*)recs, (const uint8_t*)krecs);
+  // Each (sequence, head) chain is sequential over its chunks.  While two 4-wave
+  // workgroups per chain (64 dv columns each, one wave per SIMD) fit on the chip
+  // at once, they give the shortest chain; beyond that one 8-wave workgroup per
+  // chain (two waves per SIMD, operands staged once for all 128 columns) gives
+  // the higher throughput.
+  const int64_t pairs = (int64_t)a.Ns * a.Hv;
+  const int64_t cus = a.cu_count > 0 ? a.cu_count : 256;
+  if (pairs * SweepSizes<IO, 4>::NBLK <= cus)
+    hipLaunchKernelGGL((chunk_sweep_kernel<IO, 4>), dim3((unsigned)(pairs * SweepSizes<IO, 4>::NBLK)),
+                       dim3(SweepSizes<IO, 4>::THR), 0, st, a, (const int32_t*)cmap,
+                       (const uint8_t*)recs, (const uint8_t*)krecs);
+  else
+    hipLaunchKernelGGL((chunk_sweep_kernel<IO, 8>), dim3((unsigned)(pairs * SweepSizes<IO, 8>::NBLK)),
+                       dim3(SweepSizes<IO, 8>::THR), 0, st, a, (const int32_t*)cmap,
+                       (const uint8_t*)recs, (const uint8_t*)krecs);
   return hipGetLastError();
 }
 

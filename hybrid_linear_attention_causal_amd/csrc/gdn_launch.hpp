@@ -40,6 +40,7 @@ struct ChunkArgs {
   int Hk, Hv;
   float scale;
   int use_l2;
+  int cu_count;           // compute units of the device (launch shape choice; <= 0: 256)
 };
 
 struct StepArgs {

@@ -116,6 +116,22 @@ def test_chunk_prefill_parity_small(io, hk, hv):
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_chunk_prefill_parity_many_chains(io):
+    """More (sequence, head) chains than twice the compute units (40 x 4 x 2 > 256):
+    the sweep runs as one 8-wave workgroup per chain instead of two 4-wave ones."""
+    hk, hv = 2, 4
+    lens = [1, 17, 63, 64, 65, 100, 0, 130] * 5
+    inp = _case(hk, hv, io, 41, seqlens=lens, init_state=True)
+    assert inp["Ns"] * hv * 2 > torch.cuda.get_device_properties(0).multi_processor_count
+    y, o, s = _run_prefill(inp, io)
+    o_ref, s_ref = G.prefill(y[:, :hk * D], y[:, hk * D:2 * hk * D], y[:, 2 * hk * D:],
+                             inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv, D, D,
+                             inp["state_in"], inp["cu_seqlens"])
+    assert_out(o, G.to_io(o_ref, io), io, "prefill o")
+    assert_state(s, s_ref, "prefill state")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_chunk_prefill_zero_state_single_sequence(io):
     inp = _case(2, 4, io, 31, seqlens=[257], init_state=False)
     y, o, s = _run_prefill(inp, io, with_state=False)
