@@ -37,6 +37,8 @@
 // + lo); every fp32 operand that feeds the state or the output (S in K S and
 // Q S, R and T' in T' R, P and U in P U, U in the state update) is split into
 // bf16 hi + lo, which leaves ~1e-5 of the output RMS.
+#include <type_traits>
+
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
@@ -47,7 +49,6 @@ constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int NTHR = 256;              // prep workgroup
 constexpr int KS_STRIDE = DK + 8;      // u16 per staged K/Q row
-constexpr int KT_STRIDE = CH + 8;      // u16 per staged K^T row
 constexpr int T_STRIDE = CH + 8;       // u16 per staged T'/P row
 constexpr int F_STRIDE = CH + 4;       // floats per A/T row
 
@@ -56,18 +57,17 @@ constexpr int F_STRIDE = CH + 4;       // floats per A/T row
 //   per (global chunk c, value head h), 37888 bytes: T' hi, T' lo, P hi, P lo as
 //     row-major 64 x 72 (padded) bf16 planes, then 4 x 64 fp32 factors
 //     e^gamma/|k|, e^gamma/|q|, e^{gamma_L - gamma}/|k|, e^{gamma_L};
-//   per (global chunk c, key head kh): bf16 io: K^T as 128 x 72 bf16 (18432 bytes);
-//     fp32 io: K hi, K lo, Q hi, Q lo rows (64 x 136 bf16 each) then K^T hi, K^T lo.
+//   fp32 io only, per (global chunk c, key head kh): K hi, K lo, Q hi, Q lo rows
+//     (64 x 136 bf16 each); bf16 io stages K and Q straight from the input rows.
 constexpr int64_t WS_PL_BYTES = (int64_t)CH * T_STRIDE * 2;          // 9216 per plane
 constexpr int64_t WS_FAC_OFF = 4 * WS_PL_BYTES;                       // 36864
 constexpr int64_t WS_REC_BYTES = WS_FAC_OFF + 4 * CH * 4;             // 37888
 constexpr int64_t WS_ROWS_BYTES = (int64_t)CH * KS_STRIDE * 2;       // 17408 per row plane
-constexpr int64_t WS_KT_BYTES = (int64_t)DK * KT_STRIDE * 2;          // 18432 per K^T plane
 
 static int64_t ws_map_bytes(int Ns) { return (((int64_t)Ns + 1) * 4 + 255) / 256 * 256; }
 static int64_t ws_max_chunks(int64_t N, int Ns) { return (N + CH - 1) / CH + Ns; }
 __host__ __device__ constexpr int64_t ws_krec_bytes(bool f32) {
-  return f32 ? 4 * WS_ROWS_BYTES + 2 * WS_KT_BYTES : WS_KT_BYTES;
+  return f32 ? 4 * WS_ROWS_BYTES : 0;
 }
 
 size_t chunk_workspace_bytes(int64_t N, int Ns, int Hk, int Hv, bool f32) {
@@ -120,6 +120,21 @@ __device__ __forceinline__ bf16x8 pack8(uint2 lo, uint2 hi) {
 __device__ __forceinline__ bf16x8 frag_rows(const u16* m, int stride, int row0, int k0, int lane) {
   const u16* p = m + (row0 + (lane & 15)) * stride + k0 + 4 * (lane >> 4);
   return pack8(*reinterpret_cast<const uint2*>(p), *reinterpret_cast<const uint2*>(p + 16));
+}
+
+// A-operand of K^T (rows d0 .. d0+15, tokens k0 + perm(g, e)) read from row-major K rows
+// in LDS with two transposing reads.  Within each 16-lane group, ds_read_b64_tr_b16
+// hands lane t element e of source lane 4 e + t / 4, at that lane's position t % 4; so
+// source lane j of group g points at token k0 + 4 g + j / 4 (16 tokens further for the
+// second read), dk columns d0 + 4 (j % 4) .. d0 + 4 (j % 4) + 3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ bf16x8 frag_kt(const u16* krows, int d0, int k0, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const u16* p = krows + (k0 + 4 * g + (j >> 2)) * KS_STRIDE + d0 + 4 * (j & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * KS_STRIDE));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // B-operand from two stacked accumulator tiles (rows 0..15 and 16..31 of a
@@ -432,28 +447,11 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
           src[i];
     }
   }
-  // K record of this (chunk, key head), written once by its first value head: K^T (from the
-  // staged rows, 8 tokens per 16-byte word) and, for fp32 io, the hi/lo K and Q rows
-  if (h % (Hv / p.Hk) == 0) {
-    uint8_t* krec = krecs + ((int64_t)c * p.Hk + kh_) * ws_krec_bytes(F32);
-    uint8_t* kt_dst = krec + (F32 ? 4 * WS_ROWS_BYTES : 0);
-#pragma unroll
-    for (int pl = 0; pl < (F32 ? 2 : 1); ++pl) {
-      const u16* srcp = pl ? sm.kl : sm.kh;
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int i = tid + NTHR * it;          // K^T row d = i >> 3, tokens 8j .. 8j+7
-        const int d = i >> 3, j = i & 7;
-        uint32_t w[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          w[u] = (uint32_t)srcp[(8 * j + 2 * u) * KS_STRIDE + d] |
-                 ((uint32_t)srcp[(8 * j + 2 * u + 1) * KS_STRIDE + d] << 16);
-        *reinterpret_cast<uint4*>(kt_dst + pl * WS_KT_BYTES + d * (KT_STRIDE * 2) + j * 16) =
-            make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
-    if constexpr (F32) {
+  // fp32 io: the hi/lo K and Q rows of this (chunk, key head), written once by its
+  // first value head
+  if constexpr (F32) {
+    if (h % (Hv / p.Hk) == 0) {
+      uint8_t* krec = krecs + ((int64_t)c * p.Hk + kh_) * ws_krec_bytes(F32);
       const u16* planes[4] = {sm.kh, sm.kl, sm.qh, sm.ql};
 #pragma unroll
       for (int pl = 0; pl < 4; ++pl) {
@@ -620,8 +618,6 @@ struct SweepSizes {
   static constexpr int V_STRIDE = DVB + 8;             // u16 per staged V row
   static constexpr int ROWS = CH * KS_STRIDE;          // K or Q rows (u16)
   static constexpr int ROWS_LO = F32 ? ROWS : 8;
-  static constexpr int KT = DK * KT_STRIDE;            // K^T (u16)
-  static constexpr int KT_LO = F32 ? KT : 8;
   static constexpr int PL2 = 2 * CH * T_STRIDE;        // a hi|lo plane pair (u16)
   static constexpr int OST = F32 ? 8 : CH * O_STRIDE;
   static constexpr int VST = F32 ? 8 : CH * V_STRIDE;
@@ -638,14 +634,16 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   constexpr bool F32 = (IO == IO_F32);
   typedef SweepSizes<IO, NW> Z;
   constexpr int DVB = Z::DVB, NBLK = Z::NBLK, O_STRIDE = Z::O_STRIDE, V_STRIDE = Z::V_STRIDE;
-  __shared__ __attribute__((aligned(16))) u16 s_kh[Z::ROWS];    // K rows (bf16 / hi)  phase A
-  __shared__ __attribute__((aligned(16))) u16 s_kl[Z::ROWS_LO];
+  // K rows are double-buffered by chunk parity: chunk n's rows serve its K S products
+  // and, read transposed, its state update, while chunk n+1's rows land
+  __shared__ __attribute__((aligned(16))) u16 s_k0[Z::ROWS];    // K rows (bf16 / hi), even chunks
+  __shared__ __attribute__((aligned(16))) u16 s_k1[Z::ROWS];    // K rows (bf16 / hi), odd chunks
+  __shared__ __attribute__((aligned(16))) u16 s_kl0[Z::ROWS_LO];
+  __shared__ __attribute__((aligned(16))) u16 s_kl1[Z::ROWS_LO];
   __shared__ __attribute__((aligned(16))) u16 s_qh[Z::ROWS];    // Q rows              phase A
   __shared__ __attribute__((aligned(16))) u16 s_ql[Z::ROWS_LO];
   __shared__ __attribute__((aligned(16))) u16 s_tp[Z::PL2];     // T' hi | lo          phase A
   __shared__ __attribute__((aligned(16))) u16 s_pp[Z::PL2];     // P hi | lo           phase B
-  __shared__ __attribute__((aligned(16))) u16 s_kth[Z::KT];     // K^T                 phase B
-  __shared__ __attribute__((aligned(16))) u16 s_ktl[Z::KT_LO];
   __shared__ __attribute__((aligned(16))) float s_fac[4 * CH];  // per-token factors    phase A
   __shared__ __attribute__((aligned(16))) u16 s_ost[Z::OST];    // output tile (bf16 io)
   __shared__ __attribute__((aligned(16))) u16 s_v[Z::VST];      // V slice (bf16 io)   phase A
@@ -692,8 +690,8 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 
   // Operands of chunk n, copied in pieces so that the copies issue between the
   // matrix products of the other phase.  Phase A (K, Q rows, T' planes, factors, the
-  // V slice) lands while the previous chunk's phase B runs, phase B (P planes, K^T)
-  // while chunk n's phase A runs.
+  // V slice) lands while the previous chunk's phase B runs, phase B (P planes) while
+  // chunk n's phase A runs.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   constexpr int VW = Z::VW;
   uint32_t ktab[RowDma<16, NW>::J], vtab[RowDma<VW, NW>::J];
@@ -707,7 +705,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   T vraw[4][4];   // fp32 io: the V slice goes through registers
   // (sched_barrier keeps the instruction scheduler from sinking a piece past the
   // products it is meant to overlap)
-  auto stage_a = [&](int n, int part) {
+  auto stage_a = [&](int n, int part, u16* kdst, u16* kldst) {
     __builtin_amdgcn_sched_barrier(0);
     const int64_t t0 = b0 + (int64_t)n * CH;
     const int L = (int)min((int64_t)CH, b1 - t0);
@@ -715,10 +713,11 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
     if (part == 0) {
       if constexpr (F32) {
-        dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec, s_kh, wave_u, lane);
-        dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec + WS_ROWS_BYTES, s_kl, wave_u, lane);
+        dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec, kdst, wave_u, lane);
+        dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec + WS_ROWS_BYTES, kldst, wave_u, lane);
       } else {
-        dma_rows<16, NW>((const uint8_t*)kg + t0 * krow_bytes, krow_bytes, L, ktab, s_kh, wave_u);
+        (void)kldst;
+        dma_rows<16, NW>((const uint8_t*)kg + t0 * krow_bytes, krow_bytes, L, ktab, kdst, wave_u);
       }
     } else if (part == 1) {
       if constexpr (F32) {
@@ -746,18 +745,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto stage_b = [&](int n, int part) {
+  auto stage_b = [&](int n) {
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * WS_REC_BYTES;
-    const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
-    if (part == 0) {
-      dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec + 2 * WS_PL_BYTES, s_pp, wave_u, lane);
-    } else if constexpr (F32) {
-      dma_linear<(WS_KT_BYTES) / 16, NW>(krec + 4 * WS_ROWS_BYTES, s_kth, wave_u, lane);
-      dma_linear<(WS_KT_BYTES) / 16, NW>(krec + 4 * WS_ROWS_BYTES + WS_KT_BYTES, s_ktl, wave_u, lane);
-    } else {
-      dma_linear<(WS_KT_BYTES) / 16, NW>(krec, s_kth, wave_u, lane);
-    }
+    dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec + 2 * WS_PL_BYTES, s_pp, wave_u, lane);
     __builtin_amdgcn_sched_barrier(0);
   };
   // bf16 io: a chunk's output stays in registers (packed pairs of rows) through the
@@ -793,10 +784,16 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 
   if (nch > 0) {
 #pragma unroll
-    for (int part = 0; part < 4; ++part) stage_a(0, part);
+    for (int part = 0; part < 4; ++part) stage_a(0, part, s_k0, s_kl0);
   }
 
-  for (int n = 0; n < nch; ++n) {
+  // one chunk; PAR = n & 1 picks the K buffers at compile time
+  auto chunk = [&](int n, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    u16* const kcur = PAR ? s_k1 : s_k0;
+    u16* const kcl = PAR ? s_kl1 : s_kl0;
+    u16* const knext = PAR ? s_k0 : s_k1;
+    u16* const knl = PAR ? s_kl0 : s_kl1;
     const int64_t t0 = b0 + (int64_t)n * CH;
     const int L = (b1 - t0) < CH ? (int)(b1 - t0) : CH;
 
@@ -805,7 +802,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     if constexpr (!F32) {
       if (n > 0) write_ost();
     }
-    stage_b(n, 0);
+    stage_b(n);
 
     // ================= phase A: K S and Q S (S hi/lo), R, U = T' R
     float vr[4][4];
@@ -829,7 +826,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
         bf16x8 ak[4], aq[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          ak[m] = frag_rows(s_kh, KS_STRIDE, 16 * I, 32 * m, lane);
+          ak[m] = frag_rows(kcur, KS_STRIDE, 16 * I, 32 * m, lane);
           aq[m] = frag_rows(s_qh, KS_STRIDE, 16 * I, 32 * m, lane);
         }
         f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
@@ -840,7 +837,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
           ks = mma(ak[m], sl[m], ks);
           qs = mma(aq[m], sl[m], qs);
           if constexpr (F32) {
-            ks = mma(frag_rows(s_kl, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], ks);
+            ks = mma(frag_rows(kcl, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], ks);
             qs = mma(frag_rows(s_ql, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], qs);
           }
         }
@@ -854,7 +851,6 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
         R[I][1] = vr[I][1] - c4.y * ks[1];
         R[I][2] = vr[I][2] - c4.z * ks[2];
         R[I][3] = vr[I][3] - c4.w * ks[3];
-        if (I == 1) stage_b(n, 1);
       }
     }
     // U = T' R   (T' lower triangular: row tile I needs token slabs 0 .. I/2)
@@ -901,7 +897,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     // the last chunk reloads its own phase-A operands (unread in phase B) so that the
     // copies stay unconditional and keep their places between the products
     const int na = n + 1 < nch ? n + 1 : n;
-    stage_a(na, 0);
+    stage_a(na, 0, knext, knl);
     if constexpr (!F32) {
       if (n > 0) store_o(n - 1);
     }
@@ -937,28 +933,33 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
           opk[I][0] = cvt2(ov[0], ov[1]);
           opk[I][1] = cvt2(ov[2], ov[3]);
         }
-        if (I == 1) stage_a(na, 1);
+        if (I == 1) stage_a(na, 1, knext, knl);
       }
     }
-    stage_a(na, 2);
-    // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U
+    stage_a(na, 2, knext, knl);
+    // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U, K^T read transposed
+    // from this chunk's K rows
     {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         bf16x8 ak[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) ak[m] = frag_rows(s_kth, KT_STRIDE, 16 * i, 32 * m, lane);
+        for (int m = 0; m < 2; ++m) ak[m] = frag_kt(kcur, 16 * i, 32 * m, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[i][e] *= egl;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           S[i] = mma(ak[m], wh[m], S[i]);
           S[i] = mma(ak[m], wl[m], S[i]);
-          if constexpr (F32) S[i] = mma(frag_rows(s_ktl, KT_STRIDE, 16 * i, 32 * m, lane), wh[m], S[i]);
+          if constexpr (F32) S[i] = mma(frag_kt(kcl, 16 * i, 32 * m, lane), wh[m], S[i]);
         }
-        if (i == 3) stage_a(na, 3);
+        if (i == 3) stage_a(na, 3, knext, knl);
       }
     }
+  };
+  for (int n = 0; n < nch; n += 2) {
+    chunk(n, std::integral_constant<int, 0>());
+    if (n + 1 < nch) chunk(n + 1, std::integral_constant<int, 1>());
   }
   if constexpr (!F32) {
     if (nch > 0) {
