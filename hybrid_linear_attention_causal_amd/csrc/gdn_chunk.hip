@@ -15,16 +15,19 @@
 //   S'   = e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U
 //
 // Three launches:
-//   1. chunk map: chunk offsets of the packed sequences (one small workgroup).
-//   2. chunk prep: one workgroup per (chunk, value head), all in parallel.  Stages
-//      raw K and Q rows in LDS, forms K K^T and Q K^T on MFMA, inverts I + A by
-//      blocked fp32 forward substitution, and writes T' = T diag(beta) and P as
-//      bf16 hi/lo planes plus the per-token factors to the workspace.
-//   3. sweep: one workgroup per (sequence, value head, 64-column block of dv).
-//      Each of its 4 waves keeps a 128 x 16 slice of the fp32 state in MFMA
-//      accumulator registers for the whole sequence and walks the chunks in
-//      order; per chunk only the S-dependent products run (K S, T' R, Q S + P U,
-//      K^T U), on operands staged in LDS, while the next chunk's operands load.
+//   1. chunk map: chunk offsets of the packed sequences and a per-chunk table
+//      (sequence, valid rows, first token); one small workgroup.
+//   2. chunk prep: one workgroup per (chunk, key head), all in parallel.  Stages
+//      raw K and Q rows in LDS, forms K K^T and Q K^T on MFMA once for the value
+//      heads sharing the key head, then per value head inverts I + A (blocked:
+//      fp32 forward substitution on the diagonal blocks, fp32 MFMA products off
+//      it) and writes T' = T diag(beta) and P as bf16 hi/lo planes plus the
+//      per-token factors to the workspace.
+//   3. sweep: one workgroup per (sequence, value head, block of dv columns; 4 or 8
+//      waves of 16 columns).  Each wave keeps a 128 x 16 slice of the fp32 state in
+//      registers for the whole sequence and walks the chunks in order; per chunk
+//      only the S-dependent products run (K S, T' R, Q S + P U, K^T U), on
+//      operands staged in LDS by DMA while the other phase's products run.
 //
 // MFMA use: v_mfma_f32_16x16x32_bf16.  Operand fragments use a permuted
 // contraction index (lane group g, element e -> k = 4g + e for e < 4, 16 + 4g
@@ -53,7 +56,9 @@ constexpr int T_STRIDE = CH + 8;       // u16 per staged T'/P row
 constexpr int F_STRIDE = CH + 4;       // floats per A/T row
 
 // Workspace (all LDS-ready, so the sweep stages operands with plain DMA copies):
-//   chunk offsets: int32 [Ns + 1], padded to 256 bytes;
+//   chunk offsets: int32 [Ns + 1], padded to 256 bytes; chunk table: int4 [cmax]
+//     {sequence, valid rows, first token lo, hi}, padded to 256 bytes
+//     (cmax = ceil(N / 64) + Ns bounds the chunk count);
 //   per (global chunk c, value head h), 37888 bytes: T' hi, T' lo, P hi, P lo as
 //     row-major 64 x 72 (padded) bf16 planes, then 4 x 64 fp32 factors
 //     e^gamma/|k|, e^gamma/|q|, e^{gamma_L - gamma}/|k|, e^{gamma_L};
@@ -64,15 +69,18 @@ constexpr int64_t WS_FAC_OFF = 4 * WS_PL_BYTES;                       // 36864
 constexpr int64_t WS_REC_BYTES = WS_FAC_OFF + 4 * CH * 4;             // 37888
 constexpr int64_t WS_ROWS_BYTES = (int64_t)CH * KS_STRIDE * 2;       // 17408 per row plane
 
-static int64_t ws_map_bytes(int Ns) { return (((int64_t)Ns + 1) * 4 + 255) / 256 * 256; }
 static int64_t ws_max_chunks(int64_t N, int Ns) { return (N + CH - 1) / CH + Ns; }
+static int64_t ws_cmap_bytes(int Ns) { return (((int64_t)Ns + 1) * 4 + 255) / 256 * 256; }
+static int64_t ws_map_bytes(int64_t N, int Ns) {
+  return ws_cmap_bytes(Ns) + (ws_max_chunks(N, Ns) * 16 + 255) / 256 * 256;
+}
 __host__ __device__ constexpr int64_t ws_krec_bytes(bool f32) {
   return f32 ? 4 * WS_ROWS_BYTES : 0;
 }
 
 size_t chunk_workspace_bytes(int64_t N, int Ns, int Hk, int Hv, bool f32) {
   const int64_t cmax = ws_max_chunks(N, Ns);
-  return (size_t)(ws_map_bytes(Ns) + cmax * Hv * WS_REC_BYTES + cmax * Hk * ws_krec_bytes(f32));
+  return (size_t)(ws_map_bytes(N, Ns) + cmax * Hv * WS_REC_BYTES + cmax * Hk * ws_krec_bytes(f32));
 }
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -227,11 +235,18 @@ __device__ __forceinline__ void put_row8(u16* hi, u16* lo, int off, const float*
 }
 
 // ============================================================================ 1. chunk map
-// cmap[s] = number of 64-token chunks before sequence s; cmap[Ns] = total.
+// cmap[s] = number of 64-token chunks before sequence s, cmap[Ns] = total; and for every
+// global chunk c < cmax, cinfo[c] = {sequence, valid rows L, first token (lo, hi)},
+// L = 0 past the total.  One workgroup; the chunk -> sequence search runs on an LDS copy
+// of cmap when it fits.
+constexpr int MAP_LDS = 8192;
 __global__ void __launch_bounds__(256) chunk_map_kernel(const int32_t* cu, int Ns, int64_t N,
-                                                        int32_t* cmap) {
+                                                        int64_t cmax, int32_t* cmap,
+                                                        int4* cinfo) {
   __shared__ int wtot[4];
+  __shared__ int lmap[MAP_LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool in_lds = Ns + 1 <= MAP_LDS;
   int carry = 0;
   for (int base = 0; base < Ns; base += 256) {
     const int s = base + tid;
@@ -247,34 +262,74 @@ __global__ void __launch_bounds__(256) chunk_map_kernel(const int32_t* cu, int N
     __syncthreads();
     int before = carry;
     for (int w = 0; w < wave; ++w) before += wtot[w];
-    if (s < Ns) cmap[s] = before + (int)incl - n;
+    if (s < Ns) {
+      cmap[s] = before + (int)incl - n;
+      if (in_lds) lmap[s] = before + (int)incl - n;
+    }
     carry += wtot[0] + wtot[1] + wtot[2] + wtot[3];
     __syncthreads();
   }
-  if (tid == 0) cmap[Ns] = carry;
+  if (tid == 0) {
+    cmap[Ns] = carry;
+    if (in_lds) lmap[Ns] = carry;
+  }
+  __syncthreads();   // also orders this workgroup's cmap stores before the reads below
+  const int* map = in_lds ? lmap : cmap;
+  for (int64_t c = tid; c < cmax; c += 256) {
+    int4 info = make_int4(0, 0, 0, 0);
+    if (c < carry) {
+      int lo = 0, hi = Ns - 1;          // the last sequence starting at or before chunk c
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (map[mid] <= c) lo = mid; else hi = mid - 1;
+      }
+      int64_t b0, b1;
+      seq_bounds(cu, N, lo, b0, b1);
+      const int64_t t0 = b0 + (c - map[lo]) * CH;
+      info = make_int4(lo, (int)min((int64_t)CH, b1 - t0), (int)(uint32_t)t0, (int)(t0 >> 32));
+    }
+    cinfo[c] = info;
+  }
 }
 
 // ============================================================================ 2. chunk prep
+// One workgroup per (global chunk, key head), for the r = Hv / Hk value heads that
+// share the key head: the K and Q rows, their norms and the raw Gram tiles
+// (K^ K^T and Q^ K^T with the 1/|k|, 1/|q| factors) are formed once; then, per value
+// head, its decay and write strength scale the tiles into A and P, I + A is inverted,
+// and the head's record is written.
+constexpr int PREP_RB = 4;                // value heads whose gates are staged at once
+static_assert(PREP_RB == NTHR / 64, "one wave stages the gates of one value head");
+
 template <int IO>
 struct PrepSmem {
   static constexpr bool F32 = (IO == IO_F32);
-  // every member a multiple of 16 bytes, so that vector LDS accesses stay aligned
-  alignas(16) u16 kh[CH * KS_STRIDE];                 // K rows (bf16 / hi part)
-  alignas(16) u16 kl[F32 ? CH * KS_STRIDE : 8];
-  alignas(16) u16 qh[CH * KS_STRIDE];
-  alignas(16) u16 ql[F32 ? CH * KS_STRIDE : 8];
-  alignas(16) float af[CH * F_STRIDE];                // strictly lower A (fp32)
-  alignas(16) float tf[CH * F_STRIDE];                // T (fp32); first holds the staged P planes
-  alignas(16) float msc[32 * 36];                     // block products of the solve
-  alignas(16) float gam[CH];                          // in-chunk cumulative log decay
-  alignas(16) float beta[CH];
-  alignas(16) float rnk[CH];                          // 1/|k_t| (1 without the L2 norm)
+  // phase 0 holds the K and Q rows; once the Gram tiles are in registers the same
+  // bytes hold A and T of the current value head (every member 16-byte aligned)
+  struct Rows {
+    alignas(16) u16 kh[CH * KS_STRIDE];   // K rows (bf16 / hi part)
+    alignas(16) u16 qh[CH * KS_STRIDE];
+    alignas(16) u16 kl[F32 ? CH * KS_STRIDE : 8];
+    alignas(16) u16 ql[F32 ? CH * KS_STRIDE : 8];
+  };
+  struct Mats {
+    alignas(16) float af[CH * F_STRIDE];  // strictly lower A (fp32); its dead top rows
+                                          // serve as scratch of the block products
+    alignas(16) float tf[CH * F_STRIDE];  // T (fp32); first holds the staged P planes
+  };
+  union alignas(16) {
+    Rows r;
+    Mats m;
+  } u;
+  alignas(16) float gam[PREP_RB][CH];     // in-chunk cumulative log decay per value head
+  alignas(16) float beta[PREP_RB][CH];
+  alignas(16) float rnk[CH];              // 1/|k_t| (1 without the L2 norm)
   alignas(16) float rnq[CH];
 };
 
 template <int IO>
-__global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? 2 : 1)
-chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __restrict__ recs,
+__global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? 3 : 2)
+chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restrict__ recs,
                   uint8_t* __restrict__ krecs) {
   typedef Io<IO> io;
   typedef typename io::T T;
@@ -282,40 +337,21 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
   __shared__ PrepSmem<IO> sm;
 
   const int c = blockIdx.x;               // global chunk
-  const int h = blockIdx.y;               // value head
-  const int Ns = p.Ns, Hv = p.Hv;
-  if (c >= cmap[Ns]) return;
-  int lo = 0, hi = Ns - 1;                // the sequence holding chunk c
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cmap[mid] <= c) lo = mid; else hi = mid - 1;
-  }
-  const int s = lo;
-  int64_t b0, b1;
-  seq_bounds(p.cu, p.N, s, b0, b1);
-  const int64_t t0 = b0 + (int64_t)(c - cmap[s]) * CH;
-  const int L = (int)min((int64_t)CH, b1 - t0);
+  const int kh_ = blockIdx.y;             // key head
+  const int Hv = p.Hv, r = Hv / p.Hk;
+  const int4 ci = cinfo[c];
+  const int L = ci.y;
+  if (L == 0) return;                     // past the last chunk
+  const int64_t t0 = ((int64_t)ci.w << 32) | (uint32_t)ci.z;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int kh_ = h / (Hv / p.Hk);
 
-  // ---- stage K and Q rows, row norms (16 lanes of a DPP row share a token row)
+  // ---- phase 0: K and Q rows to LDS, row norms (16 lanes of a DPP row share a row)
   {
     RowBlock<IO> kb, qb;
     load_rows<IO>(kb, (const T*)p.k + (int64_t)kh_ * DK, p.stride_k, t0, L, tid);
     load_rows<IO>(qb, (const T*)p.q + (int64_t)kh_ * DK, p.stride_q, t0, L, tid);
-    float ga = 0.f, gb = 0.f;
-    if (tid < 64) {
-      const int64_t idx = (t0 + (lane < L ? lane : L - 1)) * Hv + h;
-      if (p.g_opt) {
-        ga = p.g_opt[idx];
-        gb = p.beta_opt[idx];
-      } else {
-        ga = io::ld((const T*)p.a, idx);
-        gb = io::ld((const T*)p.b, idx);
-      }
-    }
     const int c8 = tid & 15, rq = tid >> 4;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -325,8 +361,8 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
       row_vals<IO>(kb, u, ok, kv);
       row_vals<IO>(qb, u, ok, qv);
       uint4 hw, lw;
-      put_row8<IO>(sm.kh, sm.kl, row * KS_STRIDE + c8 * 8, kv, hw, lw);
-      put_row8<IO>(sm.qh, sm.ql, row * KS_STRIDE + c8 * 8, qv, hw, lw);
+      put_row8<IO>(sm.u.r.kh, sm.u.r.kl, row * KS_STRIDE + c8 * 8, kv, hw, lw);
+      put_row8<IO>(sm.u.r.qh, sm.u.r.ql, row * KS_STRIDE + c8 * 8, qv, hw, lw);
       float sk = 0.f, sq = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -340,206 +376,250 @@ chunk_prep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, uint8_t* __rest
         sm.rnq[row] = p.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
       }
     }
-    if (wave == 0) {
-      float g = 0.f, beta = 0.f;
-      if (lane < L) {
-        if (p.g_opt) {
-          g = ga;
-          beta = gb;
-        } else {
-          gate_pair(ga, gb, p.A_log[h], p.dt_bias[h], g, beta);
-        }
-      }
-      g = wave_prefix_sum(g);       // in-chunk cumulative log decay (padding adds 0)
-      sm.gam[lane] = g;
-      sm.beta[lane] = beta;
-    }
   }
   __syncthreads();
 
-  uint8_t* rec = recs + ((int64_t)c * Hv + h) * WS_REC_BYTES;
-  // ---- per-token factors for the sweep
-  if (tid < 64) {
-    const float gl = sm.gam[CH - 1];
-    const float gt = sm.gam[tid];
-    const float eg = __expf(gt);
-    float* fac = reinterpret_cast<float*>(rec + WS_FAC_OFF);
-    fac[tid] = eg * sm.rnk[tid];
-    fac[CH + tid] = eg * sm.rnq[tid];
-    fac[2 * CH + tid] = __expf(gl - gt) * sm.rnk[tid];
-    fac[3 * CH + tid] = __expf(gl);
-  }
-
-  // ---- Gram tiles: 10 lower (I >= J) tile pairs A (from K K^T) and P (from Q K^T)
-  // share the K_J fragments; P's strictly-upper tiles are zero.  P is staged as
-  // two row-major 64 x 64 bf16 planes in the (not yet used) T buffer.
-  u16* pst = reinterpret_cast<u16*>(sm.tf);
-  for (int n = wave; n < 16; n += 4) {
-    int I, J;
+  // ---- raw Gram tiles, kept in registers: the 10 lower (I >= J) 16 x 16 tiles of
+  // rnk_i rnk_j (k_i . k_j) and rnq_i rnk_j (q_i . k_j); wave w holds tiles w, w+4, w+8
+  f32x4 gk[3], gq[3];
+#pragma unroll
+  for (int tt = 0; tt < 3; ++tt) {
+    const int n = wave + 4 * tt;
+    gk[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gq[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (n < 10) {
+      int I, J;
       tri_tile(n, I, J);
       bf16x8 bk[4], ak[4], aq[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        bk[m] = frag_rows(sm.kh, KS_STRIDE, 16 * J, 32 * m, lane);
-        ak[m] = frag_rows(sm.kh, KS_STRIDE, 16 * I, 32 * m, lane);
-        aq[m] = frag_rows(sm.qh, KS_STRIDE, 16 * I, 32 * m, lane);
+        bk[m] = frag_rows(sm.u.r.kh, KS_STRIDE, 16 * J, 32 * m, lane);
+        ak[m] = frag_rows(sm.u.r.kh, KS_STRIDE, 16 * I, 32 * m, lane);
+        aq[m] = frag_rows(sm.u.r.qh, KS_STRIDE, 16 * I, 32 * m, lane);
       }
-      f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+      f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        gk = mma(ak[m], bk[m], gk);
-        gq = mma(aq[m], bk[m], gq);
+        a1 = mma(ak[m], bk[m], a1);
+        a2 = mma(aq[m], bk[m], a2);
       }
       if constexpr (F32) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const bf16x8 bl = frag_rows(sm.kl, KS_STRIDE, 16 * J, 32 * m, lane);
-          gk = mma(frag_rows(sm.kl, KS_STRIDE, 16 * I, 32 * m, lane), bk[m], gk);
-          gk = mma(ak[m], bl, gk);
-          gq = mma(frag_rows(sm.ql, KS_STRIDE, 16 * I, 32 * m, lane), bk[m], gq);
-          gq = mma(aq[m], bl, gq);
+          const bf16x8 bl = frag_rows(sm.u.r.kl, KS_STRIDE, 16 * J, 32 * m, lane);
+          a1 = mma(frag_rows(sm.u.r.kl, KS_STRIDE, 16 * I, 32 * m, lane), bk[m], a1);
+          a1 = mma(ak[m], bl, a1);
+          a2 = mma(frag_rows(sm.u.r.ql, KS_STRIDE, 16 * I, 32 * m, lane), bk[m], a2);
+          a2 = mma(aq[m], bl, a2);
         }
       }
-      const int j = 16 * J + c16;
-      const int i0 = 16 * I + 4 * g4;
-      const float gj = sm.gam[j], rkj = sm.rnk[j];
-      const float4 gi4 = *reinterpret_cast<const float4*>(&sm.gam[i0]);
-      const float4 bi4 = *reinterpret_cast<const float4*>(&sm.beta[i0]);
+      const int j = 16 * J + c16, i0 = 16 * I + 4 * g4;
+      const float rkj = sm.rnk[j];
       const float4 ki4 = *reinterpret_cast<const float4*>(&sm.rnk[i0]);
       const float4 qi4 = *reinterpret_cast<const float4*>(&sm.rnq[i0]);
-      const float gi[4] = {gi4.x, gi4.y, gi4.z, gi4.w};
-      const float bi[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
       const float ki[4] = {ki4.x, ki4.y, ki4.z, ki4.w};
       const float qi[4] = {qi4.x, qi4.y, qi4.z, qi4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = i0 + e;
-        const float d = (i >= j) ? __expf(gi[e] - gj) * rkj : 0.f;   // exponent <= 0
-        sm.af[i * F_STRIDE + j] = (i > j) ? bi[e] * ki[e] * d * gk[e] : 0.f;
-        uint32_t ph, pl;
-        split2(qi[e] * d * gq[e], 0.f, ph, pl);
-        pst[i * CH + j] = (u16)ph;
-        pst[CH * CH + i * CH + j] = (u16)pl;
-      }
-    } else {
-      // strictly-upper tiles (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-      const int m = n - 10;
-      I = (m >= 5) ? 2 : (m >= 3) ? 1 : 0;
-      J = m - (I == 0 ? 0 : I == 1 ? 3 : 5) + I + 1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * I + 4 * g4 + e, j = 16 * J + c16;
-        pst[i * CH + j] = 0;
-        pst[CH * CH + i * CH + j] = 0;
+        gk[tt][e] = ki[e] * rkj * a1[e];
+        gq[tt][e] = qi[e] * rkj * a2[e];
       }
     }
   }
-  __syncthreads();
-  // P planes to the workspace record, rows padded to 72 (four 16-byte words per thread)
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(pst);
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int i = tid + NTHR * it;            // plane i >> 9, row (i & 511) >> 3, word i & 7
-      const int plane = i >> 9, row = (i & 511) >> 3, w = i & 7;
-      *reinterpret_cast<uint4*>(rec + (2 + plane) * WS_PL_BYTES + row * (T_STRIDE * 2) + w * 16) =
-          src[i];
-    }
-  }
-  // fp32 io: the hi/lo K and Q rows of this (chunk, key head), written once by its
-  // first value head
+  // fp32 io: the hi/lo K and Q rows of this (chunk, key head) for the sweep
   if constexpr (F32) {
-    if (h % (Hv / p.Hk) == 0) {
-      uint8_t* krec = krecs + ((int64_t)c * p.Hk + kh_) * ws_krec_bytes(F32);
-      const u16* planes[4] = {sm.kh, sm.kl, sm.qh, sm.ql};
+    uint8_t* krec = krecs + ((int64_t)c * p.Hk + kh_) * ws_krec_bytes(F32);
+    const u16* planes[4] = {sm.u.r.kh, sm.u.r.kl, sm.u.r.qh, sm.u.r.ql};
 #pragma unroll
-      for (int pl = 0; pl < 4; ++pl) {
-        const uint4* src = reinterpret_cast<const uint4*>(planes[pl]);
-        uint4* dst = reinterpret_cast<uint4*>(krec + pl * WS_ROWS_BYTES);
-        for (int i = tid; i < (int)(WS_ROWS_BYTES / 16); i += NTHR) dst[i] = src[i];
-      }
+    for (int pl = 0; pl < 4; ++pl) {
+      const uint4* src = reinterpret_cast<const uint4*>(planes[pl]);
+      uint4* dst = reinterpret_cast<uint4*>(krec + pl * WS_ROWS_BYTES);
+      for (int i = tid; i < (int)(WS_ROWS_BYTES / 16); i += NTHR) dst[i] = src[i];
     }
   }
-  __syncthreads();   // the T buffer is reused below
 
-  // ---- T = (I + A)^{-1}, blocked: 16 x 16 diagonal blocks by forward substitution
-  // (one column per lane); then T_10, T_32 = -T_ii A_ij T_jj; then the lower
-  // 32 x 32 block T[32:64, 0:32] = -T[32:64, 32:64] A[32:64, 0:32] T[0:32, 0:32]
-  if (g4 == 0) {
-    const int b = wave;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float* arow = &sm.af[(16 * b + i) * F_STRIDE + 16 * b];
-      float a[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(arow + 4 * q4);
-        a[4 * q4] = t4.x; a[4 * q4 + 1] = t4.y; a[4 * q4 + 2] = t4.z; a[4 * q4 + 3] = t4.w;
+  float* const af = sm.u.m.af;
+  float* const tf = sm.u.m.tf;
+  for (int hb = 0; hb < r; hb += PREP_RB) {
+    // ---- gates of value heads hb .. hb+3 (wave w: head hb + w, lane: token)
+    __syncthreads();     // K/Q rows (phase 0) or the previous heads' T are no longer read
+    {
+      const int jh = hb + wave;
+      float g = 0.f, beta = 0.f;
+      if (jh < r) {
+        const int h = kh_ * r + jh;
+        const int64_t idx = (t0 + (lane < L ? lane : L - 1)) * Hv + h;
+        float ga, gb;
+        if (p.g_opt) {
+          ga = p.g_opt[idx];
+          gb = p.beta_opt[idx];
+        } else {
+          ga = io::ld((const T*)p.a, idx);
+          gb = io::ld((const T*)p.b, idx);
+        }
+        if (lane < L) {
+          if (p.g_opt) {
+            g = ga;
+            beta = gb;
+          } else {
+            gate_pair(ga, gb, p.A_log[h], p.dt_bias[h], g, beta);
+          }
+        }
       }
-      float sacc = (i == c16) ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < i; ++j) sacc = fmaf(-a[j], x[j], sacc);
-      x[i] = sacc;
+      g = wave_prefix_sum(g);       // in-chunk cumulative log decay (padding adds 0)
+      sm.gam[wave][lane] = g;
+      sm.beta[wave][lane] = beta;
     }
+    for (int jb = 0; jb < PREP_RB && hb + jb < r; ++jb) {
+      const int h = kh_ * r + hb + jb;
+      const float* gam = sm.gam[jb];
+      const float* bet = sm.beta[jb];
+      uint8_t* rec = recs + ((int64_t)c * Hv + h) * WS_REC_BYTES;
+      __syncthreads();   // gates staged; the previous head's T is no longer read
+
+      // ---- per-token factors for the sweep
+      if (tid < 64) {
+        const float gl = gam[CH - 1];
+        const float gt = gam[tid];
+        const float eg = __expf(gt);
+        float* fac = reinterpret_cast<float*>(rec + WS_FAC_OFF);
+        fac[tid] = eg * sm.rnk[tid];
+        fac[CH + tid] = eg * sm.rnq[tid];
+        fac[2 * CH + tid] = __expf(gl - gt) * sm.rnk[tid];
+        fac[3 * CH + tid] = __expf(gl);
+      }
+
+      // ---- A (fp32) and P (bf16 hi/lo planes, staged in the T buffer) of this head;
+      // P's strictly-upper tiles are zero
+      u16* pst = reinterpret_cast<u16*>(tf);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm.tf[(16 * b + i) * F_STRIDE + 16 * b + c16] = x[i];
-  } else if (g4 == 1 && (wave & 1) == 0) {
-    // the strictly-upper blocks T_01 and T_23 enter the 32 x 32 products below: zero
+      for (int tt = 0; tt < 4; ++tt) {
+        const int n = wave + 4 * tt;
+        if (n < 10) {
+          int I, J;
+          tri_tile(n, I, J);
+          const int j = 16 * J + c16, i0 = 16 * I + 4 * g4;
+          const float gj = gam[j];
+          const float4 gi4 = *reinterpret_cast<const float4*>(&gam[i0]);
+          const float4 bi4 = *reinterpret_cast<const float4*>(&bet[i0]);
+          const float gi[4] = {gi4.x, gi4.y, gi4.z, gi4.w};
+          const float bi[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm.tf[(16 * wave + i) * F_STRIDE + 16 * wave + 16 + c16] = 0.f;
-  }
-  __syncthreads();
-  // blocks (1,0) (wave 0) and (3,2) (wave 1): T_IJ = -T_II (A_IJ T_JJ), 16 x 16 fp32
-  // MFMA products; the intermediate goes through a wave-private LDS tile
-  if (wave < 2) {
-    const int I = 2 * wave + 1, J = 2 * wave;
-    float* mt = sm.msc + wave * (16 * 20);
-    f32x4 m = tile_mma_f32<16>(&sm.af[16 * I * F_STRIDE + 16 * J], F_STRIDE,
-                               &sm.tf[16 * J * F_STRIDE + 16 * J], F_STRIDE, lane);
+          for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            const float d = (i >= j) ? __expf(gi[e] - gj) : 0.f;   // exponent <= 0
+            af[i * F_STRIDE + j] = (i > j) ? bi[e] * d * gk[tt < 3 ? tt : 0][e] : 0.f;
+            uint32_t ph, pl;
+            split2(d * gq[tt < 3 ? tt : 0][e], 0.f, ph, pl);
+            pst[i * CH + j] = (u16)ph;
+            pst[CH * CH + i * CH + j] = (u16)pl;
+          }
+        } else if (n < 16) {
+          // strictly-upper tiles (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+          const int m = n - 10;
+          const int I = (m >= 5) ? 2 : (m >= 3) ? 1 : 0;
+          const int J = m - (I == 0 ? 0 : I == 1 ? 3 : 5) + I + 1;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) mt[(4 * g4 + e) * 20 + c16] = m[e];
-    const f32x4 t = tile_mma_f32<16>(&sm.tf[16 * I * F_STRIDE + 16 * I], F_STRIDE, mt, 20, lane);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * g4 + e, j = 16 * J + c16;
+            pst[i * CH + j] = 0;
+            pst[CH * CH + i * CH + j] = 0;
+          }
+        }
+      }
+      __syncthreads();
+      // P planes to the workspace record, rows padded to 72 (four 16-byte words per thread)
+      {
+        const uint4* src = reinterpret_cast<const uint4*>(pst);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.tf[(16 * I + 4 * g4 + e) * F_STRIDE + 16 * J + c16] = -t[e];
-  }
-  __syncthreads();
-  // lower 32 x 32 block: T[32:64, 0:32] = -T[32:64, 32:64] (A[32:64, 0:32] T[0:32, 0:32]),
-  // one 16 x 16 output tile per wave
-  {
-    const int ti = wave >> 1, tj = wave & 1;
-    const f32x4 m = tile_mma_f32<32>(&sm.af[(32 + 16 * ti) * F_STRIDE], F_STRIDE,
-                                     &sm.tf[16 * tj], F_STRIDE, lane);
+        for (int it = 0; it < 4; ++it) {
+          const int i = tid + NTHR * it;        // plane i >> 9, row (i & 511) >> 3, word i & 7
+          const int plane = i >> 9, row = (i & 511) >> 3, w = i & 7;
+          *reinterpret_cast<uint4*>(rec + (2 + plane) * WS_PL_BYTES + row * (T_STRIDE * 2) +
+                                    w * 16) = src[i];
+        }
+      }
+      __syncthreads();   // the T buffer is reused below
+
+      // ---- T = (I + A)^{-1}, blocked: 16 x 16 diagonal blocks by forward substitution
+      // (one column per lane); then T_10, T_32 = -T_ii A_ij T_jj; then the lower
+      // 32 x 32 block T[32:64, 0:32] = -T[32:64, 32:64] A[32:64, 0:32] T[0:32, 0:32]
+      if (g4 == 0) {
+        const int b = wave;
+        float x[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.msc[(16 * ti + 4 * g4 + e) * 36 + 16 * tj + c16] = m[e];
-    __syncthreads();
-    const f32x4 t = tile_mma_f32<32>(&sm.tf[(32 + 16 * ti) * F_STRIDE + 32], F_STRIDE,
-                                     &sm.msc[16 * tj], 36, lane);
+        for (int i = 0; i < 16; ++i) {
+          const float* arow = &af[(16 * b + i) * F_STRIDE + 16 * b];
+          float a[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      sm.tf[(32 + 16 * ti + 4 * g4 + e) * F_STRIDE + 16 * tj + c16] = -t[e];
-    __syncthreads();
-  }
-  // ---- T' = T diag(beta), lower triangle, as bf16 hi/lo planes straight to the
-  // workspace (4 consecutive columns per thread per step: 8-byte stores)
-  {
-    u16* tph = reinterpret_cast<u16*>(rec);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 t4 = *reinterpret_cast<const float4*>(arow + 4 * q4);
+            a[4 * q4] = t4.x; a[4 * q4 + 1] = t4.y; a[4 * q4 + 2] = t4.z; a[4 * q4 + 3] = t4.w;
+          }
+          float sacc = (i == c16) ? 1.f : 0.f;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = tid + NTHR * it;          // row i, column group j0
-      const int i = idx >> 4, j0 = (idx & 15) * 4;
-      const float4 t4 = *reinterpret_cast<const float4*>(&sm.tf[i * F_STRIDE + j0]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[j0]);
-      const float v0 = (j0 <= i) ? t4.x * b4.x : 0.f;
-      const float v1 = (j0 + 1 <= i) ? t4.y * b4.y : 0.f;
-      const float v2 = (j0 + 2 <= i) ? t4.z * b4.z : 0.f;
-      const float v3 = (j0 + 3 <= i) ? t4.w * b4.w : 0.f;
-      uint32_t h0, l0, h1, l1;
-      split2(v0, v1, h0, l0);
-      split2(v2, v3, h1, l1);
-      *reinterpret_cast<uint2*>(tph + i * T_STRIDE + j0) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(tph + CH * T_STRIDE + i * T_STRIDE + j0) = make_uint2(l0, l1);
+          for (int j = 0; j < i; ++j) sacc = fmaf(-a[j], x[j], sacc);
+          x[i] = sacc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tf[(16 * b + i) * F_STRIDE + 16 * b + c16] = x[i];
+      } else if (g4 == 1 && (wave & 1) == 0) {
+        // the strictly-upper blocks T_01 and T_23 enter the 32 x 32 products below: zero
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tf[(16 * wave + i) * F_STRIDE + 16 * wave + 16 + c16] = 0.f;
+      }
+      __syncthreads();
+      // blocks (1,0) (wave 0) and (3,2) (wave 1): T_IJ = -T_II (A_IJ T_JJ), 16 x 16 fp32
+      // MFMA products; the intermediate goes through a wave-private LDS tile
+      if (wave < 2) {
+        const int I = 2 * wave + 1, J = 2 * wave;
+        float* mt = af + wave * (16 * 20);   // rows 0..9 of A: dead by now
+        f32x4 m = tile_mma_f32<16>(&af[16 * I * F_STRIDE + 16 * J], F_STRIDE,
+                                   &tf[16 * J * F_STRIDE + 16 * J], F_STRIDE, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mt[(4 * g4 + e) * 20 + c16] = m[e];
+        const f32x4 t = tile_mma_f32<16>(&tf[16 * I * F_STRIDE + 16 * I], F_STRIDE, mt, 20, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tf[(16 * I + 4 * g4 + e) * F_STRIDE + 16 * J + c16] = -t[e];
+      }
+      __syncthreads();
+      // lower 32 x 32 block: T[32:64, 0:32] = -T[32:64, 32:64] (A[32:64, 0:32] T[0:32, 0:32]),
+      // one 16 x 16 output tile per wave
+      {
+        const int ti = wave >> 1, tj = wave & 1;
+        const f32x4 m = tile_mma_f32<32>(&af[(32 + 16 * ti) * F_STRIDE], F_STRIDE,
+                                         &tf[16 * tj], F_STRIDE, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) af[(16 * ti + 4 * g4 + e) * 36 + 16 * tj + c16] = m[e];
+        __syncthreads();
+        const f32x4 t = tile_mma_f32<32>(&tf[(32 + 16 * ti) * F_STRIDE + 32], F_STRIDE,
+                                         &af[16 * tj], 36, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          tf[(32 + 16 * ti + 4 * g4 + e) * F_STRIDE + 16 * tj + c16] = -t[e];
+        __syncthreads();
+      }
+      // ---- T' = T diag(beta), lower triangle, as bf16 hi/lo planes straight to the
+      // workspace (4 consecutive columns per thread per step: 8-byte stores)
+      {
+        u16* tph = reinterpret_cast<u16*>(rec);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int idx = tid + NTHR * it;          // row i, column group j0
+          const int i = idx >> 4, j0 = (idx & 15) * 4;
+          const float4 t4 = *reinterpret_cast<const float4*>(&tf[i * F_STRIDE + j0]);
+          const float4 b4 = *reinterpret_cast<const float4*>(&bet[j0]);
+          const float v0 = (j0 <= i) ? t4.x * b4.x : 0.f;
+          const float v1 = (j0 + 1 <= i) ? t4.y * b4.y : 0.f;
+          const float v2 = (j0 + 2 <= i) ? t4.z * b4.z : 0.f;
+          const float v3 = (j0 + 3 <= i) ? t4.w * b4.w : 0.f;
+          uint32_t h0, l0, h1, l1;
+          split2(v0, v1, h0, l0);
+          split2(v2, v3, h1, l1);
+          *reinterpret_cast<uint2*>(tph + i * T_STRIDE + j0) = make_uint2(h0, h1);
+          *reinterpret_cast<uint2*>(tph + CH * T_STRIDE + i * T_STRIDE + j0) = make_uint2(l0, l1);
+        }
+      }
     }
   }
 }
@@ -983,14 +1063,16 @@ template <int IO>
 static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   const int64_t cmax = ws_max_chunks(a.N, a.Ns);
   int32_t* cmap = reinterpret_cast<int32_t*>(ws);
-  uint8_t* recs = reinterpret_cast<uint8_t*>(ws) + ws_map_bytes(a.Ns);
+  int4* cinfo = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(ws) + ws_cmap_bytes(a.Ns));
+  uint8_t* recs = reinterpret_cast<uint8_t*>(ws) + ws_map_bytes(a.N, a.Ns);
   uint8_t* krecs = recs + cmax * a.Hv * WS_REC_BYTES;
-  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, st, a.cu, a.Ns, a.N, cmap);
+  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, st, a.cu, a.Ns, a.N, cmax, cmap,
+                     cinfo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.N > 0) {
-    hipLaunchKernelGGL(chunk_prep_kernel<IO>, dim3((unsigned)cmax, (unsigned)a.Hv), dim3(NTHR), 0,
-                       st, a, (const int32_t*)cmap, recs, krecs);
+    hipLaunchKernelGGL(chunk_prep_kernel<IO>, dim3((unsigned)cmax, (unsigned)a.Hk), dim3(NTHR), 0,
+                       st, a, (const int4*)cinfo, recs, krecs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
