@@ -14,6 +14,7 @@ from HIP events recorded on the stream the kernels run on (torch's current strea
 Inputs are resident in HBM before timing starts.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --calib-copy MIB   (one plain copy, for PMC byte scaling)
 """
 from __future__ import annotations
 
@@ -31,6 +32,32 @@ D = 128
 CHUNK = 64
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+
+
+CSRC = os.path.join(ROOT, "hybrid_linear_attention_causal_amd", "csrc")
+KERNEL_SOURCES = {"gdn_chunk_prefill": ("gdn_chunk.hip", "gdn_common.hpp", "gdn_launch.hpp"),
+                  "gdn_recurrent_step": ("gdn_step.hip", "gdn_common.hpp", "gdn_launch.hpp")}
+# HBM bytes per launch on this workload from rocprofv3 PMC FETCH_SIZE and WRITE_SIZE,
+# each scaled by what the counter reads for a plain 256 MiB copy (the summary with the
+# commands is profiles/pmc_bytes_bench_qwen35_9b_prefill_T4096_decode_B256.txt).  Each
+# figure belongs to the kernel sources with the given digest and is not reported once
+# they change.
+MEASURED_TRAFFIC = {"gdn_chunk_prefill": ("1eefc25bc1ec710d", 476.7e6),
+                    "gdn_recurrent_step": ("59133283f80345cf", 1106.0e6)}
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    digest, nbytes = MEASURED_TRAFFIC[kernel]
+    return nbytes if source_digest(kernel) == digest else None
 
 
 def chunk_core_flops(n_tokens: int, hk: int, hv: int, seqlens=None) -> float:
@@ -129,6 +156,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only run one device-to-device copy of MIB MiB and exit: the "
+                         "reference kernel that scales PMC byte counters to bytes")
     ap.add_argument("--cpu-heads", type=int, default=None,
                     help="value heads in the CPU-oracle sample (default: all)")
     args = ap.parse_args()
@@ -141,6 +171,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calib_copy:
+        nbytes = args.calib_copy << 20
+        torch.cuda.set_device(0)
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": nbytes}), flush=True)
+        return
 
     import hybrid_linear_attention_causal_amd as gdn
     from hybrid_linear_attention_causal_amd import synth
@@ -241,11 +282,13 @@ def main():
         "kernel_ms": ms,
         "roofline": {"kernel": "gdn_chunk_prefill", "bound": "mfma", "achieved": chunk_tflops,
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                     "frac": chunk_tflops * 1e12 / PEAK_BF16_FLOPS, "traffic": None,
+                     "frac": chunk_tflops * 1e12 / PEAK_BF16_FLOPS,
+                     "traffic": measured_traffic("gdn_chunk_prefill"),
                      "algorithmic_per_launch": flops},
         "roofline_decode": {"kernel": "gdn_recurrent_step", "bound": "hbm", "achieved": step_gbs,
                             "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-                            "frac": step_gbs * 1e9 / PEAK_HBM_BYTES, "traffic": None,
+                            "frac": step_gbs * 1e9 / PEAK_HBM_BYTES,
+                            "traffic": measured_traffic("gdn_recurrent_step"),
                             "algorithmic_per_launch": dbytes},
         "cpu_baseline": None,
     }
