@@ -115,7 +115,7 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
   if (Ns < 1 || N < 0) return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: Ns=%d N=%lld", Ns, (long long)N);
   if (!cu_seqlens && Ns != 1)
     return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: cu_seqlens is NULL but Ns=%d", Ns);
-  if ((int64_t)Ns * Hv * 2 > 0x7fffffffLL)
+  if (((int64_t)Ns * Hk + 8) * (Hv / Hk) * 2 > 0x7fffffffLL)
     return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: too many (sequence, head) pairs");
   if (stride_q < (int64_t)Hk * dk || stride_k < (int64_t)Hk * dk || stride_v < (int64_t)Hv * dv ||
       stride_q % 8 || stride_k % 8 || stride_v % 8 || stride_q > GDN_MAX_ROW_STRIDE ||

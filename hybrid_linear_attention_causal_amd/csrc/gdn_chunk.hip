@@ -78,9 +78,35 @@ __host__ __device__ constexpr int64_t ws_krec_bytes(bool f32) {
   return f32 ? 4 * WS_ROWS_BYTES : 0;
 }
 
+// Intra-sequence scan: at most SEG_MAX segments per sequence, each of at least
+// SEG_MIN_CHUNKS chunks on average, for at most SEG_MAX_CHAINS (sequence, head) chains;
+// the workspace reserves (SEG_MAX - 1) (A, B) pairs per chain when the chain count allows.
+constexpr int SEG_MAX = 8;
+constexpr int SEG_MIN_CHUNKS = 4;
+constexpr int64_t SEG_MAX_CHAINS = 64;
+constexpr int64_t SEG_PAIR_BYTES = 2LL * DK * DV * 4;   // A then B, fp32
+
+static int64_t ws_seg_bytes(int Ns, int Hv) {
+  const int64_t chains = (int64_t)Ns * Hv;
+  return chains <= SEG_MAX_CHAINS ? (SEG_MAX - 1) * chains * SEG_PAIR_BYTES : 0;
+}
+
+// Segments per sequence: enough to fill the compute units with the normal launch's two
+// 4-wave workgroups per (chain, segment), at least 3 (two segments take as long as
+// one: the transition pass is as long as the normal one), else 1.
+static int seg_count(int64_t N, int Ns, int Hv, int64_t cus) {
+  const int64_t chains = (int64_t)Ns * Hv;
+  if (chains > SEG_MAX_CHAINS || N <= 0) return 1;
+  int64_t G = cus / (2 * chains);
+  G = min(G, (int64_t)SEG_MAX);
+  G = min(G, ((N + CH - 1) / CH) / Ns / SEG_MIN_CHUNKS);
+  return G >= 3 ? (int)G : 1;
+}
+
 size_t chunk_workspace_bytes(int64_t N, int Ns, int Hk, int Hv, bool f32) {
   const int64_t cmax = ws_max_chunks(N, Ns);
-  return (size_t)(ws_map_bytes(N, Ns) + cmax * Hv * WS_REC_BYTES + cmax * Hk * ws_krec_bytes(f32));
+  return (size_t)(ws_map_bytes(N, Ns) + cmax * Hv * WS_REC_BYTES + cmax * Hk * ws_krec_bytes(f32) +
+                  ws_seg_bytes(Ns, Hv));
 }
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -705,10 +731,23 @@ struct SweepSizes {
   static constexpr int OW = DVB / 8;                   // 16-byte words per bf16 output row
 };
 
-template <int IO, int NW>
+// Segments of a sequence (the intra-sequence scan).  A sequence's nch chunks split into
+// G segments, segment g = chunks [g nch / G, (g+1) nch / G).  The transition launch
+// (TRANS) runs segments 0 .. G-2 from the augmented start state [0 | I] with no output:
+// columns driven by V from zero give B_g, columns started at the identity with V = 0 give
+// the segment's transition A_g, so that S(end of g) = A_g S(start of g) + B_g.  The normal
+// launch then starts segment g from S = A_{g-1}(... (A_0 S_in + B_0) ...) + B_{g-1}.
+struct SegArgs {
+  int G;          // segments per sequence (1: none)
+  int seg_base;   // first segment of this launch (normal launch)
+  int seg_count;  // segments covered by this launch
+  float* scratch; // per (sequence, head, segment < G-1): A (dk x dk), then B (dk x dv), fp32
+};
+
+template <int IO, int NW, bool TRANS>
 __global__ void __launch_bounds__(64 * NW)
 chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs,
-                   const uint8_t* __restrict__ krecs) {
+                   const uint8_t* __restrict__ krecs, SegArgs sg) {
   typedef Io<IO> io;
   typedef typename io::T T;
   constexpr bool F32 = (IO == IO_F32);
@@ -734,18 +773,35 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   const int g4 = lane >> 4;
   const int c16 = lane & 15;
 
-  int bid = blockIdx.x;
-  const int blk = bid % NBLK;
-  bid /= NBLK;
-  const int Hv = p.Hv;
-  const int h = bid % Hv;
-  const int s = bid / Hv;
-  const int kh = h / (Hv / p.Hk);
+  // Workgroups come in groups (sequence, key head, segment of this launch); a group's
+  // members are its value heads times its column blocks (a transition launch has twice
+  // the column blocks: half 0 the V-driven columns, half 1 the transition).  The device
+  // deals consecutive workgroups to its 8 XCDs in turn, so a group's members get ids
+  // congruent mod 8 and share one XCD's L2 (the K/Q rows, and each head's records across
+  // its column blocks); the last octet of groups is padded.
+  constexpr int NB = TRANS ? 2 * NBLK : NBLK;
+  const int Hv = p.Hv, r = Hv / p.Hk;
+  const int GS = r * NB;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int member = slot % GS;
+  const int group = (slot / GS) * 8 + xcd;
+  if (group >= p.Ns * p.Hk * sg.seg_count) return;
+  const int blk_all = member % NB;
+  const int half = blk_all / NBLK;                   // transition launch: 1 = the A columns
+  const int blk = blk_all % NBLK;
+  const int gi = group % sg.seg_count;
+  const int kh = (group / sg.seg_count) % p.Hk;
+  const int s = group / sg.seg_count / p.Hk;
+  const int h = kh * r + member / NB;
+  const int g = sg.seg_base + gi;                    // this workgroup's segment
   int64_t b0, b1;
   seq_bounds(p.cu, p.N, s, b0, b1);
   const int c0 = cmap[s];
   const int nch = (int)((b1 - b0 + CH - 1) / CH);
+  const int nb = (int)((int64_t)g * nch / sg.G);        // chunks [nb, ne) of the segment
+  const int ne = (int)((int64_t)(g + 1) * nch / sg.G);
   const int col = blk * DVB + wave * 16 + c16;      // this lane's dv column
+  float* const seg_rec = sg.scratch + (((int64_t)s * Hv + h) * (sg.G - 1)) * (2 * DK * DV);
 
   const T* qg = (const T*)p.q + (int64_t)kh * DK;
   const T* kg = (const T*)p.k + (int64_t)kh * DK;
@@ -756,7 +812,13 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 
   // ---- recurrent state slice: S[i] holds rows 16 i + 4 g4 + e of column col
   f32x4 S[8];
-  if (p.state_in) {
+  if (TRANS) {
+    // zero for the V-driven part, the identity's column col for the transition part
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[i][e] = (half == 1 && 16 * i + 4 * g4 + e == col) ? 1.f : 0.f;
+  } else if (p.state_in) {
     const float* sp = p.state_in + ((int64_t)s * Hv + h) * DK * DV + col;
     float tmp[32];
 #pragma unroll
@@ -766,6 +828,39 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if constexpr (!TRANS) {
+    // segment g > 0 starts from A_{g-1}(... (A_0 S_in + B_0) ...) + B_{g-1}: MFMA products
+    // with A split into bf16 hi/lo and S split into hi/lo (three passes)
+    for (int j = 0; j < g; ++j) {
+      const float* Aj = seg_rec + (int64_t)j * (2 * DK * DV);
+      const float* Bj = Aj + DK * DV;
+      bf16x8 sh[4], sl[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) frag_acc_split(S[2 * m], S[2 * m + 1], sh[m], sl[m]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = Bj[(16 * i + 4 * g4 + e) * DV + col];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float* ar = Aj + (16 * i + c16) * DK + 32 * m + 4 * g4;
+          const float4 x0 = *reinterpret_cast<const float4*>(ar);
+          const float4 x1 = *reinterpret_cast<const float4*>(ar + 16);
+          uint4 vh, vl;
+          split2(x0.x, x0.y, vh.x, vl.x);
+          split2(x0.z, x0.w, vh.y, vl.y);
+          split2(x1.x, x1.y, vh.z, vl.z);
+          split2(x1.z, x1.w, vh.w, vl.w);
+          const bf16x8 ah = __builtin_bit_cast(bf16x8, vh), al = __builtin_bit_cast(bf16x8, vl);
+          acc = mma(ah, sh[m], acc);
+          acc = mma(al, sh[m], acc);
+          acc = mma(ah, sl[m], acc);
+        }
+        S[i] = acc;
+      }
+    }
   }
 
   // Operands of chunk n, copied in pieces so that the copies issue between the
@@ -800,7 +895,8 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
         dma_rows<16, NW>((const uint8_t*)kg + t0 * krow_bytes, krow_bytes, L, ktab, kdst, wave_u);
       }
     } else if (part == 1) {
-      if constexpr (F32) {
+      if constexpr (TRANS) {
+      } else if constexpr (F32) {
         dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec + 2 * WS_ROWS_BYTES, s_qh, wave_u, lane);
         dma_linear<(WS_ROWS_BYTES) / 16, NW>(krec + 3 * WS_ROWS_BYTES, s_ql, wave_u, lane);
       } else {
@@ -809,7 +905,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     } else if (part == 2) {
       dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec, s_tp, wave_u, lane);
       dma_linear<4 * CH * 4 / 16, NW>(rec + WS_FAC_OFF, s_fac, wave_u, lane);
-    } else {
+    } else if (!TRANS || half == 0) {
       const uint8_t* vb = vg0 + t0 * vrow_bytes;
       if constexpr (F32) {
 #pragma unroll
@@ -826,6 +922,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     __builtin_amdgcn_sched_barrier(0);
   };
   auto stage_b = [&](int n) {
+    if constexpr (TRANS) return;
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * WS_REC_BYTES;
     dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec + 2 * WS_PL_BYTES, s_pp, wave_u, lane);
@@ -862,9 +959,9 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     }
   };
 
-  if (nch > 0) {
+  if (ne > nb) {
 #pragma unroll
-    for (int part = 0; part < 4; ++part) stage_a(0, part, s_k0, s_kl0);
+    for (int part = 0; part < 4; ++part) stage_a(nb, part, s_k0, s_kl0);
   }
 
   // one chunk; PAR = n & 1 picks the K buffers at compile time
@@ -879,8 +976,8 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 
     wait_vmem();
     __syncthreads();       // phase-A operands of chunk n are in LDS; phase B of n-1 is done
-    if constexpr (!F32) {
-      if (n > 0) write_ost();
+    if constexpr (!F32 && !TRANS) {
+      if (n > nb) write_ost();
     }
     stage_b(n);
 
@@ -891,9 +988,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * I + 4 * g4 + e;
-        // rows past the chunk end hold copies of its last row: read, then zero
+        // rows past the chunk end hold copies of its last row: read, then zero (and
+        // V = 0 for the transition columns of a transition launch)
         const float x = F32 ? (float)vraw[I][e] : bf2f(s_v[t * V_STRIDE + wave * 16 + c16]);
-        vr[I][e] = t < L ? x : 0.f;
+        vr[I][e] = (t < L && !(TRANS && half == 1)) ? x : 0.f;
       }
 
     f32x4 R[4], QS[4];
@@ -907,25 +1005,27 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           ak[m] = frag_rows(kcur, KS_STRIDE, 16 * I, 32 * m, lane);
-          aq[m] = frag_rows(s_qh, KS_STRIDE, 16 * I, 32 * m, lane);
+          if constexpr (!TRANS) aq[m] = frag_rows(s_qh, KS_STRIDE, 16 * I, 32 * m, lane);
         }
         f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           ks = mma(ak[m], sh[m], ks);
-          qs = mma(aq[m], sh[m], qs);
+          if constexpr (!TRANS) qs = mma(aq[m], sh[m], qs);
           ks = mma(ak[m], sl[m], ks);
-          qs = mma(aq[m], sl[m], qs);
+          if constexpr (!TRANS) qs = mma(aq[m], sl[m], qs);
           if constexpr (F32) {
             ks = mma(frag_rows(kcl, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], ks);
-            qs = mma(frag_rows(s_ql, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], qs);
+            if constexpr (!TRANS) qs = mma(frag_rows(s_ql, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], qs);
           }
         }
-        const float4 cq = *reinterpret_cast<const float4*>(&s_fac[CH + 16 * I + 4 * g4]);
-        QS[I][0] = cq.x * qs[0];
-        QS[I][1] = cq.y * qs[1];
-        QS[I][2] = cq.z * qs[2];
-        QS[I][3] = cq.w * qs[3];
+        if constexpr (!TRANS) {
+          const float4 cq = *reinterpret_cast<const float4*>(&s_fac[CH + 16 * I + 4 * g4]);
+          QS[I][0] = cq.x * qs[0];
+          QS[I][1] = cq.y * qs[1];
+          QS[I][2] = cq.z * qs[2];
+          QS[I][3] = cq.w * qs[3];
+        }
         const float4 c4 = *reinterpret_cast<const float4*>(&s_fac[16 * I + 4 * g4]);
         R[I][0] = vr[I][0] - c4.x * ks[0];
         R[I][1] = vr[I][1] - c4.y * ks[1];
@@ -976,14 +1076,14 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     __syncthreads();       // phase-B operands of chunk n are in LDS; phase A of n is done
     // the last chunk reloads its own phase-A operands (unread in phase B) so that the
     // copies stay unconditional and keep their places between the products
-    const int na = n + 1 < nch ? n + 1 : n;
+    const int na = n + 1 < ne ? n + 1 : n;
     stage_a(na, 0, knext, knl);
-    if constexpr (!F32) {
-      if (n > 0) store_o(n - 1);
+    if constexpr (!F32 && !TRANS) {
+      if (n > nb) store_o(n - 1);
     }
 
     // ================= phase B: O = scale (diag(e^g/|q|) Q S + P U); state update
-    {
+    if constexpr (!TRANS) {
       bf16x8 uh[2], ul[2];
       frag_acc_split(U[0], U[1], uh[0], ul[0]);
       frag_acc_split(U[2], U[3], uh[1], ul[1]);
@@ -1037,20 +1137,30 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
       }
     }
   };
-  for (int n = 0; n < nch; n += 2) {
+  for (int n = nb; n < ne; n += 2) {
     chunk(n, std::integral_constant<int, 0>());
-    if (n + 1 < nch) chunk(n + 1, std::integral_constant<int, 1>());
+    if (n + 1 < ne) chunk(n + 1, std::integral_constant<int, 1>());
   }
-  if constexpr (!F32) {
-    if (nch > 0) {
-      __syncthreads();     // every wave has read the tile of chunk nch-2
+  if constexpr (!F32 && !TRANS) {
+    if (ne > nb) {
+      __syncthreads();     // every wave has read the tile of chunk ne-2
       write_ost();
       __syncthreads();
-      store_o(nch - 1);
+      store_o(ne - 1);
     }
   }
 
-  if (p.state_out) {
+  if constexpr (TRANS) {
+    // A_g (transition columns) or B_g (V-driven columns) of this segment
+    float* sp = seg_rec + (int64_t)g * (2 * DK * DV) + (half == 1 ? 0 : DK * DV) + col;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp[(16 * i + 4 * g4 + e) * DV] = S[i][e];
+    return;
+  }
+
+  if (p.state_out && g == sg.G - 1) {
     float* sp = p.state_out + ((int64_t)s * Hv + h) * DK * DV + col;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -1066,6 +1176,7 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   int4* cinfo = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(ws) + ws_cmap_bytes(a.Ns));
   uint8_t* recs = reinterpret_cast<uint8_t*>(ws) + ws_map_bytes(a.N, a.Ns);
   uint8_t* krecs = recs + cmax * a.Hv * WS_REC_BYTES;
+  float* segs = reinterpret_cast<float*>(krecs + cmax * a.Hk * ws_krec_bytes(IO == IO_F32));
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, st, a.cu, a.Ns, a.N, cmax, cmap,
                      cinfo);
   hipError_t e = hipGetLastError();
@@ -1080,17 +1191,35 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   // workgroups per chain (64 dv columns each, one wave per SIMD) fit on the chip
   // at once, they give the shortest chain; beyond that one 8-wave workgroup per
   // chain (two waves per SIMD, operands staged once for all 128 columns) gives
-  // the higher throughput.
+  // the higher throughput.  With few chains and long sequences, each chain also
+  // splits into G segments (the intra-sequence scan): a transition launch and a
+  // normal launch, each filling the compute units.
   const int64_t pairs = (int64_t)a.Ns * a.Hv;
   const int64_t cus = a.cu_count > 0 ? a.cu_count : 256;
-  if (pairs * SweepSizes<IO, 4>::NBLK <= cus)
-    hipLaunchKernelGGL((chunk_sweep_kernel<IO, 4>), dim3((unsigned)(pairs * SweepSizes<IO, 4>::NBLK)),
-                       dim3(SweepSizes<IO, 4>::THR), 0, st, a, (const int32_t*)cmap,
-                       (const uint8_t*)recs, (const uint8_t*)krecs);
-  else
-    hipLaunchKernelGGL((chunk_sweep_kernel<IO, 8>), dim3((unsigned)(pairs * SweepSizes<IO, 8>::NBLK)),
+  const int G = seg_count(a.N, a.Ns, a.Hv, cus);
+  // grid of a sweep launch: groups (sequence, key head, segment) padded to a multiple of 8,
+  // times the members of a group (value heads of the key head x column blocks)
+  auto grid = [&](int segs_in_launch, int nb) {
+    const int64_t groups = (int64_t)a.Ns * a.Hk * segs_in_launch;
+    return dim3((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * nb));
+  };
+  SegArgs sg{G, 0, G, segs};
+  if (G > 1) {
+    SegArgs tr{G, 0, G - 1, segs};
+    hipLaunchKernelGGL((chunk_sweep_kernel<IO, 8, true>), grid(G - 1, 2 * SweepSizes<IO, 8>::NBLK),
                        dim3(SweepSizes<IO, 8>::THR), 0, st, a, (const int32_t*)cmap,
-                       (const uint8_t*)recs, (const uint8_t*)krecs);
+                       (const uint8_t*)recs, (const uint8_t*)krecs, tr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (pairs * G * SweepSizes<IO, 4>::NBLK <= cus)
+    hipLaunchKernelGGL((chunk_sweep_kernel<IO, 4, false>), grid(G, SweepSizes<IO, 4>::NBLK),
+                       dim3(SweepSizes<IO, 4>::THR), 0, st, a, (const int32_t*)cmap,
+                       (const uint8_t*)recs, (const uint8_t*)krecs, sg);
+  else
+    hipLaunchKernelGGL((chunk_sweep_kernel<IO, 8, false>), grid(G, SweepSizes<IO, 8>::NBLK),
+                       dim3(SweepSizes<IO, 8>::THR), 0, st, a, (const int32_t*)cmap,
+                       (const uint8_t*)recs, (const uint8_t*)krecs, sg);
   return hipGetLastError();
 }
 

@@ -132,6 +132,23 @@ def test_chunk_prefill_parity_many_chains(io):
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("lens", [[1600], [1500, 37, 2000, 0]], ids=["one", "varlen"])
+def test_chunk_prefill_parity_segmented(io, lens):
+    """Few chains and long sequences: each chain splits into segments (6 for one
+    1600-token sequence at 2 heads, 3 for the varlen case, where the 37-token and the
+    empty sequence leave segments without chunks) that run in parallel from transition
+    matrices formed by a first pass."""
+    hk, hv = 1, 2
+    inp = _case(hk, hv, io, 51 + len(lens), seqlens=lens, init_state=True)
+    y, o, s = _run_prefill(inp, io)
+    o_ref, s_ref = G.prefill(y[:, :hk * D], y[:, hk * D:2 * hk * D], y[:, 2 * hk * D:],
+                             inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv, D, D,
+                             inp["state_in"], inp["cu_seqlens"])
+    assert_out(o, G.to_io(o_ref, io), io, "prefill o")
+    assert_state(s, s_ref, "prefill state")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_chunk_prefill_zero_state_single_sequence(io):
     inp = _case(2, 4, io, 31, seqlens=[257], init_state=False)
     y, o, s = _run_prefill(inp, io, with_state=False)
