@@ -21,13 +21,14 @@
 //      raw K and Q rows in LDS, forms K K^T and Q K^T on MFMA once for the value
 //      heads sharing the key head, then per value head inverts I + A (blocked:
 //      fp32 forward substitution on the diagonal blocks, fp32 MFMA products off
-//      it) and writes T' = T diag(beta) and P as bf16 hi/lo planes plus the
-//      per-token factors to the workspace.
+//      it) and writes T' = T diag(beta) as bf16 hi/lo planes plus the per-token
+//      factors to the workspace.
 //   3. sweep: one workgroup per (sequence, value head, block of dv columns; 4 or 8
 //      waves of 16 columns).  Each wave keeps a 128 x 16 slice of the fp32 state in
 //      registers for the whole sequence and walks the chunks in order; per chunk
-//      only the S-dependent products run (K S, T' R, Q S + P U, K^T U), on
-//      operands staged in LDS by DMA while the other phase's products run.
+//      the S-dependent products (K S, T' R, Q S + P U, K^T U) and the chunk's P
+//      (from the Q and K rows it stages) run on operands staged in LDS by DMA
+//      while the other phase's products run.
 //
 // MFMA use: v_mfma_f32_16x16x32_bf16.  Operand fragments use a permuted
 // contraction index (lane group g, element e -> k = 4g + e for e < 4, 16 + 4g
@@ -59,14 +60,20 @@ constexpr int F_STRIDE = CH + 4;       // floats per A/T row
 //   chunk offsets: int32 [Ns + 1], padded to 256 bytes; chunk table: int4 [cmax]
 //     {sequence, valid rows, first token lo, hi}, padded to 256 bytes
 //     (cmax = ceil(N / 64) + Ns bounds the chunk count);
-//   per (global chunk c, value head h), 37888 bytes: T' hi, T' lo, P hi, P lo as
-//     row-major 64 x 72 (padded) bf16 planes, then 4 x 64 fp32 factors
-//     e^gamma/|k|, e^gamma/|q|, e^{gamma_L - gamma}/|k|, e^{gamma_L};
+//   per (global chunk c, value head h): T' hi, T' lo as row-major 64 x 72 (padded) bf16
+//     planes, then 8 x 64 fp32 per-token rows e^gamma/|k|, e^gamma/|q|,
+//     e^{gamma_L - gamma}/|k|, e^{gamma_L}, gamma, 1/|k|, 1/|q| (and one of padding),
+//     then, for the 4-wave sweep, P hi, P lo planes (38912 bytes; 20480 without P:
+//     the 8-wave sweep forms P from the Q and K rows it stages anyway);
 //   fp32 io only, per (global chunk c, key head kh): K hi, K lo, Q hi, Q lo rows
 //     (64 x 136 bf16 each); bf16 io stages K and Q straight from the input rows.
 constexpr int64_t WS_PL_BYTES = (int64_t)CH * T_STRIDE * 2;          // 9216 per plane
-constexpr int64_t WS_FAC_OFF = 4 * WS_PL_BYTES;                       // 36864
-constexpr int64_t WS_REC_BYTES = WS_FAC_OFF + 4 * CH * 4;             // 37888
+constexpr int64_t WS_FAC_OFF = 2 * WS_PL_BYTES;                       // 18432
+constexpr int FAC_ROWS = 8;    // factor rows of 64 fp32 (row 7 is padding)
+constexpr int64_t WS_P_OFF = WS_FAC_OFF + FAC_ROWS * CH * 4;          // 20480
+__host__ __device__ constexpr int64_t ws_rec_bytes(bool with_p) {
+  return WS_P_OFF + (with_p ? 2 * WS_PL_BYTES : 0);                   // 38912 / 20480
+}
 constexpr int64_t WS_ROWS_BYTES = (int64_t)CH * KS_STRIDE * 2;       // 17408 per row plane
 
 static int64_t ws_max_chunks(int64_t N, int Ns) { return (N + CH - 1) / CH + Ns; }
@@ -105,7 +112,7 @@ static int seg_count(int64_t N, int Ns, int Hv, int64_t cus) {
 
 size_t chunk_workspace_bytes(int64_t N, int Ns, int Hk, int Hv, bool f32) {
   const int64_t cmax = ws_max_chunks(N, Ns);
-  return (size_t)(ws_map_bytes(N, Ns) + cmax * Hv * WS_REC_BYTES + cmax * Hk * ws_krec_bytes(f32) +
+  return (size_t)(ws_map_bytes(N, Ns) + cmax * Hv * ws_rec_bytes(true) + cmax * Hk * ws_krec_bytes(f32) +
                   ws_seg_bytes(Ns, Hv));
 }
 
@@ -353,8 +360,8 @@ struct PrepSmem {
   alignas(16) float rnq[CH];
 };
 
-template <int IO>
-__global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? 3 : 2)
+template <int IO, bool WITHP>
+__global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? (WITHP ? 3 : 4) : 2)
 chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restrict__ recs,
                   uint8_t* __restrict__ krecs) {
   typedef Io<IO> io;
@@ -406,7 +413,8 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   __syncthreads();
 
   // ---- raw Gram tiles, kept in registers: the 10 lower (I >= J) 16 x 16 tiles of
-  // rnk_i rnk_j (k_i . k_j) and rnq_i rnk_j (q_i . k_j); wave w holds tiles w, w+4, w+8
+  // rnk_i rnk_j (k_i . k_j) and, when P goes to the record, rnq_i rnk_j (q_i . k_j);
+  // wave w holds tiles w, w+4, w+8
   f32x4 gk[3], gq[3];
 #pragma unroll
   for (int tt = 0; tt < 3; ++tt) {
@@ -421,13 +429,13 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
       for (int m = 0; m < 4; ++m) {
         bk[m] = frag_rows(sm.u.r.kh, KS_STRIDE, 16 * J, 32 * m, lane);
         ak[m] = frag_rows(sm.u.r.kh, KS_STRIDE, 16 * I, 32 * m, lane);
-        aq[m] = frag_rows(sm.u.r.qh, KS_STRIDE, 16 * I, 32 * m, lane);
+        if constexpr (WITHP) aq[m] = frag_rows(sm.u.r.qh, KS_STRIDE, 16 * I, 32 * m, lane);
       }
       f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         a1 = mma(ak[m], bk[m], a1);
-        a2 = mma(aq[m], bk[m], a2);
+        if constexpr (WITHP) a2 = mma(aq[m], bk[m], a2);
       }
       if constexpr (F32) {
 #pragma unroll
@@ -435,8 +443,10 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
           const bf16x8 bl = frag_rows(sm.u.r.kl, KS_STRIDE, 16 * J, 32 * m, lane);
           a1 = mma(frag_rows(sm.u.r.kl, KS_STRIDE, 16 * I, 32 * m, lane), bk[m], a1);
           a1 = mma(ak[m], bl, a1);
-          a2 = mma(frag_rows(sm.u.r.ql, KS_STRIDE, 16 * I, 32 * m, lane), bk[m], a2);
-          a2 = mma(aq[m], bl, a2);
+          if constexpr (WITHP) {
+            a2 = mma(frag_rows(sm.u.r.ql, KS_STRIDE, 16 * I, 32 * m, lane), bk[m], a2);
+            a2 = mma(aq[m], bl, a2);
+          }
         }
       }
       const int j = 16 * J + c16, i0 = 16 * I + 4 * g4;
@@ -500,7 +510,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
       const int h = kh_ * r + hb + jb;
       const float* gam = sm.gam[jb];
       const float* bet = sm.beta[jb];
-      uint8_t* rec = recs + ((int64_t)c * Hv + h) * WS_REC_BYTES;
+      uint8_t* rec = recs + ((int64_t)c * Hv + h) * ws_rec_bytes(WITHP);
       __syncthreads();   // gates staged; the previous head's T is no longer read
 
       // ---- per-token factors for the sweep
@@ -513,10 +523,14 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
         fac[CH + tid] = eg * sm.rnq[tid];
         fac[2 * CH + tid] = __expf(gl - gt) * sm.rnk[tid];
         fac[3 * CH + tid] = __expf(gl);
+        fac[4 * CH + tid] = gt;
+        fac[5 * CH + tid] = sm.rnk[tid];
+        fac[6 * CH + tid] = sm.rnq[tid];
+        fac[7 * CH + tid] = 0.f;
       }
 
-      // ---- A (fp32) and P (bf16 hi/lo planes, staged in the T buffer) of this head;
-      // P's strictly-upper tiles are zero
+      // ---- A (fp32) and, for the 4-wave sweep, P (bf16 hi/lo planes staged in the T
+      // buffer, strictly-upper tiles zero) of this head
       u16* pst = reinterpret_cast<u16*>(tf);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
@@ -535,12 +549,14 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
             const int i = i0 + e;
             const float d = (i >= j) ? __expf(gi[e] - gj) : 0.f;   // exponent <= 0
             af[i * F_STRIDE + j] = (i > j) ? bi[e] * d * gk[tt < 3 ? tt : 0][e] : 0.f;
-            uint32_t ph, pl;
-            split2(d * gq[tt < 3 ? tt : 0][e], 0.f, ph, pl);
-            pst[i * CH + j] = (u16)ph;
-            pst[CH * CH + i * CH + j] = (u16)pl;
+            if constexpr (WITHP) {
+              uint32_t ph, pl;
+              split2(d * gq[tt < 3 ? tt : 0][e], 0.f, ph, pl);
+              pst[i * CH + j] = (u16)ph;
+              pst[CH * CH + i * CH + j] = (u16)pl;
+            }
           }
-        } else if (n < 16) {
+        } else if (WITHP && n < 16) {
           // strictly-upper tiles (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
           const int m = n - 10;
           const int I = (m >= 5) ? 2 : (m >= 3) ? 1 : 0;
@@ -554,18 +570,18 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
         }
       }
       __syncthreads();
-      // P planes to the workspace record, rows padded to 72 (four 16-byte words per thread)
-      {
+      if constexpr (WITHP) {
+        // P planes to the record, rows padded to 72 (four 16-byte words per thread)
         const uint4* src = reinterpret_cast<const uint4*>(pst);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const int i = tid + NTHR * it;        // plane i >> 9, row (i & 511) >> 3, word i & 7
           const int plane = i >> 9, row = (i & 511) >> 3, w = i & 7;
-          *reinterpret_cast<uint4*>(rec + (2 + plane) * WS_PL_BYTES + row * (T_STRIDE * 2) +
+          *reinterpret_cast<uint4*>(rec + WS_P_OFF + plane * WS_PL_BYTES + row * (T_STRIDE * 2) +
                                     w * 16) = src[i];
         }
+        __syncthreads();   // the T buffer is reused below
       }
-      __syncthreads();   // the T buffer is reused below
 
       // ---- T = (I + A)^{-1}, blocked: 16 x 16 diagonal blocks by forward substitution
       // (one column per lane); then T_10, T_32 = -T_ii A_ij T_jj; then the lower
@@ -742,6 +758,7 @@ struct SegArgs {
   int seg_base;   // first segment of this launch (normal launch)
   int seg_count;  // segments covered by this launch
   float* scratch; // per (sequence, head, segment < G-1): A (dk x dk), then B (dk x dv), fp32
+  int64_t rec_bytes;  // stride of the (chunk, head) records: with or without P
 };
 
 template <int IO, int NW, bool TRANS>
@@ -751,6 +768,9 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   typedef Io<IO> io;
   typedef typename io::T T;
   constexpr bool F32 = (IO == IO_F32);
+  // P: copied from the record by the 4-wave (latency-bound) shape, formed in the sweep
+  // from the staged Q and K rows by the 8-wave (throughput-bound) shape
+  constexpr bool PREC = (NW == 4);
   typedef SweepSizes<IO, NW> Z;
   constexpr int DVB = Z::DVB, NBLK = Z::NBLK, O_STRIDE = Z::O_STRIDE, V_STRIDE = Z::V_STRIDE;
   // K rows are double-buffered by chunk parity: chunk n's rows serve its K S products
@@ -762,8 +782,8 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   __shared__ __attribute__((aligned(16))) u16 s_qh[Z::ROWS];    // Q rows              phase A
   __shared__ __attribute__((aligned(16))) u16 s_ql[Z::ROWS_LO];
   __shared__ __attribute__((aligned(16))) u16 s_tp[Z::PL2];     // T' hi | lo          phase A
-  __shared__ __attribute__((aligned(16))) u16 s_pp[Z::PL2];     // P hi | lo           phase B
-  __shared__ __attribute__((aligned(16))) float s_fac[4 * CH];  // per-token factors    phase A
+  __shared__ __attribute__((aligned(16))) u16 s_pp[Z::PL2];     // P hi | lo (formed in phase A)
+  __shared__ __attribute__((aligned(16))) float s_fac[FAC_ROWS * CH];  // per-token factors  phase A
   __shared__ __attribute__((aligned(16))) u16 s_ost[Z::OST];    // output tile (bf16 io)
   __shared__ __attribute__((aligned(16))) u16 s_v[Z::VST];      // V slice (bf16 io)   phase A
 
@@ -840,14 +860,20 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
       for (int m = 0; m < 4; ++m) frag_acc_split(S[2 * m], S[2 * m + 1], sh[m], sl[m]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        // all of row tile i's loads first, so that they are in flight together
         f32x4 acc;
+        float4 xa[4][2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float* ar = Aj + (16 * i + c16) * DK + 32 * m + 4 * g4;
+          xa[m][0] = *reinterpret_cast<const float4*>(ar);
+          xa[m][1] = *reinterpret_cast<const float4*>(ar + 16);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = Bj[(16 * i + 4 * g4 + e) * DV + col];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float* ar = Aj + (16 * i + c16) * DK + 32 * m + 4 * g4;
-          const float4 x0 = *reinterpret_cast<const float4*>(ar);
-          const float4 x1 = *reinterpret_cast<const float4*>(ar + 16);
+          const float4 x0 = xa[m][0], x1 = xa[m][1];
           uint4 vh, vl;
           split2(x0.x, x0.y, vh.x, vl.x);
           split2(x0.z, x0.w, vh.y, vl.y);
@@ -884,7 +910,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     __builtin_amdgcn_sched_barrier(0);
     const int64_t t0 = b0 + (int64_t)n * CH;
     const int L = (int)min((int64_t)CH, b1 - t0);
-    const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * WS_REC_BYTES;
+    const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * sg.rec_bytes;
     const uint8_t* krec = krecs + ((int64_t)(c0 + n) * p.Hk + kh) * krec_bytes;
     if (part == 0) {
       if constexpr (F32) {
@@ -904,7 +930,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
       }
     } else if (part == 2) {
       dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec, s_tp, wave_u, lane);
-      dma_linear<4 * CH * 4 / 16, NW>(rec + WS_FAC_OFF, s_fac, wave_u, lane);
+      dma_linear<FAC_ROWS * CH * 4 / 16, NW>(rec + WS_FAC_OFF, s_fac, wave_u, lane);
     } else if (!TRANS || half == 0) {
       const uint8_t* vb = vg0 + t0 * vrow_bytes;
       if constexpr (F32) {
@@ -919,13 +945,6 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
         dma_rows<VW, NW>(vb, vrow_bytes, L, vtab, s_v, wave_u);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto stage_b = [&](int n) {
-    if constexpr (TRANS) return;
-    __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * WS_REC_BYTES;
-    dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec + 2 * WS_PL_BYTES, s_pp, wave_u, lane);
     __builtin_amdgcn_sched_barrier(0);
   };
   // bf16 io: a chunk's output stays in registers (packed pairs of rows) through the
@@ -959,6 +978,20 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     }
   };
 
+  auto stage_p = [&](int n) {     // phase-B operand of chunk n: the P planes of its record
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * sg.rec_bytes;
+    dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec + WS_P_OFF, s_pp, wave_u, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (!TRANS && !PREC) {
+    // P U reads the strictly-upper tiles (0,1) and (2,3) of P's planes: zero them once
+    for (int idx = tid; idx < 1024; idx += Z::THR) {
+      const int t = (idx >> 8) & 1, e = idx & 255;
+      const int i = 32 * t + (e >> 4), j = 32 * t + 16 + (e & 15);
+      s_pp[(idx >> 9) * CH * T_STRIDE + i * T_STRIDE + j] = 0;
+    }
+  }
   if (ne > nb) {
 #pragma unroll
     for (int part = 0; part < 4; ++part) stage_a(nb, part, s_k0, s_kl0);
@@ -979,7 +1012,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     if constexpr (!F32 && !TRANS) {
       if (n > nb) write_ost();
     }
-    stage_b(n);
+    if constexpr (!TRANS && PREC) stage_p(n);
 
     // ================= phase A: K S and Q S (S hi/lo), R, U = T' R
     float vr[4][4];
@@ -1031,6 +1064,40 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
         R[I][1] = vr[I][1] - c4.y * ks[1];
         R[I][2] = vr[I][2] - c4.z * ks[2];
         R[I][3] = vr[I][3] - c4.w * ks[3];
+      }
+    }
+    if constexpr (!TRANS && !PREC) {
+      // P of this chunk from its staged Q and K rows: the lower 16 x 16 tiles of
+      // e^{gamma_i - gamma_j} (q_i . k_j) / (|q_i| |k_j|) for j <= i < L, as bf16 hi/lo
+      // planes, spread over the waves; P U reads them after the phase barrier
+      const float* gam = s_fac + 4 * CH;
+      const float* rnk = s_fac + 5 * CH;
+      const float* rnq = s_fac + 6 * CH;
+      for (int tn = wave_u; tn < 10; tn += NW) {
+        int I, J;
+        tri_tile(tn, I, J);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x8 aq = frag_rows(s_qh, KS_STRIDE, 16 * I, 32 * m, lane);
+          const bf16x8 bk = frag_rows(kcur, KS_STRIDE, 16 * J, 32 * m, lane);
+          acc = mma(aq, bk, acc);
+          if constexpr (F32) {
+            acc = mma(frag_rows(s_ql, KS_STRIDE, 16 * I, 32 * m, lane), bk, acc);
+            acc = mma(aq, frag_rows(kcl, KS_STRIDE, 16 * J, 32 * m, lane), acc);
+          }
+        }
+        const int j = 16 * J + c16, i0 = 16 * I + 4 * g4;
+        const float gj = gam[j], rkj = rnk[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + e;
+          const float v = (i >= j && i < L) ? __expf(gam[i] - gj) * rnq[i] * rkj * acc[e] : 0.f;
+          uint32_t ph, pl;
+          split2(v, 0.f, ph, pl);
+          s_pp[i * T_STRIDE + j] = (u16)ph;
+          s_pp[CH * T_STRIDE + i * T_STRIDE + j] = (u16)pl;
+        }
       }
     }
     // U = T' R   (T' lower triangular: row tile I needs token slabs 0 .. I/2)
@@ -1175,15 +1242,25 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   int32_t* cmap = reinterpret_cast<int32_t*>(ws);
   int4* cinfo = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(ws) + ws_cmap_bytes(a.Ns));
   uint8_t* recs = reinterpret_cast<uint8_t*>(ws) + ws_map_bytes(a.N, a.Ns);
-  uint8_t* krecs = recs + cmax * a.Hv * WS_REC_BYTES;
+  uint8_t* krecs = recs + cmax * a.Hv * ws_rec_bytes(true);
   float* segs = reinterpret_cast<float*>(krecs + cmax * a.Hk * ws_krec_bytes(IO == IO_F32));
+  // launch shapes (see below): the normal sweep runs 4-wave workgroups, with P in the
+  // records, or 8-wave ones, which form P themselves
+  const int64_t pairs = (int64_t)a.Ns * a.Hv;
+  const int64_t cus = a.cu_count > 0 ? a.cu_count : 256;
+  const int G = seg_count(a.N, a.Ns, a.Hv, cus);
+  const bool four = pairs * G * SweepSizes<IO, 4>::NBLK <= cus;
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, st, a.cu, a.Ns, a.N, cmax, cmap,
                      cinfo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.N > 0) {
-    hipLaunchKernelGGL(chunk_prep_kernel<IO>, dim3((unsigned)cmax, (unsigned)a.Hk), dim3(NTHR), 0,
-                       st, a, (const int4*)cinfo, recs, krecs);
+    if (four)
+      hipLaunchKernelGGL((chunk_prep_kernel<IO, true>), dim3((unsigned)cmax, (unsigned)a.Hk),
+                         dim3(NTHR), 0, st, a, (const int4*)cinfo, recs, krecs);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<IO, false>), dim3((unsigned)cmax, (unsigned)a.Hk),
+                         dim3(NTHR), 0, st, a, (const int4*)cinfo, recs, krecs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1194,25 +1271,23 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   // the higher throughput.  With few chains and long sequences, each chain also
   // splits into G segments (the intra-sequence scan): a transition launch and a
   // normal launch, each filling the compute units.
-  const int64_t pairs = (int64_t)a.Ns * a.Hv;
-  const int64_t cus = a.cu_count > 0 ? a.cu_count : 256;
-  const int G = seg_count(a.N, a.Ns, a.Hv, cus);
   // grid of a sweep launch: groups (sequence, key head, segment) padded to a multiple of 8,
   // times the members of a group (value heads of the key head x column blocks)
   auto grid = [&](int segs_in_launch, int nb) {
     const int64_t groups = (int64_t)a.Ns * a.Hk * segs_in_launch;
     return dim3((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * nb));
   };
-  SegArgs sg{G, 0, G, segs};
+  const int64_t rb = ws_rec_bytes(four);
+  SegArgs sg{G, 0, G, segs, rb};
   if (G > 1) {
-    SegArgs tr{G, 0, G - 1, segs};
+    SegArgs tr{G, 0, G - 1, segs, rb};
     hipLaunchKernelGGL((chunk_sweep_kernel<IO, 8, true>), grid(G - 1, 2 * SweepSizes<IO, 8>::NBLK),
                        dim3(SweepSizes<IO, 8>::THR), 0, st, a, (const int32_t*)cmap,
                        (const uint8_t*)recs, (const uint8_t*)krecs, tr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (pairs * G * SweepSizes<IO, 4>::NBLK <= cus)
+  if (four)
     hipLaunchKernelGGL((chunk_sweep_kernel<IO, 4, false>), grid(G, SweepSizes<IO, 4>::NBLK),
                        dim3(SweepSizes<IO, 4>::THR), 0, st, a, (const int32_t*)cmap,
                        (const uint8_t*)recs, (const uint8_t*)krecs, sg);

@@ -91,13 +91,13 @@ def test_prefill_rejects():
     assert _prefill(ws=P, ws_bytes=1024) == _lib.GDN_ERR_INVALID_ARG
     assert "workspace" in _msg()
     # chunk offsets (int32 [Ns + 1]) and chunk table (int4 [cmax]), each padded to 256 B,
-    # then cmax = ceil(N/64) + Ns chunks x (Hv x 37888 B + Hk x K record), K record 0 B
+    # then cmax = ceil(N/64) + Ns chunks x (Hv x 38912 B + Hk x K record), K record 0 B
     # (bf16 io: K and Q are staged from the inputs) or 69632 B (fp32 io), then for at
     # most 64 (sequence, head) chains 7 segment-transition pairs of 128 KB per chain
     ws = _lib.lib().gdn_chunk_prefill_workspace_size
-    assert ws(4096, 1, 16, 32, 128, 1) == 256 + 1280 + 65 * (32 * 37888) + 7 * 32 * 131072
-    assert ws(4096, 3, 16, 32, 128, 1) == 256 + 1280 + 67 * (32 * 37888)
-    assert ws(100, 3, 1, 2, 128, 0) == 256 + 256 + 5 * (2 * 37888 + 1 * 69632) + 7 * 6 * 131072
+    assert ws(4096, 1, 16, 32, 128, 1) == 256 + 1280 + 65 * (32 * 38912) + 7 * 32 * 131072
+    assert ws(4096, 3, 16, 32, 128, 1) == 256 + 1280 + 67 * (32 * 38912)
+    assert ws(100, 3, 1, 2, 128, 0) == 256 + 256 + 5 * (2 * 38912 + 1 * 69632) + 7 * 6 * 131072
     assert ws(-1, 1, 16, 32, 128, 1) == 0
     assert ws(64, 1, 16, 32, 64, 1) == 0
 
