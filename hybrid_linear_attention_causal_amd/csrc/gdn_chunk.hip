@@ -139,13 +139,8 @@ __device__ __forceinline__ f32x4 tile_mma_f32(const float* x, int sx, const floa
   return c;
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 // two fp32 -> packed bf16 pair (hardware round-to-nearest-even)
-__device__ __forceinline__ uint32_t cvt2(float a, float b) {
-  const bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
+__device__ __forceinline__ uint32_t cvt2(float a, float b) { return f2bf2(a, b); }
 // hi = bf16(x), lo = bf16(x - hi) for a pair of values
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
   hi = cvt2(a, b);

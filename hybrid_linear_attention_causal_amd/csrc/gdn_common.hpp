@@ -16,11 +16,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------- bf16 <-> fp32
 __device__ __forceinline__ float bf2f(u16 h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// round-to-nearest-even fp32 -> bf16 (inputs are finite)
-__device__ __forceinline__ u16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (u16)(u >> 16);
+// round-to-nearest-even fp32 -> bf16 on the hardware converter (v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16 f2bf(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
+// two values packed, a in the low half
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------- io traits
@@ -63,17 +65,21 @@ template <> struct Io<IO_BF16> {
   }
   __device__ static __forceinline__ void st8(T* p, int64_t i, const float* v) {
     uint4 a;
-    a.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    a.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-    a.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-    a.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+    a.x = f2bf2(v[0], v[1]);
+    a.y = f2bf2(v[2], v[3]);
+    a.z = f2bf2(v[4], v[5]);
+    a.w = f2bf2(v[6], v[7]);
     *reinterpret_cast<uint4*>(p + i) = a;
   }
   __device__ static __forceinline__ float round(float v) { return bf2f(f2bf(v)); }
 };
 
 // ---------------------------------------------------------------- activations
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+// x sigmoid(x) on the hardware exp2 and reciprocal (a few ulp of fp32; e^{-x} rounding to
+// +inf for very negative x gives the limit 0)
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
 // log(1 + e^x); for x > 20 the correction is below fp32 resolution
 __device__ __forceinline__ float softplus(float x) { return x > 20.0f ? x : log1pf(expf(x)); }

@@ -5,9 +5,11 @@
 // carried between calls is the one of the KerasFormers Qwen page, "Generation".
 //
 // Layout: x, y [N, Cq] row-major (channels contiguous); each thread owns 8
-// consecutive channels and walks a tile of tokens, keeping the 3-row history
-// in registers, so every row of x is read with 16-byte (bf16) or 32-byte
-// (fp32) coalesced loads and the only re-read is the 3-row halo of each tile.
+// consecutive channels of a tile of 32 (bf16) or 16 (fp32) tokens, so every row of x
+// is read with 16-byte (bf16) or 32-byte (fp32) coalesced loads and the only re-read
+// is the 3-row halo of each tile.  A tile that lies inside one sequence issues all its
+// row loads at once (the kernel is bound by HBM, not by one load's latency per token);
+// a tile that crosses a sequence end walks its tokens one by one.
 // The final conv state is written by a second kernel after the main pass has
 // consumed conv_state_in, which makes in-place state updates safe.
 #include "gdn_common.hpp"
@@ -15,7 +17,8 @@
 
 namespace gdn {
 
-constexpr int CONV_TT = 32;      // tokens per thread
+// tokens per thread: bf16 rows stay packed (4 VGPRs each), fp32 rows take 8
+template <int IO> constexpr int conv_tt() { return IO == IO_BF16 ? 32 : 16; }
 constexpr int CONV_BLOCK = 256;  // threads per block (channel groups)
 
 // largest s with cu[s] <= t: the (non-empty) sequence that holds token t
@@ -28,14 +31,44 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int Ns, int64_t t) {
   return lo;
 }
 
+// 8 consecutive io elements kept as raw words until use
+template <int IO> struct Row8;
+template <> struct Row8<IO_BF16> {
+  uint4 w;
+  __device__ __forceinline__ void load(const u16* p) { w = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void get(float* v) const {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(u[j] << 16);
+      v[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct Row8<IO_F32> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// (two workgroups per CU: a 4096-token batch of 8192 bf16 channels is one pass of
+// 512 workgroups)
 template <int IO>
-__global__ void __launch_bounds__(CONV_BLOCK)
+__global__ void __launch_bounds__(CONV_BLOCK, 2)
 conv1d_silu_kernel(const typename Io<IO>::T* __restrict__ x, const float* __restrict__ w,
                    typename Io<IO>::T* __restrict__ y, const int32_t* __restrict__ cu, int Ns,
                    int64_t N, int Cq, const typename Io<IO>::T* __restrict__ state_in) {
   typedef Io<IO> io;
   const int c0 = (blockIdx.y * CONV_BLOCK + threadIdx.x) * 8;
   if (c0 >= Cq) return;
+  constexpr int CONV_TT = conv_tt<IO>();
   const int64_t t0 = (int64_t)blockIdx.x * CONV_TT;
   if (t0 >= N) return;
   const int64_t t1 = t0 + CONV_TT < N ? t0 + CONV_TT : N;
@@ -50,6 +83,40 @@ conv1d_silu_kernel(const typename Io<IO>::T* __restrict__ x, const float* __rest
   int s = cu ? find_seq(cu, Ns, t0) : 0;
   int64_t sb = cu ? (int64_t)cu[s] : 0;
   int64_t se = cu ? (int64_t)cu[s + 1] : N;
+
+  if (t0 + CONV_TT <= se) {
+    // the whole tile lies in sequence s: rows t0-3 .. t0+CONV_TT-1, the ones before the
+    // sequence start from its conv state (or zeros)
+    Row8<IO> rows[CONV_TT + 3];
+#pragma unroll
+    for (int r = 0; r < CONV_TT + 3; ++r) {
+      const int64_t p = t0 - 3 + r;
+      if (p >= sb)
+        rows[r].load(x + p * Cq + c0);
+      else if (state_in)
+        rows[r].load(state_in + ((int64_t)s * 3 + (p - sb + 3)) * Cq + c0);
+      else
+        rows[r].zero();
+    }
+#pragma unroll
+    for (int t = 0; t < CONV_TT; ++t) {
+      float v0[8], v1[8], v2[8], v3[8], out[8];
+      rows[t].get(v0);
+      rows[t + 1].get(v1);
+      rows[t + 2].get(v2);
+      rows[t + 3].get(v3);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float acc = wt[0][j] * v0[j];
+        acc = fmaf(wt[1][j], v1[j], acc);
+        acc = fmaf(wt[2][j], v2[j], acc);
+        acc = fmaf(wt[3][j], v3[j], acc);
+        out[j] = silu(acc);
+      }
+      io::st8(y, (t0 + t) * Cq + c0, out);
+    }
+    return;
+  }
 
   // h[0] = row t-3, h[1] = row t-2, h[2] = row t-1
   float h[3][8];
@@ -138,7 +205,7 @@ static hipError_t conv_impl(const ConvArgs& a, hipStream_t st) {
   typedef typename Io<IO>::T T;
   const int groups = (a.Cq / 8 + CONV_BLOCK - 1) / CONV_BLOCK;
   if (a.N > 0) {
-    const int64_t tiles = (a.N + CONV_TT - 1) / CONV_TT;
+    const int64_t tiles = (a.N + conv_tt<IO>() - 1) / conv_tt<IO>();
     dim3 grid((unsigned)tiles, (unsigned)groups);
     hipLaunchKernelGGL(conv1d_silu_kernel<IO>, grid, dim3(CONV_BLOCK), 0, st,
                        (const T*)a.x, a.w, (T*)a.y, a.cu, a.Ns, a.N, a.Cq,
