@@ -76,6 +76,16 @@ __host__ __device__ constexpr int64_t ws_rec_bytes(bool with_p) {
 }
 constexpr int64_t WS_ROWS_BYTES = (int64_t)CH * KS_STRIDE * 2;       // 17408 per row plane
 
+// Fragment-native records of the row-split sweep (bf16 io), per (global chunk, value
+// head), FR_REC_BYTES: T' fragments [row tile j 4][token slab m 2][plane hi, lo 2] (the A
+// operand of T' R; each fragment 1 KB, lane l's 16 bytes at 16 l), P fragments in the same
+// order, then the 8 x 64 fp32 factor rows.
+constexpr int64_t FR_T_OFF = 0;
+constexpr int64_t FR_P_OFF = 16 * 1024;
+constexpr int64_t FR_FAC_OFF = 32 * 1024;
+constexpr int64_t FR_REC_BYTES = FR_FAC_OFF + FAC_ROWS * CH * 4;     // 34816
+__host__ __device__ constexpr int fr_tp(int j, int m, int plane) { return ((j * 2 + m) * 2 + plane) * 1024; }
+
 static int64_t ws_max_chunks(int64_t N, int Ns) { return (N + CH - 1) / CH + Ns; }
 static int64_t ws_cmap_bytes(int Ns) { return (((int64_t)Ns + 1) * 4 + 255) / 256 * 256; }
 static int64_t ws_map_bytes(int64_t N, int Ns) {
@@ -183,6 +193,47 @@ __device__ __forceinline__ void frag_acc_split(f32x4 top, f32x4 bot, bf16x8& hi,
   split2(bot[2], bot[3], vh.w, vl.w);
   hi = __builtin_bit_cast(bf16x8, vh);
   lo = __builtin_bit_cast(bf16x8, vl);
+}
+
+// Y = M X for a lower-triangular 64 x 64 M (bf16 hi | lo planes, rows of T_STRIDE, in
+// LDS) and a 64 x 16 X given as B-operand fragments (hi, lo) of its two 32-row slabs:
+// three passes (Mh Xh, Ml Xh, Mh Xl).  Row tile I needs slabs 0 .. I / 2.  The products
+// run slab by slab and pass by pass over the row tiles, so that each accumulator's next
+// product is four (slab 0) or two (slab 1) products away; mid() runs between the slabs.
+template <typename F>
+__device__ __forceinline__ void tri_apply(const u16* mp, const bf16x8 (&xh)[2], const bf16x8 (&xl)[2],
+                                          f32x4 (&y)[4], int lane, F mid) {
+  const u16* mh = mp;
+  const u16* ml = mp + CH * T_STRIDE;
+  bf16x8 ah[4], al[4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    ah[I] = frag_rows(mh, T_STRIDE, 16 * I, 0, lane);
+    al[I] = frag_rows(ml, T_STRIDE, 16 * I, 0, lane);
+  }
+#pragma unroll
+  for (int I = 0; I < 4; ++I) y[I] = mma(ah[I], xh[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+  for (int I = 0; I < 4; ++I) y[I] = mma(al[I], xh[0], y[I]);
+#pragma unroll
+  for (int I = 0; I < 4; ++I) y[I] = mma(ah[I], xl[0], y[I]);
+  mid();
+  bf16x8 bh[2], bl[2];
+#pragma unroll
+  for (int I = 0; I < 2; ++I) {
+    bh[I] = frag_rows(mh, T_STRIDE, 16 * (I + 2), 32, lane);
+    bl[I] = frag_rows(ml, T_STRIDE, 16 * (I + 2), 32, lane);
+  }
+#pragma unroll
+  for (int I = 0; I < 2; ++I) y[I + 2] = mma(bh[I], xh[1], y[I + 2]);
+#pragma unroll
+  for (int I = 0; I < 2; ++I) y[I + 2] = mma(bl[I], xh[1], y[I + 2]);
+#pragma unroll
+  for (int I = 0; I < 2; ++I) y[I + 2] = mma(bh[I], xl[1], y[I + 2]);
+}
+__device__ __forceinline__ void tri_apply(const u16* mp, const bf16x8 (&xh)[2], const bf16x8 (&xl)[2],
+                                          f32x4 (&y)[4], int lane) {
+  tri_apply(mp, xh, xl, y, lane, []() {});
 }
 
 // lower-triangle tile list of a 4 x 4 grid of 16 x 16 tiles
@@ -326,6 +377,9 @@ __global__ void __launch_bounds__(256) chunk_map_kernel(const int32_t* cu, int N
 // (K^ K^T and Q^ K^T with the 1/|k|, 1/|q| factors) are formed once; then, per value
 // head, its decay and write strength scale the tiles into A and P, I + A is inverted,
 // and the head's record is written.
+// record layouts the prep kernel writes: rows without P (8-wave sweep), rows with P
+// (4-wave sweep), fragment-native with P and K^T (row-split sweep)
+enum PrepMode { PREP_ROWS = 0, PREP_ROWS_P = 1, PREP_FRAG = 2 };
 constexpr int PREP_RB = 4;                // value heads whose gates are staged at once
 static_assert(PREP_RB == NTHR / 64, "one wave stages the gates of one value head");
 
@@ -355,13 +409,18 @@ struct PrepSmem {
   alignas(16) float rnq[CH];
 };
 
-template <int IO, bool WITHP>
-__global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? (WITHP ? 3 : 4) : 2)
+template <int IO, int MODE>
+__global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? (MODE != PREP_ROWS ? 3 : 4) : 2)
 chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restrict__ recs,
                   uint8_t* __restrict__ krecs) {
   typedef Io<IO> io;
   typedef typename io::T T;
   constexpr bool F32 = (IO == IO_F32);
+  constexpr bool WITHP = MODE != PREP_ROWS;
+  constexpr bool FRAG = MODE == PREP_FRAG;
+  static_assert(!(FRAG && F32), "fragment-native records are for bf16 io");
+  constexpr int64_t REC = FRAG ? FR_REC_BYTES : ws_rec_bytes(WITHP);
+  constexpr int64_t FAC_OFF = FRAG ? FR_FAC_OFF : WS_FAC_OFF;
   __shared__ PrepSmem<IO> sm;
 
   const int c = blockIdx.x;               // global chunk
@@ -505,7 +564,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
       const int h = kh_ * r + hb + jb;
       const float* gam = sm.gam[jb];
       const float* bet = sm.beta[jb];
-      uint8_t* rec = recs + ((int64_t)c * Hv + h) * ws_rec_bytes(WITHP);
+      uint8_t* rec = recs + ((int64_t)c * Hv + h) * REC;
       __syncthreads();   // gates staged; the previous head's T is no longer read
 
       // ---- per-token factors for the sweep
@@ -513,7 +572,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
         const float gl = gam[CH - 1];
         const float gt = gam[tid];
         const float eg = __expf(gt);
-        float* fac = reinterpret_cast<float*>(rec + WS_FAC_OFF);
+        float* fac = reinterpret_cast<float*>(rec + FAC_OFF);
         fac[tid] = eg * sm.rnk[tid];
         fac[CH + tid] = eg * sm.rnq[tid];
         fac[2 * CH + tid] = __expf(gl - gt) * sm.rnk[tid];
@@ -565,7 +624,21 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
         }
       }
       __syncthreads();
-      if constexpr (WITHP) {
+      if constexpr (FRAG) {
+        // P fragments to the record: unit (plane, j, m, lane) gathers the lane's two 8-byte
+        // pieces of row 16 j + (lane & 15), columns 32 m + 4 (lane >> 4) .. and + 16
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int u = tid + NTHR * it;        // plane u >> 9, j (u >> 7) & 3, m (u >> 6) & 1
+          const int plane = u >> 9, jj = (u >> 7) & 3, m = (u >> 6) & 1, l = u & 63;
+          const u16* src = pst + plane * CH * CH + (16 * jj + (l & 15)) * CH + 32 * m + 4 * (l >> 4);
+          const uint2 lo8 = *reinterpret_cast<const uint2*>(src);
+          const uint2 hi8 = *reinterpret_cast<const uint2*>(src + 16);
+          *reinterpret_cast<uint4*>(rec + FR_P_OFF + fr_tp(jj, m, plane) + l * 16) =
+              make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
+        }
+        __syncthreads();   // the T buffer is reused below
+      } else if constexpr (WITHP) {
         // P planes to the record, rows padded to 72 (four 16-byte words per thread)
         const uint4* src = reinterpret_cast<const uint4*>(pst);
 #pragma unroll
@@ -638,7 +711,34 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
       }
       // ---- T' = T diag(beta), lower triangle, as bf16 hi/lo planes straight to the
       // workspace (4 consecutive columns per thread per step: 8-byte stores)
-      {
+      if constexpr (FRAG) {
+        // fragment order: unit (j, m, lane) splits the lane's 8 values of row 16 j + (lane &
+        // 15), columns 32 m + 4 (lane >> 4) .. + 3 and 32 m + 16 + 4 (lane >> 4) .. + 3
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int u = tid + NTHR * it;          // j u >> 7, m (u >> 6) & 1, lane u & 63
+          const int jj = u >> 7, m = (u >> 6) & 1, l = u & 63;
+          const int i = 16 * jj + (l & 15);
+          float v[8];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int j0 = 32 * m + 16 * half + 4 * (l >> 4);
+            const float4 t4 = *reinterpret_cast<const float4*>(&tf[i * F_STRIDE + j0]);
+            const float4 b4 = *reinterpret_cast<const float4*>(&bet[j0]);
+            v[4 * half + 0] = (j0 <= i) ? t4.x * b4.x : 0.f;
+            v[4 * half + 1] = (j0 + 1 <= i) ? t4.y * b4.y : 0.f;
+            v[4 * half + 2] = (j0 + 2 <= i) ? t4.z * b4.z : 0.f;
+            v[4 * half + 3] = (j0 + 3 <= i) ? t4.w * b4.w : 0.f;
+          }
+          uint4 hw, lw;
+          split2(v[0], v[1], hw.x, lw.x);
+          split2(v[2], v[3], hw.y, lw.y);
+          split2(v[4], v[5], hw.z, lw.z);
+          split2(v[6], v[7], hw.w, lw.w);
+          *reinterpret_cast<uint4*>(rec + FR_T_OFF + fr_tp(jj, m, 0) + l * 16) = hw;
+          *reinterpret_cast<uint4*>(rec + FR_T_OFF + fr_tp(jj, m, 1) + l * 16) = lw;
+        }
+      } else {
         u16* tph = reinterpret_cast<u16*>(rec);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -670,15 +770,36 @@ typedef __attribute__((address_space(3))) void lds_void;
 // scalar, and the sweep workgroup's waves take turns by instruction.  Every wave issues
 // the same number of copies (a wave past the last instruction repeats it, writing the
 // same bytes again), so a piece is straight-line code that stays where it is placed.
-template <int NS, int NW>   // 16-byte slots (a multiple of 64), waves taking turns
+// One LDS DMA copy (lane l's 16 bytes at src land at dst + 16 l).  OPAQUE = false uses
+// the compiler builtin, which makes later LDS reads wait for the copy unless the compiler
+// can prove them disjoint; OPAQUE = true issues it as inline assembly the compiler does not
+// track, for kernels that order every read of a copied buffer after an explicit
+// vmcnt(0) wait and a barrier themselves.
+template <bool OPAQUE>
+__device__ __forceinline__ void lds_dma16(const uint8_t* src, void* dst) {
+  if constexpr (OPAQUE) {
+    const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)dst;
+    // M0 carries the LDS destination; the kernels using this write M0 nowhere else
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+  } else {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+  }
+}
+
+template <int NS, int NW, bool OPAQUE = false>   // 16-byte slots (a multiple of 64), waves taking turns
 __device__ __forceinline__ void dma_linear(const uint8_t* src, void* dst, int wave, int lane) {
   static_assert(NS % 64 == 0, "whole instructions only");
   constexpr int INS = NS / 64;
 #pragma unroll
   for (int j = 0; j < (INS + NW - 1) / NW; ++j) {
     const int ins = min(wave + NW * j, INS - 1);
-    __builtin_amdgcn_global_load_lds(src + ins * 1024 + lane * 16,
-                                     (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
+    lds_dma16<OPAQUE>(src + ins * 1024 + lane * 16, (char*)dst + ins * 1024);
   }
 }
 
@@ -706,7 +827,7 @@ __device__ __forceinline__ void rows_table(int wave, int lane, uint32_t (&tab)[R
 // rows t0 .. t0+63 of one chunk into LDS; rows past the chunk end (L valid rows) repeat
 // the last valid row, which the chunk algebra multiplies by zero.  base = the chunk's
 // first row (wave-uniform), row_bytes < 2^24.
-template <int DW, int NW>
+template <int DW, int NW, bool OPAQUE = false>
 __device__ __forceinline__ void dma_rows(const uint8_t* base, uint32_t row_bytes, int L,
                                          const uint32_t (&tab)[RowDma<DW, NW>::J], void* dst,
                                          int wave) {
@@ -716,12 +837,23 @@ __device__ __forceinline__ void dma_rows(const uint8_t* base, uint32_t row_bytes
     const int ins = min(wave + NW * j, R::INS - 1);
     const uint32_t row = min(tab[j] & 0xFFu, (uint32_t)(L - 1));
     const uint32_t off = __umul24(row, row_bytes) + (tab[j] >> 8);
-    __builtin_amdgcn_global_load_lds(base + off, (lds_void*)((char*)dst + ins * 1024), 16, 0, 0);
+    lds_dma16<OPAQUE>(base + off, (char*)dst + ins * 1024);
   }
 }
 
 // wait for all of this wave's outstanding vector-memory operations (incl. LDS DMA)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier that orders LDS accesses only: this wave's LDS reads and writes have
+// completed (lgkmcnt 0) when it arrives, while its global loads and LDS DMA copies stay
+// in flight (a __syncthreads() would also wait for those).  The signal fences keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // LDS buffers of the sweep, one __shared__ object each so that the compiler can tell
 // the DMA destinations of one phase from the buffers the other phase reads.
@@ -1024,41 +1156,56 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 
     f32x4 R[4], QS[4];
     {
-      bf16x8 sh[4], sl[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) frag_acc_split(S[2 * m], S[2 * m + 1], sh[m], sl[m]);
+      // contraction slab outermost: the eight accumulators (K S and Q S for four row
+      // tiles) are independent, so consecutive products never wait on each other
+      f32x4 ks[4], qs[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
+        ks[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+        qs[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        bf16x8 sh, sl;
+        frag_acc_split(S[2 * m], S[2 * m + 1], sh, sl);
         bf16x8 ak[4], aq[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          ak[m] = frag_rows(kcur, KS_STRIDE, 16 * I, 32 * m, lane);
-          if constexpr (!TRANS) aq[m] = frag_rows(s_qh, KS_STRIDE, 16 * I, 32 * m, lane);
+        for (int I = 0; I < 4; ++I) {
+          ak[I] = frag_rows(kcur, KS_STRIDE, 16 * I, 32 * m, lane);
+          if constexpr (!TRANS) aq[I] = frag_rows(s_qh, KS_STRIDE, 16 * I, 32 * m, lane);
         }
-        f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          ks = mma(ak[m], sh[m], ks);
-          if constexpr (!TRANS) qs = mma(aq[m], sh[m], qs);
-          ks = mma(ak[m], sl[m], ks);
-          if constexpr (!TRANS) qs = mma(aq[m], sl[m], qs);
-          if constexpr (F32) {
-            ks = mma(frag_rows(kcl, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], ks);
-            if constexpr (!TRANS) qs = mma(frag_rows(s_ql, KS_STRIDE, 16 * I, 32 * m, lane), sh[m], qs);
+        for (int I = 0; I < 4; ++I) {
+          ks[I] = mma(ak[I], sh, ks[I]);
+          if constexpr (!TRANS) qs[I] = mma(aq[I], sh, qs[I]);
+        }
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          ks[I] = mma(ak[I], sl, ks[I]);
+          if constexpr (!TRANS) qs[I] = mma(aq[I], sl, qs[I]);
+        }
+        if constexpr (F32) {
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            ks[I] = mma(frag_rows(kcl, KS_STRIDE, 16 * I, 32 * m, lane), sh, ks[I]);
+            if constexpr (!TRANS) qs[I] = mma(frag_rows(s_ql, KS_STRIDE, 16 * I, 32 * m, lane), sh, qs[I]);
           }
         }
+      }
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
         if constexpr (!TRANS) {
           const float4 cq = *reinterpret_cast<const float4*>(&s_fac[CH + 16 * I + 4 * g4]);
-          QS[I][0] = cq.x * qs[0];
-          QS[I][1] = cq.y * qs[1];
-          QS[I][2] = cq.z * qs[2];
-          QS[I][3] = cq.w * qs[3];
+          QS[I][0] = cq.x * qs[I][0];
+          QS[I][1] = cq.y * qs[I][1];
+          QS[I][2] = cq.z * qs[I][2];
+          QS[I][3] = cq.w * qs[I][3];
         }
         const float4 c4 = *reinterpret_cast<const float4*>(&s_fac[16 * I + 4 * g4]);
-        R[I][0] = vr[I][0] - c4.x * ks[0];
-        R[I][1] = vr[I][1] - c4.y * ks[1];
-        R[I][2] = vr[I][2] - c4.z * ks[2];
-        R[I][3] = vr[I][3] - c4.w * ks[3];
+        R[I][0] = vr[I][0] - c4.x * ks[I][0];
+        R[I][1] = vr[I][1] - c4.y * ks[I][1];
+        R[I][2] = vr[I][2] - c4.z * ks[I][2];
+        R[I][3] = vr[I][3] - c4.w * ks[I][3];
       }
     }
     if constexpr (!TRANS && !PREC) {
@@ -1095,26 +1242,15 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
         }
       }
     }
-    // U = T' R   (T' lower triangular: row tile I needs token slabs 0 .. I/2)
+    // U = T' R   (T' lower triangular: row tile I needs token slabs 0 .. I/2); the
+    // products are ordered so that each accumulator's next product is four (slab 0) or
+    // two (slab 1) products away
     f32x4 U[4];
     {
       bf16x8 rh[2], rl[2];
       frag_acc_split(R[0], R[1], rh[0], rl[0]);
       frag_acc_split(R[2], R[3], rh[1], rl[1]);
-      const u16* th = s_tp;
-      const u16* tl = s_tp + CH * T_STRIDE;
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        U[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m <= I / 2; ++m) {
-          const bf16x8 ah = frag_rows(th, T_STRIDE, 16 * I, 32 * m, lane);
-          const bf16x8 al = frag_rows(tl, T_STRIDE, 16 * I, 32 * m, lane);
-          U[I] = mma(ah, rh[m], U[I]);
-          U[I] = mma(al, rh[m], U[I]);
-          U[I] = mma(ah, rl[m], U[I]);
-        }
-      }
+      tri_apply(s_tp, rh, rl, U, lane);
     }
     // the state update's right operand diag(e^{gamma_L - gamma} / |k|) U, and e^{gamma_L}:
     // every factor is read in phase A, since the next chunk's factors land in phase B
@@ -1149,22 +1285,13 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
       bf16x8 uh[2], ul[2];
       frag_acc_split(U[0], U[1], uh[0], ul[0]);
       frag_acc_split(U[2], U[3], uh[1], ul[1]);
-      const u16* ph = s_pp;
-      const u16* pl = s_pp + CH * T_STRIDE;
+      f32x4 pu[4];
+      tri_apply(s_pp, uh, ul, pu, lane, [&]() { stage_a(na, 1, knext, knl); });
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        f32x4 pu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m <= I / 2; ++m) {
-          const bf16x8 ah = frag_rows(ph, T_STRIDE, 16 * I, 32 * m, lane);
-          const bf16x8 al = frag_rows(pl, T_STRIDE, 16 * I, 32 * m, lane);
-          pu = mma(ah, uh[m], pu);
-          pu = mma(al, uh[m], pu);
-          pu = mma(ah, ul[m], pu);
-        }
         float ov[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = p.scale * (QS[I][e] + pu[e]);
+        for (int e = 0; e < 4; ++e) ov[e] = p.scale * (QS[I][e] + pu[I][e]);
         if constexpr (F32) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -1175,27 +1302,31 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
           opk[I][0] = cvt2(ov[0], ov[1]);
           opk[I][1] = cvt2(ov[2], ov[3]);
         }
-        if (I == 1) stage_a(na, 1, knext, knl);
       }
     }
     stage_a(na, 2, knext, knl);
     // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U, K^T read transposed
-    // from this chunk's K rows
+    // from this chunk's K rows; token slab outermost, so the eight row tiles' products
+    // are independent
     {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bf16x8 ak[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) ak[m] = frag_kt(kcur, 16 * i, 32 * m, lane);
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[i][e] *= egl;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          S[i] = mma(ak[m], wh[m], S[i]);
-          S[i] = mma(ak[m], wl[m], S[i]);
-          if constexpr (F32) S[i] = mma(frag_kt(kcl, 16 * i, 32 * m, lane), wh[m], S[i]);
+      for (int m = 0; m < 2; ++m) {
+        bf16x8 ak[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ak[i] = frag_kt(kcur, 16 * i, 32 * m, lane);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) S[i] = mma(ak[i], wh[m], S[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) S[i] = mma(ak[i], wl[m], S[i]);
+        if constexpr (F32) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) S[i] = mma(frag_kt(kcl, 16 * i, 32 * m, lane), wh[m], S[i]);
         }
-        if (i == 3) stage_a(na, 3, knext, knl);
+        if (m == 0) stage_a(na, 3, knext, knl);
       }
     }
   };
@@ -1231,6 +1362,310 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   }
 }
 
+// ============================================================================ 3b. row-split sweep
+// For few (sequence, head) chains (bf16 io): one 4-wave workgroup per (sequence, value
+// head, 16 dv columns).  Wave j keeps state rows 32 j .. 32 j + 31 of the 16 columns (two
+// accumulator tiles) and owns token row tile j (tokens 16 j .. 16 j + 15) of the chunk's
+// R, U and O, so each wave does a quarter of the column's products and hi/lo splits.
+// The K and Q rows are copied to LDS by DMA (K double-buffered by chunk parity: its rows
+// serve K S and, read transposed, the state update); each wave's T' and P fragments, its
+// factors and V come from the fragment-native records and the input straight into
+// registers, one chunk ahead.  Per chunk, three barriers separate:
+//   A  (after barrier 1): K S and Q S for row tile j from the four waves' state slabs
+//      (exchanged as ready bf16 hi/lo fragments), R = V - diag(e^g/|k|) K S;
+//   A2 (after barrier 2): U = T' R for row tile j from the exchanged R tiles;
+//   B  (after barrier 3): O = scale (diag(e^g/|q|) Q S + P U) for row tile j, stored
+//      directly, and the update of the wave's state slab from the exchanged U tiles.
+// The copies of chunk n+1's K rows issue in pieces between chunk n's phase-A products, its
+// Q rows between the phase-B products, so that no wave stalls on a full memory queue.
+// the row-split sweep is used while its workgroups fill the compute units at most this
+// many times over
+constexpr int ROWSPLIT_CU_ROUNDS = 2;
+namespace rs {
+constexpr int NW = 4;
+constexpr int THR = 64 * NW;
+constexpr int DVB = 16;                  // dv columns per workgroup
+constexpr int NBLK = DV / DVB;           // workgroups per chain
+constexpr int ROWS = CH * KS_STRIDE;
+constexpr int KJ = RowDma<16, NW>::J;    // K or Q row copies per wave
+}  // namespace rs
+
+// one chunk's register operands of wave j
+struct RsOps {
+  bf16x8 th[2], tl[2];      // T' row tile j, token slabs 0, 1 (hi, lo)
+  bf16x8 ph[2], pl[2];      // P row tile j
+  float4 ck, cq, c2;        // e^g/|k|, e^g/|q|, e^{g_L - g}/|k| for tokens 16 j + 4 g4 ..
+  float egl;                // e^{g_L}
+  u16 v[4];                 // V of the lane's 4 tokens (the last row repeats past the end)
+};
+
+// the j-th row copy of this wave (see dma_rows), OPAQUE
+template <int DW, int NW>
+__device__ __forceinline__ void dma_row_piece(const uint8_t* base, uint32_t row_bytes, int L,
+                                              uint32_t tab, void* dst, int wave, int jp) {
+  typedef RowDma<DW, NW> R;
+  const int ins = min(wave + NW * jp, R::INS - 1);
+  const uint32_t row = min(tab & 0xFFu, (uint32_t)(L - 1));
+  lds_dma16<true>(base + __umul24(row, row_bytes) + (tab >> 8), (char*)dst + ins * 1024);
+}
+
+__global__ void __launch_bounds__(rs::THR, 2)
+chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
+  typedef Io<IO_BF16> io;
+  typedef io::T T;
+  using namespace rs;
+  __shared__ __attribute__((aligned(16))) u16 s_k0[ROWS];     // K rows, even chunks
+  __shared__ __attribute__((aligned(16))) u16 s_k1[ROWS];     // K rows, odd chunks
+  __shared__ __attribute__((aligned(16))) u16 s_q[ROWS];      // Q rows
+  __shared__ __attribute__((aligned(16))) uint4 s_sx[4][2][64];        // state slabs: hi, lo fragments
+  __shared__ __attribute__((aligned(16))) f32x4 s_rx[4][64];           // R row tiles
+  __shared__ __attribute__((aligned(16))) uint2 s_ux[4][4][64];        // U tiles: U hi, U lo, Us hi, Us lo
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int j = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave's row group
+  const int g4 = lane >> 4;
+  const int c16 = lane & 15;
+
+  // workgroups come in groups (sequence, key head) of r value heads x NBLK column blocks;
+  // a group's members get ids congruent mod 8, so they share one XCD's L2
+  const int Hv = p.Hv, r = Hv / p.Hk;
+  const int GS = r * NBLK;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int member = slot % GS;
+  const int group = (slot / GS) * 8 + xcd;
+  if (group >= p.Ns * p.Hk) return;
+  const int blk = member % NBLK;
+  const int kh = group % p.Hk;
+  const int s = group / p.Hk;
+  const int h = kh * r + member / NBLK;
+  int64_t b0, b1;
+  seq_bounds(p.cu, p.N, s, b0, b1);
+  const int c0 = cmap[s];
+  const int ne = (int)((b1 - b0 + CH - 1) / CH);
+  const int col = blk * DVB + c16;
+
+  const uint8_t* qg = (const uint8_t*)((const T*)p.q + (int64_t)kh * DK);
+  const uint8_t* kg = (const uint8_t*)((const T*)p.k + (int64_t)kh * DK);
+  const uint32_t qrow_bytes = (uint32_t)(p.stride_q * (int64_t)sizeof(T));
+  const uint32_t krow_bytes = (uint32_t)(p.stride_k * (int64_t)sizeof(T));
+  const T* vg = (const T*)p.v + (int64_t)h * DV + col;
+  T* og = (T*)p.o + (int64_t)h * DV + col;
+  const int64_t o_stride = (int64_t)Hv * DV;
+  uint32_t ktab[KJ];
+  rows_table<16, NW>(j, lane, ktab);
+
+  // ---- state slab: St[t] holds rows 32 j + 16 t + 4 g4 + e of column col
+  f32x4 St[2];
+  if (p.state_in) {
+    const float* sp = p.state_in + ((int64_t)s * Hv + h) * DK * DV + col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) St[t][e] = sp[(32 * j + 16 * t + 4 * g4 + e) * DV];
+  } else {
+    St[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    St[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto put_slab = [&]() {
+    bf16x8 hi, lo;
+    frag_acc_split(St[0], St[1], hi, lo);
+    s_sx[j][0][lane] = __builtin_bit_cast(uint4, hi);
+    s_sx[j][1][lane] = __builtin_bit_cast(uint4, lo);
+  };
+  auto chunk_rows = [&](int n, int64_t& t0, int& L) {
+    t0 = b0 + (int64_t)n * CH;
+    L = (int)min((int64_t)CH, b1 - t0);
+  };
+
+  // register operands of chunk n (every load unconditional, so that the compiler's count
+  // of loads in flight stays exact; token slab 1 of T' and P is zero for row tiles 0, 1)
+  auto load_ops = [&](int n, RsOps& o) {
+    int64_t t0;
+    int L;
+    chunk_rows(n, t0, L);
+    const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * FR_REC_BYTES;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      o.th[m] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, m, 0) + lane * 16);
+      o.tl[m] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, m, 1) + lane * 16);
+      o.ph[m] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, m, 0) + lane * 16);
+      o.pl[m] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, m, 1) + lane * 16);
+    }
+    const float* fac = reinterpret_cast<const float*>(rec + FR_FAC_OFF);
+    o.ck = *reinterpret_cast<const float4*>(fac + 16 * j + 4 * g4);
+    o.cq = *reinterpret_cast<const float4*>(fac + CH + 16 * j + 4 * g4);
+    o.c2 = *reinterpret_cast<const float4*>(fac + 2 * CH + 16 * j + 4 * g4);
+    o.egl = fac[3 * CH];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o.v[e] = vg[(t0 + min(16 * j + 4 * g4 + e, L - 1)) * p.stride_v];
+  };
+
+  RsOps oa, ob;
+  if (ne > 0) {
+    int64_t t0;
+    int L;
+    chunk_rows(0, t0, L);
+#pragma unroll
+    for (int jp = 0; jp < KJ; ++jp) {
+      dma_row_piece<16, NW>(kg + t0 * krow_bytes, krow_bytes, L, ktab[jp], s_k0, j, jp);
+      dma_row_piece<16, NW>(qg + t0 * qrow_bytes, qrow_bytes, L, ktab[jp], s_q, j, jp);
+    }
+    load_ops(0, oa);
+  }
+  put_slab();
+
+  auto chunk = [&](int n, const RsOps& cur, RsOps& nxt, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    const u16* const kcur = PAR ? s_k1 : s_k0;
+    u16* const knext = PAR ? s_k0 : s_k1;
+    int64_t t0;
+    int L;
+    chunk_rows(n, t0, L);
+    const int na = n + 1 < ne ? n + 1 : n;   // the last chunk reloads its own (unused)
+    int64_t ta;
+    int La;
+    chunk_rows(na, ta, La);
+    const uint8_t* kga = kg + ta * krow_bytes;
+    const uint8_t* qga = qg + ta * qrow_bytes;
+
+    wait_vmem();
+    lds_barrier();     // (1) chunk n's K and Q rows and the state slabs are in LDS
+    load_ops(na, nxt);
+
+    // ---- A: K S and Q S for row tile j (hi and lo passes in separate accumulators); the
+    // copies of chunk n+1's K rows go out between the products
+    f32x4 QS, R;
+    {
+      f32x4 ka = {0.f, 0.f, 0.f, 0.f}, kb = ka, qa = ka, qb = ka;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const bf16x8 sh = __builtin_bit_cast(bf16x8, s_sx[m][0][lane]);
+        const bf16x8 sl = __builtin_bit_cast(bf16x8, s_sx[m][1][lane]);
+        const bf16x8 ak = frag_rows(kcur, KS_STRIDE, 16 * j, 32 * m, lane);
+        const bf16x8 aq = frag_rows(s_q, KS_STRIDE, 16 * j, 32 * m, lane);
+        ka = mma(ak, sh, ka);
+        qa = mma(aq, sh, qa);
+        kb = mma(ak, sl, kb);
+        qb = mma(aq, sl, qb);
+        if (m < KJ) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[m], knext, j, m);
+      }
+#pragma unroll
+      for (int jp = 4; jp < KJ; ++jp) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[jp], knext, j, jp);
+      const float ckv[4] = {cur.ck.x, cur.ck.y, cur.ck.z, cur.ck.w};
+      const float cqv[4] = {cur.cq.x, cur.cq.y, cur.cq.z, cur.cq.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // V past the chunk end is zero
+        const float vv = 16 * j + 4 * g4 + e < L ? bf2f(cur.v[e]) : 0.f;
+        R[e] = vv - ckv[e] * (ka[e] + kb[e]);
+        QS[e] = cqv[e] * (qa[e] + qb[e]);
+      }
+      s_rx[j][lane] = R;
+    }
+    lds_barrier();     // (2) R tiles exchanged; every wave has read the state slabs and Q
+
+    // ---- A2: U = T' R for row tile j
+    {
+      bf16x8 rh, rl;
+      frag_acc_split(s_rx[0][lane], s_rx[1][lane], rh, rl);
+      f32x4 ua = mma(cur.th[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 ub = mma(cur.tl[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
+      ua = mma(cur.th[0], rl, ua);
+      if (j >= 2) {
+        bf16x8 rh1, rl1;
+        frag_acc_split(s_rx[2][lane], s_rx[3][lane], rh1, rl1);
+        ub = mma(cur.th[1], rh1, ub);
+        ua = mma(cur.tl[1], rh1, ua);
+        ub = mma(cur.th[1], rl1, ub);
+      }
+      const f32x4 U = ua + ub;
+      uint32_t uh0, ul0, uh1, ul1, wh0, wl0, wh1, wl1;
+      split2(U[0], U[1], uh0, ul0);
+      split2(U[2], U[3], uh1, ul1);
+      split2(cur.c2.x * U[0], cur.c2.y * U[1], wh0, wl0);
+      split2(cur.c2.z * U[2], cur.c2.w * U[3], wh1, wl1);
+      s_ux[j][0][lane] = make_uint2(uh0, uh1);
+      s_ux[j][1][lane] = make_uint2(ul0, ul1);
+      s_ux[j][2][lane] = make_uint2(wh0, wh1);
+      s_ux[j][3][lane] = make_uint2(wl0, wl1);
+    }
+    lds_barrier();     // (3) U tiles exchanged; every wave has read the R tiles
+
+    // ---- B: O = scale (Q S + P U) for row tile j; the copies of chunk n+1's Q rows go
+    // out between the products
+    {
+      const bf16x8 uh = pack8(s_ux[0][0][lane], s_ux[1][0][lane]);
+      const bf16x8 ul = pack8(s_ux[0][1][lane], s_ux[1][1][lane]);
+      f32x4 pa = mma(cur.ph[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 pb = mma(cur.pl[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
+      pa = mma(cur.ph[0], ul, pa);
+      dma_row_piece<16, NW>(qga, qrow_bytes, La, ktab[0], s_q, j, 0);
+      if (j >= 2) {
+        const bf16x8 uh1 = pack8(s_ux[2][0][lane], s_ux[3][0][lane]);
+        const bf16x8 ul1 = pack8(s_ux[2][1][lane], s_ux[3][1][lane]);
+        pb = mma(cur.ph[1], uh1, pb);
+        pa = mma(cur.pl[1], uh1, pa);
+        pb = mma(cur.ph[1], ul1, pb);
+      }
+      dma_row_piece<16, NW>(qga, qrow_bytes, La, ktab[1], s_q, j, 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * j + 4 * g4 + e;
+        if (t < L) og[(t0 + t) * o_stride] = f2bf(p.scale * (QS[e] + pa[e] + pb[e]));
+      }
+    }
+    // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U for state rows 32 j ..
+    // 32 j + 31, K^T read transposed from this chunk's K rows
+    {
+      bf16x8 wh[2], wl[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        wh[m] = pack8(s_ux[2 * m][2][lane], s_ux[2 * m + 1][2][lane]);
+        wl[m] = pack8(s_ux[2 * m][3][lane], s_ux[2 * m + 1][3][lane]);
+      }
+      bf16x8 ak[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) ak[t][m] = frag_kt(kcur, 32 * j + 16 * t, 32 * m, lane);
+      f32x4 sb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) St[t][e] *= cur.egl;
+        sb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          St[t] = mma(ak[t][m], wh[m], St[t]);
+          sb[t] = mma(ak[t][m], wl[m], sb[t]);
+        }
+        dma_row_piece<16, NW>(qga, qrow_bytes, La, ktab[2 + m], s_q, j, 2 + m);
+      }
+      St[0] += sb[0];
+      St[1] += sb[1];
+    }
+#pragma unroll
+    for (int jp = 4; jp < KJ; ++jp) dma_row_piece<16, NW>(qga, qrow_bytes, La, ktab[jp], s_q, j, jp);
+    put_slab();
+  };
+  for (int n = 0; n < ne; n += 2) {
+    chunk(n, oa, ob, std::integral_constant<int, 0>());
+    if (n + 1 < ne) chunk(n + 1, ob, oa, std::integral_constant<int, 1>());
+  }
+  wait_vmem();         // no copy is in flight when the workgroup ends
+  if (p.state_out) {
+    float* sp = p.state_out + ((int64_t)s * Hv + h) * DK * DV + col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp[(32 * j + 16 * t + 4 * g4 + e) * DV] = St[t][e];
+  }
+}
+
 template <int IO>
 static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   const int64_t cmax = ws_max_chunks(a.N, a.Ns);
@@ -1243,19 +1678,27 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   // records, or 8-wave ones, which form P themselves
   const int64_t pairs = (int64_t)a.Ns * a.Hv;
   const int64_t cus = a.cu_count > 0 ? a.cu_count : 256;
-  const int G = seg_count(a.N, a.Ns, a.Hv, cus);
-  const bool four = pairs * G * SweepSizes<IO, 4>::NBLK <= cus;
+  // bf16 io with few chains: the row-split sweep (eight 4-wave workgroups per chain)
+  const bool rowsplit = IO == IO_BF16 && pairs * rs::NBLK <= ROWSPLIT_CU_ROUNDS * cus;
+  const int G = rowsplit ? 1 : seg_count(a.N, a.Ns, a.Hv, cus);
+  const bool four = rowsplit || pairs * G * SweepSizes<IO, 4>::NBLK <= cus;
   hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, st, a.cu, a.Ns, a.N, cmax, cmap,
                      cinfo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.N > 0) {
-    if (four)
-      hipLaunchKernelGGL((chunk_prep_kernel<IO, true>), dim3((unsigned)cmax, (unsigned)a.Hk),
-                         dim3(NTHR), 0, st, a, (const int4*)cinfo, recs, krecs);
-    else
-      hipLaunchKernelGGL((chunk_prep_kernel<IO, false>), dim3((unsigned)cmax, (unsigned)a.Hk),
-                         dim3(NTHR), 0, st, a, (const int4*)cinfo, recs, krecs);
+    const dim3 pgrid((unsigned)cmax, (unsigned)a.Hk);
+    if constexpr (IO == IO_BF16) {
+      if (rowsplit)
+        hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG>), pgrid, dim3(NTHR), 0, st, a,
+                           (const int4*)cinfo, recs, krecs);
+    }
+    if (!rowsplit && four)
+      hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS_P>), pgrid, dim3(NTHR), 0, st, a,
+                         (const int4*)cinfo, recs, krecs);
+    else if (!rowsplit)
+      hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS>), pgrid, dim3(NTHR), 0, st, a,
+                         (const int4*)cinfo, recs, krecs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1273,6 +1716,13 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
     return dim3((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * nb));
   };
   const int64_t rb = ws_rec_bytes(four);
+  if (rowsplit) {
+    const int64_t groups = (int64_t)a.Ns * a.Hk;
+    const dim3 grid((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * rs::NBLK));
+    hipLaunchKernelGGL(chunk_rowsplit_kernel, grid, dim3(rs::THR), 0, st, a, (const int32_t*)cmap,
+                       (const uint8_t*)recs);
+    return hipGetLastError();
+  }
   SegArgs sg{G, 0, G, segs, rb};
   if (G > 1) {
     SegArgs tr{G, 0, G - 1, segs, rb};
