@@ -1367,17 +1367,20 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 // head, 16 dv columns).  Wave j keeps state rows 32 j .. 32 j + 31 of the 16 columns (two
 // accumulator tiles) and owns token row tile j (tokens 16 j .. 16 j + 15) of the chunk's
 // R, U and O, so each wave does a quarter of the column's products and hi/lo splits.
-// The K and Q rows are copied to LDS by DMA (K double-buffered by chunk parity: its rows
-// serve K S and, read transposed, the state update); each wave's T' and P fragments, its
-// factors and V come from the fragment-native records and the input straight into
-// registers, one chunk ahead.  Per chunk, three barriers separate:
+// Per chunk, three barriers separate:
 //   A  (after barrier 1): K S and Q S for row tile j from the four waves' state slabs
 //      (exchanged as ready bf16 hi/lo fragments), R = V - diag(e^g/|k|) K S;
 //   A2 (after barrier 2): U = T' R for row tile j from the exchanged R tiles;
-//   B  (after barrier 3): O = scale (diag(e^g/|q|) Q S + P U) for row tile j, stored
-//      directly, and the update of the wave's state slab from the exchanged U tiles.
-// The copies of chunk n+1's K rows issue in pieces between chunk n's phase-A products, its
-// Q rows between the phase-B products, so that no wave stalls on a full memory queue.
+//   B  (after barrier 3): O = scale (diag(e^g/|q|) Q S + P U) for row tile j and the
+//      update of the wave's state slab from the exchanged U tiles.
+// Operands: the K rows (double-buffered by chunk parity: they serve K S and, read
+// transposed, the state update), the Q rows, the factor rows and the V slice are copied
+// to LDS by DMA; each wave's T' and P fragments load from the fragment-native records
+// straight into registers, one chunk ahead.  Chunk n+1's K rows are copied in pieces
+// between chunk n's phase-A products, its Q rows, factors and V slice right after barrier
+// 2 (their chunk-n copies are read only in phase A).  Outputs leave through an LDS tile as
+// 16-byte rows after the next chunk's first barrier.  The LDS stays below half a CU's, so
+// two workgroups share a CU when the chains need it.
 // the row-split sweep is used while its workgroups fill the compute units at most this
 // many times over
 constexpr int ROWSPLIT_CU_ROUNDS = 2;
@@ -1388,18 +1391,18 @@ constexpr int DVB = 16;                  // dv columns per workgroup
 constexpr int NBLK = DV / DVB;           // workgroups per chain
 constexpr int ROWS = CH * KS_STRIDE;
 constexpr int KJ = RowDma<16, NW>::J;    // K or Q row copies per wave
+constexpr int VW = DVB * 2 / 16;         // 16-byte words per V row slice
+constexpr int V_STRIDE = DVB + 8;        // u16 per staged V row
+constexpr int O_STRIDE = DVB + 8;        // u16 per staged output row
 }  // namespace rs
 
-// one chunk's register operands of wave j
+// one chunk's register operands of wave j: T' and P of row tile j, token slabs 0, 1
 struct RsOps {
-  bf16x8 th[2], tl[2];      // T' row tile j, token slabs 0, 1 (hi, lo)
-  bf16x8 ph[2], pl[2];      // P row tile j
-  float4 ck, cq, c2;        // e^g/|k|, e^g/|q|, e^{g_L - g}/|k| for tokens 16 j + 4 g4 ..
-  float egl;                // e^{g_L}
-  u16 v[4];                 // V of the lane's 4 tokens (the last row repeats past the end)
+  bf16x8 th[2], tl[2];
+  bf16x8 ph[2], pl[2];
 };
 
-// the j-th row copy of this wave (see dma_rows), OPAQUE
+// the jp-th row copy of this wave (see dma_rows), issued as OPAQUE inline assembly
 template <int DW, int NW>
 __device__ __forceinline__ void dma_row_piece(const uint8_t* base, uint32_t row_bytes, int L,
                                               uint32_t tab, void* dst, int wave, int jp) {
@@ -1417,9 +1420,12 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
   __shared__ __attribute__((aligned(16))) u16 s_k0[ROWS];     // K rows, even chunks
   __shared__ __attribute__((aligned(16))) u16 s_k1[ROWS];     // K rows, odd chunks
   __shared__ __attribute__((aligned(16))) u16 s_q[ROWS];      // Q rows
+  __shared__ __attribute__((aligned(16))) float s_f[FAC_ROWS * CH];    // factor rows
+  __shared__ __attribute__((aligned(16))) u16 s_v[CH * V_STRIDE];      // V slice
   __shared__ __attribute__((aligned(16))) uint4 s_sx[4][2][64];        // state slabs: hi, lo fragments
-  __shared__ __attribute__((aligned(16))) f32x4 s_rx[4][64];           // R row tiles
+  __shared__ __attribute__((aligned(16))) uint2 s_rx[4][2][64];        // R tiles: hi, lo
   __shared__ __attribute__((aligned(16))) uint2 s_ux[4][4][64];        // U tiles: U hi, U lo, Us hi, Us lo
+  __shared__ __attribute__((aligned(16))) u16 s_ost[CH * O_STRIDE];    // output tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1447,13 +1453,15 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
 
   const uint8_t* qg = (const uint8_t*)((const T*)p.q + (int64_t)kh * DK);
   const uint8_t* kg = (const uint8_t*)((const T*)p.k + (int64_t)kh * DK);
+  const uint8_t* vg = (const uint8_t*)((const T*)p.v + (int64_t)h * DV + blk * DVB);
   const uint32_t qrow_bytes = (uint32_t)(p.stride_q * (int64_t)sizeof(T));
   const uint32_t krow_bytes = (uint32_t)(p.stride_k * (int64_t)sizeof(T));
-  const T* vg = (const T*)p.v + (int64_t)h * DV + col;
-  T* og = (T*)p.o + (int64_t)h * DV + col;
+  const uint32_t vrow_bytes = (uint32_t)(p.stride_v * (int64_t)sizeof(T));
+  T* og0 = (T*)p.o + (int64_t)h * DV + blk * DVB;
   const int64_t o_stride = (int64_t)Hv * DV;
-  uint32_t ktab[KJ];
+  uint32_t ktab[KJ], vtab[RowDma<VW, NW>::J];
   rows_table<16, NW>(j, lane, ktab);
+  rows_table<VW, NW>(j, lane, vtab);
 
   // ---- state slab: St[t] holds rows 32 j + 16 t + 4 g4 + e of column col
   f32x4 St[2];
@@ -1477,14 +1485,12 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
     t0 = b0 + (int64_t)n * CH;
     L = (int)min((int64_t)CH, b1 - t0);
   };
+  auto rec_of = [&](int n) { return recs + ((int64_t)(c0 + n) * Hv + h) * FR_REC_BYTES; };
 
-  // register operands of chunk n (every load unconditional, so that the compiler's count
-  // of loads in flight stays exact; token slab 1 of T' and P is zero for row tiles 0, 1)
+  // T' and P fragments of chunk n (every load unconditional, so that the compiler's count
+  // of loads in flight stays exact; token slab 1 is zero for row tiles 0, 1)
   auto load_ops = [&](int n, RsOps& o) {
-    int64_t t0;
-    int L;
-    chunk_rows(n, t0, L);
-    const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * FR_REC_BYTES;
+    const uint8_t* rec = rec_of(n);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       o.th[m] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, m, 0) + lane * 16);
@@ -1492,13 +1498,30 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
       o.ph[m] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, m, 0) + lane * 16);
       o.pl[m] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, m, 1) + lane * 16);
     }
-    const float* fac = reinterpret_cast<const float*>(rec + FR_FAC_OFF);
-    o.ck = *reinterpret_cast<const float4*>(fac + 16 * j + 4 * g4);
-    o.cq = *reinterpret_cast<const float4*>(fac + CH + 16 * j + 4 * g4);
-    o.c2 = *reinterpret_cast<const float4*>(fac + 2 * CH + 16 * j + 4 * g4);
-    o.egl = fac[3 * CH];
+  };
+  // copies of chunk n's Q rows, factor rows and V slice (single LDS buffers)
+  auto stage_qfv = [&](int n) {
+    int64_t t0;
+    int L;
+    chunk_rows(n, t0, L);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.v[e] = vg[(t0 + min(16 * j + 4 * g4 + e, L - 1)) * p.stride_v];
+    for (int jp = 0; jp < KJ; ++jp)
+      dma_row_piece<16, NW>(qg + t0 * qrow_bytes, qrow_bytes, L, ktab[jp], s_q, j, jp);
+    dma_linear<FAC_ROWS * CH * 4 / 16, NW, true>(rec_of(n) + FR_FAC_OFF, s_f, j, lane);
+    dma_rows<VW, NW, true>(vg + t0 * vrow_bytes, vrow_bytes, L, vtab, s_v, j);
+  };
+  // rows of the output tile of chunk n to global memory (16-byte pieces)
+  auto store_o = [&](int n) {
+    int64_t t0;
+    int L;
+    chunk_rows(n, t0, L);
+    constexpr int WPR = DVB / 8;
+    if (tid < CH * WPR) {
+      const int row = tid / WPR, w = tid % WPR;
+      if (row < L)
+        *reinterpret_cast<uint4*>(og0 + (t0 + row) * o_stride + w * 8) =
+            *reinterpret_cast<const uint4*>(&s_ost[row * O_STRIDE + w * 8]);
+    }
   };
 
   RsOps oa, ob;
@@ -1507,10 +1530,9 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
     int L;
     chunk_rows(0, t0, L);
 #pragma unroll
-    for (int jp = 0; jp < KJ; ++jp) {
+    for (int jp = 0; jp < KJ; ++jp)
       dma_row_piece<16, NW>(kg + t0 * krow_bytes, krow_bytes, L, ktab[jp], s_k0, j, jp);
-      dma_row_piece<16, NW>(qg + t0 * qrow_bytes, qrow_bytes, L, ktab[jp], s_q, j, jp);
-    }
+    stage_qfv(0);
     load_ops(0, oa);
   }
   put_slab();
@@ -1519,23 +1541,22 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
     constexpr int PAR = decltype(par)::value;
     const u16* const kcur = PAR ? s_k1 : s_k0;
     u16* const knext = PAR ? s_k0 : s_k1;
-    int64_t t0;
-    int L;
-    chunk_rows(n, t0, L);
     const int na = n + 1 < ne ? n + 1 : n;   // the last chunk reloads its own (unused)
     int64_t ta;
     int La;
     chunk_rows(na, ta, La);
     const uint8_t* kga = kg + ta * krow_bytes;
-    const uint8_t* qga = qg + ta * qrow_bytes;
 
     wait_vmem();
-    lds_barrier();     // (1) chunk n's K and Q rows and the state slabs are in LDS
+    lds_barrier();     // (1) chunk n's copies and the state slabs are in LDS
+    if (n > 0) store_o(n - 1);
     load_ops(na, nxt);
 
     // ---- A: K S and Q S for row tile j (hi and lo passes in separate accumulators); the
     // copies of chunk n+1's K rows go out between the products
     f32x4 QS, R;
+    float4 c2;
+    float egl;
     {
       f32x4 ka = {0.f, 0.f, 0.f, 0.f}, kb = ka, qa = ka, qb = ka;
 #pragma unroll
@@ -1552,29 +1573,43 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
       }
 #pragma unroll
       for (int jp = 4; jp < KJ; ++jp) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[jp], knext, j, jp);
-      const float ckv[4] = {cur.ck.x, cur.ck.y, cur.ck.z, cur.ck.w};
-      const float cqv[4] = {cur.cq.x, cur.cq.y, cur.cq.z, cur.cq.w};
+      // every factor and V are read here: their next copies land from barrier 2 on
+      const float4 ck = *reinterpret_cast<const float4*>(&s_f[16 * j + 4 * g4]);
+      const float4 cq = *reinterpret_cast<const float4*>(&s_f[CH + 16 * j + 4 * g4]);
+      c2 = *reinterpret_cast<const float4*>(&s_f[2 * CH + 16 * j + 4 * g4]);
+      egl = s_f[3 * CH];
+      const float ckv[4] = {ck.x, ck.y, ck.z, ck.w};
+      const float cqv[4] = {cq.x, cq.y, cq.z, cq.w};
+      int64_t t0;
+      int L;
+      chunk_rows(n, t0, L);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // V past the chunk end is zero
-        const float vv = 16 * j + 4 * g4 + e < L ? bf2f(cur.v[e]) : 0.f;
+        // rows past the chunk end hold copies of its last row: V is zero there
+        const int t = 16 * j + 4 * g4 + e;
+        const float vv = t < L ? bf2f(s_v[t * V_STRIDE + c16]) : 0.f;
         R[e] = vv - ckv[e] * (ka[e] + kb[e]);
         QS[e] = cqv[e] * (qa[e] + qb[e]);
       }
-      s_rx[j][lane] = R;
+      uint32_t rh0, rl0, rh1, rl1;
+      split2(R[0], R[1], rh0, rl0);
+      split2(R[2], R[3], rh1, rl1);
+      s_rx[j][0][lane] = make_uint2(rh0, rh1);
+      s_rx[j][1][lane] = make_uint2(rl0, rl1);
     }
-    lds_barrier();     // (2) R tiles exchanged; every wave has read the state slabs and Q
+    lds_barrier();     // (2) R tiles exchanged; every wave has read the slabs, Q, factors, V
+    stage_qfv(na);
 
     // ---- A2: U = T' R for row tile j
     {
-      bf16x8 rh, rl;
-      frag_acc_split(s_rx[0][lane], s_rx[1][lane], rh, rl);
+      const bf16x8 rh = pack8(s_rx[0][0][lane], s_rx[1][0][lane]);
+      const bf16x8 rl = pack8(s_rx[0][1][lane], s_rx[1][1][lane]);
       f32x4 ua = mma(cur.th[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 ub = mma(cur.tl[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
       ua = mma(cur.th[0], rl, ua);
       if (j >= 2) {
-        bf16x8 rh1, rl1;
-        frag_acc_split(s_rx[2][lane], s_rx[3][lane], rh1, rl1);
+        const bf16x8 rh1 = pack8(s_rx[2][0][lane], s_rx[3][0][lane]);
+        const bf16x8 rl1 = pack8(s_rx[2][1][lane], s_rx[3][1][lane]);
         ub = mma(cur.th[1], rh1, ub);
         ua = mma(cur.tl[1], rh1, ua);
         ub = mma(cur.th[1], rl1, ub);
@@ -1583,8 +1618,8 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
       uint32_t uh0, ul0, uh1, ul1, wh0, wl0, wh1, wl1;
       split2(U[0], U[1], uh0, ul0);
       split2(U[2], U[3], uh1, ul1);
-      split2(cur.c2.x * U[0], cur.c2.y * U[1], wh0, wl0);
-      split2(cur.c2.z * U[2], cur.c2.w * U[3], wh1, wl1);
+      split2(c2.x * U[0], c2.y * U[1], wh0, wl0);
+      split2(c2.z * U[2], c2.w * U[3], wh1, wl1);
       s_ux[j][0][lane] = make_uint2(uh0, uh1);
       s_ux[j][1][lane] = make_uint2(ul0, ul1);
       s_ux[j][2][lane] = make_uint2(wh0, wh1);
@@ -1592,15 +1627,13 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
     }
     lds_barrier();     // (3) U tiles exchanged; every wave has read the R tiles
 
-    // ---- B: O = scale (Q S + P U) for row tile j; the copies of chunk n+1's Q rows go
-    // out between the products
+    // ---- B: O = scale (Q S + P U) for row tile j, to the LDS output tile
     {
       const bf16x8 uh = pack8(s_ux[0][0][lane], s_ux[1][0][lane]);
       const bf16x8 ul = pack8(s_ux[0][1][lane], s_ux[1][1][lane]);
       f32x4 pa = mma(cur.ph[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 pb = mma(cur.pl[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
       pa = mma(cur.ph[0], ul, pa);
-      dma_row_piece<16, NW>(qga, qrow_bytes, La, ktab[0], s_q, j, 0);
       if (j >= 2) {
         const bf16x8 uh1 = pack8(s_ux[2][0][lane], s_ux[3][0][lane]);
         const bf16x8 ul1 = pack8(s_ux[2][1][lane], s_ux[3][1][lane]);
@@ -1608,12 +1641,9 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
         pa = mma(cur.pl[1], uh1, pa);
         pb = mma(cur.ph[1], ul1, pb);
       }
-      dma_row_piece<16, NW>(qga, qrow_bytes, La, ktab[1], s_q, j, 1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * j + 4 * g4 + e;
-        if (t < L) og[(t0 + t) * o_stride] = f2bf(p.scale * (QS[e] + pa[e] + pb[e]));
-      }
+      for (int e = 0; e < 4; ++e)
+        s_ost[(16 * j + 4 * g4 + e) * O_STRIDE + c16] = f2bf(p.scale * (QS[e] + pa[e] + pb[e]));
     }
     // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U for state rows 32 j ..
     // 32 j + 31, K^T read transposed from this chunk's K rows
@@ -1633,23 +1663,19 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) St[t][e] *= cur.egl;
+        for (int e = 0; e < 4; ++e) St[t][e] *= egl;
         sb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           St[t] = mma(ak[t][m], wh[m], St[t]);
           sb[t] = mma(ak[t][m], wl[m], sb[t]);
         }
-        dma_row_piece<16, NW>(qga, qrow_bytes, La, ktab[2 + m], s_q, j, 2 + m);
-      }
       St[0] += sb[0];
       St[1] += sb[1];
     }
-#pragma unroll
-    for (int jp = 4; jp < KJ; ++jp) dma_row_piece<16, NW>(qga, qrow_bytes, La, ktab[jp], s_q, j, jp);
     put_slab();
   };
   for (int n = 0; n < ne; n += 2) {
@@ -1657,6 +1683,10 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
     if (n + 1 < ne) chunk(n + 1, ob, oa, std::integral_constant<int, 1>());
   }
   wait_vmem();         // no copy is in flight when the workgroup ends
+  if (ne > 0) {
+    lds_barrier();     // the last chunk's output tile is complete
+    store_o(ne - 1);
+  }
   if (p.state_out) {
     float* sp = p.state_out + ((int64_t)s * Hv + h) * DK * DV + col;
 #pragma unroll
