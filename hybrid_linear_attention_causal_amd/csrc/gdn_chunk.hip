@@ -792,6 +792,19 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* src, void* dst) {
   }
 }
 
+// the same as lds_dma16<true> with the source as a wave-uniform base plus a 32-bit
+// per-lane byte offset (the scalar-base form: no 64-bit address arithmetic per copy)
+__device__ __forceinline__ void lds_dma16_sbase(const uint8_t* base, uint32_t off, void* dst) {
+  const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)dst;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(m)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 template <int NS, int NW, bool OPAQUE = false>   // 16-byte slots (a multiple of 64), waves taking turns
 __device__ __forceinline__ void dma_linear(const uint8_t* src, void* dst, int wave, int lane) {
   static_assert(NS % 64 == 0, "whole instructions only");
@@ -1409,7 +1422,7 @@ __device__ __forceinline__ void dma_row_piece(const uint8_t* base, uint32_t row_
   typedef RowDma<DW, NW> R;
   const int ins = min(wave + NW * jp, R::INS - 1);
   const uint32_t row = min(tab & 0xFFu, (uint32_t)(L - 1));
-  lds_dma16<true>(base + __umul24(row, row_bytes) + (tab >> 8), (char*)dst + ins * 1024);
+  lds_dma16_sbase(base, __umul24(row, row_bytes) + (tab >> 8), (char*)dst + ins * 1024);
 }
 
 __global__ void __launch_bounds__(rs::THR, 2)
@@ -1507,8 +1520,13 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
 #pragma unroll
     for (int jp = 0; jp < KJ; ++jp)
       dma_row_piece<16, NW>(qg + t0 * qrow_bytes, qrow_bytes, L, ktab[jp], s_q, j, jp);
-    dma_linear<FAC_ROWS * CH * 4 / 16, NW, true>(rec_of(n) + FR_FAC_OFF, s_f, j, lane);
-    dma_rows<VW, NW, true>(vg + t0 * vrow_bytes, vrow_bytes, L, vtab, s_v, j);
+    {   // the factor rows: two 1 KB copies (wave 2, 3 repeat the second)
+      const int ins = min(j, 1);
+      lds_dma16_sbase(rec_of(n) + FR_FAC_OFF, ins * 1024 + lane * 16, (char*)s_f + ins * 1024);
+    }
+#pragma unroll
+    for (int jp = 0; jp < RowDma<VW, NW>::J; ++jp)
+      dma_row_piece<VW, NW>(vg + t0 * vrow_bytes, vrow_bytes, L, vtab[jp], s_v, j, jp);
   };
   // rows of the output tile of chunk n to global memory (16-byte pieces)
   auto store_o = [&](int n) {
