@@ -1500,17 +1500,21 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
   };
   auto rec_of = [&](int n) { return recs + ((int64_t)(c0 + n) * Hv + h) * FR_REC_BYTES; };
 
-  // T' and P fragments of chunk n (every load unconditional, so that the compiler's count
-  // of loads in flight stays exact; token slab 1 is zero for row tiles 0, 1)
+  // T' and P fragments of chunk n.  Token slab 1 is zero for row tiles 0 and 1, so only
+  // waves 2 and 3 load it, first: every load is consumed after the next chunk's wait for
+  // all loads, so the compiler's count of loads in flight never has to cover the branch.
   auto load_ops = [&](int n, RsOps& o) {
     const uint8_t* rec = rec_of(n);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      o.th[m] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, m, 0) + lane * 16);
-      o.tl[m] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, m, 1) + lane * 16);
-      o.ph[m] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, m, 0) + lane * 16);
-      o.pl[m] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, m, 1) + lane * 16);
+    if (j >= 2) {
+      o.th[1] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, 1, 0) + lane * 16);
+      o.tl[1] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, 1, 1) + lane * 16);
+      o.ph[1] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, 1, 0) + lane * 16);
+      o.pl[1] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, 1, 1) + lane * 16);
     }
+    o.th[0] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, 0, 0) + lane * 16);
+    o.tl[0] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, 0, 1) + lane * 16);
+    o.ph[0] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, 0, 0) + lane * 16);
+    o.pl[0] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, 0, 1) + lane * 16);
   };
   // copies of chunk n's Q rows, factor rows and V slice (single LDS buffers)
   auto stage_qfv = [&](int n) {
