@@ -444,23 +444,41 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
     for (int u = 0; u < 4; ++u) {
       const int row = 4 * rq + u;
       const bool ok = row < L;
-      float kv[8], qv[8];
-      row_vals<IO>(kb, u, ok, kv);
-      row_vals<IO>(qb, u, ok, qv);
-      uint4 hw, lw;
-      put_row8<IO>(sm.u.r.kh, sm.u.r.kl, row * KS_STRIDE + c8 * 8, kv, hw, lw);
-      put_row8<IO>(sm.u.r.qh, sm.u.r.ql, row * KS_STRIDE + c8 * 8, qv, hw, lw);
       float sk = 0.f, sq = 0.f;
+      if constexpr (F32) {
+        float kv[8], qv[8];
+        row_vals<IO>(kb, u, ok, kv);
+        row_vals<IO>(qb, u, ok, qv);
+        uint4 hw, lw;
+        put_row8<IO>(sm.u.r.kh, sm.u.r.kl, row * KS_STRIDE + c8 * 8, kv, hw, lw);
+        put_row8<IO>(sm.u.r.qh, sm.u.r.ql, row * KS_STRIDE + c8 * 8, qv, hw, lw);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        sk = fmaf(kv[j], kv[j], sk);
-        sq = fmaf(qv[j], qv[j], sq);
+        for (int j = 0; j < 8; ++j) {
+          sk = fmaf(kv[j], kv[j], sk);
+          sq = fmaf(qv[j], qv[j], sq);
+        }
+      } else {
+        // bf16 rows go to LDS as they are (zero past the chunk end); the squares come
+        // from the two halves of each word
+        const uint4 kw = ok ? kb.w[u][0] : make_uint4(0, 0, 0, 0);
+        const uint4 qw = ok ? qb.w[u][0] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(sm.u.r.kh + row * KS_STRIDE + c8 * 8) = kw;
+        *reinterpret_cast<uint4*>(sm.u.r.qh + row * KS_STRIDE + c8 * 8) = qw;
+        const uint32_t kx[4] = {kw.x, kw.y, kw.z, kw.w}, qx[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float k0 = __uint_as_float(kx[j] << 16), k1 = __uint_as_float(kx[j] & 0xFFFF0000u);
+          const float q0 = __uint_as_float(qx[j] << 16), q1 = __uint_as_float(qx[j] & 0xFFFF0000u);
+          sk = fmaf(k1, k1, fmaf(k0, k0, sk));
+          sq = fmaf(q1, q1, fmaf(q0, q0, sq));
+        }
       }
       sk = row16_sum(sk);
       sq = row16_sum(sq);
       if (c8 == 0) {
-        sm.rnk[row] = p.use_l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
-        sm.rnq[row] = p.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+        // hardware reciprocal square root (about 1 ulp)
+        sm.rnk[row] = p.use_l2 ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 1.0f;
+        sm.rnq[row] = p.use_l2 ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.0f;
       }
     }
   }
@@ -483,13 +501,13 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
       for (int m = 0; m < 4; ++m) {
         bk[m] = frag_rows(sm.u.r.kh, KS_STRIDE, 16 * J, 32 * m, lane);
         ak[m] = frag_rows(sm.u.r.kh, KS_STRIDE, 16 * I, 32 * m, lane);
-        if constexpr (WITHP) aq[m] = frag_rows(sm.u.r.qh, KS_STRIDE, 16 * I, 32 * m, lane);
+        if constexpr (WITHP && !FRAG) aq[m] = frag_rows(sm.u.r.qh, KS_STRIDE, 16 * I, 32 * m, lane);
       }
       f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         a1 = mma(ak[m], bk[m], a1);
-        if constexpr (WITHP) a2 = mma(aq[m], bk[m], a2);
+        if constexpr (WITHP && !FRAG) a2 = mma(aq[m], bk[m], a2);
       }
       if constexpr (F32) {
 #pragma unroll
@@ -513,6 +531,29 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
       for (int e = 0; e < 4; ++e) {
         gk[tt][e] = ki[e] * rkj * a1[e];
         gq[tt][e] = qi[e] * rkj * a2[e];
+      }
+    }
+  }
+  // fragment-native records: wave w forms row tile w of P transposed, (K Q^T) tiles (J, w)
+  // for J <= w, whose accumulators (lane g4, c16, element e) hold
+  // rnq_i rnk_j (q_i . k_j) at i = 16 w + c16, j = 16 J + 4 g4 + e: tiles J = 2m, 2m+1
+  // together are the layout of P's A-operand fragment [row tile w][token slab m]
+  f32x4 pq[4];
+  if constexpr (FRAG) {
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      pq[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (J <= wave) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          pq[J] = mma(frag_rows(sm.u.r.kh, KS_STRIDE, 16 * J, 32 * m, lane),
+                      frag_rows(sm.u.r.qh, KS_STRIDE, 16 * wave, 32 * m, lane), pq[J]);
+        const float4 kj4 = *reinterpret_cast<const float4*>(&sm.rnk[16 * J + 4 * g4]);
+        const float qi = sm.rnq[16 * wave + c16];
+        pq[J][0] *= qi * kj4.x;
+        pq[J][1] *= qi * kj4.y;
+        pq[J][2] *= qi * kj4.z;
+        pq[J][3] *= qi * kj4.w;
       }
     }
   }
@@ -603,14 +644,14 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
             const int i = i0 + e;
             const float d = (i >= j) ? __expf(gi[e] - gj) : 0.f;   // exponent <= 0
             af[i * F_STRIDE + j] = (i > j) ? bi[e] * d * gk[tt < 3 ? tt : 0][e] : 0.f;
-            if constexpr (WITHP) {
+            if constexpr (WITHP && !FRAG) {
               uint32_t ph, pl;
               split2(d * gq[tt < 3 ? tt : 0][e], 0.f, ph, pl);
               pst[i * CH + j] = (u16)ph;
               pst[CH * CH + i * CH + j] = (u16)pl;
             }
           }
-        } else if (WITHP && n < 16) {
+        } else if (WITHP && !FRAG && n < 16) {
           // strictly-upper tiles (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
           const int m = n - 10;
           const int I = (m >= 5) ? 2 : (m >= 3) ? 1 : 0;
@@ -623,22 +664,32 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
           }
         }
       }
-      __syncthreads();
       if constexpr (FRAG) {
-        // P fragments to the record: unit (plane, j, m, lane) gathers the lane's two 8-byte
-        // pieces of row 16 j + (lane & 15), columns 32 m + 4 (lane >> 4) .. and + 16
+        // P fragments of row tile w straight from the transposed tiles:
+        // P_ij = e^{gamma_i - gamma_j} rnq_i rnk_j (q_i . k_j) for j <= i < L
+        const int i = 16 * wave + c16;
+        const float gi = gam[i];
+        f32x4 pv[4];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int u = tid + NTHR * it;        // plane u >> 9, j (u >> 7) & 3, m (u >> 6) & 1
-          const int plane = u >> 9, jj = (u >> 7) & 3, m = (u >> 6) & 1, l = u & 63;
-          const u16* src = pst + plane * CH * CH + (16 * jj + (l & 15)) * CH + 32 * m + 4 * (l >> 4);
-          const uint2 lo8 = *reinterpret_cast<const uint2*>(src);
-          const uint2 hi8 = *reinterpret_cast<const uint2*>(src + 16);
-          *reinterpret_cast<uint4*>(rec + FR_P_OFF + fr_tp(jj, m, plane) + l * 16) =
-              make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
+        for (int J = 0; J < 4; ++J) {
+          const float4 gj4 = *reinterpret_cast<const float4*>(&gam[16 * J + 4 * g4]);
+          const float gj[4] = {gj4.x, gj4.y, gj4.z, gj4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int jj = 16 * J + 4 * g4 + e;
+            pv[J][e] = (jj <= i) ? __expf(gi - gj[e]) * pq[J][e] : 0.f;   // exponent <= 0
+          }
         }
-        __syncthreads();   // the T buffer is reused below
-      } else if constexpr (WITHP) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          bf16x8 hi, lo;
+          frag_acc_split(pv[2 * m], pv[2 * m + 1], hi, lo);
+          *reinterpret_cast<uint4*>(rec + FR_P_OFF + fr_tp(wave, m, 0) + lane * 16) = __builtin_bit_cast(uint4, hi);
+          *reinterpret_cast<uint4*>(rec + FR_P_OFF + fr_tp(wave, m, 1) + lane * 16) = __builtin_bit_cast(uint4, lo);
+        }
+      }
+      __syncthreads();
+      if constexpr (WITHP && !FRAG) {
         // P planes to the record, rows padded to 72 (four 16-byte words per thread)
         const uint4* src = reinterpret_cast<const uint4*>(pst);
 #pragma unroll
