@@ -410,7 +410,7 @@ struct PrepSmem {
 };
 
 template <int IO, int MODE>
-__global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? (MODE != PREP_ROWS ? 3 : 4) : 2)
+__global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? (MODE != PREP_ROWS_P ? 4 : 3) : 2)
 chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restrict__ recs,
                   uint8_t* __restrict__ krecs) {
   typedef Io<IO> io;
