@@ -431,8 +431,31 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   if (L == 0) return;                     // past the last chunk
   const int64_t t0 = ((int64_t)ci.w << 32) | (uint32_t)ci.z;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
+
+  // raw gate inputs of value head kh_ r + hb + wave for this lane's token
+  auto gate_in = [&](int hb, float& ga, float& gb, float& al, float& dt) {
+    const int jh = hb + wave;
+    ga = gb = al = dt = 0.f;
+    if (jh < r) {
+      const int h = kh_ * r + jh;
+      const int64_t idx = (t0 + (lane < L ? lane : L - 1)) * Hv + h;
+      if (p.g_opt) {
+        ga = p.g_opt[idx];
+        gb = p.beta_opt[idx];
+      } else {
+        ga = io::ld((const T*)p.a, idx);
+        gb = io::ld((const T*)p.b, idx);
+        al = p.A_log[h];
+        dt = p.dt_bias[h];
+      }
+    }
+  };
+  // the first batch's gate inputs go out before the rows, so their latency hides there
+  float ga0, gb0, al0, dt0;
+  gate_in(0, ga0, gb0, al0, dt0);
 
   // ---- phase 0: K and Q rows to LDS, row norms (16 lanes of a DPP row share a row)
   {
@@ -575,26 +598,15 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
     // ---- gates of value heads hb .. hb+3 (wave w: head hb + w, lane: token)
     __syncthreads();     // K/Q rows (phase 0) or the previous heads' T are no longer read
     {
-      const int jh = hb + wave;
+      float ga = ga0, gb = gb0, al = al0, dt = dt0;
+      if (hb > 0) gate_in(hb, ga, gb, al, dt);
       float g = 0.f, beta = 0.f;
-      if (jh < r) {
-        const int h = kh_ * r + jh;
-        const int64_t idx = (t0 + (lane < L ? lane : L - 1)) * Hv + h;
-        float ga, gb;
+      if (hb + wave < r && lane < L) {
         if (p.g_opt) {
-          ga = p.g_opt[idx];
-          gb = p.beta_opt[idx];
+          g = ga;
+          beta = gb;
         } else {
-          ga = io::ld((const T*)p.a, idx);
-          gb = io::ld((const T*)p.b, idx);
-        }
-        if (lane < L) {
-          if (p.g_opt) {
-            g = ga;
-            beta = gb;
-          } else {
-            gate_pair(ga, gb, p.A_log[h], p.dt_bias[h], g, beta);
-          }
+          gate_pair(ga, gb, al, dt, g, beta);
         }
       }
       g = wave_prefix_sum(g);       // in-chunk cumulative log decay (padding adds 0)
