@@ -426,7 +426,16 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   const int c = blockIdx.x;               // global chunk
   const int kh_ = blockIdx.y;             // key head
   const int Hv = p.Hv, r = Hv / p.Hk;
-  const int4 ci = cinfo[c];
+  // (one sequence: the chunk map is not built; chunk c is tokens b0 + 64 c .. of it)
+  int4 ci;
+  if (p.Ns == 1) {
+    int64_t sb, se;
+    seq_bounds(p.cu, p.N, 0, sb, se);
+    const int64_t tc = sb + (int64_t)c * CH;
+    ci = make_int4(0, (int)max((int64_t)0, min((int64_t)CH, se - tc)), (int)(uint32_t)tc, (int)(tc >> 32));
+  } else {
+    ci = cinfo[c];
+  }
   const int L = ci.y;
   if (L == 0) return;                     // past the last chunk
   const int64_t t0 = ((int64_t)ci.w << 32) | (uint32_t)ci.z;
@@ -1019,7 +1028,7 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   const int g = sg.seg_base + gi;                    // this workgroup's segment
   int64_t b0, b1;
   seq_bounds(p.cu, p.N, s, b0, b1);
-  const int c0 = cmap[s];
+  const int c0 = p.Ns == 1 ? 0 : cmap[s];   // (one sequence: no chunk map)
   const int nch = (int)((b1 - b0 + CH - 1) / CH);
   const int nb = (int)((int64_t)g * nch / sg.G);        // chunks [nb, ne) of the segment
   const int ne = (int)((int64_t)(g + 1) * nch / sg.G);
@@ -1523,7 +1532,7 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
   const int h = kh * r + member / NBLK;
   int64_t b0, b1;
   seq_bounds(p.cu, p.N, s, b0, b1);
-  const int c0 = cmap[s];
+  const int c0 = p.Ns == 1 ? 0 : cmap[s];   // (one sequence: no chunk map)
   const int ne = (int)((b1 - b0 + CH - 1) / CH);
   const int col = blk * DVB + c16;
 
@@ -1797,10 +1806,14 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   const bool rowsplit = IO == IO_BF16 && pairs * rs::NBLK <= ROWSPLIT_CU_ROUNDS * cus;
   const int G = rowsplit ? 1 : seg_count(a.N, a.Ns, a.Hv, cus);
   const bool four = rowsplit || pairs * G * SweepSizes<IO, 4>::NBLK <= cus;
-  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, st, a.cu, a.Ns, a.N, cmax, cmap,
-                     cinfo);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // the chunk map of packed sequences (one sequence needs none: its chunks are in order)
+  hipError_t e = hipSuccess;
+  if (a.Ns > 1) {
+    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, st, a.cu, a.Ns, a.N, cmax, cmap,
+                       cinfo);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.N > 0) {
     const dim3 pgrid((unsigned)cmax, (unsigned)a.Hk);
     if constexpr (IO == IO_BF16) {
