@@ -12,7 +12,8 @@
 // runs the r value heads HPP (1 or 2) at a time with 256 threads per head.
 //
 // State traffic (the roofline): each head's 128 x 128 fp32 state is read once
-// and written once.  Thread (rg, cg) of a head holds rows 16*rg .. 16*rg+15 of
+// and written once, with nontemporal loads and stores (the state is touched once per
+// step, so it need not displace anything in the caches).  Thread (rg, cg) of a head holds rows 16*rg .. 16*rg+15 of
 // columns 4*cg .. 4*cg+3 in registers (16 float4 loads, each wave covering two
 // contiguous 512-byte rows per instruction).  S^T k and S^T q are column sums
 // over rows: reduced over the 8 row groups with one cross-lane shuffle and an
@@ -54,12 +55,28 @@ recurrent_step_kernel(StepArgs p) {
   const int hi_half = (t256 >> 5) & 1;
 
   // issue the first pass's state loads before the conv so HBM latency overlaps it
-  float4 Sv[16];
+  f32x4 Sv[16];
   {
     const float* Sp = p.state + (((int64_t)bseq * Hv + kh * r + hl) * SD) * SD;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      Sv[i] = *reinterpret_cast<const float4*>(Sp + (rg * 16 + i) * SD + cg * 4);
+      Sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + (rg * 16 + i) * SD + cg * 4));
+  }
+
+  // the gate inputs of the r value heads (threads 64 .. 64 + r - 1), also loaded before
+  // the conv so that their latency hides under it
+  float gin_a = 0.f, gin_b = 0.f, gin_al = 0.f, gin_dt = 0.f;
+  if (tid >= 64 && tid < 64 + r) {
+    const int h = kh * r + (tid - 64);
+    if (p.g_opt) {
+      gin_a = p.g_opt[(int64_t)bseq * Hv + h];
+      gin_b = p.beta_opt[(int64_t)bseq * Hv + h];
+    } else {
+      gin_a = io::ld((const T*)p.a, (int64_t)bseq * Hv + h);
+      gin_b = io::ld((const T*)p.b, (int64_t)bseq * Hv + h);
+      gin_al = p.A_log[h];
+      gin_dt = p.dt_bias[h];
+    }
   }
 
   // ---- conv window + SiLU for this group's channels; shift the conv state
@@ -91,20 +108,18 @@ recurrent_step_kernel(StepArgs p) {
     float sq = group_sum<64>(q0 * q0 + q1 * q1);
     float sk = group_sum<64>(k0 * k0 + k1 * k1);
     if (tid == 0) {
-      nsh[0] = p.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-      nsh[1] = p.use_l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+      // hardware reciprocal square root (about 1 ulp)
+      nsh[0] = p.use_l2 ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.0f;
+      nsh[1] = p.use_l2 ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 1.0f;
     }
   } else if (tid >= 64 && tid < 64 + r) {
     const int j = tid - 64;
-    const int h = kh * r + j;
     float g, beta;
     if (p.g_opt) {
-      g = p.g_opt[(int64_t)bseq * Hv + h];
-      beta = p.beta_opt[(int64_t)bseq * Hv + h];
+      g = gin_a;
+      beta = gin_b;
     } else {
-      const float av = io::ld((const T*)p.a, (int64_t)bseq * Hv + h);
-      const float bv = io::ld((const T*)p.b, (int64_t)bseq * Hv + h);
-      gate_pair(av, bv, p.A_log[h], p.dt_bias[h], g, beta);
+      gate_pair(gin_a, gin_b, gin_al, gin_dt, g, beta);
     }
     gsh[j] = expf(g);
     bsh[j] = beta;
@@ -120,7 +135,7 @@ recurrent_step_kernel(StepArgs p) {
     if (h0 > 0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        Sv[i] = *reinterpret_cast<const float4*>(Sp + (rg * 16 + i) * SD + cg * 4);
+        Sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + (rg * 16 + i) * SD + cg * 4));
     }
 
     // p = S^T k^ (undecayed)
@@ -128,10 +143,10 @@ recurrent_step_kernel(StepArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float kv = yv[SD + rg * 16 + i] * rk;
-      pk[0] = fmaf(Sv[i].x, kv, pk[0]);
-      pk[1] = fmaf(Sv[i].y, kv, pk[1]);
-      pk[2] = fmaf(Sv[i].z, kv, pk[2]);
-      pk[3] = fmaf(Sv[i].w, kv, pk[3]);
+      pk[0] = fmaf(Sv[i][0], kv, pk[0]);
+      pk[1] = fmaf(Sv[i][1], kv, pk[1]);
+      pk[2] = fmaf(Sv[i][2], kv, pk[2]);
+      pk[3] = fmaf(Sv[i][3], kv, pk[3]);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) pk[c] += __shfl_xor(pk[c], 32, 64);
@@ -156,15 +171,15 @@ recurrent_step_kernel(StepArgs p) {
     for (int i = 0; i < 16; ++i) {
       const float kv = yv[SD + rg * 16 + i] * rk;
       const float qv = yv[rg * 16 + i] * rq;
-      Sv[i].x = fmaf(eg, Sv[i].x, kv * u[0]);
-      Sv[i].y = fmaf(eg, Sv[i].y, kv * u[1]);
-      Sv[i].z = fmaf(eg, Sv[i].z, kv * u[2]);
-      Sv[i].w = fmaf(eg, Sv[i].w, kv * u[3]);
-      po[0] = fmaf(Sv[i].x, qv, po[0]);
-      po[1] = fmaf(Sv[i].y, qv, po[1]);
-      po[2] = fmaf(Sv[i].z, qv, po[2]);
-      po[3] = fmaf(Sv[i].w, qv, po[3]);
-      *reinterpret_cast<float4*>(Sp + (rg * 16 + i) * SD + cg * 4) = Sv[i];
+      Sv[i][0] = fmaf(eg, Sv[i][0], kv * u[0]);
+      Sv[i][1] = fmaf(eg, Sv[i][1], kv * u[1]);
+      Sv[i][2] = fmaf(eg, Sv[i][2], kv * u[2]);
+      Sv[i][3] = fmaf(eg, Sv[i][3], kv * u[3]);
+      po[0] = fmaf(Sv[i][0], qv, po[0]);
+      po[1] = fmaf(Sv[i][1], qv, po[1]);
+      po[2] = fmaf(Sv[i][2], qv, po[2]);
+      po[3] = fmaf(Sv[i][3], qv, po[3]);
+      __builtin_nontemporal_store(Sv[i], reinterpret_cast<f32x4*>(Sp + (rg * 16 + i) * SD + cg * 4));
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) po[c] += __shfl_xor(po[c], 32, 64);
