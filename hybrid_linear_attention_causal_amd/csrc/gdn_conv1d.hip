@@ -36,6 +36,12 @@ template <int IO> struct Row8;
 template <> struct Row8<IO_BF16> {
   uint4 w;
   __device__ __forceinline__ void load(const u16* p) { w = *reinterpret_cast<const uint4*>(p); }
+  // nontemporal: x is read once per call (its halo rows come from L2 either way)
+  __device__ __forceinline__ void load_nt(const u16* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    w = make_uint4(v[0], v[1], v[2], v[3]);
+  }
   __device__ __forceinline__ void zero() { w = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void get(float* v) const {
     const uint32_t u[4] = {w.x, w.y, w.z, w.w};
@@ -53,6 +59,7 @@ template <> struct Row8<IO_F32> {
     b = *reinterpret_cast<const float4*>(p + 4);
   }
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void load_nt(const float* p) { load(p); }   // (fp32: plain)
   __device__ __forceinline__ void get(float* v) const {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
@@ -92,7 +99,7 @@ conv1d_silu_kernel(const typename Io<IO>::T* __restrict__ x, const float* __rest
     for (int r = 0; r < CONV_TT + 3; ++r) {
       const int64_t p = t0 - 3 + r;
       if (p >= sb)
-        rows[r].load(x + p * Cq + c0);
+        rows[r].load_nt(x + p * Cq + c0);
       else if (state_in)
         rows[r].load(state_in + ((int64_t)s * 3 + (p - sb + 3)) * Cq + c0);
       else
