@@ -131,13 +131,30 @@ def test_chunk_prefill_parity_many_chains(io):
     assert_state(s, s_ref, "prefill state")
 
 
+def test_chunk_prefill_parity_rowsplit_two_rounds():
+    """bf16 with 48 (sequence, head) chains: the row-split sweep's 384 workgroups are more
+    than one per compute unit, so two share a CU (ragged, full and empty sequences)."""
+    io, hk, hv = "bf16", 2, 4
+    lens = [1, 17, 63, 64, 65, 130, 0, 200, 5, 64, 129, 33]
+    inp = _case(hk, hv, io, 61, seqlens=lens, init_state=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert cus < inp["Ns"] * hv * 8 <= 2 * cus
+    y, o, s = _run_prefill(inp, io)
+    o_ref, s_ref = G.prefill(y[:, :hk * D], y[:, hk * D:2 * hk * D], y[:, 2 * hk * D:],
+                             inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv, D, D,
+                             inp["state_in"], inp["cu_seqlens"])
+    assert_out(o, G.to_io(o_ref, io), io, "prefill o")
+    assert_state(s, s_ref, "prefill state")
+
+
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("lens", [[1600], [1500, 37, 2000, 0]], ids=["one", "varlen"])
 def test_chunk_prefill_parity_segmented(io, lens):
-    """Few chains and long sequences: each chain splits into segments (6 for one
+    """Few chains and long sequences.  fp32: each chain splits into segments (6 for one
     1600-token sequence at 2 heads, 3 for the varlen case, where the 37-token and the
     empty sequence leave segments without chunks) that run in parallel from transition
-    matrices formed by a first pass."""
+    matrices formed by a first pass.  bf16: the row-split sweep walks the long chains
+    (25 and 32 chunks) with eight workgroups each."""
     hk, hv = 1, 2
     inp = _case(hk, hv, io, 51 + len(lens), seqlens=lens, init_state=True)
     y, o, s = _run_prefill(inp, io)
