@@ -6,6 +6,8 @@ One step = the hot path over one batch of synthetic input:
       gdn_conv1d_fwd -> gdn_chunk_prefill -> gdn_gated_rmsnorm
   decode step on the Qwen3.5-9B shape, 256 sequences, bf16 io, fp32 state:
       gdn_recurrent_step (conv + state updated in place) -> gdn_gated_rmsnorm
+  and, timed beside the step, the decode step on a bf16-stored state
+  (gdn_recurrent_step_bf16_state, roofline_decode_bf16_state).
 
 Reported ("value"): layer prefill tokens/s = 4096 / (conv + chunk + norm time),
 with the chunked core against the bf16 dense MFMA peak (roofline) and the decode
@@ -74,11 +76,11 @@ def chunk_core_flops(n_tokens: int, hk: int, hv: int, seqlens=None) -> float:
     return tot
 
 
-def decode_bytes(B: int, hk: int, hv: int, io_bytes: int = 2) -> float:
-    """Compulsory HBM bytes of one decode step: fp32 state read + write, conv state
-    read + write, x, a, b, conv weight, o."""
+def decode_bytes(B: int, hk: int, hv: int, io_bytes: int = 2, state_bytes: int = 4) -> float:
+    """Compulsory HBM bytes of one decode step: state read + write (fp32, or bf16 for a
+    bf16-stored state), conv state read + write, x, a, b, conv weight, o."""
     cq = 2 * hk * D + hv * D
-    state = 2.0 * B * hv * D * D * 4
+    state = 2.0 * B * hv * D * D * state_bytes
     conv_state = 2.0 * B * 3 * cq * io_bytes
     x = B * cq * io_bytes
     ab = 2.0 * B * hv * io_bytes
@@ -222,6 +224,7 @@ def main():
         Dd[name] = dev(dec[name], True)
     Dd["o"] = torch.empty((B, hv, D), dtype=torch.bfloat16, device="cuda")
     Dd["yn"] = torch.empty_like(Dd["o"])
+    Dd["state_bf16"] = Dd["state_in"].to(torch.bfloat16)
     zd = Dd["z"].view(B, hv, D)
     torch.cuda.synchronize()
 
@@ -258,6 +261,22 @@ def main():
     wall = time.perf_counter() - t0
     names = ["conv1d", "chunk_prefill", "prefill_norm", "recurrent_step", "decode_norm"]
     ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+
+    # Beside the step: the same decode step on a bf16-stored recurrent state.
+    def step_bf16_state():
+        gdn_recurrent_step(Dd["x"], Dd["conv_w"], Dd["conv_state_in"], Dd["a"], Dd["b"],
+                           Dd["A_log"], Dd["dt_bias"], Dd["state_bf16"], Dd["o"], hk, hv)
+
+    for _ in range(args.warmup):
+        step_bf16_state()
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for i in range(args.steps):
+        ev_b[2 * i].record()
+        step_bf16_state()
+        ev_b[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ms_bf16_state = float(np.mean([ev_b[2 * i].elapsed_time(ev_b[2 * i + 1])
+                                   for i in range(args.steps)]))
     prefill_ms = ms["conv1d"] + ms["chunk_prefill"] + ms["prefill_norm"]
     tokens_per_s = N / (prefill_ms * 1e-3)
 
@@ -265,6 +284,7 @@ def main():
     chunk_tflops = flops / (ms["chunk_prefill"] * 1e-3) / 1e12
     dbytes = decode_bytes(B, hk, hv)
     step_gbs = dbytes / (ms["recurrent_step"] * 1e-3) / 1e9
+    dbytes_bf = decode_bytes(B, hk, hv, state_bytes=2)
 
     res = {
         "metric": "GDN layer prefill tokens/s (%MFMA peak) + decode step state GB/s (%HBM peak)",
@@ -293,6 +313,11 @@ def main():
                             "frac": step_gbs * 1e9 / PEAK_HBM_BYTES,
                             "traffic": measured_traffic("gdn_recurrent_step"),
                             "algorithmic_per_launch": dbytes},
+        "roofline_decode_bf16_state": {
+            "kernel": "gdn_recurrent_step_bf16_state", "bound": "hbm", "ms": ms_bf16_state,
+            "achieved": dbytes_bf / (ms_bf16_state * 1e-3) / 1e9, "peak": PEAK_HBM_BYTES / 1e9,
+            "unit": "GB/s", "frac": dbytes_bf / (ms_bf16_state * 1e-3) / PEAK_HBM_BYTES,
+            "algorithmic_per_launch": dbytes_bf},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -38,6 +38,9 @@ _SIGS = {
                            _sz, _i32, _vp], _i32),
     "gdn_recurrent_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                             _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp], _i32),
+    "gdn_recurrent_step_bf16_state": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp],
+                                      _i32),
     "gdn_gated_rmsnorm": ([_vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32, _vp], _i32),
 }
 
@@ -152,9 +155,19 @@ def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None,
 def gdn_recurrent_step(x, w, conv_state, a, b, A_log, dt_bias, state, o, Hk, Hv, g_opt=None,
                        beta_opt=None, scale=0.0, use_qk_l2norm=True, K=4, stream=None,
                        dk=128, dv=128):
-    """One decode token per sequence; conv_state and state are updated in place."""
+    """One decode token per sequence; conv_state and state are updated in place.
+    A bfloat16 state goes to gdn_recurrent_step_bf16_state, a float32 one to
+    gdn_recurrent_step."""
     _dev(x, w, conv_state, a, b, A_log, dt_bias, state, o, g_opt, beta_opt)
     B = x.shape[0]
+    if state.dtype == torch.bfloat16:
+        _check("gdn_recurrent_step_bf16_state", lib().gdn_recurrent_step_bf16_state(
+            _p(x), _p(w), _p(conv_state), _p(a), _p(b), _p(A_log), _p(dt_bias), _p(g_opt),
+            _p(beta_opt), _p(state), _p(o), B, Hk, Hv, dk, dv, K, float(scale),
+            int(bool(use_qk_l2norm)), _io(x), _stream(stream)))
+        return
+    if state.dtype != torch.float32:
+        raise TypeError(f"the recurrent state must be float32 or bfloat16, got {state.dtype}")
     _check("gdn_recurrent_step", lib().gdn_recurrent_step(
         _p(x), _p(w), _p(conv_state), _p(a), _p(b), _p(A_log), _p(dt_bias), _p(g_opt),
         _p(beta_opt), _p(state), _p(o), B, Hk, Hv, dk, dv, K, float(scale),

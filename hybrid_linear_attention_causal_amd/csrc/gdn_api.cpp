@@ -153,39 +153,65 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
   return e == hipSuccess ? GDN_OK : hip_fail(e, "chunk_prefill launch");
 }
 
-gdn_status_t gdn_recurrent_step(const void* x, const float* w, void* conv_state, const void* a,
-                                const void* b, const float* A_log, const float* dt_bias,
-                                const float* g_opt, const float* beta_opt, float* state, void* o,
-                                int B, int Hk, int Hv, int dk, int dv, int K, float scale,
-                                int use_qk_l2norm, gdn_dtype_t io, void* stream) {
+namespace {
+
+gdn_status_t recurrent_step_impl(const char* name, const void* x, const float* w, void* conv_state,
+                                 const void* a, const void* b, const float* A_log,
+                                 const float* dt_bias, const float* g_opt, const float* beta_opt,
+                                 void* state, int state_bf16, void* o, int B, int Hk, int Hv,
+                                 int dk, int dv, int K, float scale, int use_qk_l2norm,
+                                 gdn_dtype_t io, void* stream) {
   g_err[0] = 0;
-  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "recurrent_step: unknown io dtype %d", (int)io);
-  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "recurrent_step: kernel width %d (only 4)", K);
+  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "%s: unknown io dtype %d", name, (int)io);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "%s: kernel width %d (only 4)", name, K);
   if (dk != 128 || dv != 128)
-    return fail(GDN_ERR_UNSUPPORTED, "recurrent_step: head widths %d/%d (only 128/128)", dk, dv);
+    return fail(GDN_ERR_UNSUPPORTED, "%s: head widths %d/%d (only 128/128)", name, dk, dv);
   if (B < 0 || Hk < 1 || Hv < 1 || Hv % Hk != 0 || Hv / Hk > 128)
-    return fail(GDN_ERR_INVALID_ARG, "recurrent_step: B=%d Hk=%d Hv=%d", B, Hk, Hv);
+    return fail(GDN_ERR_INVALID_ARG, "%s: B=%d Hk=%d Hv=%d", name, B, Hk, Hv);
   if ((int64_t)B * Hk > 0x7fffffffLL)
-    return fail(GDN_ERR_INVALID_ARG, "recurrent_step: too many (sequence, key head) pairs");
+    return fail(GDN_ERR_INVALID_ARG, "%s: too many (sequence, key head) pairs", name);
   const bool have_g = g_opt != nullptr, have_b = beta_opt != nullptr;
   if (have_g != have_b)
-    return fail(GDN_ERR_INVALID_ARG, "recurrent_step: give both g_opt and beta_opt or neither");
+    return fail(GDN_ERR_INVALID_ARG, "%s: give both g_opt and beta_opt or neither", name);
   if (B > 0) {
     if (!x || !w || !conv_state || !state || !o)
-      return fail(GDN_ERR_INVALID_ARG, "recurrent_step: NULL x, w, conv_state, state or o");
+      return fail(GDN_ERR_INVALID_ARG, "%s: NULL x, w, conv_state, state or o", name);
     if (!have_g && (!a || !b || !A_log || !dt_bias))
-      return fail(GDN_ERR_INVALID_ARG, "recurrent_step: NULL a, b, A_log or dt_bias");
+      return fail(GDN_ERR_INVALID_ARG, "%s: NULL a, b, A_log or dt_bias", name);
     if (!aligned(state, 16) || !aligned(w, 16))
-      return fail(GDN_ERR_INVALID_ARG, "recurrent_step: state and w must be 16-byte aligned");
+      return fail(GDN_ERR_INVALID_ARG, "%s: state and w must be 16-byte aligned", name);
   }
   if (scale <= 0.f) scale = 1.0f / sqrtf((float)dk);
   gdn_status_t st = check_device();
   if (st != GDN_OK) return st;
   gdn::StepArgs args{x, w, conv_state, a, b, A_log, dt_bias, g_opt, beta_opt, state, o, B, Hk, Hv,
-                     scale, use_qk_l2norm ? 1 : 0};
+                     scale, use_qk_l2norm ? 1 : 0, state_bf16};
   hipError_t e = gdn::launch_recurrent_step(args, io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
                                             (hipStream_t)stream);
   return e == hipSuccess ? GDN_OK : hip_fail(e, "recurrent_step launch");
+}
+
+}  // namespace
+
+gdn_status_t gdn_recurrent_step(const void* x, const float* w, void* conv_state, const void* a,
+                                const void* b, const float* A_log, const float* dt_bias,
+                                const float* g_opt, const float* beta_opt, float* state, void* o,
+                                int B, int Hk, int Hv, int dk, int dv, int K, float scale,
+                                int use_qk_l2norm, gdn_dtype_t io, void* stream) {
+  return recurrent_step_impl("recurrent_step", x, w, conv_state, a, b, A_log, dt_bias, g_opt,
+                             beta_opt, state, 0, o, B, Hk, Hv, dk, dv, K, scale, use_qk_l2norm, io,
+                             stream);
+}
+
+gdn_status_t gdn_recurrent_step_bf16_state(const void* x, const float* w, void* conv_state,
+                                           const void* a, const void* b, const float* A_log,
+                                           const float* dt_bias, const float* g_opt,
+                                           const float* beta_opt, void* state, void* o, int B,
+                                           int Hk, int Hv, int dk, int dv, int K, float scale,
+                                           int use_qk_l2norm, gdn_dtype_t io, void* stream) {
+  return recurrent_step_impl("recurrent_step_bf16_state", x, w, conv_state, a, b, A_log, dt_bias,
+                             g_opt, beta_opt, state, 1, o, B, Hk, Hv, dk, dv, K, scale,
+                             use_qk_l2norm, io, stream);
 }
 
 gdn_status_t gdn_gated_rmsnorm(const void* o, const void* z, const float* w, void* y,

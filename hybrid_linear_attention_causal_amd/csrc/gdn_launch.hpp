@@ -53,11 +53,12 @@ struct StepArgs {
   const float* dt_bias;
   const float* g_opt;
   const float* beta_opt;
-  float* state;
+  void* state;            // fp32, or bf16 when state_bf16
   void* o;
   int B, Hk, Hv;
   float scale;
   int use_l2;
+  int state_bf16;         // 1: the state is stored as bf16 (read, computed in fp32, rounded back)
 };
 
 struct NormArgs {

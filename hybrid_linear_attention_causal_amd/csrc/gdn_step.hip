@@ -11,9 +11,10 @@
 // every conv-state element is read and rewritten by exactly one thread, and it
 // runs the r value heads HPP (1 or 2) at a time with 256 threads per head.
 //
-// State traffic (the roofline): each head's 128 x 128 fp32 state is read once
-// and written once, with nontemporal loads and stores (the state is touched once per
-// step, so it need not displace anything in the caches).  Thread (rg, cg) of a head holds rows 16*rg .. 16*rg+15 of
+// State traffic (the roofline): each head's 128 x 128 state (fp32, or bf16 in the
+// bf16-state variant: read, computed in fp32, rounded back) is read once and written
+// once, with nontemporal loads and stores (the state is touched once per step, so it
+// need not displace anything in the caches).  Thread (rg, cg) of a head holds rows 16*rg .. 16*rg+15 of
 // columns 4*cg .. 4*cg+3 in registers (16 float4 loads, each wave covering two
 // contiguous 512-byte rows per instruction).  S^T k and S^T q are column sums
 // over rows: reduced over the 8 row groups with one cross-lane shuffle and an
@@ -25,10 +26,43 @@ namespace gdn {
 
 constexpr int SD = 128;  // head width (dk = dv)
 
-template <int IO, int HPP>
-__global__ void __launch_bounds__(256 * HPP)
+// Four consecutive state values (columns 4 cg .. 4 cg + 3 of one row) at element offset
+// i, as stored: fp32 (f32x4) or bf16 (two packed words, kept packed in registers so the
+// bf16 variant holds half the registers).  Nontemporal: the state is touched once per step.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <bool SBF> struct StateQuad;
+template <> struct StateQuad<false> {
+  typedef f32x4 Raw;
+  static __device__ __forceinline__ Raw ld(const void* base, uint32_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>((const float*)base + i));
+  }
+  static __device__ __forceinline__ f32x4 f32(Raw w) { return w; }
+  static __device__ __forceinline__ void st(void* base, uint32_t i, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>((float*)base + i));
+  }
+};
+template <> struct StateQuad<true> {
+  typedef u32x2 Raw;
+  static __device__ __forceinline__ Raw ld(const void* base, uint32_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>((const u16*)base + i));
+  }
+  static __device__ __forceinline__ f32x4 f32(Raw w) {
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+  }
+  static __device__ __forceinline__ void st(void* base, uint32_t i, f32x4 v) {
+    const u32x2 w = {f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};   // round to nearest even
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>((u16*)base + i));
+  }
+};
+
+// The bf16-state variant holds its state packed and fits four waves per SIMD (two
+// 512-thread workgroups per CU); the fp32 one holds 64 state registers and runs three.
+template <int IO, int HPP, bool SBF>
+__global__ void __launch_bounds__(256 * HPP, 4)
 recurrent_step_kernel(StepArgs p) {
   typedef Io<IO> io;
+  typedef StateQuad<SBF> SQ;
   typedef typename io::T T;
   extern __shared__ float smem[];
   const int Hk = p.Hk, Hv = p.Hv;
@@ -47,20 +81,25 @@ recurrent_step_kernel(StepArgs p) {
   float* bsh = gsh + r;                      // r: beta
   float* nsh = bsh + r;                      // 2: 1/|q|, 1/|k|
 
-  const int hl = tid >> 8;        // head slot inside a pass
+  const int hl = __builtin_amdgcn_readfirstlane(tid >> 8);   // head slot inside a pass
   const int t256 = tid & 255;
   const int cg = t256 & 31;       // column group: columns 4cg .. 4cg+3
   const int rg = t256 >> 5;       // row group: rows 16rg .. 16rg+15
   const int wv = (t256 >> 6);     // wave within the head's 256 threads
   const int hi_half = (t256 >> 5) & 1;
+  // a head's state base is wave-uniform (scalar); the thread's rows and columns are a
+  // 32-bit offset from it, row i of the thread's 16 at a further i * SD
+  const uint32_t toff = (uint32_t)(rg * 16 * SD + cg * 4);
+  auto head_state = [&](int h) {
+    return (char*)p.state + (((int64_t)bseq * Hv + h) * SD) * SD * (SBF ? 2 : 4);
+  };
 
   // issue the first pass's state loads before the conv so HBM latency overlaps it
-  f32x4 Sv[16];
+  typename SQ::Raw Sv[16];
   {
-    const float* Sp = p.state + (((int64_t)bseq * Hv + kh * r + hl) * SD) * SD;
+    const char* sb = head_state(kh * r + hl);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      Sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + (rg * 16 + i) * SD + cg * 4));
+    for (int i = 0; i < 16; ++i) Sv[i] = SQ::ld(sb, toff + i * SD);
   }
 
   // the gate inputs of the r value heads (threads 64 .. 64 + r - 1), also loaded before
@@ -131,11 +170,10 @@ recurrent_step_kernel(StepArgs p) {
   for (int h0 = 0; h0 < r; h0 += HPP) {
     const int j = h0 + hl;        // value head inside the group
     const int h = kh * r + j;
-    float* Sp = p.state + (((int64_t)bseq * Hv + h) * SD) * SD;
+    char* sb = head_state(h);
     if (h0 > 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        Sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + (rg * 16 + i) * SD + cg * 4));
+      for (int i = 0; i < 16; ++i) Sv[i] = SQ::ld(sb, toff + i * SD);
     }
 
     // p = S^T k^ (undecayed)
@@ -143,10 +181,11 @@ recurrent_step_kernel(StepArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float kv = yv[SD + rg * 16 + i] * rk;
-      pk[0] = fmaf(Sv[i][0], kv, pk[0]);
-      pk[1] = fmaf(Sv[i][1], kv, pk[1]);
-      pk[2] = fmaf(Sv[i][2], kv, pk[2]);
-      pk[3] = fmaf(Sv[i][3], kv, pk[3]);
+      const f32x4 sv = SQ::f32(Sv[i]);
+      pk[0] = fmaf(sv[0], kv, pk[0]);
+      pk[1] = fmaf(sv[1], kv, pk[1]);
+      pk[2] = fmaf(sv[2], kv, pk[2]);
+      pk[3] = fmaf(sv[3], kv, pk[3]);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) pk[c] += __shfl_xor(pk[c], 32, 64);
@@ -155,6 +194,12 @@ recurrent_step_kernel(StepArgs p) {
       for (int c = 0; c < 4; ++c) red1[(hl * 4 + wv) * SD + cg * 4 + c] = pk[c];
     }
     __syncthreads();
+    if constexpr (SBF) {
+      // keep the bf16 state packed across the exchange: without this the compiler keeps
+      // the values unpacked for the first product alive for the update (64 more registers)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(Sv[i]));
+    }
     float u[4];
     const float eg = gsh[j], beta = bsh[j];
 #pragma unroll
@@ -171,15 +216,16 @@ recurrent_step_kernel(StepArgs p) {
     for (int i = 0; i < 16; ++i) {
       const float kv = yv[SD + rg * 16 + i] * rk;
       const float qv = yv[rg * 16 + i] * rq;
-      Sv[i][0] = fmaf(eg, Sv[i][0], kv * u[0]);
-      Sv[i][1] = fmaf(eg, Sv[i][1], kv * u[1]);
-      Sv[i][2] = fmaf(eg, Sv[i][2], kv * u[2]);
-      Sv[i][3] = fmaf(eg, Sv[i][3], kv * u[3]);
-      po[0] = fmaf(Sv[i][0], qv, po[0]);
-      po[1] = fmaf(Sv[i][1], qv, po[1]);
-      po[2] = fmaf(Sv[i][2], qv, po[2]);
-      po[3] = fmaf(Sv[i][3], qv, po[3]);
-      __builtin_nontemporal_store(Sv[i], reinterpret_cast<f32x4*>(Sp + (rg * 16 + i) * SD + cg * 4));
+      f32x4 sv = SQ::f32(Sv[i]);
+      sv[0] = fmaf(eg, sv[0], kv * u[0]);
+      sv[1] = fmaf(eg, sv[1], kv * u[1]);
+      sv[2] = fmaf(eg, sv[2], kv * u[2]);
+      sv[3] = fmaf(eg, sv[3], kv * u[3]);
+      po[0] = fmaf(sv[0], qv, po[0]);     // o from the updated state before any rounding
+      po[1] = fmaf(sv[1], qv, po[1]);
+      po[2] = fmaf(sv[2], qv, po[2]);
+      po[3] = fmaf(sv[3], qv, po[3]);
+      SQ::st(sb, toff + i * SD, sv);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) po[c] += __shfl_xor(po[c], 32, 64);
@@ -206,8 +252,12 @@ template <int IO, int HPP>
 static hipError_t step_launch(const StepArgs& a, hipStream_t s) {
   const int r = a.Hv / a.Hk;
   const size_t lds = sizeof(float) * (256 + r * SD + 2 * HPP * 4 * SD + 2 * r + 2);
-  hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP>), dim3((unsigned)(a.B * a.Hk)),
-                     dim3(256 * HPP), lds, s, a);
+  if (a.state_bf16)
+    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, true>), dim3((unsigned)(a.B * a.Hk)),
+                       dim3(256 * HPP), lds, s, a);
+  else
+    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, false>), dim3((unsigned)(a.B * a.Hk)),
+                       dim3(256 * HPP), lds, s, a);
   return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens
 
 def decode_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w, Hk, Hv,
                 eps=1e-6, bufs=None, stream=None):
-    """One token per sequence.  conv_state [B,3,Cq] and state [B,Hv,128,128] update in place."""
+    """One token per sequence.  conv_state [B,3,Cq] and state [B,Hv,128,128] update in place;
+    the state may be float32 or bfloat16 (stored bf16, stepped in fp32)."""
     B = x.shape[0]
     bufs = {} if bufs is None else bufs
     o = bufs.get("o")

@@ -187,6 +187,24 @@ gdn_status_t gdn_recurrent_step(const void* x, const float* w, void* conv_state,
                                 int use_qk_l2norm, gdn_dtype_t io, void* stream);
 
 /*
+ * gdn_recurrent_step_bf16_state -- gdn_recurrent_step with the recurrent state
+ * stored as bf16 (llm-architectures-explained, Qwen3.5 397B-A17B page, "Modelled
+ * costs": its cost model keeps the linear-attention state in BF16), which halves the
+ * state traffic that bounds decode.  Each step reads the bf16 state, computes the step
+ * in fp32 exactly as gdn_recurrent_step does (o from the updated fp32 state), and
+ * writes the updated state back rounded to bf16 (round-to-nearest-even).
+ *
+ *   state           [B, Hv, dk, dv]     bf16  read and rewritten in place
+ * All other arguments, layouts and errors as for gdn_recurrent_step.
+ */
+gdn_status_t gdn_recurrent_step_bf16_state(const void* x, const float* w, void* conv_state,
+                                           const void* a, const void* b, const float* A_log,
+                                           const float* dt_bias, const float* g_opt,
+                                           const float* beta_opt, void* state, void* o, int B,
+                                           int Hk, int Hv, int dk, int dv, int K, float scale,
+                                           int use_qk_l2norm, gdn_dtype_t io, void* stream);
+
+/*
  * gdn_gated_rmsnorm -- z-gated RMSNorm over rows of D values:
  *   y[r, :] = w * o[r, :] / sqrt(mean(o[r, :]^2) + eps) * silu(z[r, :])
  * (llm-arch-viz Qwen3.5-9B page: Qwen3_5RMSNormGated with a [128] weight shared

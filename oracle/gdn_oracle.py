@@ -225,11 +225,15 @@ def gated_rmsnorm(o, z, w, eps=RMS_EPS):
 # --------------------------------------------------------------------------
 def recurrent_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, Hk, Hv, dk, dv,
                    scale=None, use_qk_l2norm=True, g=None, beta=None, io="bf16",
-                   pairs=None):
+                   pairs=None, state_io="f64"):
     """x: [B, Cq]; conv_state: [B, K-1, Cq]; state: [B, Hv, dk, dv].
 
     Returns (o [B, Hv, dv] fp64, conv_state_new [B, K-1, Cq], state_new).  The
     conv output is rounded to io before the core, as at the prefill boundary.
+    state_io="bf16" is the bf16-stored state (llm-architectures-explained, Qwen3.5
+    397B-A17B page, "Modelled costs": the state kept in BF16): the step runs on the
+    stored values and only the state written back is rounded to bf16; o comes from the
+    updated state before that rounding.
     """
     bsz = x.shape[0]
     cu = np.arange(bsz + 1)
@@ -242,6 +246,8 @@ def recurrent_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, Hk, Hv, d
         pairs = [(s, h) for s in range(bsz) for h in range(Hv)]
     o, state_new = prefill(q, k, v, a, b, A_log, dt_bias, Hk, Hv, dk, dv, state, cu, scale,
                            use_qk_l2norm, g, beta, pairs=pairs)
+    if state_io == "bf16":
+        state_new = to_io(state_new, "bf16")
     return o, conv_state_new, state_new
 
 

@@ -13,6 +13,10 @@ Tolerances (stated once, used everywhere):
   with the oracle alone: 1-ulp flips of 1% of o give a gated error of 8e-2 RMS
   at s = 2^-8 and 7e-3 RMS at s = 3 * 2^-8.)
 * final recurrent state: per sequence ||dS||_F / ||S_ref||_F <= 1e-3.
+* a bf16-stored state: the same Frobenius bound, and element by element
+  |a - b| <= 2^-8 (|a| + |b|) + 1e-5 RMS (each side's bf16 store moves a value by
+  half an ulp; 1e-5 RMS covers the fp32 arithmetic before it), with a != b on at
+  most 1% of the elements.
 * conv state: bit-exact (it is a copy of input rows).
 """
 from __future__ import annotations
@@ -77,3 +81,23 @@ def assert_state(gpu, ref, what=""):
         worst = max(worst, rel)
     assert worst <= STATE_REL_TOL, f"{what}: state rel err {worst:.3e} > {STATE_REL_TOL}"
     return worst
+
+
+def assert_bf16_state(gpu, ref, what="", max_flip=0.01):
+    """gpu, ref: bf16-valued states; equal up to rounding neighbours on few elements.
+
+    Before the bf16 store the two sides differ by the fp32 arithmetic error e of the
+    step (taken as 1e-5 RMS(ref), about ten times a 128-term fp32 dot product's); each
+    store then moves a value by at most half an ulp, 2^-8 |x|.  So element by element
+    |a - b| <= 2^-8 (|a| + |b|) + e, and a and b differ on at most max_flip of them."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert_state(gpu, ref, what)
+    d = np.abs(gpu - ref)
+    e = 1e-5 * float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    excess = d - (BF16_HALF_ULP * (np.abs(gpu) + np.abs(ref)) + e)
+    worst = float(excess.max(initial=-1.0))
+    assert worst <= 0, f"{what}: a bf16 state element exceeds the rounding bound by {worst:.3e}"
+    flips = float(np.mean(d > 0)) if d.size else 0.0
+    assert flips <= max_flip, f"{what}: {flips:.2%} of the bf16 state elements differ"
+    return flips

@@ -11,7 +11,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libgdn.so not built (run __graft_entry__.build())")
 
 EXPECTED = {"gdn_last_error", "gdn_version", "gdn_conv1d_fwd", "gdn_chunk_prefill_workspace_size",
-            "gdn_chunk_prefill", "gdn_recurrent_step", "gdn_gated_rmsnorm"}
+            "gdn_chunk_prefill", "gdn_recurrent_step", "gdn_recurrent_step_bf16_state",
+            "gdn_gated_rmsnorm"}
 
 
 def test_header_declares_the_calls():
@@ -102,11 +103,11 @@ def test_prefill_rejects():
     assert ws(64, 1, 16, 32, 64, 1) == 0
 
 
-def _step(**kw):
+def _step(fn="gdn_recurrent_step", **kw):
     args = dict(x=P, w=P, cs=P, a=P, b=P, A_log=P, dt_bias=P, g=None, beta=None, st=P, o=P,
                 B=4, Hk=16, Hv=32, dk=128, dv=128, K=4, scale=0.0, l2=1, io=1)
     args.update(kw)
-    return _L().gdn_recurrent_step(*args.values(), None)
+    return getattr(_L(), fn)(*args.values(), None)
 
 
 def test_step_rejects():
@@ -117,6 +118,18 @@ def test_step_rejects():
     assert _step(st=None) == _lib.GDN_ERR_INVALID_ARG
     assert _step(beta=P) == _lib.GDN_ERR_INVALID_ARG
     assert _step(st=ctypes.c_void_p(20)) == _lib.GDN_ERR_INVALID_ARG
+
+
+def test_step_bf16_state_rejects():
+    fn = "gdn_recurrent_step_bf16_state"
+    assert _step(fn, K=2) == _lib.GDN_ERR_UNSUPPORTED
+    assert "recurrent_step_bf16_state" in _msg()
+    assert _step(fn, dk=64) == _lib.GDN_ERR_UNSUPPORTED
+    assert _step(fn, Hv=20) == _lib.GDN_ERR_INVALID_ARG
+    assert _step(fn, st=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _step(fn, g=P) == _lib.GDN_ERR_INVALID_ARG
+    assert _step(fn, st=ctypes.c_void_p(24)) == _lib.GDN_ERR_INVALID_ARG
+    assert _step(fn, io=7) != 0
 
 
 def test_norm_rejects():

@@ -13,7 +13,7 @@ from hybrid_linear_attention_causal_amd import synth
 from hybrid_linear_attention_causal_amd.mixer import qkv_views
 from oracle import gdn_oracle as G
 
-from parity import assert_out, assert_state, f32_dev, host, to_dev
+from parity import assert_bf16_state, assert_out, assert_state, f32_dev, host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -233,6 +233,62 @@ def test_recurrent_step_parity(io, hk, hv):
     assert_out(host(o), G.to_io(o_ref, io), io, "step o")
     np.testing.assert_array_equal(host(cs), cs_ref)
     assert_state(host(st), st_ref, "step state")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("hk,hv", [(2, 4), (1, 3)])
+def test_recurrent_step_bf16_state_parity(io, hk, hv):
+    """The step on a bf16-stored state: o as from the stored values, state rounded back."""
+    inp = _case(hk, hv, io, 60 + hv, batch=5, init_state=True, kind="decode")
+    B = 5
+    s_bf = G.to_io(inp["state_in"], "bf16")
+    x = to_dev(inp["x"], io)
+    cs = to_dev(inp["conv_state_in"], io)
+    st = to_dev(s_bf, "bf16")
+    o = torch.empty((B, hv, D), dtype=x.dtype, device="cuda")
+    gdn.gdn_recurrent_step(x, f32_dev(inp["conv_w"]), cs, to_dev(inp["a"], io),
+                           to_dev(inp["b"], io), f32_dev(inp["A_log"]), f32_dev(inp["dt_bias"]),
+                           st, o, hk, hv)
+    torch.cuda.synchronize()
+    assert st.dtype == torch.bfloat16
+    o_ref, cs_ref, st_ref = G.recurrent_step(inp["x"], inp["conv_w"], inp["conv_state_in"],
+                                             inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+                                             s_bf, hk, hv, D, D, io=io, state_io="bf16")
+    assert_out(host(o), G.to_io(o_ref, io), io, "bf16-state step o")
+    np.testing.assert_array_equal(host(cs), cs_ref)
+    assert_bf16_state(host(st), st_ref, "bf16-state step state")
+
+
+def test_recurrent_step_bf16_state_many_steps():
+    """24 steps on one bf16 state buffer against the oracle stepping a bf16 state."""
+    io, hk, hv, B, n = "bf16", 2, 4, 3, 24
+    rng = np.random.default_rng(71)
+    inp = _case(hk, hv, io, 71, batch=B, init_state=True, kind="decode")
+    C = (2 * hk + hv) * D
+    xs = G.to_io(rng.standard_normal((n, B, C)), io)
+    as_ = G.to_io(rng.standard_normal((n, B, hv)), io)
+    bs = G.to_io(rng.standard_normal((n, B, hv)), io)
+    w, A_log, dt = inp["conv_w"], inp["A_log"], inp["dt_bias"]
+    s_ref = G.to_io(inp["state_in"], "bf16")
+    cs_ref = inp["conv_state_in"]
+    st = to_dev(s_ref, "bf16")
+    cs = to_dev(cs_ref, io)
+    wd, Ad, dd = f32_dev(w), f32_dev(A_log), f32_dev(dt)
+    os_gpu, os_ref = [], []
+    for t in range(n):
+        o = torch.empty((B, hv, D), dtype=torch.bfloat16, device="cuda")
+        gdn.gdn_recurrent_step(to_dev(xs[t], io), wd, cs, to_dev(as_[t], io), to_dev(bs[t], io),
+                               Ad, dd, st, o, hk, hv)
+        os_gpu.append(o)
+        o_r, cs_ref, s_ref = G.recurrent_step(xs[t], w, cs_ref, as_[t], bs[t], A_log, dt, s_ref,
+                                              hk, hv, D, D, io=io, state_io="bf16")
+        os_ref.append(G.to_io(o_r, io))
+    torch.cuda.synchronize()
+    assert_out(np.stack([host(o) for o in os_gpu]), np.stack(os_ref), io, "bf16-state steps o")
+    np.testing.assert_array_equal(host(cs), cs_ref)
+    # One-ulp neighbours at one step carry into the next, so over many steps only the
+    # Frobenius bound holds element-blind.
+    assert_state(host(st), s_ref, "bf16-state steps state")
 
 
 def test_prefill_then_steps_equals_prefill():

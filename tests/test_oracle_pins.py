@@ -348,3 +348,47 @@ def test_decode_steps_equal_prefill():
         np.testing.assert_allclose(G.to_io(o[0], "f32"), full["o"][t], rtol=1e-6, atol=1e-7)
     np.testing.assert_allclose(st, full["state_out"], rtol=1e-12, atol=1e-14)
     np.testing.assert_array_equal(cs, full["conv_state_out"])
+
+
+def _step_inputs(rng, hk, hv, d, bsz):
+    cq = 2 * hk * d + hv * d
+    return dict(x=rng.standard_normal((bsz, cq)), w=0.25 * rng.standard_normal((cq, 4)),
+                cs=rng.standard_normal((bsz, 3, cq)), a=rng.standard_normal((bsz, hv)),
+                b=rng.standard_normal((bsz, hv)), A_log=rng.uniform(0, np.log(16), hv),
+                dt=np.log(np.expm1(rng.uniform(1e-3, 0.1, hv))))
+
+
+def test_bf16_state_step_pass_through():
+    # beta = 0, g = 0: the bf16-stored state comes back bit for bit (a bf16 value rounds to
+    # itself) and o = scale S0^T q^ reads the stored values
+    rng = _rng(27)
+    hk, hv, d, bsz = 1, 2, 8, 3
+    p = _step_inputs(rng, hk, hv, d, bsz)
+    S0 = G.to_io(0.02 * rng.standard_normal((bsz, hv, d, d)), "bf16")
+    zeros = np.zeros((bsz, hv))
+    o, _, S1 = G.recurrent_step(p["x"], p["w"], p["cs"], p["a"], p["b"], p["A_log"], p["dt"], S0,
+                                hk, hv, d, d, io="f32", g=zeros, beta=zeros, state_io="bf16")
+    np.testing.assert_array_equal(S1, S0)
+    y, _ = G.conv1d_fwd(p["x"], p["w"], np.arange(bsz + 1), p["cs"])
+    q = G.l2_normalize(G.to_io(y, "f32")[:, :d])
+    for s in range(bsz):
+        for h in range(hv):
+            np.testing.assert_allclose(o[s, h], S0[s, h].T @ q[s] / np.sqrt(d), rtol=1e-12,
+                                       atol=1e-15)
+
+
+def test_bf16_state_step_is_the_step_rounded():
+    # the bf16-state step: o equal to the full-precision step's from the same stored state,
+    # and the written state within half a bf16 ulp of the full-precision one (RNE)
+    rng = _rng(28)
+    hk, hv, d, bsz = 2, 4, 8, 2
+    p = _step_inputs(rng, hk, hv, d, bsz)
+    S0 = G.to_io(0.02 * rng.standard_normal((bsz, hv, d, d)), "bf16")
+    args = (p["x"], p["w"], p["cs"], p["a"], p["b"], p["A_log"], p["dt"], S0, hk, hv, d, d)
+    o_f, cs_f, S_f = G.recurrent_step(*args, io="bf16")
+    o_b, cs_b, S_b = G.recurrent_step(*args, io="bf16", state_io="bf16")
+    np.testing.assert_array_equal(o_b, o_f)
+    np.testing.assert_array_equal(cs_b, cs_f)
+    assert np.all(np.abs(S_b - S_f) <= 2.0 ** -8 * np.abs(S_f) * (1 + 2.0 ** -15))
+    assert np.array_equal(G.to_io(S_b, "bf16"), S_b)          # representable in bf16
+    assert not np.array_equal(S_b, S_f)                          # and actually rounded
