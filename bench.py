@@ -7,7 +7,9 @@ One step = the hot path over one batch of synthetic input:
   decode step on the Qwen3.5-9B shape, 256 sequences, bf16 io, fp32 state:
       gdn_recurrent_step (conv + state updated in place) -> gdn_gated_rmsnorm
   and, timed beside the step, the decode step on a bf16-stored state
-  (gdn_recurrent_step_bf16_state, roofline_decode_bf16_state).
+  (gdn_recurrent_step_bf16_state, roofline_decode_bf16_state) and the prompt -> decode
+  replay (one sequence: 1024-token prompt, then 256 decode steps eager and as one HIP
+  graph; "replay").
 
 Reported ("value"): layer prefill tokens/s = 4096 / (conv + chunk + norm time),
 with the chunked core against the bf16 dense MFMA peak (roofline) and the decode
@@ -153,6 +155,73 @@ def cpu_baseline(inp, budget_heads=None, reps=2):
                        f"run {reps} times, {procs} worker processes; tokens/s scaled by heads/{hv}")}
 
 
+def replay_leg(reps: int, warmup: int) -> dict:
+    """Beside the step: the prompt -> decode replay on one 9B-shaped layer, B=1: the
+    1024-token prompt through the prefill layer, then 256 decode steps (recurrent step +
+    gated norm) on the carried state, eagerly and as one captured HIP graph."""
+    import numpy as np
+    import torch
+
+    import hybrid_linear_attention_causal_amd as gdn
+    from hybrid_linear_attention_causal_amd import synth
+
+    inp = synth.make(synth.replay_workload())
+    T, T1, hk, hv = inp["N"], synth.REPLAY_PROMPT, inp["Hk"], inp["Hv"]
+    n = T - T1
+
+    def dev(a, f32=False):
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+        return (t if f32 else t.to(torch.bfloat16)).cuda()
+
+    x, a, b, z = (dev(inp[k]) for k in ("x", "a", "b", "z"))
+    z = z.view(T, hv, D)
+    w, A_log, dt, nw = (dev(inp[k], True) for k in ("conv_w", "A_log", "dt_bias", "norm_w"))
+    bufs = {}
+    prefill = lambda: gdn.prefill_layer(x[:T1], w, a[:T1], b[:T1], A_log, dt, z[:T1], nw, hk,
+                                        hv, bufs=bufs)
+    out = prefill()
+    for k in ("y_conv", "o", "y", "conv_state_out", "state_out"):
+        bufs[k] = out[k]
+    cs, st = out["conv_state_out"], out["state_out"]
+    xs = x[T1:].reshape(n, 1, -1).clone()
+    As, Bs = a[T1:].reshape(n, 1, hv).clone(), b[T1:].reshape(n, 1, hv).clone()
+    zs = z[T1:].reshape(n, 1, hv, D).clone()
+    dbufs = {"o": torch.empty((1, hv, D), dtype=torch.bfloat16, device="cuda"),
+             "y": torch.empty((1, hv, D), dtype=torch.bfloat16, device="cuda")}
+
+    def decode_eager():
+        for t in range(n):
+            gdn.decode_step(xs[t], w, cs, As[t], Bs[t], A_log, dt, st, zs[t], nw, hk, hv,
+                            bufs=dbufs)
+
+    graph = gdn.DecodeGraph(xs, w, cs, As, Bs, A_log, dt, st, zs, nw, hk, hv)
+
+    def timed(fn, k):
+        for _ in range(warmup):
+            fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(k):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / k
+
+    pre_ms = timed(prefill, reps)
+    eager_ms = timed(decode_eager, max(2, reps // 4))
+    graph_ms = timed(graph.replay, reps)
+    state_bytes = 2.0 * hv * D * D * 4
+    return {"workload": f"Qwen3.5-9B GDN layer, one sequence: {T1}-token prompt then {n} "
+                        "decode steps (bf16 io, fp32 state)",
+            "prompt_tokens": T1, "decode_steps": n,
+            "prefill_layer_ms": pre_ms,
+            "decode_eager_us_per_token": eager_ms * 1e3 / n,
+            "decode_graph_us_per_token": graph_ms * 1e3 / n,
+            "decode_graph_tokens_per_s": n / (graph_ms * 1e-3),
+            "decode_graph_state_GBps": state_bytes * n / (graph_ms * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +346,7 @@ def main():
     torch.cuda.synchronize()
     ms_bf16_state = float(np.mean([ev_b[2 * i].elapsed_time(ev_b[2 * i + 1])
                                    for i in range(args.steps)]))
+    replay = replay_leg(args.steps, args.warmup)
     prefill_ms = ms["conv1d"] + ms["chunk_prefill"] + ms["prefill_norm"]
     tokens_per_s = N / (prefill_ms * 1e-3)
 
@@ -318,6 +388,7 @@ def main():
             "achieved": dbytes_bf / (ms_bf16_state * 1e-3) / 1e9, "peak": PEAK_HBM_BYTES / 1e9,
             "unit": "GB/s", "frac": dbytes_bf / (ms_bf16_state * 1e-3) / PEAK_HBM_BYTES,
             "algorithmic_per_launch": dbytes_bf},
+        "replay": replay,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -41,6 +41,9 @@ _SIGS = {
     "gdn_recurrent_step_bf16_state": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp],
                                       _i32),
+    "gdn_recurrent_step_slots": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                  _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                  _vp], _i32),
     "gdn_gated_rmsnorm": ([_vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32, _vp], _i32),
 }
 
@@ -172,6 +175,21 @@ def gdn_recurrent_step(x, w, conv_state, a, b, A_log, dt_bias, state, o, Hk, Hv,
         _p(x), _p(w), _p(conv_state), _p(a), _p(b), _p(A_log), _p(dt_bias), _p(g_opt),
         _p(beta_opt), _p(state), _p(o), B, Hk, Hv, dk, dv, K, float(scale),
         int(bool(use_qk_l2norm)), _io(x), _stream(stream)))
+
+
+def gdn_recurrent_step_slots(x, w, conv_state_pool, a, b, A_log, dt_bias, state_pool, slots, o,
+                             Hk, Hv, g_opt=None, beta_opt=None, scale=0.0, use_qk_l2norm=True,
+                             K=4, stream=None, dk=128, dv=128):
+    """One decode token per row; row i's conv and recurrent states are entry slots[i] of
+    the pools (int32 slots; a negative or out-of-range slot marks a padding row)."""
+    _dev(x, w, conv_state_pool, a, b, A_log, dt_bias, state_pool, slots, o, g_opt, beta_opt)
+    if slots.dtype != torch.int32:
+        raise TypeError(f"slots must be int32, got {slots.dtype}")
+    B = x.shape[0]
+    _check("gdn_recurrent_step_slots", lib().gdn_recurrent_step_slots(
+        _p(x), _p(w), _p(conv_state_pool), _p(a), _p(b), _p(A_log), _p(dt_bias), _p(g_opt),
+        _p(beta_opt), _p(state_pool), _io(state_pool), _p(slots), state_pool.shape[0], _p(o), B,
+        Hk, Hv, dk, dv, K, float(scale), int(bool(use_qk_l2norm)), _io(x), _stream(stream)))
 
 
 def gdn_gated_rmsnorm(o, z, w, y, eps=1e-6, stream=None):

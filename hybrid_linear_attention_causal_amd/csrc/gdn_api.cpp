@@ -160,7 +160,8 @@ gdn_status_t recurrent_step_impl(const char* name, const void* x, const float* w
                                  const float* dt_bias, const float* g_opt, const float* beta_opt,
                                  void* state, int state_bf16, void* o, int B, int Hk, int Hv,
                                  int dk, int dv, int K, float scale, int use_qk_l2norm,
-                                 gdn_dtype_t io, void* stream) {
+                                 gdn_dtype_t io, void* stream, const int32_t* slots = nullptr,
+                                 int n_slots = 0) {
   g_err[0] = 0;
   if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "%s: unknown io dtype %d", name, (int)io);
   if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "%s: kernel width %d (only 4)", name, K);
@@ -180,12 +181,14 @@ gdn_status_t recurrent_step_impl(const char* name, const void* x, const float* w
       return fail(GDN_ERR_INVALID_ARG, "%s: NULL a, b, A_log or dt_bias", name);
     if (!aligned(state, 16) || !aligned(w, 16))
       return fail(GDN_ERR_INVALID_ARG, "%s: state and w must be 16-byte aligned", name);
+    if (slots && !aligned(slots, 4))
+      return fail(GDN_ERR_INVALID_ARG, "%s: slots must be 4-byte aligned", name);
   }
   if (scale <= 0.f) scale = 1.0f / sqrtf((float)dk);
   gdn_status_t st = check_device();
   if (st != GDN_OK) return st;
   gdn::StepArgs args{x, w, conv_state, a, b, A_log, dt_bias, g_opt, beta_opt, state, o, B, Hk, Hv,
-                     scale, use_qk_l2norm ? 1 : 0, state_bf16};
+                     scale, use_qk_l2norm ? 1 : 0, state_bf16, slots, n_slots};
   hipError_t e = gdn::launch_recurrent_step(args, io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
                                             (hipStream_t)stream);
   return e == hipSuccess ? GDN_OK : hip_fail(e, "recurrent_step launch");
@@ -212,6 +215,26 @@ gdn_status_t gdn_recurrent_step_bf16_state(const void* x, const float* w, void* 
   return recurrent_step_impl("recurrent_step_bf16_state", x, w, conv_state, a, b, A_log, dt_bias,
                              g_opt, beta_opt, state, 1, o, B, Hk, Hv, dk, dv, K, scale,
                              use_qk_l2norm, io, stream);
+}
+
+gdn_status_t gdn_recurrent_step_slots(const void* x, const float* w, void* conv_state_pool,
+                                      const void* a, const void* b, const float* A_log,
+                                      const float* dt_bias, const float* g_opt,
+                                      const float* beta_opt, void* state_pool,
+                                      gdn_dtype_t state_dtype, const int32_t* slots, int n_slots,
+                                      void* o, int B, int Hk, int Hv, int dk, int dv, int K,
+                                      float scale, int use_qk_l2norm, gdn_dtype_t io,
+                                      void* stream) {
+  g_err[0] = 0;
+  if (state_dtype != GDN_F32 && state_dtype != GDN_BF16)
+    return fail(GDN_ERR_INVALID_ARG, "recurrent_step_slots: unknown state dtype %d",
+                (int)state_dtype);
+  if (n_slots < 1 || (B > 0 && !slots))
+    return fail(GDN_ERR_INVALID_ARG, "recurrent_step_slots: n_slots=%d, slots %s", n_slots,
+                slots ? "given" : "NULL");
+  return recurrent_step_impl("recurrent_step_slots", x, w, conv_state_pool, a, b, A_log, dt_bias,
+                             g_opt, beta_opt, state_pool, state_dtype == GDN_BF16 ? 1 : 0, o, B,
+                             Hk, Hv, dk, dv, K, scale, use_qk_l2norm, io, stream, slots, n_slots);
 }
 
 gdn_status_t gdn_gated_rmsnorm(const void* o, const void* z, const float* w, void* y,

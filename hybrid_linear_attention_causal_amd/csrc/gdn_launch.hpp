@@ -59,6 +59,8 @@ struct StepArgs {
   float scale;
   int use_l2;
   int state_bf16;         // 1: the state is stored as bf16 (read, computed in fp32, rounded back)
+  const int32_t* slots;   // NULL: row b uses state b; else slots[b] in [0, n_slots), other = padding
+  int n_slots;
 };
 
 struct NormArgs {

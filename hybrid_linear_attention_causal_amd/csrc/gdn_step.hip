@@ -58,7 +58,7 @@ template <> struct StateQuad<true> {
 
 // The bf16-state variant holds its state packed and fits four waves per SIMD (two
 // 512-thread workgroups per CU); the fp32 one holds 64 state registers and runs three.
-template <int IO, int HPP, bool SBF>
+template <int IO, int HPP, bool SBF, bool SLOTS>
 __global__ void __launch_bounds__(256 * HPP, 4)
 recurrent_step_kernel(StepArgs p) {
   typedef Io<IO> io;
@@ -90,8 +90,19 @@ recurrent_step_kernel(StepArgs p) {
   // a head's state base is wave-uniform (scalar); the thread's rows and columns are a
   // 32-bit offset from it, row i of the thread's 16 at a further i * SD
   const uint32_t toff = (uint32_t)(rg * 16 * SD + cg * 4);
+  // the state and conv-state row of this sequence: its slot in the pools, or the row itself
+  int slot = bseq;
+  if constexpr (SLOTS) {
+    slot = p.slots[bseq];
+    if (slot < 0 || slot >= p.n_slots) {
+      // padding row: no state is read or written; the group's o rows are zero
+      T* ob = (T*)p.o + ((int64_t)bseq * Hv + kh * r) * SD;
+      for (int i = tid; i < r * SD; i += nthr) io::st(ob, i, 0.f);
+      return;   // uniform over the workgroup
+    }
+  }
   auto head_state = [&](int h) {
-    return (char*)p.state + (((int64_t)bseq * Hv + h) * SD) * SD * (SBF ? 2 : 4);
+    return (char*)p.state + (((int64_t)slot * Hv + h) * SD) * SD * (SBF ? 2 : 4);
   };
 
   // issue the first pass's state loads before the conv so HBM latency overlaps it
@@ -120,7 +131,7 @@ recurrent_step_kernel(StepArgs p) {
 
   // ---- conv window + SiLU for this group's channels; shift the conv state
   const T* xb = (const T*)p.x + (int64_t)bseq * Cq;
-  T* cs = (T*)p.conv_state + (int64_t)bseq * 3 * Cq;
+  T* cs = (T*)p.conv_state + (int64_t)slot * 3 * Cq;
   const int nch = 256 + r * SD;
   for (int i = tid; i < nch; i += nthr) {
     int c;
@@ -248,15 +259,15 @@ recurrent_step_kernel(StepArgs p) {
   }
 }
 
-template <int IO, int HPP>
+template <int IO, int HPP, bool SBF>
 static hipError_t step_launch(const StepArgs& a, hipStream_t s) {
   const int r = a.Hv / a.Hk;
   const size_t lds = sizeof(float) * (256 + r * SD + 2 * HPP * 4 * SD + 2 * r + 2);
-  if (a.state_bf16)
-    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, true>), dim3((unsigned)(a.B * a.Hk)),
+  if (a.slots)
+    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, SBF, true>), dim3((unsigned)(a.B * a.Hk)),
                        dim3(256 * HPP), lds, s, a);
   else
-    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, false>), dim3((unsigned)(a.B * a.Hk)),
+    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, SBF, false>), dim3((unsigned)(a.B * a.Hk)),
                        dim3(256 * HPP), lds, s, a);
   return hipGetLastError();
 }
@@ -265,8 +276,9 @@ template <int IO>
 static hipError_t step_impl(const StepArgs& a, hipStream_t s) {
   const int r = a.Hv / a.Hk;
   // two heads per pass at most: 512 threads leave 256 VGPRs per lane (no spills)
-  if (r % 2 == 0) return step_launch<IO, 2>(a, s);
-  return step_launch<IO, 1>(a, s);
+  if (r % 2 == 0)
+    return a.state_bf16 ? step_launch<IO, 2, true>(a, s) : step_launch<IO, 2, false>(a, s);
+  return a.state_bf16 ? step_launch<IO, 1, true>(a, s) : step_launch<IO, 1, false>(a, s);
 }
 
 hipError_t launch_recurrent_step(const StepArgs& a, int io, hipStream_t s) {

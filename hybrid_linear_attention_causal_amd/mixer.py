@@ -2,6 +2,7 @@
 
 prefill_layer:  conv1d+SiLU -> chunked delta rule -> z-gated RMSNorm
 decode_step:    recurrent step (conv + delta rule, in place) -> z-gated RMSNorm
+DecodeGraph:    n decode steps captured once as a HIP graph, replayed as one launch
 """
 from __future__ import annotations
 
@@ -70,3 +71,32 @@ def decode_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w, H
         yn = torch.empty_like(o)
     gdn_gated_rmsnorm(o, z, norm_w, yn, eps, stream=stream)
     return {"o": o, "y": yn}
+
+
+class DecodeGraph:
+    """n consecutive decode steps (gdn_recurrent_step -> gdn_gated_rmsnorm per step) of
+    one layer, captured once as a HIP graph and replayed with one launch.
+
+    The graph reads x[t], a[t], b[t], z[t] from the static buffers given here
+    (x [n, B, Cq], a and b [n, B, Hv], z [n, B, Hv, 128]) and writes o[t] and y[t] of its
+    own buffers; conv_state and state are updated in place by every replay, as n calls
+    of decode_step would.  Write the next inputs into the same buffers and replay.
+    The calls enqueue no memset and allocate nothing, so they capture as plain kernel
+    nodes.
+    """
+
+    def __init__(self, x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w, Hk, Hv,
+                 eps=1e-6):
+        n, B = x.shape[0], x.shape[1]
+        self.o = torch.empty((n, B, Hv, D), dtype=x.dtype, device=x.device)
+        self.y = torch.empty_like(self.o)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for t in range(n):
+                gdn_recurrent_step(x[t], conv_w, conv_state, a[t], b[t], A_log, dt_bias, state,
+                                   self.o[t], Hk, Hv)
+                gdn_gated_rmsnorm(self.o[t], z[t], norm_w, self.y[t], eps)
+
+    def replay(self):
+        self.graph.replay()
+        return self.y

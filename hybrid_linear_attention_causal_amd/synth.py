@@ -103,6 +103,21 @@ def workload(idx: int) -> Workload:
     raise ValueError(f"no workload {idx}")
 
 
+# the prompt -> decode replay: one sequence, a 1024-token prompt then 256 decode tokens
+# (HF transformers docs, Qwen3.5 page, "Usage tips and notes": its one measured generation
+# has a 1024-token prompt and 256 greedily decoded tokens; that measurement is of a whole
+# 27B model, here it is one linear-attention layer of the 9B shape)
+REPLAY_PROMPT, REPLAY_STEPS = 1024, 256
+
+
+def replay_workload(shape: Shape = QWEN35_9B, prompt: int = REPLAY_PROMPT,
+                    steps: int = REPLAY_STEPS, seed: int = 5) -> Workload:
+    """All prompt + steps tokens of the replay as one sequence; the first `prompt` go to
+    the chunked prefill and the rest to decode steps on the carried state."""
+    return Workload(f"replay_{shape.name}_p{prompt}_d{steps}_bf16", "prefill", shape, "bf16",
+                    seed, [prompt + steps])
+
+
 def custom(shape: Shape, io: str, seed: int, seqlens=None, batch: int = 0,
            init_state: bool = False, kind: str = "prefill") -> Workload:
     return Workload(f"custom_{shape.name}_{io}_s{seed}", kind, shape, io, seed,

@@ -205,6 +205,34 @@ gdn_status_t gdn_recurrent_step_bf16_state(const void* x, const float* w, void* 
                                            int use_qk_l2norm, gdn_dtype_t io, void* stream);
 
 /*
+ * gdn_recurrent_step_slots -- gdn_recurrent_step for a batch whose states live in
+ * pools of n_slots entries: row b of x, a, b, g_opt, beta_opt and o belongs to the
+ * sequence whose conv state and recurrent state are entry slots[b] of the pools.
+ * (KerasFormers Qwen page, "Generation": each sequence carries its own per-layer conv
+ * and recurrent state from step to step; a serving batch picks those states out of a
+ * pool by index rather than copying them into a dense batch.)
+ *
+ *   conv_state_pool [n_slots, K-1, Cq]      io           entries slots[b] rewritten in place
+ *   state_pool      [n_slots, Hv, dk, dv]   state_dtype  entries slots[b] rewritten in place
+ *   state_dtype     GDN_F32, or GDN_BF16 (stored bf16, as gdn_recurrent_step_bf16_state)
+ *   slots           [B] int32, device memory
+ *   n_slots         >= 1
+ * A row whose slot is negative or >= n_slots is padding: no pool entry is read or
+ * written and its o row is set to zero.  Two rows with the same valid slot race on it
+ * (the result is undefined, but no memory outside the pools and o is touched).
+ * All other arguments, layouts and errors as for gdn_recurrent_step; also
+ * INVALID_ARG for n_slots < 1, NULL slots with B > 0, or an unknown state_dtype.
+ */
+gdn_status_t gdn_recurrent_step_slots(const void* x, const float* w, void* conv_state_pool,
+                                      const void* a, const void* b, const float* A_log,
+                                      const float* dt_bias, const float* g_opt,
+                                      const float* beta_opt, void* state_pool,
+                                      gdn_dtype_t state_dtype, const int32_t* slots, int n_slots,
+                                      void* o, int B, int Hk, int Hv, int dk, int dv, int K,
+                                      float scale, int use_qk_l2norm, gdn_dtype_t io,
+                                      void* stream);
+
+/*
  * gdn_gated_rmsnorm -- z-gated RMSNorm over rows of D values:
  *   y[r, :] = w * o[r, :] / sqrt(mean(o[r, :]^2) + eps) * silu(z[r, :])
  * (llm-arch-viz Qwen3.5-9B page: Qwen3_5RMSNormGated with a [128] weight shared

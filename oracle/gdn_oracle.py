@@ -251,6 +251,35 @@ def recurrent_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, Hk, Hv, d
     return o, conv_state_new, state_new
 
 
+def recurrent_step_slots(x, conv_w, conv_pool, a, b, A_log, dt_bias, state_pool, slots, Hk, Hv,
+                         dk, dv, io="bf16", state_io="f64", **kw):
+    """The step for a batch whose states are entries of pools (KerasFormers Qwen page,
+    "Generation": each sequence carries its own conv and recurrent state; here they
+    are picked from a pool by index).  Row i uses entry slots[i]; a negative or
+    out-of-range slot is a padding row: its o is zero and no entry changes.
+
+    Returns (o [B, Hv, dv], conv_pool_new, state_pool_new) as new arrays.
+    """
+    slots = np.asarray(slots)
+    n = state_pool.shape[0]
+    live = [i for i, s in enumerate(slots) if 0 <= s < n]
+    o = np.zeros((x.shape[0], Hv, dv))
+    conv_new = np.array(conv_pool, dtype=np.float64, copy=True)
+    state_new = np.array(state_pool, dtype=np.float64, copy=True)
+    if live:
+        idx = slots[live]
+        assert len(set(idx.tolist())) == len(idx), "two rows share a slot"
+        g = None if kw.get("g") is None else kw.pop("g")[live]
+        beta = None if kw.get("beta") is None else kw.pop("beta")[live]
+        o_l, cs_l, st_l = recurrent_step(x[live], conv_w, conv_pool[idx], a[live], b[live], A_log,
+                                         dt_bias, state_pool[idx], Hk, Hv, dk, dv, io=io,
+                                         state_io=state_io, g=g, beta=beta, **kw)
+        o[live] = o_l
+        conv_new[idx] = cs_l
+        state_new[idx] = st_l
+    return o, conv_new, state_new
+
+
 # --------------------------------------------------------------------------
 # the whole mixer, rounding to io at each call boundary
 # --------------------------------------------------------------------------

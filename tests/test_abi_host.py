@@ -12,7 +12,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
 
 EXPECTED = {"gdn_last_error", "gdn_version", "gdn_conv1d_fwd", "gdn_chunk_prefill_workspace_size",
             "gdn_chunk_prefill", "gdn_recurrent_step", "gdn_recurrent_step_bf16_state",
-            "gdn_gated_rmsnorm"}
+            "gdn_recurrent_step_slots", "gdn_gated_rmsnorm"}
 
 
 def test_header_declares_the_calls():
@@ -138,3 +138,23 @@ def test_norm_rejects():
     assert L.gdn_gated_rmsnorm(P, P, P, P, -1, 128, 1e-6, 1, None) == _lib.GDN_ERR_INVALID_ARG
     assert L.gdn_gated_rmsnorm(P, None, P, P, 10, 128, 1e-6, 1, None) == _lib.GDN_ERR_INVALID_ARG
     assert L.gdn_gated_rmsnorm(P, P, P, P, 10, 128, -1.0, 1, None) == _lib.GDN_ERR_INVALID_ARG
+
+
+def _slots(**kw):
+    args = dict(x=P, w=P, cs=P, a=P, b=P, A_log=P, dt_bias=P, g=None, beta=None, st=P,
+                sdt=_lib.GDN_F32, slots=P, n_slots=8, o=P, B=4, Hk=16, Hv=32, dk=128, dv=128,
+                K=4, scale=0.0, l2=1, io=1)
+    args.update(kw)
+    return _L().gdn_recurrent_step_slots(*args.values(), None)
+
+
+def test_step_slots_rejects():
+    assert _slots(sdt=5) == _lib.GDN_ERR_INVALID_ARG
+    assert "state dtype" in _msg()
+    assert _slots(n_slots=0) == _lib.GDN_ERR_INVALID_ARG
+    assert _slots(slots=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _slots(slots=ctypes.c_void_p(18)) == _lib.GDN_ERR_INVALID_ARG
+    assert _slots(K=3) == _lib.GDN_ERR_UNSUPPORTED
+    assert "recurrent_step_slots" in _msg()
+    assert _slots(Hv=20) == _lib.GDN_ERR_INVALID_ARG
+    assert _slots(st=None) == _lib.GDN_ERR_INVALID_ARG

@@ -291,6 +291,41 @@ def test_recurrent_step_bf16_state_many_steps():
     assert_state(host(st), s_ref, "bf16-state steps state")
 
 
+@pytest.mark.parametrize("state_io", ["f32", "bf16"])
+def test_recurrent_step_slots_parity(state_io):
+    """Slot-indexed decode: rows pick pool entries; padding rows touch nothing, o = 0."""
+    io, hk, hv, B, n = "bf16", 2, 4, 5, 9
+    rng = np.random.default_rng(90)
+    inp = _case(hk, hv, io, 90, batch=B, init_state=True, kind="decode")
+    C = (2 * hk + hv) * D
+    conv_pool = G.to_io(rng.standard_normal((n, 3, C)), io)
+    pool = G.to_io(0.02 * rng.standard_normal((n, hv, D, D)), state_io)
+    slots = np.array([7, -1, 2, 12, 4], dtype=np.int32)
+    cp = to_dev(conv_pool, io)
+    sp = to_dev(pool, "bf16") if state_io == "bf16" else f32_dev(pool)
+    o = torch.full((B, hv, D), 3.0, dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_recurrent_step_slots(to_dev(inp["x"], io), f32_dev(inp["conv_w"]), cp,
+                                 to_dev(inp["a"], io), to_dev(inp["b"], io),
+                                 f32_dev(inp["A_log"]), f32_dev(inp["dt_bias"]), sp,
+                                 torch.from_numpy(slots).cuda(), o, hk, hv)
+    torch.cuda.synchronize()
+    o_ref, cp_ref, sp_ref = G.recurrent_step_slots(
+        inp["x"], inp["conv_w"], conv_pool, inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
+        pool, slots, hk, hv, D, D, io=io, state_io="bf16" if state_io == "bf16" else "f64")
+    og = host(o)
+    assert np.all(og[[1, 3]] == 0.0)
+    assert_out(og, G.to_io(o_ref, io), io, "slot step o")
+    np.testing.assert_array_equal(host(cp), cp_ref)
+    spg = host(sp)
+    live = [7, 2, 4]
+    for s in sorted(set(range(n)) - set(live)):
+        np.testing.assert_array_equal(spg[s], pool[s])
+    if state_io == "bf16":
+        assert_bf16_state(spg[live], sp_ref[live], "slot step bf16 state")
+    else:
+        assert_state(spg[live], sp_ref[live], "slot step state")
+
+
 def test_prefill_then_steps_equals_prefill():
     """Prefill of T1 tokens then T - T1 decode steps on carried state == prefill of T."""
     io = "bf16"

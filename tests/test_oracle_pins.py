@@ -392,3 +392,35 @@ def test_bf16_state_step_is_the_step_rounded():
     assert np.all(np.abs(S_b - S_f) <= 2.0 ** -8 * np.abs(S_f) * (1 + 2.0 ** -15))
     assert np.array_equal(G.to_io(S_b, "bf16"), S_b)          # representable in bf16
     assert not np.array_equal(S_b, S_f)                          # and actually rounded
+
+
+def test_slot_step_picks_pool_entries():
+    # Row i of a slot-indexed batch is the single-sequence step of pool entry slots[i];
+    # a padding row (negative or out-of-range slot) yields o = 0; untouched entries and
+    # padding leave the pools bit for bit as they were.
+    rng = _rng(31)
+    hk, hv, d, bsz, n = 1, 2, 8, 4, 6
+    p = _step_inputs(rng, hk, hv, d, bsz)
+    cq = 2 * hk * d + hv * d
+    conv_pool = rng.standard_normal((n, 3, cq))
+    pool = 0.05 * rng.standard_normal((n, hv, d, d))
+    slots = np.array([4, -1, 0, 9])
+    o, cp, sp = G.recurrent_step_slots(p["x"], p["w"], conv_pool, p["a"], p["b"], p["A_log"],
+                                       p["dt"], pool, slots, hk, hv, d, d, io="f32")
+    for i, s in enumerate(slots):
+        if not 0 <= s < n:
+            assert np.all(o[i] == 0.0)
+            continue
+        o1, c1, s1 = G.recurrent_step(p["x"][i:i + 1], p["w"], conv_pool[s:s + 1],
+                                      p["a"][i:i + 1], p["b"][i:i + 1], p["A_log"], p["dt"],
+                                      pool[s:s + 1], hk, hv, d, d, io="f32")
+        np.testing.assert_array_equal(o[i], o1[0])
+        np.testing.assert_array_equal(cp[s], c1[0])
+        np.testing.assert_array_equal(sp[s], s1[0])
+    for s in sorted(set(range(n)) - {4, 0}):
+        np.testing.assert_array_equal(cp[s], conv_pool[s])
+        np.testing.assert_array_equal(sp[s], pool[s])
+    # the pools themselves are not modified
+    assert not np.shares_memory(sp, pool)
+    # a slot-indexed step changes its entries: the pin would catch a no-op gather
+    assert np.abs(sp[4] - pool[4]).max() > 1e-3
