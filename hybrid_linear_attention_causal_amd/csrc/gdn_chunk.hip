@@ -1652,6 +1652,17 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
     float4 c2;
     float egl;
     {
+      // every factor and V are read here, before the products so that their latency
+      // hides under them (their next copies land from barrier 2 on).  V is read
+      // unconditionally: rows past the chunk end hold copies of its last row and are
+      // zeroed by a select, which keeps the four reads in one wait
+      const float4 ck = *reinterpret_cast<const float4*>(&s_f[16 * j + 4 * g4]);
+      const float4 cq = *reinterpret_cast<const float4*>(&s_f[CH + 16 * j + 4 * g4]);
+      c2 = *reinterpret_cast<const float4*>(&s_f[2 * CH + 16 * j + 4 * g4]);
+      egl = s_f[3 * CH];
+      u16 vraw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vraw[e] = s_v[(16 * j + 4 * g4 + e) * V_STRIDE + c16];
       f32x4 ka = {0.f, 0.f, 0.f, 0.f}, kb = ka, qa = ka, qb = ka;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -1667,11 +1678,6 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
       }
 #pragma unroll
       for (int jp = 4; jp < KJ; ++jp) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[jp], knext, j, jp);
-      // every factor and V are read here: their next copies land from barrier 2 on
-      const float4 ck = *reinterpret_cast<const float4*>(&s_f[16 * j + 4 * g4]);
-      const float4 cq = *reinterpret_cast<const float4*>(&s_f[CH + 16 * j + 4 * g4]);
-      c2 = *reinterpret_cast<const float4*>(&s_f[2 * CH + 16 * j + 4 * g4]);
-      egl = s_f[3 * CH];
       const float ckv[4] = {ck.x, ck.y, ck.z, ck.w};
       const float cqv[4] = {cq.x, cq.y, cq.z, cq.w};
       int64_t t0;
@@ -1679,9 +1685,8 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
       chunk_rows(n, t0, L);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // rows past the chunk end hold copies of its last row: V is zero there
         const int t = 16 * j + 4 * g4 + e;
-        const float vv = t < L ? bf2f(s_v[t * V_STRIDE + c16]) : 0.f;
+        const float vv = t < L ? bf2f(vraw[e]) : 0.f;
         R[e] = vv - ckv[e] * (ka[e] + kb[e]);
         QS[e] = cqv[e] * (qa[e] + qb[e]);
       }
@@ -1696,14 +1701,16 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
 
     // ---- A2: U = T' R for row tile j
     {
+      // (all four R tiles are read by every wave, so that the reads share one wait)
       const bf16x8 rh = pack8(s_rx[0][0][lane], s_rx[1][0][lane]);
       const bf16x8 rl = pack8(s_rx[0][1][lane], s_rx[1][1][lane]);
+      bf16x8 rh1 = pack8(s_rx[2][0][lane], s_rx[3][0][lane]);
+      bf16x8 rl1 = pack8(s_rx[2][1][lane], s_rx[3][1][lane]);
+      asm volatile("" : "+v"(rh1), "+v"(rl1));   // keeps the reads out of the branch below
       f32x4 ua = mma(cur.th[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 ub = mma(cur.tl[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
       ua = mma(cur.th[0], rl, ua);
       if (j >= 2) {
-        const bf16x8 rh1 = pack8(s_rx[2][0][lane], s_rx[3][0][lane]);
-        const bf16x8 rl1 = pack8(s_rx[2][1][lane], s_rx[3][1][lane]);
         ub = mma(cur.th[1], rh1, ub);
         ua = mma(cur.tl[1], rh1, ua);
         ub = mma(cur.th[1], rl1, ub);
@@ -1725,12 +1732,13 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
     {
       const bf16x8 uh = pack8(s_ux[0][0][lane], s_ux[1][0][lane]);
       const bf16x8 ul = pack8(s_ux[0][1][lane], s_ux[1][1][lane]);
+      bf16x8 uh1 = pack8(s_ux[2][0][lane], s_ux[3][0][lane]);
+      bf16x8 ul1 = pack8(s_ux[2][1][lane], s_ux[3][1][lane]);
+      asm volatile("" : "+v"(uh1), "+v"(ul1));   // keeps the reads out of the branch below
       f32x4 pa = mma(cur.ph[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 pb = mma(cur.pl[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
       pa = mma(cur.ph[0], ul, pa);
       if (j >= 2) {
-        const bf16x8 uh1 = pack8(s_ux[2][0][lane], s_ux[3][0][lane]);
-        const bf16x8 ul1 = pack8(s_ux[2][1][lane], s_ux[3][1][lane]);
         pb = mma(cur.ph[1], uh1, pb);
         pa = mma(cur.pl[1], uh1, pa);
         pb = mma(cur.ph[1], ul1, pb);
