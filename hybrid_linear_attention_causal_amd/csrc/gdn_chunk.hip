@@ -517,11 +517,61 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   __syncthreads();
 
   // ---- raw Gram tiles, kept in registers: the 10 lower (I >= J) 16 x 16 tiles of
-  // rnk_i rnk_j (k_i . k_j) and, when P goes to the record, rnq_i rnk_j (q_i . k_j);
-  // wave w holds tiles w, w+4, w+8
-  f32x4 gk[3], gq[3];
+  // rnk_i rnk_j (k_i . k_j) and, when P goes to the record, rnq_i rnk_j (q_i . k_j).
+  // Fragment-native records: wave w holds row tile 3 - w of the K Gram (tiles (3 - w, J),
+  // J <= 3 - w, in gk[J]) and the transposed Q Gram tiles (J, w), J <= w (pq[J], below):
+  // five tiles per wave, and each K row block's fragments are read once per wave and
+  // serve both products.  Otherwise wave w holds K Gram tiles w, w+4, w+8 (tri_tile
+  // order) and, for P in rows, the Q Gram tiles at the same places.
+  constexpr int NG = FRAG ? 4 : 3;
+  f32x4 gk[NG], gq[3];
+  f32x4 pq[4];
+  const int ia = 3 - wave;          // FRAG: this wave's K Gram row tile
+  if constexpr (FRAG) {
+    // J runs downwards, so block ia is read (as kj) before the tiles J < ia need it (as ka)
+    bf16x8 ka[4], qw[4];
 #pragma unroll
-  for (int tt = 0; tt < 3; ++tt) {
+    for (int m = 0; m < 4; ++m) qw[m] = frag_rows(sm.u.r.qh, KS_STRIDE, 16 * wave, 32 * m, lane);
+    const float4 ki4 = *reinterpret_cast<const float4*>(&sm.rnk[16 * ia + 4 * g4]);
+    const float qi = sm.rnq[16 * wave + c16];
+#pragma unroll
+    for (int J = 3; J >= 0; --J) {
+      gk[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pq[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (J <= ia || J <= wave) {
+        bf16x8 kj[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) kj[m] = frag_rows(sm.u.r.kh, KS_STRIDE, 16 * J, 32 * m, lane);
+        if (J == ia) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) ka[m] = kj[m];
+        }
+        if (J <= ia) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) gk[J] = mma(ka[m], kj[m], gk[J]);
+          const float rkj = sm.rnk[16 * J + c16];
+          gk[J][0] *= ki4.x * rkj;
+          gk[J][1] *= ki4.y * rkj;
+          gk[J][2] *= ki4.z * rkj;
+          gk[J][3] *= ki4.w * rkj;
+        }
+        if (J <= wave) {
+          // (K Q^T) tile (J, w): accumulators hold rnq_i rnk_j (q_i . k_j) at
+          // i = 16 w + c16, j = 16 J + 4 g4 + e; tiles J = 2m, 2m+1 together are the
+          // layout of P's A-operand fragment [row tile w][token slab m]
+#pragma unroll
+          for (int m = 0; m < 4; ++m) pq[J] = mma(kj[m], qw[m], pq[J]);
+          const float4 kj4 = *reinterpret_cast<const float4*>(&sm.rnk[16 * J + 4 * g4]);
+          pq[J][0] *= qi * kj4.x;
+          pq[J][1] *= qi * kj4.y;
+          pq[J][2] *= qi * kj4.z;
+          pq[J][3] *= qi * kj4.w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < 3 && !FRAG; ++tt) {
     const int n = wave + 4 * tt;
     gk[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     gq[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -563,29 +613,6 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
       for (int e = 0; e < 4; ++e) {
         gk[tt][e] = ki[e] * rkj * a1[e];
         gq[tt][e] = qi[e] * rkj * a2[e];
-      }
-    }
-  }
-  // fragment-native records: wave w forms row tile w of P transposed, (K Q^T) tiles (J, w)
-  // for J <= w, whose accumulators (lane g4, c16, element e) hold
-  // rnq_i rnk_j (q_i . k_j) at i = 16 w + c16, j = 16 J + 4 g4 + e: tiles J = 2m, 2m+1
-  // together are the layout of P's A-operand fragment [row tile w][token slab m]
-  f32x4 pq[4];
-  if constexpr (FRAG) {
-#pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      pq[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (J <= wave) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          pq[J] = mma(frag_rows(sm.u.r.kh, KS_STRIDE, 16 * J, 32 * m, lane),
-                      frag_rows(sm.u.r.qh, KS_STRIDE, 16 * wave, 32 * m, lane), pq[J]);
-        const float4 kj4 = *reinterpret_cast<const float4*>(&sm.rnk[16 * J + 4 * g4]);
-        const float qi = sm.rnq[16 * wave + c16];
-        pq[J][0] *= qi * kj4.x;
-        pq[J][1] *= qi * kj4.y;
-        pq[J][2] *= qi * kj4.z;
-        pq[J][3] *= qi * kj4.w;
       }
     }
   }
@@ -648,8 +675,28 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
       // ---- A (fp32) and, for the 4-wave sweep, P (bf16 hi/lo planes staged in the T
       // buffer, strictly-upper tiles zero) of this head
       u16* pst = reinterpret_cast<u16*>(tf);
+      if constexpr (FRAG) {
+        // A row tile ia = 3 - w: tiles (ia, J), J <= ia
+        const int i0 = 16 * ia + 4 * g4;
+        const float4 gi4 = *reinterpret_cast<const float4*>(&gam[i0]);
+        const float4 bi4 = *reinterpret_cast<const float4*>(&bet[i0]);
+        const float gi[4] = {gi4.x, gi4.y, gi4.z, gi4.w};
+        const float bi[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
+        for (int J = 0; J < 4; ++J) {
+          if (J <= ia) {
+            const int j = 16 * J + c16;
+            const float gj = gam[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = i0 + e;
+              af[i * F_STRIDE + j] = (i > j) ? bi[e] * __expf(gi[e] - gj) * gk[J][e] : 0.f;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4 && !FRAG; ++tt) {
         const int n = wave + 4 * tt;
         if (n < 10) {
           int I, J;
@@ -693,12 +740,15 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
         f32x4 pv[4];
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
-          const float4 gj4 = *reinterpret_cast<const float4*>(&gam[16 * J + 4 * g4]);
-          const float gj[4] = {gj4.x, gj4.y, gj4.z, gj4.w};
+          pv[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (J <= wave) {       // tiles right of the diagonal tile are zero
+            const float4 gj4 = *reinterpret_cast<const float4*>(&gam[16 * J + 4 * g4]);
+            const float gj[4] = {gj4.x, gj4.y, gj4.z, gj4.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int jj = 16 * J + 4 * g4 + e;
-            pv[J][e] = (jj <= i) ? __expf(gi - gj[e]) * pq[J][e] : 0.f;   // exponent <= 0
+            for (int e = 0; e < 4; ++e) {
+              const int jj = 16 * J + 4 * g4 + e;
+              pv[J][e] = (jj <= i) ? __expf(gi - gj[e]) * pq[J][e] : 0.f;   // exponent <= 0
+            }
           }
         }
 #pragma unroll
