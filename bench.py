@@ -158,7 +158,8 @@ def cpu_baseline(inp, budget_heads=None, reps=2):
 def replay_leg(reps: int, warmup: int) -> dict:
     """Beside the step: the prompt -> decode replay on one 9B-shaped layer, B=1: the
     1024-token prompt through the prefill layer, then 256 decode steps (recurrent step +
-    gated norm) on the carried state, eagerly and as one captured HIP graph."""
+    gated norm in one launch) on the carried state, eagerly and as one captured HIP graph;
+    also the graph of the unfused steps (two launches per token)."""
     import numpy as np
     import torch
 
@@ -195,6 +196,7 @@ def replay_leg(reps: int, warmup: int) -> dict:
                             bufs=dbufs)
 
     graph = gdn.DecodeGraph(xs, w, cs, As, Bs, A_log, dt, st, zs, nw, hk, hv)
+    graph2 = gdn.DecodeGraph(xs, w, cs, As, Bs, A_log, dt, st, zs, nw, hk, hv, fused=False)
 
     def timed(fn, k):
         for _ in range(warmup):
@@ -211,6 +213,7 @@ def replay_leg(reps: int, warmup: int) -> dict:
     pre_ms = timed(prefill, reps)
     eager_ms = timed(decode_eager, max(2, reps // 4))
     graph_ms = timed(graph.replay, reps)
+    graph2_ms = timed(graph2.replay, reps)
     state_bytes = 2.0 * hv * D * D * 4
     return {"workload": f"Qwen3.5-9B GDN layer, one sequence: {T1}-token prompt then {n} "
                         "decode steps (bf16 io, fp32 state)",
@@ -218,6 +221,7 @@ def replay_leg(reps: int, warmup: int) -> dict:
             "prefill_layer_ms": pre_ms,
             "decode_eager_us_per_token": eager_ms * 1e3 / n,
             "decode_graph_us_per_token": graph_ms * 1e3 / n,
+            "decode_graph_unfused_us_per_token": graph2_ms * 1e3 / n,
             "decode_graph_tokens_per_s": n / (graph_ms * 1e-3),
             "decode_graph_state_GBps": state_bytes * n / (graph_ms * 1e-3) / 1e9}
 

@@ -44,6 +44,9 @@ _SIGS = {
     "gdn_recurrent_step_slots": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                   _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
                                   _vp], _i32),
+    "gdn_recurrent_step_norm": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                 _vp, _f32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                 _i32, _i32, _vp], _i32),
     "gdn_gated_rmsnorm": ([_vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32, _vp], _i32),
 }
 
@@ -190,6 +193,19 @@ def gdn_recurrent_step_slots(x, w, conv_state_pool, a, b, A_log, dt_bias, state_
         _p(x), _p(w), _p(conv_state_pool), _p(a), _p(b), _p(A_log), _p(dt_bias), _p(g_opt),
         _p(beta_opt), _p(state_pool), _io(state_pool), _p(slots), state_pool.shape[0], _p(o), B,
         Hk, Hv, dk, dv, K, float(scale), int(bool(use_qk_l2norm)), _io(x), _stream(stream)))
+
+
+def gdn_recurrent_step_norm(x, w, conv_state, a, b, A_log, dt_bias, state, z, norm_w, y, Hk, Hv,
+                            o=None, eps=1e-6, g_opt=None, beta_opt=None, scale=0.0,
+                            use_qk_l2norm=True, K=4, stream=None, dk=128, dv=128):
+    """The decode step and the z-gated RMSNorm of its output in one launch: y [B, Hv, dv];
+    o is written too when given.  The state may be float32 or bfloat16."""
+    _dev(x, w, conv_state, a, b, A_log, dt_bias, state, z, norm_w, y, o, g_opt, beta_opt)
+    B = x.shape[0]
+    _check("gdn_recurrent_step_norm", lib().gdn_recurrent_step_norm(
+        _p(x), _p(w), _p(conv_state), _p(a), _p(b), _p(A_log), _p(dt_bias), _p(g_opt),
+        _p(beta_opt), _p(state), _io(state), _p(z), _p(norm_w), float(eps), _p(o), _p(y), B, Hk,
+        Hv, dk, dv, K, float(scale), int(bool(use_qk_l2norm)), _io(x), _stream(stream)))
 
 
 def gdn_gated_rmsnorm(o, z, w, y, eps=1e-6, stream=None):

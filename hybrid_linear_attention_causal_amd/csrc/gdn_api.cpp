@@ -161,7 +161,9 @@ gdn_status_t recurrent_step_impl(const char* name, const void* x, const float* w
                                  void* state, int state_bf16, void* o, int B, int Hk, int Hv,
                                  int dk, int dv, int K, float scale, int use_qk_l2norm,
                                  gdn_dtype_t io, void* stream, const int32_t* slots = nullptr,
-                                 int n_slots = 0) {
+                                 int n_slots = 0, const void* z = nullptr,
+                                 const float* norm_w = nullptr, void* y = nullptr,
+                                 float eps = 0.f) {
   g_err[0] = 0;
   if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "%s: unknown io dtype %d", name, (int)io);
   if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "%s: kernel width %d (only 4)", name, K);
@@ -175,8 +177,13 @@ gdn_status_t recurrent_step_impl(const char* name, const void* x, const float* w
   if (have_g != have_b)
     return fail(GDN_ERR_INVALID_ARG, "%s: give both g_opt and beta_opt or neither", name);
   if (B > 0) {
-    if (!x || !w || !conv_state || !state || !o)
+    if (!x || !w || !conv_state || !state || (!o && !y))
       return fail(GDN_ERR_INVALID_ARG, "%s: NULL x, w, conv_state, state or o", name);
+    if (y && (!z || !norm_w))
+      return fail(GDN_ERR_INVALID_ARG, "%s: NULL z or norm_w", name);
+    if (y && (!aligned(norm_w, 16) || !aligned(z, 8) || !aligned(y, 8) || (o && !aligned(o, 8))))
+      return fail(GDN_ERR_INVALID_ARG, "%s: z, y, o must be 8-byte and norm_w 16-byte aligned",
+                  name);
     if (!have_g && (!a || !b || !A_log || !dt_bias))
       return fail(GDN_ERR_INVALID_ARG, "%s: NULL a, b, A_log or dt_bias", name);
     if (!aligned(state, 16) || !aligned(w, 16))
@@ -188,7 +195,8 @@ gdn_status_t recurrent_step_impl(const char* name, const void* x, const float* w
   gdn_status_t st = check_device();
   if (st != GDN_OK) return st;
   gdn::StepArgs args{x, w, conv_state, a, b, A_log, dt_bias, g_opt, beta_opt, state, o, B, Hk, Hv,
-                     scale, use_qk_l2norm ? 1 : 0, state_bf16, slots, n_slots};
+                     scale, use_qk_l2norm ? 1 : 0, state_bf16, slots, n_slots, z, norm_w, y,
+                     eps};
   hipError_t e = gdn::launch_recurrent_step(args, io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
                                             (hipStream_t)stream);
   return e == hipSuccess ? GDN_OK : hip_fail(e, "recurrent_step launch");
@@ -235,6 +243,26 @@ gdn_status_t gdn_recurrent_step_slots(const void* x, const float* w, void* conv_
   return recurrent_step_impl("recurrent_step_slots", x, w, conv_state_pool, a, b, A_log, dt_bias,
                              g_opt, beta_opt, state_pool, state_dtype == GDN_BF16 ? 1 : 0, o, B,
                              Hk, Hv, dk, dv, K, scale, use_qk_l2norm, io, stream, slots, n_slots);
+}
+
+gdn_status_t gdn_recurrent_step_norm(const void* x, const float* w, void* conv_state,
+                                     const void* a, const void* b, const float* A_log,
+                                     const float* dt_bias, const float* g_opt,
+                                     const float* beta_opt, void* state, gdn_dtype_t state_dtype,
+                                     const void* z, const float* norm_w, float eps, void* o_opt,
+                                     void* y, int B, int Hk, int Hv, int dk, int dv, int K,
+                                     float scale, int use_qk_l2norm, gdn_dtype_t io,
+                                     void* stream) {
+  g_err[0] = 0;
+  if (state_dtype != GDN_F32 && state_dtype != GDN_BF16)
+    return fail(GDN_ERR_INVALID_ARG, "recurrent_step_norm: unknown state dtype %d",
+                (int)state_dtype);
+  if (!(eps >= 0.f)) return fail(GDN_ERR_INVALID_ARG, "recurrent_step_norm: eps=%g", (double)eps);
+  if (B > 0 && !y) return fail(GDN_ERR_INVALID_ARG, "recurrent_step_norm: NULL y");
+  return recurrent_step_impl("recurrent_step_norm", x, w, conv_state, a, b, A_log, dt_bias, g_opt,
+                             beta_opt, state, state_dtype == GDN_BF16 ? 1 : 0, o_opt, B, Hk, Hv,
+                             dk, dv, K, scale, use_qk_l2norm, io, stream, nullptr, 0, z, norm_w,
+                             y, eps);
 }
 
 gdn_status_t gdn_gated_rmsnorm(const void* o, const void* z, const float* w, void* y,

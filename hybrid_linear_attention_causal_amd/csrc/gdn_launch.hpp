@@ -61,6 +61,12 @@ struct StepArgs {
   int state_bf16;         // 1: the state is stored as bf16 (read, computed in fp32, rounded back)
   const int32_t* slots;   // NULL: row b uses state b; else slots[b] in [0, n_slots), other = padding
   int n_slots;
+  // fused z-gated RMSNorm of o (y != NULL): y = norm_w * o / sqrt(mean(o^2) + eps) * silu(z),
+  // o taken as stored (rounded to io); o itself is written only when o != NULL
+  const void* z;
+  const float* norm_w;
+  void* y;
+  float eps;
 };
 
 struct NormArgs {

@@ -58,7 +58,7 @@ template <> struct StateQuad<true> {
 
 // The bf16-state variant holds its state packed and fits four waves per SIMD (two
 // 512-thread workgroups per CU); the fp32 one holds 64 state registers and runs three.
-template <int IO, int HPP, bool SBF, bool SLOTS>
+template <int IO, int HPP, bool SBF, bool SLOTS, bool NORM>
 __global__ void __launch_bounds__(256 * HPP, 4)
 recurrent_step_kernel(StepArgs p) {
   typedef Io<IO> io;
@@ -80,6 +80,8 @@ recurrent_step_kernel(StepArgs p) {
   float* gsh = red2 + HPP * 4 * SD;          // r: decay e^g
   float* bsh = gsh + r;                      // r: beta
   float* nsh = bsh + r;                      // 2: 1/|q|, 1/|k|
+  float* zsh = nsh + 2;                      // NORM: r * 128 gate values z
+  float* wsh = zsh + (NORM ? r * SD : 0);    // NORM: 128 norm weights
 
   const int hl = __builtin_amdgcn_readfirstlane(tid >> 8);   // head slot inside a pass
   const int t256 = tid & 255;
@@ -129,6 +131,19 @@ recurrent_step_kernel(StepArgs p) {
     }
   }
 
+  // the fused norm's z rows of the r heads (four values per thread) and its weights, loaded
+  // with the conv inputs (whose wait covers them) and parked in LDS
+  float zr[4] = {0.f, 0.f, 0.f, 0.f};
+  float4 wr = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (NORM) {
+    if (tid < r * 32) {
+      const T* zp = (const T*)p.z + ((int64_t)bseq * Hv + kh * r) * SD + tid * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) zr[c] = io::ld(zp, c);
+    }
+    if (tid < 32) wr = *reinterpret_cast<const float4*>(p.norm_w + tid * 4);
+  }
+
   // ---- conv window + SiLU for this group's channels; shift the conv state
   const T* xb = (const T*)p.x + (int64_t)bseq * Cq;
   T* cs = (T*)p.conv_state + (int64_t)slot * 3 * Cq;
@@ -149,6 +164,13 @@ recurrent_step_kernel(StepArgs p) {
     cs[c] = c1;
     cs[Cq + c] = c2;
     cs[2 * Cq + c] = xc;
+  }
+  if constexpr (NORM) {
+    if (tid < r * 32) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) zsh[tid * 4 + c] = zr[c];
+    }
+    if (tid < 32) *reinterpret_cast<float4*>(&wsh[tid * 4]) = wr;
   }
   __syncthreads();
 
@@ -246,13 +268,31 @@ recurrent_step_kernel(StepArgs p) {
     }
     __syncthreads();
     if (t256 < 32) {
-      T* op = (T*)p.o + ((int64_t)bseq * Hv + h) * SD + cg * 4;
+      float ov[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float tot = 0.f;
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) tot += red2[(hl * 4 + w4) * SD + cg * 4 + c];
-        io::st(op, c, p.scale * tot);
+        ov[c] = io::round(p.scale * tot);      // o as stored
+      }
+      const int64_t ob = ((int64_t)bseq * Hv + h) * SD + cg * 4;
+      if (p.o) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) io::st((T*)p.o + ob, c, ov[c]);
+      }
+      if constexpr (NORM) {
+        // z-gated RMSNorm of the head's row: lanes 0 .. 31 hold its 128 values
+        float ss = ov[0] * ov[0];
+        ss = fmaf(ov[1], ov[1], ss);
+        ss = fmaf(ov[2], ov[2], ss);
+        ss = fmaf(ov[3], ov[3], ss);
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) ss += __shfl_xor(ss, m, 64);
+        const float inv = 1.0f / sqrtf(ss * (1.0f / SD) + p.eps);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          io::st((T*)p.y + ob, c, wsh[cg * 4 + c] * (ov[c] * inv) * silu(zsh[j * SD + cg * 4 + c]));
       }
     }
     __syncthreads();  // red1/red2 are reused by the next pass
@@ -262,13 +302,16 @@ recurrent_step_kernel(StepArgs p) {
 template <int IO, int HPP, bool SBF>
 static hipError_t step_launch(const StepArgs& a, hipStream_t s) {
   const int r = a.Hv / a.Hk;
-  const size_t lds = sizeof(float) * (256 + r * SD + 2 * HPP * 4 * SD + 2 * r + 2);
-  if (a.slots)
-    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, SBF, true>), dim3((unsigned)(a.B * a.Hk)),
-                       dim3(256 * HPP), lds, s, a);
+  const bool norm = a.y != nullptr;
+  const size_t lds = sizeof(float) * (256 + r * SD + 2 * HPP * 4 * SD + 2 * r + 2 +
+                                      (norm ? r * SD + SD : 0));
+  const dim3 grid((unsigned)(a.B * a.Hk)), block(256 * HPP);
+  if (norm)   // (the fused norm takes no slots)
+    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, SBF, false, true>), grid, block, lds, s, a);
+  else if (a.slots)
+    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, SBF, true, false>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, SBF, false>), dim3((unsigned)(a.B * a.Hk)),
-                       dim3(256 * HPP), lds, s, a);
+    hipLaunchKernelGGL((recurrent_step_kernel<IO, HPP, SBF, false, false>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 

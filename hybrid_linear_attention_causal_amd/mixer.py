@@ -1,7 +1,8 @@
 """Thin helpers that allocate outputs with torch and chain the libgdn calls.
 
 prefill_layer:  conv1d+SiLU -> chunked delta rule -> z-gated RMSNorm
-decode_step:    recurrent step (conv + delta rule, in place) -> z-gated RMSNorm
+decode_step:    recurrent step (conv + delta rule, in place) + z-gated RMSNorm, fused in one
+                launch by default
 DecodeGraph:    n decode steps captured once as a HIP graph, replayed as one launch
 """
 from __future__ import annotations
@@ -9,7 +10,7 @@ from __future__ import annotations
 import torch
 
 from ._lib import (gdn_chunk_prefill, gdn_chunk_prefill_workspace_size, gdn_conv1d_fwd,
-                   gdn_gated_rmsnorm, gdn_recurrent_step)
+                   gdn_gated_rmsnorm, gdn_recurrent_step, gdn_recurrent_step_norm)
 
 D = 128
 
@@ -56,26 +57,32 @@ def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens
 
 
 def decode_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w, Hk, Hv,
-                eps=1e-6, bufs=None, stream=None):
+                eps=1e-6, bufs=None, stream=None, fused=True):
     """One token per sequence.  conv_state [B,3,Cq] and state [B,Hv,128,128] update in place;
-    the state may be float32 or bfloat16 (stored bf16, stepped in fp32)."""
+    the state may be float32 or bfloat16 (stored bf16, stepped in fp32).  fused: the step
+    and the gated norm in one launch (gdn_recurrent_step_norm), else two calls."""
     B = x.shape[0]
     bufs = {} if bufs is None else bufs
     o = bufs.get("o")
     if o is None:
         o = torch.empty((B, Hv, D), dtype=x.dtype, device=x.device)
-    gdn_recurrent_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, o, Hk, Hv,
-                       stream=stream)
     yn = bufs.get("y")
     if yn is None:
         yn = torch.empty_like(o)
-    gdn_gated_rmsnorm(o, z, norm_w, yn, eps, stream=stream)
+    if fused:
+        gdn_recurrent_step_norm(x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w,
+                                yn, Hk, Hv, o=o, eps=eps, stream=stream)
+    else:
+        gdn_recurrent_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, o, Hk, Hv,
+                           stream=stream)
+        gdn_gated_rmsnorm(o, z, norm_w, yn, eps, stream=stream)
     return {"o": o, "y": yn}
 
 
 class DecodeGraph:
-    """n consecutive decode steps (gdn_recurrent_step -> gdn_gated_rmsnorm per step) of
-    one layer, captured once as a HIP graph and replayed with one launch.
+    """n consecutive decode steps (one gdn_recurrent_step_norm per step, or with
+    fused=False gdn_recurrent_step -> gdn_gated_rmsnorm) of one layer, captured once as a
+    HIP graph and replayed with one launch.
 
     The graph reads x[t], a[t], b[t], z[t] from the static buffers given here
     (x [n, B, Cq], a and b [n, B, Hv], z [n, B, Hv, 128]) and writes o[t] and y[t] of its
@@ -86,16 +93,21 @@ class DecodeGraph:
     """
 
     def __init__(self, x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w, Hk, Hv,
-                 eps=1e-6):
+                 eps=1e-6, fused=True):
         n, B = x.shape[0], x.shape[1]
         self.o = torch.empty((n, B, Hv, D), dtype=x.dtype, device=x.device)
         self.y = torch.empty_like(self.o)
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
             for t in range(n):
-                gdn_recurrent_step(x[t], conv_w, conv_state, a[t], b[t], A_log, dt_bias, state,
-                                   self.o[t], Hk, Hv)
-                gdn_gated_rmsnorm(self.o[t], z[t], norm_w, self.y[t], eps)
+                if fused:
+                    gdn_recurrent_step_norm(x[t], conv_w, conv_state, a[t], b[t], A_log, dt_bias,
+                                            state, z[t], norm_w, self.y[t], Hk, Hv, o=self.o[t],
+                                            eps=eps)
+                else:
+                    gdn_recurrent_step(x[t], conv_w, conv_state, a[t], b[t], A_log, dt_bias,
+                                       state, self.o[t], Hk, Hv)
+                    gdn_gated_rmsnorm(self.o[t], z[t], norm_w, self.y[t], eps)
 
     def replay(self):
         self.graph.replay()

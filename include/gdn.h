@@ -233,6 +233,34 @@ gdn_status_t gdn_recurrent_step_slots(const void* x, const float* w, void* conv_
                                       void* stream);
 
 /*
+ * gdn_recurrent_step_norm -- the decode step and the z-gated RMSNorm of its output in one
+ * launch: the same results as gdn_recurrent_step (or its bf16-state form) followed by
+ * gdn_gated_rmsnorm on o (llm-arch-viz Qwen3.5-9B page, module tree: the linear-attention
+ * block holds the gated norm, of width 128, next to its output projection; HF Qwen3.5 docs
+ * page, "Usage tips": the single-token recurrence is bandwidth-bound, so o need not make a
+ * round trip through memory).  o is normalised as the unfused call stores it (rounded
+ * to io); the row sums of squares are accumulated in another order, so y may differ from
+ * the two-call result by a rounding.
+ *
+ *   state_dtype     GDN_F32 (as gdn_recurrent_step) or GDN_BF16 (as
+ *                   gdn_recurrent_step_bf16_state)
+ *   z               [B, Hv, dv]   io
+ *   norm_w          [dv]          fp32
+ *   o_opt           [B, Hv, dv]   io, or NULL: o is then not written
+ *   y               [B, Hv, dv]   io
+ * Errors as for gdn_recurrent_step and gdn_gated_rmsnorm; also INVALID_ARG for NULL y, z
+ * or norm_w, eps < 0 or an unknown state_dtype.
+ */
+gdn_status_t gdn_recurrent_step_norm(const void* x, const float* w, void* conv_state,
+                                     const void* a, const void* b, const float* A_log,
+                                     const float* dt_bias, const float* g_opt,
+                                     const float* beta_opt, void* state, gdn_dtype_t state_dtype,
+                                     const void* z, const float* norm_w, float eps, void* o_opt,
+                                     void* y, int B, int Hk, int Hv, int dk, int dv, int K,
+                                     float scale, int use_qk_l2norm, gdn_dtype_t io,
+                                     void* stream);
+
+/*
  * gdn_gated_rmsnorm -- z-gated RMSNorm over rows of D values:
  *   y[r, :] = w * o[r, :] / sqrt(mean(o[r, :]^2) + eps) * silu(z[r, :])
  * (llm-arch-viz Qwen3.5-9B page: Qwen3_5RMSNormGated with a [128] weight shared

@@ -12,7 +12,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
 
 EXPECTED = {"gdn_last_error", "gdn_version", "gdn_conv1d_fwd", "gdn_chunk_prefill_workspace_size",
             "gdn_chunk_prefill", "gdn_recurrent_step", "gdn_recurrent_step_bf16_state",
-            "gdn_recurrent_step_slots", "gdn_gated_rmsnorm"}
+            "gdn_recurrent_step_slots", "gdn_recurrent_step_norm", "gdn_gated_rmsnorm"}
 
 
 def test_header_declares_the_calls():
@@ -158,3 +158,23 @@ def test_step_slots_rejects():
     assert "recurrent_step_slots" in _msg()
     assert _slots(Hv=20) == _lib.GDN_ERR_INVALID_ARG
     assert _slots(st=None) == _lib.GDN_ERR_INVALID_ARG
+
+
+def _stepnorm(**kw):
+    args = dict(x=P, w=P, cs=P, a=P, b=P, A_log=P, dt_bias=P, g=None, beta=None, st=P,
+                sdt=_lib.GDN_F32, z=P, nw=P, eps=1e-6, o=None, y=P, B=4, Hk=16, Hv=32, dk=128,
+                dv=128, K=4, scale=0.0, l2=1, io=1)
+    args.update(kw)
+    return _L().gdn_recurrent_step_norm(*args.values(), None)
+
+
+def test_step_norm_rejects():
+    assert _stepnorm(sdt=9) == _lib.GDN_ERR_INVALID_ARG
+    assert _stepnorm(eps=-1.0) == _lib.GDN_ERR_INVALID_ARG
+    assert _stepnorm(y=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _stepnorm(z=None) == _lib.GDN_ERR_INVALID_ARG
+    assert "recurrent_step_norm" in _msg()
+    assert _stepnorm(nw=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _stepnorm(nw=ctypes.c_void_p(24)) == _lib.GDN_ERR_INVALID_ARG
+    assert _stepnorm(y=ctypes.c_void_p(20)) == _lib.GDN_ERR_INVALID_ARG
+    assert _stepnorm(dv=64) == _lib.GDN_ERR_UNSUPPORTED

@@ -326,6 +326,45 @@ def test_recurrent_step_slots_parity(state_io):
         assert_state(spg[live], sp_ref[live], "slot step state")
 
 
+@pytest.mark.parametrize("io,state_io", [("bf16", "f32"), ("bf16", "bf16"), ("f32", "f32")])
+def test_recurrent_step_norm_parity(io, state_io):
+    """The fused step + gated norm: y against the oracle's step -> norm, and o and the state
+    bit for bit equal to the unfused step's."""
+    hk, hv, B = 2, 4, 6
+    inp = _case(hk, hv, io, 95, batch=B, init_state=True, kind="decode")
+    rng = np.random.default_rng(95)
+    z = G.to_io(rng.standard_normal((B, hv, D)), io)
+    nw = 1.0 + 0.1 * rng.standard_normal(D)
+    s0 = G.to_io(inp["state_in"], state_io)
+    args = [f32_dev(inp["conv_w"]), None, to_dev(inp["a"], io), to_dev(inp["b"], io),
+            f32_dev(inp["A_log"]), f32_dev(inp["dt_bias"])]
+    x = to_dev(inp["x"], io)
+    sdev = lambda: to_dev(s0, "bf16") if state_io == "bf16" else f32_dev(s0)
+    # fused
+    cs1, st1 = to_dev(inp["conv_state_in"], io), sdev()
+    o1 = torch.empty((B, hv, D), dtype=x.dtype, device="cuda")
+    y1 = torch.empty_like(o1)
+    a1 = list(args)
+    a1[1] = cs1
+    gdn.gdn_recurrent_step_norm(x, *a1, st1, to_dev(z, io), f32_dev(nw), y1, hk, hv, o=o1)
+    # unfused
+    cs2, st2 = to_dev(inp["conv_state_in"], io), sdev()
+    o2 = torch.empty_like(o1)
+    a2 = list(args)
+    a2[1] = cs2
+    gdn.gdn_recurrent_step(x, *a2, st2, o2, hk, hv)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(st1, st2)
+    assert torch.equal(cs1, cs2)
+    o_ref, _, _ = G.recurrent_step(inp["x"], inp["conv_w"], inp["conv_state_in"], inp["a"],
+                                   inp["b"], inp["A_log"], inp["dt_bias"], s0, hk, hv, D, D,
+                                   io=io, state_io="bf16" if state_io == "bf16" else "f64")
+    y_ref = G.gated_rmsnorm(G.to_io(o_ref, io), z, nw)
+    assert_out(host(o1), G.to_io(o_ref, io), io, "fused step o")
+    assert_out(host(y1), G.to_io(y_ref, io), io, "fused step y", upstream_bf16=1)
+
+
 def test_prefill_then_steps_equals_prefill():
     """Prefill of T1 tokens then T - T1 decode steps on carried state == prefill of T."""
     io = "bf16"

@@ -39,14 +39,16 @@ def _prefill(d, T1, hk, hv):
                              d["dt_bias"], d["z"][:T1], d["norm_w"], hk, hv)
 
 
-def test_replay_eager_matches_oracle(replay):
+@pytest.mark.parametrize("fused", [True, False])
+def test_replay_eager_matches_oracle(replay, fused):
     inp, d, T, T1, hk, hv = replay
     out = _prefill(d, T1, hk, hv)
     cs, st = out["conv_state_out"], out["state_out"]
     ys = [out["y"]]
     for t in range(T1, T):
         r = gdn.decode_step(d["x"][t:t + 1], d["conv_w"], cs, d["a"][t:t + 1], d["b"][t:t + 1],
-                            d["A_log"], d["dt_bias"], st, d["z"][t:t + 1], d["norm_w"], hk, hv)
+                            d["A_log"], d["dt_bias"], st, d["z"][t:t + 1], d["norm_w"], hk, hv,
+                            fused=fused)
         ys.append(r["y"])
     y = torch.cat(ys)
     torch.cuda.synchronize()
