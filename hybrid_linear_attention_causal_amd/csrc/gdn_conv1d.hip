@@ -65,18 +65,22 @@ template <> struct Row8<IO_F32> {
   }
 };
 
-// (two workgroups per CU: a 4096-token batch of 8192 bf16 channels is one pass of
-// 512 workgroups)
+// Two workgroups per CU: a 4096-token batch of 8192 bf16 channels is one pass of 512
+// workgroups.  Workgroup b takes channel group b % groups of token tile b / groups: the
+// groups that share a tile's rows are consecutive in launch order, so each row is
+// fetched from HBM by workgroups that run together.
 template <int IO>
 __global__ void __launch_bounds__(CONV_BLOCK, 2)
 conv1d_silu_kernel(const typename Io<IO>::T* __restrict__ x, const float* __restrict__ w,
                    typename Io<IO>::T* __restrict__ y, const int32_t* __restrict__ cu, int Ns,
-                   int64_t N, int Cq, const typename Io<IO>::T* __restrict__ state_in) {
+                   int64_t N, int Cq, const typename Io<IO>::T* __restrict__ state_in,
+                   int groups) {
   typedef Io<IO> io;
-  const int c0 = (blockIdx.y * CONV_BLOCK + threadIdx.x) * 8;
+  const int64_t b = blockIdx.x;
+  const int c0 = ((int)(b % groups) * CONV_BLOCK + threadIdx.x) * 8;
   if (c0 >= Cq) return;
   constexpr int CONV_TT = conv_tt<IO>();
-  const int64_t t0 = (int64_t)blockIdx.x * CONV_TT;
+  const int64_t t0 = (b / groups) * CONV_TT;
   if (t0 >= N) return;
   const int64_t t1 = t0 + CONV_TT < N ? t0 + CONV_TT : N;
 
@@ -120,7 +124,15 @@ conv1d_silu_kernel(const typename Io<IO>::T* __restrict__ x, const float* __rest
         acc = fmaf(wt[3][j], v3[j], acc);
         out[j] = silu(acc);
       }
-      io::st8(y, (t0 + t) * Cq + c0, out);
+      // nontemporal: y is written once here and read by the next call
+      if constexpr (IO == IO_BF16) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = {f2bf2(out[0], out[1]), f2bf2(out[2], out[3]), f2bf2(out[4], out[5]),
+                         f2bf2(out[6], out[7])};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y + (t0 + t) * Cq + c0));
+      } else {
+        io::st8(y, (t0 + t) * Cq + c0, out);
+      }
     }
     return;
   }
@@ -213,10 +225,10 @@ static hipError_t conv_impl(const ConvArgs& a, hipStream_t st) {
   const int groups = (a.Cq / 8 + CONV_BLOCK - 1) / CONV_BLOCK;
   if (a.N > 0) {
     const int64_t tiles = (a.N + conv_tt<IO>() - 1) / conv_tt<IO>();
-    dim3 grid((unsigned)tiles, (unsigned)groups);
-    hipLaunchKernelGGL(conv1d_silu_kernel<IO>, grid, dim3(CONV_BLOCK), 0, st,
-                       (const T*)a.x, a.w, (T*)a.y, a.cu, a.Ns, a.N, a.Cq,
-                       (const T*)a.state_in);
+    if (tiles * groups > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(conv1d_silu_kernel<IO>, dim3((unsigned)(tiles * groups)),
+                       dim3(CONV_BLOCK), 0, st, (const T*)a.x, a.w, (T*)a.y, a.cu, a.Ns, a.N,
+                       a.Cq, (const T*)a.state_in, groups);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
