@@ -40,14 +40,17 @@ PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
 
 CSRC = os.path.join(ROOT, "hybrid_linear_attention_causal_amd", "csrc")
 KERNEL_SOURCES = {"gdn_chunk_prefill": ("gdn_chunk.hip", "gdn_common.hpp", "gdn_launch.hpp"),
-                  "gdn_recurrent_step": ("gdn_step.hip", "gdn_common.hpp", "gdn_launch.hpp")}
+                  "gdn_recurrent_step": ("gdn_step.hip", "gdn_common.hpp", "gdn_launch.hpp"),
+                  "gdn_recurrent_step_bf16_state": ("gdn_step.hip", "gdn_common.hpp",
+                                                    "gdn_launch.hpp")}
 # HBM bytes per launch on this workload from rocprofv3 PMC FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy (the summary with the
 # commands is profiles/pmc_bytes_bench_qwen35_9b_prefill_T4096_decode_B256.txt).  Each
 # figure belongs to the kernel sources with the given digest and is not reported once
 # they change.
-MEASURED_TRAFFIC = {"gdn_chunk_prefill": ("09680cea8fbf7dbd", 285.9e6),
-                    "gdn_recurrent_step": ("97aad529d65d7d46", 1106.0e6)}
+MEASURED_TRAFFIC = {"gdn_chunk_prefill": ("29b49e746692f8f1", 274.0e6),
+                    "gdn_recurrent_step": ("bf1f8ee0338506c6", 1105.8e6),
+                    "gdn_recurrent_step_bf16_state": ("bf1f8ee0338506c6", 568.9e6)}
 
 
 def source_digest(kernel: str) -> str:
@@ -391,6 +394,7 @@ def main():
             "kernel": "gdn_recurrent_step_bf16_state", "bound": "hbm", "ms": ms_bf16_state,
             "achieved": dbytes_bf / (ms_bf16_state * 1e-3) / 1e9, "peak": PEAK_HBM_BYTES / 1e9,
             "unit": "GB/s", "frac": dbytes_bf / (ms_bf16_state * 1e-3) / PEAK_HBM_BYTES,
+            "traffic": measured_traffic("gdn_recurrent_step_bf16_state"),
             "algorithmic_per_launch": dbytes_bf},
         "replay": replay,
         "cpu_baseline": None,

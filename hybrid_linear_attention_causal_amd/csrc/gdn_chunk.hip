@@ -776,8 +776,10 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
       // ---- T = (I + A)^{-1}, blocked: 16 x 16 diagonal blocks by forward substitution
       // (one column per lane); then T_10, T_32 = -T_ii A_ij T_jj; then the lower
       // 32 x 32 block T[32:64, 0:32] = -T[32:64, 32:64] A[32:64, 0:32] T[0:32, 0:32]
-      if (g4 == 0) {
-        const int b = wave;
+      // (wave 0 solves all four diagonal blocks, block g4 in lane group g4: the same
+      // latency as one block per wave, a quarter of the VALU instructions)
+      if (wave == 0) {
+        const int b = g4;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -795,10 +797,11 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) tf[(16 * b + i) * F_STRIDE + 16 * b + c16] = x[i];
-      } else if (g4 == 1 && (wave & 1) == 0) {
+      } else if (wave == 1 && g4 < 2) {
         // the strictly-upper blocks T_01 and T_23 enter the 32 x 32 products below: zero
+        const int bb = 2 * g4;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tf[(16 * wave + i) * F_STRIDE + 16 * wave + 16 + c16] = 0.f;
+        for (int i = 0; i < 16; ++i) tf[(16 * bb + i) * F_STRIDE + 16 * bb + 16 + c16] = 0.f;
       }
       __syncthreads();
       // blocks (1,0) (wave 0) and (3,2) (wave 1): T_IJ = -T_II (A_IJ T_JJ), 16 x 16 fp32

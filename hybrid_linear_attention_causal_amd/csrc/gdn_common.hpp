@@ -80,14 +80,25 @@ template <> struct Io<IO_BF16> {
 __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
-__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
-// log(1 + e^x); for x > 20 the correction is below fp32 resolution
-__device__ __forceinline__ float softplus(float x) { return x > 20.0f ? x : log1pf(expf(x)); }
+// 1 / (1 + e^{-x}) on the hardware exp2 and reciprocal (a few ulp)
+__device__ __forceinline__ float sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+// log(1 + e^x) on the hardware exp2 and log2, a few ulp relative: with u = 1 + e^x rounded,
+// log1p(e) = log(u) e / (u - 1) cancels the rounding of u (Goldberg's log1p), and u == 1
+// (e below half an ulp of 1) gives e itself; for x > 20 the correction is below fp32
+// resolution
+__device__ __forceinline__ float softplus(float x) {
+  if (x > 20.0f) return x;
+  const float e = __expf(x);
+  const float u = 1.0f + e;
+  return u == 1.0f ? e : __logf(u) * (e * __builtin_amdgcn_rcpf(u - 1.0f));
+}
 
 // gate pair of the gated delta rule: g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b)
 __device__ __forceinline__ void gate_pair(float a, float b, float A_log, float dt_bias, float& g,
                                           float& beta) {
-  g = -expf(A_log) * softplus(a + dt_bias);
+  g = -__expf(A_log) * softplus(a + dt_bias);
   beta = sigmoid(b);
 }
 
