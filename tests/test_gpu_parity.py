@@ -326,11 +326,13 @@ def test_recurrent_step_slots_parity(state_io):
         assert_state(spg[live], sp_ref[live], "slot step state")
 
 
-@pytest.mark.parametrize("io,state_io", [("bf16", "f32"), ("bf16", "bf16"), ("f32", "f32")])
-def test_recurrent_step_norm_parity(io, state_io):
+@pytest.mark.parametrize("io,state_io,hk,hv", [("bf16", "f32", 2, 4), ("bf16", "bf16", 2, 4),
+                                              ("f32", "f32", 2, 4), ("bf16", "f32", 1, 3),
+                                              ("f32", "bf16", 1, 3)])
+def test_recurrent_step_norm_parity(io, state_io, hk, hv):
     """The fused step + gated norm: y against the oracle's step -> norm, and o and the state
-    bit for bit equal to the unfused step's."""
-    hk, hv, B = 2, 4, 6
+    bit for bit equal to the unfused step's (value heads two per pass, or one)."""
+    B = 6
     inp = _case(hk, hv, io, 95, batch=B, init_state=True, kind="decode")
     rng = np.random.default_rng(95)
     z = G.to_io(rng.standard_normal((B, hv, D)), io)
@@ -363,6 +365,26 @@ def test_recurrent_step_norm_parity(io, state_io):
     y_ref = G.gated_rmsnorm(G.to_io(o_ref, io), z, nw)
     assert_out(host(o1), G.to_io(o_ref, io), io, "fused step o")
     assert_out(host(y1), G.to_io(y_ref, io), io, "fused step y", upstream_bf16=1)
+
+
+def test_step_entry_points_accept_an_empty_batch():
+    """B = 0: every decode entry point returns without launching anything."""
+    hk, hv = 2, 4
+    C = (2 * hk + hv) * D
+    e = torch.empty((0, C), dtype=torch.bfloat16, device="cuda")
+    eh = torch.empty((0, hv), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((C, 4), device="cuda")
+    hv_f = torch.zeros(hv, device="cuda")
+    cs = torch.empty((1, 3, C), dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros((1, hv, D, D), device="cuda")
+    o = torch.empty((0, hv, D), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_recurrent_step(e, w, cs, eh, eh, hv_f, hv_f, st, o, hk, hv)
+    gdn.gdn_recurrent_step_slots(e, w, cs, eh, eh, hv_f, hv_f, st,
+                                 torch.empty(0, dtype=torch.int32, device="cuda"), o, hk, hv)
+    gdn.gdn_recurrent_step_norm(e, w, cs, eh, eh, hv_f, hv_f, st, o, torch.ones(D, device="cuda"),
+                                torch.empty_like(o), hk, hv)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(st) == 0
 
 
 def test_prefill_then_steps_equals_prefill():
