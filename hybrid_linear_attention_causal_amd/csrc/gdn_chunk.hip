@@ -79,7 +79,8 @@ constexpr int64_t WS_ROWS_BYTES = (int64_t)CH * KS_STRIDE * 2;       // 17408 pe
 // Fragment-native records of the row-split sweep (bf16 io), per (global chunk, value
 // head), FR_REC_BYTES: T' fragments [row tile j 4][token slab m 2][plane hi, lo 2] (the A
 // operand of T' R; each fragment 1 KB, lane l's 16 bytes at 16 l), P fragments in the same
-// order, then the 8 x 64 fp32 factor rows.
+// order, then the 8 x 64 fp32 factor rows.  The fragments of token slab 1 for row tiles 0
+// and 1 are zero; they are neither written nor read.
 constexpr int64_t FR_T_OFF = 0;
 constexpr int64_t FR_P_OFF = 16 * 1024;
 constexpr int64_t FR_FAC_OFF = 32 * 1024;
@@ -753,6 +754,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
+          if (m == 1 && wave < 2) continue;   // zero: tokens 32.. lie right of row tiles 0, 1
           bf16x8 hi, lo;
           frag_acc_split(pv[2 * m], pv[2 * m + 1], hi, lo);
           *reinterpret_cast<uint4*>(rec + FR_P_OFF + fr_tp(wave, m, 0) + lane * 16) = __builtin_bit_cast(uint4, hi);
@@ -843,6 +845,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
         for (int it = 0; it < 2; ++it) {
           const int u = tid + NTHR * it;          // j u >> 7, m (u >> 6) & 1, lane u & 63
           const int jj = u >> 7, m = (u >> 6) & 1, l = u & 63;
+          if (m == 1 && jj < 2) continue;    // zero fragments, never read
           const int i = 16 * jj + (l & 15);
           float v[8];
 #pragma unroll
