@@ -4,7 +4,7 @@ The compute lives in libgdn.so (hand-written HIP kernels behind a C ABI,
 include/gdn.h); this package is its Python binding plus thin helpers that
 allocate outputs with torch and chain the four calls.
 """
-from ._lib import (GDN_BF16, GDN_F32, GdnError, gdn_chunk_prefill,  # noqa: F401
+from ._lib import (GDN_BF16, GDN_F32, GdnError, gdn_chunk_prefill, gdn_conv_chunk_prefill,  # noqa: F401
                    gdn_chunk_prefill_workspace_size, gdn_conv1d_fwd, gdn_gated_rmsnorm,
                    gdn_recurrent_step, gdn_recurrent_step_norm, gdn_recurrent_step_slots, lib,
                    library_path, version)

@@ -36,6 +36,9 @@ _SIGS = {
     "gdn_chunk_prefill": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                            _sz, _i32, _vp], _i32),
+    "gdn_conv_chunk_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                _vp, _sz, _i32, _vp], _i32),
     "gdn_recurrent_step": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                             _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp], _i32),
     "gdn_recurrent_step_bf16_state": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -156,6 +159,31 @@ def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None,
         _p(dt_bias), _p(g_opt), _p(beta_opt), _p(state_in), _p(state_out), _p(o),
         _p(cu_seqlens), Ns, N, Hk, Hv, dk, dv, float(scale), int(bool(use_qk_l2norm)),
         _p(workspace), ws_bytes, _io(q), _stream(stream)))
+
+
+def gdn_conv_chunk_prefill(x, conv_w, y, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None,
+                           conv_state_in=None, conv_state_out=None, state_in=None,
+                           state_out=None, g_opt=None, beta_opt=None, scale=0.0,
+                           use_qk_l2norm=True, workspace=None, stream=None, K=4, dk=128,
+                           dv=128):
+    """gdn_conv1d_fwd + gdn_chunk_prefill in one call: y (the conv output) is written and
+    the chunked delta rule reads q, k, v from it."""
+    _dev(x, conv_w, y, a, b, A_log, dt_bias, o, cu_seqlens, conv_state_in, conv_state_out,
+         state_in, state_out, g_opt, beta_opt, workspace)
+    N = x.shape[0]
+    Ns = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    for t in (x, y):
+        if not t.is_contiguous():
+            raise ValueError("x and y must be contiguous [N, Cq]")
+    if workspace is None:
+        need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk, _io(x))
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("gdn_conv_chunk_prefill", lib().gdn_conv_chunk_prefill(
+        _p(x), _p(conv_w), _p(conv_state_in), _p(conv_state_out), _p(y), _p(a), _p(b),
+        _p(A_log), _p(dt_bias), _p(g_opt), _p(beta_opt), _p(state_in), _p(state_out), _p(o),
+        _p(cu_seqlens), Ns, N, Hk, Hv, dk, dv, K, float(scale), int(bool(use_qk_l2norm)),
+        _p(workspace), ws_bytes, _io(x), _stream(stream)))
 
 
 def gdn_recurrent_step(x, w, conv_state, a, b, A_log, dt_bias, state, o, Hk, Hv, g_opt=None,

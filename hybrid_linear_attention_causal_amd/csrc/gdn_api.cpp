@@ -98,6 +98,66 @@ size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d
   return gdn::chunk_workspace_bytes(N, Ns, Hk, Hv, io == GDN_F32);
 }
 
+}  // extern "C"
+
+namespace {
+
+// validation and launch shared by gdn_chunk_prefill and gdn_conv_chunk_prefill
+gdn_status_t chunk_prefill_impl(const char* name, gdn::ChunkArgs args, int dk, int dv,
+                                void* workspace, size_t ws_bytes, gdn_dtype_t io, void* stream) {
+  const int64_t N = args.N;
+  const int Ns = args.Ns, Hk = args.Hk, Hv = args.Hv;
+  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "%s: unknown io dtype %d", name, (int)io);
+  if (dk != 128 || dv != 128)
+    return fail(GDN_ERR_UNSUPPORTED, "%s: head widths %d/%d (only 128/128)", name, dk, dv);
+  if (Hk < 1 || Hv < 1 || Hv % Hk != 0)
+    return fail(GDN_ERR_INVALID_ARG, "%s: Hv=%d must be a positive multiple of Hk=%d", name, Hv,
+                Hk);
+  if (Ns < 1 || N < 0) return fail(GDN_ERR_INVALID_ARG, "%s: Ns=%d N=%lld", name, Ns, (long long)N);
+  if (!args.cu && Ns != 1)
+    return fail(GDN_ERR_INVALID_ARG, "%s: cu_seqlens is NULL but Ns=%d", name, Ns);
+  if (((int64_t)Ns * Hk + 8) * (Hv / Hk) * 2 > 0x7fffffffLL)
+    return fail(GDN_ERR_INVALID_ARG, "%s: too many (sequence, head) pairs", name);
+  const int64_t sq = args.stride_q, sk = args.stride_k, sv = args.stride_v;
+  if (sq < (int64_t)Hk * dk || sk < (int64_t)Hk * dk || sv < (int64_t)Hv * dv || sq % 8 ||
+      sk % 8 || sv % 8 || sq > GDN_MAX_ROW_STRIDE || sk > GDN_MAX_ROW_STRIDE ||
+      sv > GDN_MAX_ROW_STRIDE)
+    return fail(GDN_ERR_INVALID_ARG,
+                "%s: strides must cover a row, be multiples of 8 and at most 2^20 "
+                "(q %lld k %lld v %lld)",
+                name, (long long)sq, (long long)sk, (long long)sv);
+  const bool have_g = args.g_opt != nullptr, have_b = args.beta_opt != nullptr;
+  if (have_g != have_b)
+    return fail(GDN_ERR_INVALID_ARG, "%s: give both g_opt and beta_opt or neither", name);
+  if (N > 0) {
+    if (!args.q || !args.k || !args.v || !args.o)
+      return fail(GDN_ERR_INVALID_ARG, "%s: NULL q, k, v or o", name);
+    if (!have_g && (!args.a || !args.b || !args.A_log || !args.dt_bias))
+      return fail(GDN_ERR_INVALID_ARG, "%s: NULL a, b, A_log or dt_bias", name);
+    if (!aligned(args.q, 16) || !aligned(args.k, 16) || !aligned(args.v, 16) ||
+        !aligned(args.o, 16))
+      return fail(GDN_ERR_INVALID_ARG, "%s: q, k, v, o must be 16-byte aligned", name);
+  }
+  const size_t need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk, io);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+    return fail(GDN_ERR_INVALID_ARG,
+                "%s: workspace must be a 256-byte aligned buffer of >= %zu bytes", name, need);
+  if ((N + 63) / 64 + Ns > 0x7fffffffLL) return fail(GDN_ERR_INVALID_ARG, "%s: too many chunks", name);
+  if (args.scale <= 0.f) args.scale = 1.0f / sqrtf((float)dk);
+  int cus = 0;
+  gdn_status_t st = check_device(&cus);
+  if (st != GDN_OK) return st;
+  args.cu_count = cus;
+  hipError_t e = gdn::launch_chunk_prefill(args, workspace,
+                                           io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? GDN_OK : hip_fail(e, "chunk_prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
 gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int64_t stride_q,
                                int64_t stride_k, int64_t stride_v, const void* a, const void* b,
                                const float* A_log, const float* dt_bias, const float* g_opt,
@@ -106,51 +166,44 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
                                int Hv, int dk, int dv, float scale, int use_qk_l2norm,
                                void* workspace, size_t ws_bytes, gdn_dtype_t io, void* stream) {
   g_err[0] = 0;
-  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: unknown io dtype %d", (int)io);
-  if (dk != 128 || dv != 128)
-    return fail(GDN_ERR_UNSUPPORTED, "chunk_prefill: head widths %d/%d (only 128/128)", dk, dv);
-  if (Hk < 1 || Hv < 1 || Hv % Hk != 0)
-    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: Hv=%d must be a positive multiple of Hk=%d",
-                Hv, Hk);
-  if (Ns < 1 || N < 0) return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: Ns=%d N=%lld", Ns, (long long)N);
-  if (!cu_seqlens && Ns != 1)
-    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: cu_seqlens is NULL but Ns=%d", Ns);
-  if (((int64_t)Ns * Hk + 8) * (Hv / Hk) * 2 > 0x7fffffffLL)
-    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: too many (sequence, head) pairs");
-  if (stride_q < (int64_t)Hk * dk || stride_k < (int64_t)Hk * dk || stride_v < (int64_t)Hv * dv ||
-      stride_q % 8 || stride_k % 8 || stride_v % 8 || stride_q > GDN_MAX_ROW_STRIDE ||
-      stride_k > GDN_MAX_ROW_STRIDE || stride_v > GDN_MAX_ROW_STRIDE)
-    return fail(GDN_ERR_INVALID_ARG,
-                "chunk_prefill: strides must cover a row, be multiples of 8 and at most 2^20 "
-                "(q %lld k %lld v %lld)",
-                (long long)stride_q, (long long)stride_k, (long long)stride_v);
-  const bool have_g = g_opt != nullptr, have_b = beta_opt != nullptr;
-  if (have_g != have_b)
-    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: give both g_opt and beta_opt or neither");
-  if (N > 0) {
-    if (!q || !k || !v || !o) return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: NULL q, k, v or o");
-    if (!have_g && (!a || !b || !A_log || !dt_bias))
-      return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: NULL a, b, A_log or dt_bias");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
-      return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: q, k, v, o must be 16-byte aligned");
-  }
-  const size_t need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk, io);
-  if (!workspace || ws_bytes < need || !aligned(workspace, 256))
-    return fail(GDN_ERR_INVALID_ARG,
-                "chunk_prefill: workspace must be a 256-byte aligned buffer of >= %zu bytes", need);
-  if ((N + 63) / 64 + Ns > 0x7fffffffLL)
-    return fail(GDN_ERR_INVALID_ARG, "chunk_prefill: too many chunks");
-  if (scale <= 0.f) scale = 1.0f / sqrtf((float)dk);
-  int cus = 0;
-  gdn_status_t st = check_device(&cus);
-  if (st != GDN_OK) return st;
   gdn::ChunkArgs args{q, k, v, stride_q, stride_k, stride_v, a, b, A_log, dt_bias, g_opt,
                       beta_opt, state_in, state_out, o, cu_seqlens, Ns, N, Hk, Hv, scale,
-                      use_qk_l2norm ? 1 : 0, cus};
-  hipError_t e = gdn::launch_chunk_prefill(args, workspace,
-                                           io == GDN_BF16 ? gdn::IO_BF16 : gdn::IO_F32,
-                                           (hipStream_t)stream);
-  return e == hipSuccess ? GDN_OK : hip_fail(e, "chunk_prefill launch");
+                      use_qk_l2norm ? 1 : 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0};
+  return chunk_prefill_impl("chunk_prefill", args, dk, dv, workspace, ws_bytes, io, stream);
+}
+
+gdn_status_t gdn_conv_chunk_prefill(const void* x, const float* conv_w, const void* conv_state_in,
+                                    void* conv_state_out, void* y, const void* a, const void* b,
+                                    const float* A_log, const float* dt_bias, const float* g_opt,
+                                    const float* beta_opt, const float* state_in,
+                                    float* state_out, void* o, const int32_t* cu_seqlens, int Ns,
+                                    int64_t N, int Hk, int Hv, int dk, int dv, int K, float scale,
+                                    int use_qk_l2norm, void* workspace, size_t ws_bytes,
+                                    gdn_dtype_t io, void* stream) {
+  g_err[0] = 0;
+  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: unknown io dtype %d", (int)io);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "conv_chunk_prefill: kernel width %d (only 4)", K);
+  if (Hk < 1 || Hv < 1 || dk != 128 || dv != 128)
+    return fail(dk != 128 || dv != 128 ? GDN_ERR_UNSUPPORTED : GDN_ERR_INVALID_ARG,
+                "conv_chunk_prefill: Hk=%d Hv=%d dk=%d dv=%d", Hk, Hv, dk, dv);
+  const int64_t cq = 2LL * Hk * dk + (int64_t)Hv * dv;
+  if (cq > GDN_MAX_ROW_STRIDE)
+    return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: %lld conv channels", (long long)cq);
+  if (N > 0 && (!x || !conv_w || !y))
+    return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: NULL x, conv_w or y");
+  if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)) || (conv_w && !aligned(conv_w, 16)) ||
+      (conv_state_in && !aligned(conv_state_in, 16)) ||
+      (conv_state_out && !aligned(conv_state_out, 16)))
+    return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: pointers must be 16-byte aligned");
+  if (x && y && x == y) return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: y must not alias x");
+  const size_t esz = io == GDN_BF16 ? 2 : 4;
+  const char* yb = static_cast<const char*>(y);
+  gdn::ChunkArgs args{yb, yb ? yb + (size_t)Hk * dk * esz : nullptr,
+                      yb ? yb + (size_t)2 * Hk * dk * esz : nullptr, cq, cq, cq, a, b, A_log,
+                      dt_bias, g_opt, beta_opt, state_in, state_out, o, cu_seqlens, Ns, N, Hk,
+                      Hv, scale, use_qk_l2norm ? 1 : 0, 0, x, conv_w, conv_state_in,
+                      conv_state_out, y, (int)cq};
+  return chunk_prefill_impl("conv_chunk_prefill", args, dk, dv, workspace, ws_bytes, io, stream);
 }
 
 namespace {

@@ -410,7 +410,110 @@ struct PrepSmem {
   alignas(16) float rnq[CH];
 };
 
-template <int IO, int MODE>
+// Fused conv of the prep kernel (bf16 io): the conv window + SiLU of this key head's q, k
+// and v channels over the chunk's rows, rounded to bf16 as the conv call stores them
+// (the operation of gdn_conv1d_fwd: llm-arch-viz Qwen3.5-9B page, module tree, conv1d
+// 8192x1x4, depthwise, no bias).  The rows go to y, where the sweep reads q, k and v;
+// the q and k rows also go to LDS for the Gram products, with their row norms.  Per
+// pass, lane = a group of 8 channels (q 16, k 16, then 16 per value head) and wave w =
+// rows 16 w .. 16 w + 15 in two halves of 8; a half also reads the 3 rows before it
+// (from x, or before the sequence start from its conv state, or zeros).
+__device__ __forceinline__ void conv_rows(const ChunkArgs& p, int s, int64_t t0, int L, int kh,
+                                          int r, int wave, int lane, u16* k_rows, u16* q_rows,
+                                          float* rnk, float* rnq) {
+  const int Cq = p.Cq, Hk = p.Hk;
+  int64_t sb, se;
+  seq_bounds(p.cu, p.N, s, sb, se);
+  const u16* x = (const u16*)p.x;
+  const u16* cs = (const u16*)p.conv_state_in;
+  u16* y = (u16*)p.y;
+  const int G = 32 + 16 * r;
+  for (int pass = 0; pass * 64 < G; ++pass) {
+    const int cg = pass * 64 + lane;
+    const bool act = cg < G;
+    const int ch = cg < 16 ? kh * DK + cg * 8
+                 : cg < 32 ? Hk * DK + kh * DK + (cg - 16) * 8
+                           : 2 * Hk * DK + kh * r * DV + (cg - 32) * 8;
+    float wt[4][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 ww = act ? *reinterpret_cast<const float4*>(p.conv_w + (int64_t)(ch + j) * 4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      wt[0][j] = ww.x; wt[1][j] = ww.y; wt[2][j] = ww.z; wt[3][j] = ww.w;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int r0 = 16 * wave + 8 * half;
+      // rows r0 - 3 .. r0 + 7; rows past the chunk end feed only outputs past it
+      uint4 raw[11];
+#pragma unroll
+      for (int i = 0; i < 11; ++i) {
+        const int row = r0 - 3 + i;
+        const int64_t tok = t0 + row;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (act && row < L) {
+          if (tok >= sb)
+            v = *reinterpret_cast<const uint4*>(x + tok * Cq + ch);
+          else if (cs)
+            v = *reinterpret_cast<const uint4*>(cs + ((int64_t)s * 3 + (tok - sb + 3)) * Cq + ch);
+        }
+        raw[i] = v;
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int row = r0 + t;
+        float out[8];
+        {
+          const uint32_t w0[4] = {raw[t].x, raw[t].y, raw[t].z, raw[t].w};
+          const uint32_t w1[4] = {raw[t + 1].x, raw[t + 1].y, raw[t + 1].z, raw[t + 1].w};
+          const uint32_t w2[4] = {raw[t + 2].x, raw[t + 2].y, raw[t + 2].z, raw[t + 2].w};
+          const uint32_t w3[4] = {raw[t + 3].x, raw[t + 3].y, raw[t + 3].z, raw[t + 3].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const int j = 2 * q + hf;
+              auto val = [&](uint32_t wd) {
+                return __uint_as_float(hf ? (wd & 0xFFFF0000u) : (wd << 16));
+              };
+              float acc = wt[0][j] * val(w0[q]);
+              acc = fmaf(wt[1][j], val(w1[q]), acc);
+              acc = fmaf(wt[2][j], val(w2[q]), acc);
+              acc = fmaf(wt[3][j], val(w3[q]), acc);
+              out[j] = silu(acc);
+            }
+          }
+        }
+        uint4 ow = make_uint4(f2bf2(out[0], out[1]), f2bf2(out[2], out[3]),
+                              f2bf2(out[4], out[5]), f2bf2(out[6], out[7]));
+        if (act && row < L) *reinterpret_cast<uint4*>(y + (t0 + row) * Cq + ch) = ow;
+        if (pass == 0) {
+          // q (lanes 0 .. 15) and k (lanes 16 .. 31) rows to LDS (zero past the chunk end)
+          // and their squared norms over the row's 16 lanes
+          if (row >= L) ow = make_uint4(0, 0, 0, 0);
+          const uint32_t ox[4] = {ow.x, ow.y, ow.z, ow.w};
+          float ss = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float v0 = __uint_as_float(ox[q] << 16), v1 = __uint_as_float(ox[q] & 0xFFFF0000u);
+            ss = fmaf(v1, v1, fmaf(v0, v0, ss));
+          }
+          ss = row16_sum(ss);
+          const float rn = p.use_l2 ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.0f;
+          if (lane < 16) {
+            *reinterpret_cast<uint4*>(q_rows + row * KS_STRIDE + lane * 8) = ow;
+            if (lane == 0) rnq[row] = rn;
+          } else if (lane < 32) {
+            *reinterpret_cast<uint4*>(k_rows + row * KS_STRIDE + (lane - 16) * 8) = ow;
+            if (lane == 16) rnk[row] = rn;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int IO, int MODE, bool CONV = false>
 __global__ void __launch_bounds__(NTHR, IO == IO_BF16 ? (MODE != PREP_ROWS_P ? 4 : 3) : 2)
 chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restrict__ recs,
                   uint8_t* __restrict__ krecs) {
@@ -420,6 +523,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   constexpr bool WITHP = MODE != PREP_ROWS;
   constexpr bool FRAG = MODE == PREP_FRAG;
   static_assert(!(FRAG && F32), "fragment-native records are for bf16 io");
+  static_assert(!(CONV && F32), "the fused conv is for bf16 io");
   constexpr int64_t REC = FRAG ? FR_REC_BYTES : ws_rec_bytes(WITHP);
   constexpr int64_t FAC_OFF = FRAG ? FR_FAC_OFF : WS_FAC_OFF;
   __shared__ PrepSmem<IO> sm;
@@ -468,7 +572,9 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   gate_in(0, ga0, gb0, al0, dt0);
 
   // ---- phase 0: K and Q rows to LDS, row norms (16 lanes of a DPP row share a row)
-  {
+  if constexpr (CONV) {
+    conv_rows(p, ci.x, t0, L, kh_, r, wave, lane, sm.u.r.kh, sm.u.r.qh, sm.rnk, sm.rnq);
+  } else {
     RowBlock<IO> kb, qb;
     load_rows<IO>(kb, (const T*)p.k + (int64_t)kh_ * DK, p.stride_k, t0, L, tid);
     load_rows<IO>(qb, (const T*)p.q + (int64_t)kh_ * DK, p.stride_q, t0, L, tid);
@@ -1878,20 +1984,45 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // fused conv: bf16 io forms it inside the prep kernel; fp32 io runs the conv call first
+  const bool conv_in_prep = a.x != nullptr && IO == IO_BF16;
+  if (a.x != nullptr && !conv_in_prep) {
+    const ConvArgs ca{a.x, a.conv_w, a.y, a.cu, a.Ns, a.N, a.Cq, a.conv_state_in, a.conv_state_out};
+    e = launch_conv1d(ca, IO, st);
+    if (e != hipSuccess) return e;
+  }
   if (a.N > 0) {
     const dim3 pgrid((unsigned)cmax, (unsigned)a.Hk);
     if constexpr (IO == IO_BF16) {
-      if (rowsplit)
+      if (conv_in_prep) {
+        if (rowsplit)
+          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG, true>), pgrid, dim3(NTHR), 0, st,
+                             a, (const int4*)cinfo, recs, krecs);
+        else if (four)
+          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS_P, true>), pgrid, dim3(NTHR), 0, st,
+                             a, (const int4*)cinfo, recs, krecs);
+        else
+          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS, true>), pgrid, dim3(NTHR), 0, st,
+                             a, (const int4*)cinfo, recs, krecs);
+      } else if (rowsplit) {
         hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG>), pgrid, dim3(NTHR), 0, st, a,
                            (const int4*)cinfo, recs, krecs);
+      }
     }
-    if (!rowsplit && four)
+    if (!conv_in_prep && !rowsplit && four)
       hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS_P>), pgrid, dim3(NTHR), 0, st, a,
                          (const int4*)cinfo, recs, krecs);
-    else if (!rowsplit)
+    else if (!conv_in_prep && !rowsplit)
       hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS>), pgrid, dim3(NTHR), 0, st, a,
                          (const int4*)cinfo, recs, krecs);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (conv_in_prep && a.conv_state_out) {
+    // the final conv state, after every prep workgroup has read conv_state_in (the two
+    // may alias)
+    const ConvArgs ca{a.x, a.conv_w, a.y, a.cu, a.Ns, a.N, a.Cq, a.conv_state_in, a.conv_state_out};
+    e = launch_conv_state(ca, IO, st);
     if (e != hipSuccess) return e;
   }
   // Each (sequence, head) chain is sequential over its chunks.  While two 4-wave

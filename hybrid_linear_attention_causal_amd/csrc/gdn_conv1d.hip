@@ -220,10 +220,10 @@ conv_state_kernel(const typename Io<IO>::T* __restrict__ x, const int32_t* __res
 }
 
 template <int IO>
-static hipError_t conv_impl(const ConvArgs& a, hipStream_t st) {
+static hipError_t conv_impl(const ConvArgs& a, bool main_pass, hipStream_t st) {
   typedef typename Io<IO>::T T;
   const int groups = (a.Cq / 8 + CONV_BLOCK - 1) / CONV_BLOCK;
-  if (a.N > 0) {
+  if (main_pass && a.N > 0) {
     const int64_t tiles = (a.N + conv_tt<IO>() - 1) / conv_tt<IO>();
     if (tiles * groups > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(conv1d_silu_kernel<IO>, dim3((unsigned)(tiles * groups)),
@@ -242,7 +242,11 @@ static hipError_t conv_impl(const ConvArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_conv1d(const ConvArgs& a, int io, hipStream_t s) {
-  return io == IO_BF16 ? conv_impl<IO_BF16>(a, s) : conv_impl<IO_F32>(a, s);
+  return io == IO_BF16 ? conv_impl<IO_BF16>(a, true, s) : conv_impl<IO_F32>(a, true, s);
+}
+
+hipError_t launch_conv_state(const ConvArgs& a, int io, hipStream_t s) {
+  return io == IO_BF16 ? conv_impl<IO_BF16>(a, false, s) : conv_impl<IO_F32>(a, false, s);
 }
 
 }  // namespace gdn

@@ -41,6 +41,15 @@ struct ChunkArgs {
   float scale;
   int use_l2;
   int cu_count;           // compute units of the device (launch shape choice; <= 0: 256)
+  // fused conv (x != NULL): the conv window + SiLU of the raw projection rows x [N, Cq] is
+  // formed inside the call and written to y [N, Cq] (q, k, v above point into y); the
+  // final conv state goes to conv_state_out when given
+  const void* x;
+  const float* conv_w;
+  const void* conv_state_in;
+  void* conv_state_out;
+  void* y;
+  int Cq;
 };
 
 struct StepArgs {
@@ -79,6 +88,8 @@ struct NormArgs {
 };
 
 hipError_t launch_conv1d(const ConvArgs& a, int io, hipStream_t s);
+// only the final conv state of a conv call (conv_state_out from x and conv_state_in)
+hipError_t launch_conv_state(const ConvArgs& a, int io, hipStream_t s);
 // device workspace of the chunked prefill (chunk map + per (chunk, head) records)
 size_t chunk_workspace_bytes(int64_t N, int Ns, int Hk, int Hv, bool f32);
 hipError_t launch_chunk_prefill(const ChunkArgs& a, void* ws, int io, hipStream_t s);

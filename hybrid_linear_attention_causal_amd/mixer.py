@@ -1,6 +1,6 @@
 """Thin helpers that allocate outputs with torch and chain the libgdn calls.
 
-prefill_layer:  conv1d+SiLU -> chunked delta rule -> z-gated RMSNorm
+prefill_layer:  conv1d+SiLU -> chunked delta rule (one call by default) -> z-gated RMSNorm
 decode_step:    recurrent step (conv + delta rule, in place) + z-gated RMSNorm, fused in one
                 launch by default
 DecodeGraph:    n decode steps captured once as a HIP graph, replayed as one launch
@@ -10,7 +10,8 @@ from __future__ import annotations
 import torch
 
 from ._lib import (gdn_chunk_prefill, gdn_chunk_prefill_workspace_size, gdn_conv1d_fwd,
-                   gdn_gated_rmsnorm, gdn_recurrent_step, gdn_recurrent_step_norm)
+                   gdn_conv_chunk_prefill, gdn_gated_rmsnorm, gdn_recurrent_step,
+                   gdn_recurrent_step_norm)
 
 D = 128
 
@@ -22,8 +23,9 @@ def qkv_views(y: torch.Tensor, Hk: int, Hv: int):
 
 def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens=None,
                   conv_state_in=None, state_in=None, eps=1e-6, want_states=True, bufs=None,
-                  stream=None):
-    """x [N, Cq] io; z [N, Hv*128] io.  Returns a dict of device tensors."""
+                  stream=None, fused=True):
+    """x [N, Cq] io; z [N, Hv*128] io.  Returns a dict of device tensors.  fused: the conv
+    and the chunked core in one call (gdn_conv_chunk_prefill), else two calls."""
     N, Cq = x.shape
     Ns = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
     dev, dt = x.device, x.dtype
@@ -34,7 +36,6 @@ def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens
     cs_out = bufs.get("conv_state_out")
     if cs_out is None and want_states:
         cs_out = torch.empty((Ns, 3, Cq), dtype=dt, device=dev)
-    gdn_conv1d_fwd(x, conv_w, y, cu_seqlens, conv_state_in, cs_out, stream=stream)
     q, k, v = qkv_views(y, Hk, Hv)
     o = bufs.get("o")
     if o is None:
@@ -47,8 +48,14 @@ def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         bufs["workspace"] = ws
-    gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens, state_in, s_out,
-                      workspace=ws, stream=stream)
+    if fused:
+        gdn_conv_chunk_prefill(x, conv_w, y, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens,
+                               conv_state_in, cs_out, state_in, s_out, workspace=ws,
+                               stream=stream)
+    else:
+        gdn_conv1d_fwd(x, conv_w, y, cu_seqlens, conv_state_in, cs_out, stream=stream)
+        gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens, state_in, s_out,
+                          workspace=ws, stream=stream)
     yn = bufs.get("y")
     if yn is None:
         yn = torch.empty_like(o)

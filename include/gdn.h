@@ -157,6 +157,35 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
                                void* workspace, size_t ws_bytes, gdn_dtype_t io, void* stream);
 
 /*
+ * gdn_conv_chunk_prefill -- gdn_conv1d_fwd and gdn_chunk_prefill in one call: the conv
+ * window + SiLU of the raw projection rows x is written to y and the chunked delta rule
+ * runs on q, k, v read from y (q = y[:, 0 : Hk*dk], k = y[:, Hk*dk : 2*Hk*dk],
+ * v = y[:, 2*Hk*dk :], row stride Cq = 2*Hk*dk + Hv*dv).  The results are those of the two
+ * calls (y, conv_state_out, o and state_out bit for bit as gdn_conv1d_fwd would write y).
+ * For bf16 io the conv is formed by the chunk kernels themselves, per chunk and key
+ * head, so its memory traffic overlaps their arithmetic; for fp32 io the two calls run in
+ * sequence.  (The conv and the chunked core are the steps of one linear-attention layer:
+ * llm-arch-viz Qwen3.5-9B page, module tree of Qwen3_5GatedDeltaNet; HF Qwen3.5 docs
+ * page, "Usage tips": prefill runs the chunked core.)
+ *
+ *   x                [N, Cq]          io      raw projection rows (q|k|v channels)
+ *   conv_w           [Cq, K]          fp32
+ *   conv_state_in    [Ns, K-1, Cq]    io      or NULL (zeros)
+ *   conv_state_out   [Ns, K-1, Cq]    io      or NULL; may alias conv_state_in
+ *   y                [N, Cq]          io      conv output, written (may not alias x)
+ * All other arguments, the workspace (gdn_chunk_prefill_workspace_size) and the errors
+ * as for gdn_chunk_prefill and gdn_conv1d_fwd.
+ */
+gdn_status_t gdn_conv_chunk_prefill(const void* x, const float* conv_w, const void* conv_state_in,
+                                    void* conv_state_out, void* y, const void* a, const void* b,
+                                    const float* A_log, const float* dt_bias, const float* g_opt,
+                                    const float* beta_opt, const float* state_in,
+                                    float* state_out, void* o, const int32_t* cu_seqlens, int Ns,
+                                    int64_t N, int Hk, int Hv, int dk, int dv, int K, float scale,
+                                    int use_qk_l2norm, void* workspace, size_t ws_bytes,
+                                    gdn_dtype_t io, void* stream);
+
+/*
  * gdn_recurrent_step -- one decode token for each of B independent sequences,
  * updating the conv state and the recurrent state IN PLACE.
  * (KerasFormers Qwen page, "Generation": decode carries the per-layer conv

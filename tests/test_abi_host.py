@@ -11,7 +11,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libgdn.so not built (run __graft_entry__.build())")
 
 EXPECTED = {"gdn_last_error", "gdn_version", "gdn_conv1d_fwd", "gdn_chunk_prefill_workspace_size",
-            "gdn_chunk_prefill", "gdn_recurrent_step", "gdn_recurrent_step_bf16_state",
+            "gdn_chunk_prefill", "gdn_conv_chunk_prefill", "gdn_recurrent_step", "gdn_recurrent_step_bf16_state",
             "gdn_recurrent_step_slots", "gdn_recurrent_step_norm", "gdn_gated_rmsnorm"}
 
 
@@ -178,3 +178,27 @@ def test_step_norm_rejects():
     assert _stepnorm(nw=ctypes.c_void_p(24)) == _lib.GDN_ERR_INVALID_ARG
     assert _stepnorm(y=ctypes.c_void_p(20)) == _lib.GDN_ERR_INVALID_ARG
     assert _stepnorm(dv=64) == _lib.GDN_ERR_UNSUPPORTED
+
+
+def _fused(**kw):
+    args = dict(x=P, w=P, csi=None, cso=None, y=ctypes.c_void_p(4096), a=P, b=P, A_log=P,
+                dt_bias=P, g=None, beta=None, si=None, so=None, o=P, cu=None, Ns=1, N=100, Hk=2,
+                Hv=4, dk=128, dv=128, K=4, scale=0.0, l2=1, ws=P, ws_bytes=1 << 30, io=1)
+    args.update(kw)
+    return _L().gdn_conv_chunk_prefill(*args.values(), None)
+
+
+def test_conv_chunk_prefill_rejects():
+    assert _fused(K=3) == _lib.GDN_ERR_UNSUPPORTED
+    assert "conv_chunk_prefill" in _msg()
+    assert _fused(dk=64) == _lib.GDN_ERR_UNSUPPORTED
+    assert _fused(io=5) == _lib.GDN_ERR_INVALID_ARG
+    assert _fused(x=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _fused(y=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _fused(y=P) == _lib.GDN_ERR_INVALID_ARG          # aliases x
+    assert "alias" in _msg()
+    assert _fused(csi=ctypes.c_void_p(40)) == _lib.GDN_ERR_INVALID_ARG
+    assert _fused(Hv=3) == _lib.GDN_ERR_INVALID_ARG          # not a multiple of Hk
+    assert _fused(Ns=2) == _lib.GDN_ERR_INVALID_ARG          # cu_seqlens NULL
+    assert _fused(ws=None) == _lib.GDN_ERR_INVALID_ARG
+    assert _fused(g=P) == _lib.GDN_ERR_INVALID_ARG           # g without beta

@@ -1,0 +1,88 @@
+"""gdn_conv_chunk_prefill (conv + chunked core in one call) against the two calls it
+replaces: y, o, the final recurrent state and the final conv state bit for bit, in every
+launch shape of the chunked core (row-split sweep; 4-wave and 8-wave sweeps), with
+carried states, ragged and empty sequences, in-place conv state and both io dtypes; and
+the fused layer against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_linear_attention_causal_amd as gdn
+from hybrid_linear_attention_causal_amd import synth
+from hybrid_linear_attention_causal_amd.mixer import qkv_views
+from oracle import gdn_oracle as G
+
+from parity import assert_out, assert_state, f32_dev, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+LENS = [1, 17, 63, 64, 65, 130, 0, 200, 5, 64, 129, 33]
+
+
+def _inputs(hk, hv, io, seed, lens):
+    sh = synth.Shape(f"h{hk}x{hv}", hk=hk, hv=hv)
+    inp = synth.make(synth.custom(sh, io, seed, seqlens=lens, init_state=True))
+    d = {k: to_dev(inp[k], io) for k in ("x", "a", "b", "conv_state_in")}
+    for k in ("conv_w", "A_log", "dt_bias", "state_in"):
+        d[k] = f32_dev(inp[k])
+    d["cu"] = torch.from_numpy(inp["cu_seqlens"].astype(np.int32)).cuda()
+    return inp, d
+
+
+def _both(d, hk, hv, in_place=False):
+    x = d["x"]
+    N, Cq = x.shape
+    Ns = d["cu"].numel() - 1
+    res = []
+    for fused in (True, False):
+        y = torch.empty_like(x)
+        o = torch.empty((N, hv, D), dtype=x.dtype, device="cuda")
+        s_out = torch.empty((Ns, hv, D, D), device="cuda")
+        cs_in = d["conv_state_in"].clone()
+        cs_out = cs_in if in_place else torch.empty_like(cs_in)
+        if fused:
+            gdn.gdn_conv_chunk_prefill(x, d["conv_w"], y, d["a"], d["b"], d["A_log"],
+                                       d["dt_bias"], o, hk, hv, d["cu"], cs_in, cs_out,
+                                       d["state_in"], s_out)
+        else:
+            gdn.gdn_conv1d_fwd(x, d["conv_w"], y, d["cu"], cs_in, cs_out)
+            q, k, v = qkv_views(y, hk, hv)
+            gdn.gdn_chunk_prefill(q, k, v, d["a"], d["b"], d["A_log"], d["dt_bias"], o, hk, hv,
+                                  d["cu"], d["state_in"], s_out)
+        res.append((y, o, s_out, cs_out))
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("io,hk,hv,lens,in_place", [
+    ("bf16", 2, 4, LENS, False),            # 48 chains: row-split sweep, two rounds
+    ("bf16", 1, 3, LENS[:7], True),         # 21 chains, three value heads per key head
+    ("bf16", 2, 4, LENS * 2, False),        # 96 chains: 4-wave sweep
+    ("bf16", 2, 4, LENS * 4, True),         # 192 chains: 8-wave sweep
+    ("f32", 2, 4, LENS, False),             # fp32 io: conv then the chunk call
+])
+def test_fused_equals_two_calls(io, hk, hv, lens, in_place):
+    inp, d = _inputs(hk, hv, io, 70 + len(lens), lens)
+    (y1, o1, s1, c1), (y2, o2, s2, c2) = _both(d, hk, hv, in_place)
+    assert torch.equal(y1, y2), "conv output"
+    assert torch.equal(c1, c2), "final conv state"
+    assert torch.equal(o1, o2), "core output"
+    assert torch.equal(s1, s2), "final recurrent state"
+
+
+def test_fused_layer_against_oracle():
+    io, hk, hv = "bf16", 2, 4
+    inp, d = _inputs(hk, hv, io, 91, LENS)
+    N = inp["N"]
+    z = to_dev(inp["z"], io).view(N, hv, D)
+    out = gdn.prefill_layer(d["x"], d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"], z,
+                            f32_dev(inp["norm_w"]), hk, hv, d["cu"], d["conv_state_in"],
+                            d["state_in"], fused=True)
+    torch.cuda.synchronize()
+    ref = G.layer(inp)
+    assert_out(host(out["y_conv"]), ref["y_conv"], io, "fused conv y")
+    np.testing.assert_array_equal(host(out["conv_state_out"]), ref["conv_state_out"])
+    assert_out(host(out["o"]), ref["o"], io, "fused o", upstream_bf16=1)
+    assert_out(host(out["y"]), ref["y"], io, "fused y", upstream_bf16=1)
+    assert_state(host(out["state_out"]), ref["state_out"], "fused state")
