@@ -6,7 +6,8 @@ One step = the hot path over one batch of synthetic input:
       gdn_conv1d_fwd -> gdn_chunk_prefill -> gdn_gated_rmsnorm
   decode step on the Qwen3.5-9B shape, 256 sequences, bf16 io, fp32 state:
       gdn_recurrent_step (conv + state updated in place) -> gdn_gated_rmsnorm
-  and, timed beside the step, the decode step on a bf16-stored state
+  and, timed beside the step, the same step with the conv and the chunked core in one
+  call (gdn_conv_chunk_prefill, prefill_fused), the decode step on a bf16-stored state
   (gdn_recurrent_step_bf16_state, roofline_decode_bf16_state) and the prompt -> decode
   replay (one sequence: 1024-token prompt, then 256 decode steps eager and as one HIP
   graph; "replay").
@@ -40,6 +41,8 @@ PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
 
 CSRC = os.path.join(ROOT, "hybrid_linear_attention_causal_amd", "csrc")
 KERNEL_SOURCES = {"gdn_chunk_prefill": ("gdn_chunk.hip", "gdn_common.hpp", "gdn_launch.hpp"),
+                  "gdn_conv_chunk_prefill": ("gdn_chunk.hip", "gdn_conv1d.hip", "gdn_common.hpp",
+                                             "gdn_launch.hpp"),
                   "gdn_recurrent_step": ("gdn_step.hip", "gdn_common.hpp", "gdn_launch.hpp"),
                   "gdn_recurrent_step_bf16_state": ("gdn_step.hip", "gdn_common.hpp",
                                                     "gdn_launch.hpp")}
@@ -49,6 +52,7 @@ KERNEL_SOURCES = {"gdn_chunk_prefill": ("gdn_chunk.hip", "gdn_common.hpp", "gdn_
 # figure belongs to the kernel sources with the given digest and is not reported once
 # they change.
 MEASURED_TRAFFIC = {"gdn_chunk_prefill": ("29b49e746692f8f1", 274.0e6),
+                    "gdn_conv_chunk_prefill": ("", 0.0),
                     "gdn_recurrent_step": ("bf1f8ee0338506c6", 1105.8e6),
                     "gdn_recurrent_step_bf16_state": ("bf1f8ee0338506c6", 568.9e6)}
 
@@ -267,6 +271,7 @@ def main():
     import hybrid_linear_attention_causal_amd as gdn
     from hybrid_linear_attention_causal_amd import synth
     from hybrid_linear_attention_causal_amd._lib import (gdn_chunk_prefill, gdn_conv1d_fwd,
+                                                         gdn_conv_chunk_prefill,
                                                          gdn_gated_rmsnorm, gdn_recurrent_step)
     from hybrid_linear_attention_causal_amd.mixer import qkv_views
 
@@ -304,7 +309,31 @@ def main():
     zd = Dd["z"].view(B, hv, D)
     torch.cuda.synchronize()
 
+    def decode(ev, i):
+        gdn_recurrent_step(Dd["x"], Dd["conv_w"], Dd["conv_state_in"], Dd["a"], Dd["b"],
+                           Dd["A_log"], Dd["dt_bias"], Dd["state_in"], Dd["o"], hk, hv)
+        if ev:
+            ev[i].record()
+        gdn_gated_rmsnorm(Dd["o"], zd, Dd["norm_w"], Dd["yn"])
+        if ev:
+            ev[i + 1].record()
+
+    def step_fused(ev=None):
+        # the same step with the conv and the chunked core in one call
+        if ev:
+            ev[0].record()
+        gdn_conv_chunk_prefill(P["x"], P["conv_w"], P["y"], P["a"], P["b"], P["A_log"],
+                               P["dt_bias"], P["o"], hk, hv, None, None, P["cs_out"], None,
+                               P["s_out"], workspace=P["ws"])
+        if ev:
+            ev[1].record()
+        gdn_gated_rmsnorm(P["o"], zv, P["norm_w"], P["yn"])
+        if ev:
+            ev[2].record()
+        decode(ev, 3)
+
     def step(ev=None):
+        # prefill layer: conv, chunked core, gated norm; then the decode step
         if ev:
             ev[0].record()
         gdn_conv1d_fwd(P["x"], P["conv_w"], P["y"], None, None, P["cs_out"])
@@ -317,13 +346,7 @@ def main():
         gdn_gated_rmsnorm(P["o"], zv, P["norm_w"], P["yn"])
         if ev:
             ev[3].record()
-        gdn_recurrent_step(Dd["x"], Dd["conv_w"], Dd["conv_state_in"], Dd["a"], Dd["b"],
-                           Dd["A_log"], Dd["dt_bias"], Dd["state_in"], Dd["o"], hk, hv)
-        if ev:
-            ev[4].record()
-        gdn_gated_rmsnorm(Dd["o"], zd, Dd["norm_w"], Dd["yn"])
-        if ev:
-            ev[5].record()
+        decode(ev, 4)
 
     for _ in range(args.warmup):
         step()
@@ -337,6 +360,17 @@ def main():
     wall = time.perf_counter() - t0
     names = ["conv1d", "chunk_prefill", "prefill_norm", "recurrent_step", "decode_norm"]
     ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+
+    # Beside the step: the same step with the conv and the chunked core in one call.
+    for _ in range(args.warmup):
+        step_fused()
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step_fused(evf[i])
+    torch.cuda.synchronize()
+    names_f = ["conv_chunk_prefill", "prefill_norm", "recurrent_step", "decode_norm"]
+    ms_f = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evf]))
+            for j, n in enumerate(names_f)}
 
     # Beside the step: the same decode step on a bf16-stored recurrent state.
     def step_bf16_state():
@@ -356,6 +390,7 @@ def main():
     replay = replay_leg(args.steps, args.warmup)
     prefill_ms = ms["conv1d"] + ms["chunk_prefill"] + ms["prefill_norm"]
     tokens_per_s = N / (prefill_ms * 1e-3)
+    prefill_f_ms = ms_f["conv_chunk_prefill"] + ms_f["prefill_norm"]
 
     flops = chunk_core_flops(N, hk, hv)
     chunk_tflops = flops / (ms["chunk_prefill"] * 1e-3) / 1e12
@@ -385,6 +420,11 @@ def main():
                      "frac": chunk_tflops * 1e12 / PEAK_BF16_FLOPS,
                      "traffic": measured_traffic("gdn_chunk_prefill"),
                      "algorithmic_per_launch": flops},
+        "prefill_fused": {
+            "calls": "gdn_conv_chunk_prefill -> gdn_gated_rmsnorm",
+            "kernel_ms": {n: ms_f[n] for n in ("conv_chunk_prefill", "prefill_norm")},
+            "tokens_per_s": N / (prefill_f_ms * 1e-3),
+            "traffic": measured_traffic("gdn_conv_chunk_prefill")},
         "roofline_decode": {"kernel": "gdn_recurrent_step", "bound": "hbm", "achieved": step_gbs,
                             "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                             "frac": step_gbs * 1e9 / PEAK_HBM_BYTES,
