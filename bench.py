@@ -3,17 +3,19 @@
 
 One step = the hot path over one batch of synthetic input:
   prefill layer on the Qwen3.5-9B shape, T = 4096 tokens, bf16 io:
-      gdn_conv1d_fwd -> gdn_chunk_prefill -> gdn_gated_rmsnorm
+      gdn_conv_chunk_prefill (conv + chunked core in one call) -> gdn_gated_rmsnorm
   decode step on the Qwen3.5-9B shape, 256 sequences, bf16 io, fp32 state:
       gdn_recurrent_step (conv + state updated in place) -> gdn_gated_rmsnorm
-  and, timed beside the step, the same step with the conv and the chunked core in one
-  call (gdn_conv_chunk_prefill, prefill_fused), the decode step on a bf16-stored state
+  and, timed beside the step, the same step with the conv and the chunked core as two
+  calls (prefill_unfused, with the chunked core's own roofline), the decode step on a
+  bf16-stored state
   (gdn_recurrent_step_bf16_state, roofline_decode_bf16_state) and the prompt -> decode
   replay (one sequence: 1024-token prompt, then 256 decode steps eager and as one HIP
   graph; "replay").
 
-Reported ("value"): layer prefill tokens/s = 4096 / (conv + chunk + norm time),
-with the chunked core against the bf16 dense MFMA peak (roofline) and the decode
+Reported ("value"): layer prefill tokens/s = 4096 / (conv+chunk call + norm time),
+with the core's algorithmic flops over that call's time against the bf16 dense MFMA peak
+(roofline) and the decode
 step's algorithmic bytes against the HBM peak (roofline_decode).  Kernel times come
 from HIP events recorded on the stream the kernels run on (torch's current stream).
 Inputs are resident in HBM before timing starts.
@@ -51,10 +53,10 @@ KERNEL_SOURCES = {"gdn_chunk_prefill": ("gdn_chunk.hip", "gdn_common.hpp", "gdn_
 # commands is profiles/pmc_bytes_bench_qwen35_9b_prefill_T4096_decode_B256.txt).  Each
 # figure belongs to the kernel sources with the given digest and is not reported once
 # they change.
-MEASURED_TRAFFIC = {"gdn_chunk_prefill": ("29b49e746692f8f1", 274.0e6),
-                    "gdn_conv_chunk_prefill": ("", 0.0),
-                    "gdn_recurrent_step": ("bf1f8ee0338506c6", 1105.8e6),
-                    "gdn_recurrent_step_bf16_state": ("bf1f8ee0338506c6", 568.9e6)}
+MEASURED_TRAFFIC = {"gdn_chunk_prefill": ("f1a91bac9d3aee09", 257.2e6),
+                    "gdn_conv_chunk_prefill": ("5b77a4e9680adfc7", 383.1e6),
+                    "gdn_recurrent_step": ("2ba2d508fff5b2de", 1105.8e6),
+                    "gdn_recurrent_step_bf16_state": ("2ba2d508fff5b2de", 568.9e6)}
 
 
 def source_digest(kernel: str) -> str:
@@ -318,8 +320,8 @@ def main():
         if ev:
             ev[i + 1].record()
 
-    def step_fused(ev=None):
-        # the same step with the conv and the chunked core in one call
+    def step(ev=None):
+        # prefill layer: conv + chunked core in one call, then the gated norm; then decode
         if ev:
             ev[0].record()
         gdn_conv_chunk_prefill(P["x"], P["conv_w"], P["y"], P["a"], P["b"], P["A_log"],
@@ -332,8 +334,8 @@ def main():
             ev[2].record()
         decode(ev, 3)
 
-    def step(ev=None):
-        # prefill layer: conv, chunked core, gated norm; then the decode step
+    def step_unfused(ev=None):
+        # the same step with the conv and the chunked core as two calls
         if ev:
             ev[0].record()
         gdn_conv1d_fwd(P["x"], P["conv_w"], P["y"], None, None, P["cs_out"])
@@ -351,26 +353,26 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["conv1d", "chunk_prefill", "prefill_norm", "recurrent_step", "decode_norm"]
+    names = ["conv_chunk_prefill", "prefill_norm", "recurrent_step", "decode_norm"]
     ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
 
-    # Beside the step: the same step with the conv and the chunked core in one call.
+    # Beside the step: the same step with the conv and the chunked core as two calls.
     for _ in range(args.warmup):
-        step_fused()
-    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        step_unfused()
+    evu = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step_fused(evf[i])
+        step_unfused(evu[i])
     torch.cuda.synchronize()
-    names_f = ["conv_chunk_prefill", "prefill_norm", "recurrent_step", "decode_norm"]
-    ms_f = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evf]))
-            for j, n in enumerate(names_f)}
+    names_u = ["conv1d", "chunk_prefill", "prefill_norm", "recurrent_step", "decode_norm"]
+    ms_u = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evu]))
+            for j, n in enumerate(names_u)}
 
     # Beside the step: the same decode step on a bf16-stored recurrent state.
     def step_bf16_state():
@@ -388,12 +390,15 @@ def main():
     ms_bf16_state = float(np.mean([ev_b[2 * i].elapsed_time(ev_b[2 * i + 1])
                                    for i in range(args.steps)]))
     replay = replay_leg(args.steps, args.warmup)
-    prefill_ms = ms["conv1d"] + ms["chunk_prefill"] + ms["prefill_norm"]
+    prefill_ms = ms["conv_chunk_prefill"] + ms["prefill_norm"]
     tokens_per_s = N / (prefill_ms * 1e-3)
-    prefill_f_ms = ms_f["conv_chunk_prefill"] + ms_f["prefill_norm"]
+    prefill_u_ms = ms_u["conv1d"] + ms_u["chunk_prefill"] + ms_u["prefill_norm"]
 
+    # the chunked core's algorithmic flops (the conv adds 8 flops per channel and token,
+    # under 2% of them, and is not counted)
     flops = chunk_core_flops(N, hk, hv)
-    chunk_tflops = flops / (ms["chunk_prefill"] * 1e-3) / 1e12
+    chunk_tflops = flops / (ms["conv_chunk_prefill"] * 1e-3) / 1e12
+    chunk_only_tflops = flops / (ms_u["chunk_prefill"] * 1e-3) / 1e12
     dbytes = decode_bytes(B, hk, hv)
     step_gbs = dbytes / (ms["recurrent_step"] * 1e-3) / 1e9
     dbytes_bf = decode_bytes(B, hk, hv, state_bytes=2)
@@ -415,16 +420,21 @@ def main():
                    "prefill_tokens": N, "decode_batch": B, "Hk": hk, "Hv": hv, "d": D,
                    "conv_channels": cq, "chunk": CHUNK, "io": "bf16", "state": "fp32"},
         "kernel_ms": ms,
-        "roofline": {"kernel": "gdn_chunk_prefill", "bound": "mfma", "achieved": chunk_tflops,
-                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+        "roofline": {"kernel": "gdn_conv_chunk_prefill", "bound": "mfma",
+                     "achieved": chunk_tflops, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": chunk_tflops * 1e12 / PEAK_BF16_FLOPS,
-                     "traffic": measured_traffic("gdn_chunk_prefill"),
+                     "traffic": measured_traffic("gdn_conv_chunk_prefill"),
                      "algorithmic_per_launch": flops},
-        "prefill_fused": {
-            "calls": "gdn_conv_chunk_prefill -> gdn_gated_rmsnorm",
-            "kernel_ms": {n: ms_f[n] for n in ("conv_chunk_prefill", "prefill_norm")},
-            "tokens_per_s": N / (prefill_f_ms * 1e-3),
-            "traffic": measured_traffic("gdn_conv_chunk_prefill")},
+        "prefill_unfused": {
+            "calls": "gdn_conv1d_fwd -> gdn_chunk_prefill -> gdn_gated_rmsnorm",
+            "kernel_ms": {n: ms_u[n] for n in ("conv1d", "chunk_prefill", "prefill_norm")},
+            "tokens_per_s": N / (prefill_u_ms * 1e-3),
+            "roofline_chunk_prefill": {
+                "kernel": "gdn_chunk_prefill", "bound": "mfma", "achieved": chunk_only_tflops,
+                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": chunk_only_tflops * 1e12 / PEAK_BF16_FLOPS,
+                "traffic": measured_traffic("gdn_chunk_prefill"),
+                "algorithmic_per_launch": flops}},
         "roofline_decode": {"kernel": "gdn_recurrent_step", "bound": "hbm", "achieved": step_gbs,
                             "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                             "frac": step_gbs * 1e9 / PEAK_HBM_BYTES,
