@@ -1342,13 +1342,22 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     const u16* ot = s_ost;
     constexpr int WPR = Z::OW;
     static_assert((CH * WPR) % Z::THR == 0, "whole output tile per pass");
+    // (all LDS reads first, kept out of the conditional stores so that they share one wait)
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int NIT = CH * WPR / Z::THR;
+    u32x4 w[NIT];
 #pragma unroll
-    for (int it = 0; it < CH * WPR / Z::THR; ++it) {
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + Z::THR * it;
+      w[it] = *reinterpret_cast<const u32x4*>(&ot[(idx / WPR) * O_STRIDE + (idx % WPR) * 8]);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) asm volatile("" : "+v"(w[it]));
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
       const int idx = tid + Z::THR * it;
       const int row = idx / WPR, c8 = idx % WPR;
-      if (row < L)
-        *reinterpret_cast<uint4*>(og0 + (t0 + row) * o_stride + c8 * 8) =
-            *reinterpret_cast<const uint4*>(&ot[row * O_STRIDE + c8 * 8]);
+      if (row < L) *reinterpret_cast<u32x4*>(og0 + (t0 + row) * o_stride + c8 * 8) = w[it];
     }
   };
 
