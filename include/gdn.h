@@ -100,13 +100,14 @@ gdn_status_t gdn_conv1d_fwd(const void* x, const float* w, void* y, const int32_
 
 /*
  * gdn_chunk_prefill_workspace_size -- bytes of device workspace that
- * gdn_chunk_prefill needs for N packed tokens in Ns sequences with Hk key heads,
- * Hv value heads, head width d (128) and io dtype io.  The workspace holds the
- * chunk map of the packed sequences and, for at most ceil(N/64) + Ns 64-token
- * chunks: per (chunk, value head) the chunk's 64 x 64 T' and P matrices as bf16
- * hi/lo planes plus per-token factors (37888 bytes), and per (chunk, key head)
- * the chunk's K^T (18432 bytes; fp32 io also keeps bf16 hi/lo K and Q rows,
- * 106496 bytes).  Returns 0 for invalid sizes.
+ * gdn_chunk_prefill (and gdn_conv_chunk_prefill) needs for N packed tokens in Ns
+ * sequences with Hk key heads, Hv value heads, head width d (128) and io dtype io.
+ * The workspace holds the chunk map of the packed sequences; for at most
+ * ceil(N/64) + Ns 64-token chunks, per (chunk, value head) a 38912-byte record (the
+ * chunk's 64 x 64 T' and P matrices as bf16 hi/lo parts plus per-token factors) and,
+ * for fp32 io only, per (chunk, key head) the bf16 hi/lo K and Q rows (69632 bytes);
+ * and, when at most 64 (sequence, value head) pairs are given, 7 segment-transition
+ * pairs of 128 KB per pair for the intra-sequence scan.  Returns 0 for invalid sizes.
  */
 size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d, gdn_dtype_t io);
 
