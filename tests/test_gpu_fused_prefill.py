@@ -86,3 +86,37 @@ def test_fused_layer_against_oracle():
     assert_out(host(out["o"]), ref["o"], io, "fused o", upstream_bf16=1)
     assert_out(host(out["y"]), ref["y"], io, "fused y", upstream_bf16=1)
     assert_state(host(out["state_out"]), ref["state_out"], "fused state")
+
+
+def test_fused_equals_two_calls_with_given_gates_and_no_l2norm():
+    """Precomputed g / beta and use_qk_l2norm=False take the same paths in both forms."""
+    io, hk, hv = "bf16", 2, 4
+    inp, d = _inputs(hk, hv, io, 93, LENS)
+    N = inp["N"]
+    rng = np.random.default_rng(93)
+    g = f32_dev(-rng.uniform(0.0, 0.5, (N, hv)))
+    # unnormalised keys have |k|^2 ~ 10 here: beta |k|^2 < 2 keeps the recurrence stable
+    beta = f32_dev(rng.uniform(0.0, 0.1, (N, hv)))
+    x = d["x"]
+    Ns = d["cu"].numel() - 1
+    outs = []
+    for fused in (True, False):
+        y = torch.empty_like(x)
+        o = torch.empty((N, hv, D), dtype=x.dtype, device="cuda")
+        s_out = torch.empty((Ns, hv, D, D), device="cuda")
+        cs_out = torch.empty_like(d["conv_state_in"])
+        if fused:
+            gdn.gdn_conv_chunk_prefill(x, d["conv_w"], y, None, None, None, None, o, hk, hv,
+                                       d["cu"], d["conv_state_in"], cs_out, d["state_in"], s_out,
+                                       g_opt=g, beta_opt=beta, use_qk_l2norm=False)
+        else:
+            gdn.gdn_conv1d_fwd(x, d["conv_w"], y, d["cu"], d["conv_state_in"], cs_out)
+            q, k, v = qkv_views(y, hk, hv)
+            gdn.gdn_chunk_prefill(q, k, v, None, None, None, None, o, hk, hv, d["cu"],
+                                  d["state_in"], s_out, g_opt=g, beta_opt=beta,
+                                  use_qk_l2norm=False)
+        outs.append((y, o, s_out, cs_out))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    assert torch.isfinite(outs[0][1].float()).all()
