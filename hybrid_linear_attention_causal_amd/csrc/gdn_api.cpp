@@ -168,7 +168,7 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
   g_err[0] = 0;
   gdn::ChunkArgs args{q, k, v, stride_q, stride_k, stride_v, a, b, A_log, dt_bias, g_opt,
                       beta_opt, state_in, state_out, o, cu_seqlens, Ns, N, Hk, Hv, scale,
-                      use_qk_l2norm ? 1 : 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0};
+                      use_qk_l2norm ? 1 : 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
   return chunk_prefill_impl("chunk_prefill", args, dk, dv, workspace, ws_bytes, io, stream);
 }
 
@@ -202,7 +202,11 @@ gdn_status_t gdn_conv_chunk_prefill(const void* x, const float* conv_w, const vo
                       yb ? yb + (size_t)2 * Hk * dk * esz : nullptr, cq, cq, cq, a, b, A_log,
                       dt_bias, g_opt, beta_opt, state_in, state_out, o, cu_seqlens, Ns, N, Hk,
                       Hv, scale, use_qk_l2norm ? 1 : 0, 0, x, conv_w, conv_state_in,
-                      conv_state_out, y, (int)cq};
+                      conv_state_out, y, (int)cq,
+                      // one non-empty sequence (no chunk-less sequence to cover) and no
+                      // in-place state: the prep writes the final conv state itself
+                      (io == GDN_BF16 && conv_state_out && Ns == 1 && N > 0 &&
+                       conv_state_out != conv_state_in) ? 1 : 0};
   return chunk_prefill_impl("conv_chunk_prefill", args, dk, dv, workspace, ws_bytes, io, stream);
 }
 

@@ -510,6 +510,21 @@ __device__ __forceinline__ void conv_rows(const ChunkArgs& p, int s, int64_t t0,
         }
       }
     }
+    // the final conv state (the last 3 raw rows of the sequence, from x or, for a
+    // sequence shorter than 3, from the conv state before it) when this chunk ends it
+    if (p.conv_state_in_prep && wave == 0 && act && t0 + L == se) {
+      u16* cso = (u16*)p.conv_state_out;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int64_t tok = se - 3 + i;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (tok >= sb)
+          v = *reinterpret_cast<const uint4*>(x + tok * Cq + ch);
+        else if (cs)
+          v = *reinterpret_cast<const uint4*>(cs + ((int64_t)s * 3 + (tok - sb + 3)) * Cq + ch);
+        *reinterpret_cast<uint4*>(cso + ((int64_t)s * 3 + i) * Cq + ch) = v;
+      }
+    }
   }
 }
 
@@ -2027,7 +2042,7 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (conv_in_prep && a.conv_state_out) {
+  if (conv_in_prep && a.conv_state_out && !a.conv_state_in_prep) {
     // the final conv state, after every prep workgroup has read conv_state_in (the two
     // may alias)
     const ConvArgs ca{a.x, a.conv_w, a.y, a.cu, a.Ns, a.N, a.Cq, a.conv_state_in, a.conv_state_out};

@@ -50,6 +50,8 @@ struct ChunkArgs {
   void* conv_state_out;
   void* y;
   int Cq;
+  int conv_state_in_prep;   // one non-empty sequence, conv_state_out not aliasing the input:
+                            // the prep workgroup of the last chunk writes the final state
 };
 
 struct StepArgs {

@@ -120,3 +120,38 @@ def test_fused_equals_two_calls_with_given_gates_and_no_l2norm():
     for a, b in zip(*outs):
         assert torch.equal(a, b)
     assert torch.isfinite(outs[0][1].float()).all()
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 64, 130])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_fused_single_sequence_final_conv_state(T, with_state):
+    """One sequence: the prep writes the final conv state itself (rows from x, or from the
+    conv state before a sequence shorter than 3); equal to the two calls bit for bit."""
+    io, hk, hv = "bf16", 1, 2
+    sh = synth.Shape("h1x2", hk=hk, hv=hv)
+    inp = synth.make(synth.custom(sh, io, 94 + T, seqlens=[T], init_state=with_state))
+    x = to_dev(inp["x"], io)
+    w = f32_dev(inp["conv_w"])
+    a, b = to_dev(inp["a"], io), to_dev(inp["b"], io)
+    A_log, dt = f32_dev(inp["A_log"]), f32_dev(inp["dt_bias"])
+    cs_in = to_dev(inp["conv_state_in"], io) if with_state else None
+    s_in = f32_dev(inp["state_in"]) if with_state else None
+    outs = []
+    for fused in (True, False):
+        y = torch.empty_like(x)
+        o = torch.empty((T, hv, D), dtype=x.dtype, device="cuda")
+        s_out = torch.empty((1, hv, D, D), device="cuda")
+        cs_out = torch.full((1, 3, x.shape[1]), 7.0, dtype=x.dtype, device="cuda")
+        if fused:
+            gdn.gdn_conv_chunk_prefill(x, w, y, a, b, A_log, dt, o, hk, hv, None, cs_in, cs_out,
+                                       s_in, s_out)
+        else:
+            gdn.gdn_conv1d_fwd(x, w, y, None, cs_in, cs_out)
+            q, k, v = qkv_views(y, hk, hv)
+            gdn.gdn_chunk_prefill(q, k, v, a, b, A_log, dt, o, hk, hv, None, s_in, s_out)
+        outs.append((y, o, s_out, cs_out))
+    torch.cuda.synchronize()
+    for name, u, v in zip(("y", "o", "state", "conv state"), *outs):
+        assert torch.equal(u, v), name
+    ref = G.layer(inp)
+    np.testing.assert_array_equal(host(outs[0][3]), ref["conv_state_out"])
