@@ -1830,7 +1830,6 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
     wait_vmem();
     lds_barrier();     // (1) chunk n's copies and the state slabs are in LDS
     if (n > 0) store_o(n - 1);
-    load_ops(na, nxt);
 
     // ---- A: K S and Q S for row tile j (hi and lo passes in separate accumulators); the
     // copies of chunk n+1's K rows go out between the products
@@ -1913,6 +1912,7 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
       s_ux[j][3][lane] = make_uint2(wl0, wl1);
     }
     lds_barrier();     // (3) U tiles exchanged; every wave has read the R tiles
+    load_ops(na, nxt);   // chunk n+1's T' and P fragments, away from the copies at the top
 
     // ---- B: O = scale (Q S + P U) for row tile j, to the LDS output tile
     {
