@@ -11,7 +11,8 @@ One step = the hot path over one batch of synthetic input:
   bf16-stored state
   (gdn_recurrent_step_bf16_state, roofline_decode_bf16_state) and the prompt -> decode
   replay (one sequence: 1024-token prompt, then 256 decode steps eager and as one HIP
-  graph; "replay").
+  graph; "replay"), and the chunked core and fused prefill layer on the 397B T=32768 and
+  9B 64-sequence varlen workloads ("prefill_configs").
 
 Reported ("value"): layer prefill tokens/s = 4096 / (conv+chunk call + norm time),
 with the core's algorithmic flops over that call's time against the bf16 dense MFMA peak
@@ -235,6 +236,110 @@ def replay_leg(reps: int, warmup: int) -> dict:
             "decode_graph_state_GBps": state_bytes * n / (graph_ms * 1e-3) / 1e9}
 
 
+def prefill_configs_leg(reps: int) -> dict:
+    """Beside the step: the chunked core (gdn_chunk_prefill) and the fused prefill layer
+    (gdn_conv_chunk_prefill -> gdn_gated_rmsnorm) on the two other prefill workloads, the
+    397B-A17B shape at T=32768 (one sequence) and the 9B shape over 64 packed sequences of
+    seeded lengths in [16, 2048] with carried recurrent and conv states.  Each call is timed
+    with HIP events after a 512 MiB overwrite (inputs of these sizes would otherwise sit in
+    the 256 MB last-level cache from the previous call); the median of `reps` is reported.
+    The inputs are drawn on the device (torch's seeded Philox generator) with the
+    distributions of the recipe: the values steer no kernel's control flow, and NumPy draws
+    of these sizes would take longer than the timing."""
+    import math
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import hybrid_linear_attention_causal_amd as gdn
+    from hybrid_linear_attention_causal_amd import synth
+    from hybrid_linear_attention_causal_amd._lib import (gdn_chunk_prefill, gdn_conv1d_fwd,
+                                                         gdn_conv_chunk_prefill,
+                                                         gdn_gated_rmsnorm)
+    from hybrid_linear_attention_causal_amd.mixer import qkv_views
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    for idx in (3, 4):
+        wl = synth.workload(idx)
+        sh = wl.shape
+        seqlens = (synth.draw_lengths(np.random.default_rng(wl.seed)) if wl.lengths_from_rng
+                   else list(wl.seqlens))
+        N, Ns, hk, hv, cq = sum(seqlens), len(seqlens), sh.hk, sh.hv, sh.cq
+        g = torch.Generator(device="cuda").manual_seed(wl.seed)
+        bf = lambda *shape, s=1.0, o=0.0: (o + s * torch.randn(*shape, device="cuda", generator=g)
+                                           ).to(torch.bfloat16)
+        x = bf(N, cq)
+        w = 0.25 * torch.randn(cq, 4, device="cuda", generator=g)
+        a, b = bf(N, hv), bf(N, hv)
+        A_log = torch.rand(hv, device="cuda", generator=g) * math.log(16.0)
+        dt = torch.log(torch.expm1(1e-3 + (0.1 - 1e-3) * torch.rand(hv, device="cuda", generator=g)))
+        z = bf(N, hv, D)
+        nw = 1.0 + 0.1 * torch.randn(D, device="cuda", generator=g)
+        cu = s_in = cs_in = None
+        if Ns > 1:
+            cu = torch.tensor(np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32),
+                              device="cuda")
+        if wl.init_state:
+            s_in = 0.02 * torch.randn(Ns, hv, D, D, device="cuda", generator=g)
+            cs_in = bf(Ns, 3, cq)
+        y = torch.empty_like(x)
+        o = torch.empty(N, hv, D, dtype=torch.bfloat16, device="cuda")
+        yn = torch.empty_like(o)
+        s_out = torch.empty(Ns, hv, D, D, device="cuda")
+        cs_out = torch.empty(Ns, 3, cq, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(gdn.gdn_chunk_prefill_workspace_size(N, Ns, hk, hv, io=torch.bfloat16),
+                         dtype=torch.uint8, device="cuda")
+        q, k, v = qkv_views(y, hk, hv)
+
+        def fused():
+            gdn_conv_chunk_prefill(x, w, y, a, b, A_log, dt, o, hk, hv, cu, cs_in, cs_out, s_in,
+                                   s_out, workspace=ws)
+
+        def chunk():
+            gdn_chunk_prefill(q, k, v, a, b, A_log, dt, o, hk, hv, cu, s_in, s_out, workspace=ws)
+
+        def norm():
+            gdn_gated_rmsnorm(o, z, nw, yn)
+
+        def conv():
+            gdn_conv1d_fwd(x, w, y, cu, cs_in, cs_out)
+
+        def med(fn):
+            fn()
+            ts = []
+            for _ in range(reps):
+                flush.fill_(1)
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record()
+                fn()
+                e[1].record()
+                torch.cuda.synchronize()
+                ts.append(e[0].elapsed_time(e[1]))
+            return statistics.median(ts)
+
+        fused_ms, norm_ms, conv_ms, chunk_ms = med(fused), med(norm), med(conv), med(chunk)
+        flops = chunk_core_flops(N, hk, hv, seqlens)
+        tf = flops / (chunk_ms * 1e-3) / 1e12
+        name = ("Qwen3.5-397B-A17B GDN layer prefill T=32768 (B=1)" if idx == 3 else
+                f"Qwen3.5-9B GDN layer prefill, {Ns} sequences, {N} tokens, carried states")
+        out[wl.name] = {
+            "workload": name, "tokens": N, "sequences": Ns, "Hk": hk, "Hv": hv,
+            "chunk_prefill_ms": chunk_ms, "chunk_prefill_tokens_per_s": N / (chunk_ms * 1e-3),
+            "roofline_chunk_prefill": {"kernel": "gdn_chunk_prefill", "bound": "mfma",
+                                       "achieved": tf, "peak": PEAK_BF16_FLOPS / 1e12,
+                                       "unit": "TFLOP/s", "frac": tf * 1e12 / PEAK_BF16_FLOPS,
+                                       "algorithmic_per_launch": flops},
+            "conv_chunk_prefill_ms": fused_ms, "prefill_norm_ms": norm_ms,
+            "layer_tokens_per_s": N / ((fused_ms + norm_ms) * 1e-3),
+            "conv1d_ms": conv_ms,
+            "layer_unfused_tokens_per_s": N / ((conv_ms + chunk_ms + norm_ms) * 1e-3)}
+        del x, y, z, o, yn, ws, s_out, cs_out, s_in, cs_in, q, k, v
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,6 +495,7 @@ def main():
     ms_bf16_state = float(np.mean([ev_b[2 * i].elapsed_time(ev_b[2 * i + 1])
                                    for i in range(args.steps)]))
     replay = replay_leg(args.steps, args.warmup)
+    configs = prefill_configs_leg(args.steps)
     prefill_ms = ms["conv_chunk_prefill"] + ms["prefill_norm"]
     tokens_per_s = N / (prefill_ms * 1e-3)
     prefill_u_ms = ms_u["conv1d"] + ms_u["chunk_prefill"] + ms_u["prefill_norm"]
@@ -447,6 +553,7 @@ def main():
             "traffic": measured_traffic("gdn_recurrent_step_bf16_state"),
             "algorithmic_per_launch": dbytes_bf},
         "replay": replay,
+        "prefill_configs": configs,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

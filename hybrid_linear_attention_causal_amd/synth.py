@@ -135,6 +135,12 @@ def round_io(x32: np.ndarray, io: str) -> np.ndarray:
     return torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy()
 
 
+def draw_lengths(rng) -> list:
+    """The varlen workload's 64 sequence lengths, uniform integers in [16, 2048] (the
+    first draw of its generator)."""
+    return [int(v) for v in rng.integers(16, 2049, size=64)]
+
+
 def _normal(rng, shape, scale=1.0, offset=0.0):
     return (offset + scale * rng.standard_normal(shape)).astype(np.float32)
 
@@ -145,7 +151,7 @@ def make(wl: Workload) -> dict:
     rng = np.random.default_rng(wl.seed)
     seqlens = wl.seqlens
     if wl.lengths_from_rng:
-        seqlens = [int(v) for v in rng.integers(16, 2049, size=64)]
+        seqlens = draw_lengths(rng)
         wl.seqlens = seqlens
     if wl.kind == "prefill":
         ns = len(seqlens)
