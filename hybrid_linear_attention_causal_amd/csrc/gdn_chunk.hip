@@ -2020,9 +2020,12 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   // 9B T=4096, 1024 workgroups in one round, 56 us fused against 64 us as two kernels;
   // 397B T=32768, eight rounds, 658 us against 587 us).  fp32 io always runs the conv
   // kernel first.
+  // (the prep's working workgroups: at most one chunk more per sequence boundary than
+  // the tokens fill; the grid's spare rows return at once)
   const int prep_mode = rowsplit ? PREP_FRAG : four ? PREP_ROWS_P : PREP_ROWS;
+  const int64_t chunks = (a.N + CH - 1) / CH + a.Ns - 1;
   const bool conv_in_prep = a.x != nullptr && IO == IO_BF16 &&
-                            cmax * a.Hk <= (int64_t)prep_occupancy(IO, prep_mode) * cus;
+                            chunks * a.Hk <= (int64_t)prep_occupancy(IO, prep_mode) * cus;
   if (a.x != nullptr && !conv_in_prep) {
     const ConvArgs ca{a.x, a.conv_w, a.y, a.cu, a.Ns, a.N, a.Cq, a.conv_state_in, a.conv_state_out};
     e = launch_conv1d(ca, IO, st);

@@ -61,6 +61,7 @@ def _both(d, hk, hv, in_place=False):
     ("bf16", 2, 4, LENS * 2, False),        # 96 chains: 4-wave sweep
     ("bf16", 2, 4, LENS * 4, True),         # 192 chains: 8-wave sweep
     ("f32", 2, 4, LENS, False),             # fp32 io: conv then the chunk call
+    ("bf16", 16, 32, [4096], False),        # 1024 prep workgroups, one round: conv in the prep
     # more prep workgroups than fit on the chip at once: the conv kernel runs ahead of
     # the prep inside the fused call
     ("bf16", 16, 32, [8192], False),        # 2064 prep workgroups, row-split sweep
