@@ -1989,6 +1989,325 @@ chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
   }
 }
 
+// ============================================================================ 3c. row-split sweep, chain and output waves
+// The row-split sweep with each workgroup's four waves doubled by role, for chains that
+// fit on the chip in one round of workgroups.  Chain waves j = 0..3 carry the recurrence:
+// K S for row tile j, R, U = T' R and the update of state rows 32 j .. 32 j + 31, at a
+// raised issue priority.  Output waves j = 0..3 form the chunk's output off that path:
+// Q S for row tile j in phase A and P U in phase B; they also issue every LDS copy and
+// store the output tiles.  The two roles of one row tile share a SIMD, so each fills the
+// other's waits; the per-chunk barriers and LDS buffers are those of the row-split sweep.
+// (Measured at 9B T=4096: 133 us against 138 us for the four-wave kernel; P U of the
+// previous chunk moved into phase A2, behind a second U buffer, was slower again.  With
+// two workgroups per CU the four-wave kernel is as fast, so it keeps that case.)
+namespace rs2 {
+constexpr int THR = 2 * rs::THR;
+}
+
+__global__ void __launch_bounds__(rs2::THR, 2)
+chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
+  typedef Io<IO_BF16> io;
+  typedef io::T T;
+  using namespace rs;
+  __shared__ __attribute__((aligned(16))) u16 s_k0[ROWS];     // K rows, even chunks
+  __shared__ __attribute__((aligned(16))) u16 s_k1[ROWS];     // K rows, odd chunks
+  __shared__ __attribute__((aligned(16))) u16 s_q[ROWS];      // Q rows
+  __shared__ __attribute__((aligned(16))) float s_f[FAC_ROWS * CH];    // factor rows
+  __shared__ __attribute__((aligned(16))) u16 s_v[CH * V_STRIDE];      // V slice
+  __shared__ __attribute__((aligned(16))) uint4 s_sx[4][2][64];        // state slabs: hi, lo fragments
+  __shared__ __attribute__((aligned(16))) uint2 s_rx[4][2][64];        // R tiles: hi, lo
+  __shared__ __attribute__((aligned(16))) uint2 s_ux[4][4][64];        // U tiles: U hi, U lo, Us hi, Us lo
+  __shared__ __attribute__((aligned(16))) u16 s_ost[CH * O_STRIDE];    // output tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool chain = wv < NW;        // wave-uniform role
+  if (chain) __builtin_amdgcn_s_setprio(2);
+  const int j = wv & (NW - 1);       // the wave's row group
+  const int g4 = lane >> 4;
+  const int c16 = lane & 15;
+
+  // workgroup -> (sequence, value head, column block) as in the row-split sweep
+  const int Hv = p.Hv, r = Hv / p.Hk;
+  const int GS = r * NBLK;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int member = slot % GS;
+  const int group = (slot / GS) * 8 + xcd;
+  if (group >= p.Ns * p.Hk) return;
+  const int blk = member % NBLK;
+  const int kh = group % p.Hk;
+  const int s = group / p.Hk;
+  const int h = kh * r + member / NBLK;
+  int64_t b0, b1;
+  seq_bounds(p.cu, p.N, s, b0, b1);
+  const int c0 = p.Ns == 1 ? 0 : cmap[s];
+  const int ne = (int)((b1 - b0 + CH - 1) / CH);
+  const int col = blk * DVB + c16;
+
+  const uint8_t* qg = (const uint8_t*)((const T*)p.q + (int64_t)kh * DK);
+  const uint8_t* kg = (const uint8_t*)((const T*)p.k + (int64_t)kh * DK);
+  const uint8_t* vg = (const uint8_t*)((const T*)p.v + (int64_t)h * DV + blk * DVB);
+  const uint32_t qrow_bytes = (uint32_t)(p.stride_q * (int64_t)sizeof(T));
+  const uint32_t krow_bytes = (uint32_t)(p.stride_k * (int64_t)sizeof(T));
+  const uint32_t vrow_bytes = (uint32_t)(p.stride_v * (int64_t)sizeof(T));
+  T* og0 = (T*)p.o + (int64_t)h * DV + blk * DVB;
+  const int64_t o_stride = (int64_t)Hv * DV;
+  uint32_t ktab[KJ], vtab[RowDma<VW, NW>::J];
+  rows_table<16, NW>(j, lane, ktab);
+  rows_table<VW, NW>(j, lane, vtab);
+
+  // ---- state slab (chain waves): St[t] holds rows 32 j + 16 t + 4 g4 + e of column col
+  f32x4 St[2];
+  St[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  St[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (chain && p.state_in) {
+    const float* sp = p.state_in + ((int64_t)s * Hv + h) * DK * DV + col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) St[t][e] = sp[(32 * j + 16 * t + 4 * g4 + e) * DV];
+  }
+  auto put_slab = [&]() {
+    bf16x8 hi, lo;
+    frag_acc_split(St[0], St[1], hi, lo);
+    s_sx[j][0][lane] = __builtin_bit_cast(uint4, hi);
+    s_sx[j][1][lane] = __builtin_bit_cast(uint4, lo);
+  };
+  auto chunk_rows = [&](int n, int64_t& t0, int& L) {
+    t0 = b0 + (int64_t)n * CH;
+    L = (int)min((int64_t)CH, b1 - t0);
+  };
+  auto rec_of = [&](int n) { return recs + ((int64_t)(c0 + n) * Hv + h) * FR_REC_BYTES; };
+
+  // chunk n's fragments of row tile j: T' for a chain wave, P for an output wave (token
+  // slab 1 is zero for row tiles 0 and 1; it is loaded first, see the row-split sweep)
+  auto load_ops = [&](int n, RsOps& o) {
+    const uint8_t* rec = rec_of(n) + (chain ? FR_T_OFF : FR_P_OFF);
+    if (j >= 2) {
+      o.th[1] = *reinterpret_cast<const bf16x8*>(rec + fr_tp(j, 1, 0) + lane * 16);
+      o.tl[1] = *reinterpret_cast<const bf16x8*>(rec + fr_tp(j, 1, 1) + lane * 16);
+    }
+    o.th[0] = *reinterpret_cast<const bf16x8*>(rec + fr_tp(j, 0, 0) + lane * 16);
+    o.tl[0] = *reinterpret_cast<const bf16x8*>(rec + fr_tp(j, 0, 1) + lane * 16);
+  };
+  // (output waves) copies of chunk n's Q rows, factor rows and V slice
+  auto stage_qfv = [&](int n) {
+    int64_t t0;
+    int L;
+    chunk_rows(n, t0, L);
+#pragma unroll
+    for (int jp = 0; jp < KJ; ++jp)
+      dma_row_piece<16, NW>(qg + t0 * qrow_bytes, qrow_bytes, L, ktab[jp], s_q, j, jp);
+    {
+      const int ins = min(j, 1);
+      lds_dma16_sbase(rec_of(n) + FR_FAC_OFF, ins * 1024 + lane * 16, (char*)s_f + ins * 1024);
+    }
+#pragma unroll
+    for (int jp = 0; jp < RowDma<VW, NW>::J; ++jp)
+      dma_row_piece<VW, NW>(vg + t0 * vrow_bytes, vrow_bytes, L, vtab[jp], s_v, j, jp);
+  };
+  // (output waves) rows of the output tile of chunk n to global memory
+  auto store_o = [&](int n) {
+    int64_t t0;
+    int L;
+    chunk_rows(n, t0, L);
+    constexpr int WPR = DVB / 8;
+    const int ot = tid - THR;
+    if (ot < CH * WPR) {
+      const int row = ot / WPR, w = ot % WPR;
+      if (row < L)
+        *reinterpret_cast<uint4*>(og0 + (t0 + row) * o_stride + w * 8) =
+            *reinterpret_cast<const uint4*>(&s_ost[row * O_STRIDE + w * 8]);
+    }
+  };
+
+  // RsOps th/tl hold T' (chain waves) or P (output waves)
+  RsOps oa, ob;
+  if (ne > 0) {
+    if (!chain) {
+      int64_t t0;
+      int L;
+      chunk_rows(0, t0, L);
+#pragma unroll
+      for (int jp = 0; jp < KJ; ++jp)
+        dma_row_piece<16, NW>(kg + t0 * krow_bytes, krow_bytes, L, ktab[jp], s_k0, j, jp);
+      stage_qfv(0);
+    }
+    load_ops(0, oa);
+  }
+  if (chain) put_slab();
+
+  auto chunk = [&](int n, const RsOps& cur, RsOps& nxt, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    const u16* const kcur = PAR ? s_k1 : s_k0;
+    u16* const knext = PAR ? s_k0 : s_k1;
+    const int na = n + 1 < ne ? n + 1 : n;   // the last chunk reloads its own (unused)
+
+    wait_vmem();
+    lds_barrier();     // (1) chunk n's copies and the state slabs are in LDS
+    if (!chain && n > 0) store_o(n - 1);
+
+    f32x4 QS;          // output waves: Q S of row tile j
+    float4 c2;         // chain waves: the update factors of row tile j
+    float egl;
+    if (chain) {
+      // ---- A (chain): K S for row tile j, R = V - diag(e^g/|k|) K S
+      const float4 ck = *reinterpret_cast<const float4*>(&s_f[16 * j + 4 * g4]);
+      c2 = *reinterpret_cast<const float4*>(&s_f[2 * CH + 16 * j + 4 * g4]);
+      egl = s_f[3 * CH];
+      u16 vraw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vraw[e] = s_v[(16 * j + 4 * g4 + e) * V_STRIDE + c16];
+      f32x4 ka = {0.f, 0.f, 0.f, 0.f}, kb = ka;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const bf16x8 sh = __builtin_bit_cast(bf16x8, s_sx[m][0][lane]);
+        const bf16x8 sl = __builtin_bit_cast(bf16x8, s_sx[m][1][lane]);
+        const bf16x8 ak = frag_rows(kcur, KS_STRIDE, 16 * j, 32 * m, lane);
+        ka = mma(ak, sh, ka);
+        kb = mma(ak, sl, kb);
+      }
+      const float ckv[4] = {ck.x, ck.y, ck.z, ck.w};
+      int64_t t0;
+      int L;
+      chunk_rows(n, t0, L);
+      f32x4 R;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * j + 4 * g4 + e;
+        const float vv = t < L ? bf2f(vraw[e]) : 0.f;
+        R[e] = vv - ckv[e] * (ka[e] + kb[e]);
+      }
+      uint32_t rh0, rl0, rh1, rl1;
+      split2(R[0], R[1], rh0, rl0);
+      split2(R[2], R[3], rh1, rl1);
+      s_rx[j][0][lane] = make_uint2(rh0, rh1);
+      s_rx[j][1][lane] = make_uint2(rl0, rl1);
+    } else {
+      // ---- A (output): Q S for row tile j; chunk n+1's K rows copied between the products
+      int64_t ta;
+      int La;
+      chunk_rows(na, ta, La);
+      const uint8_t* kga = kg + ta * krow_bytes;
+      const float4 cq = *reinterpret_cast<const float4*>(&s_f[CH + 16 * j + 4 * g4]);
+      f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = qa;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const bf16x8 sh = __builtin_bit_cast(bf16x8, s_sx[m][0][lane]);
+        const bf16x8 sl = __builtin_bit_cast(bf16x8, s_sx[m][1][lane]);
+        const bf16x8 aq = frag_rows(s_q, KS_STRIDE, 16 * j, 32 * m, lane);
+        qa = mma(aq, sh, qa);
+        qb = mma(aq, sl, qb);
+        if (m < KJ) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[m], knext, j, m);
+      }
+#pragma unroll
+      for (int jp = 4; jp < KJ; ++jp) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[jp], knext, j, jp);
+      const float cqv[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) QS[e] = cqv[e] * (qa[e] + qb[e]);
+    }
+    lds_barrier();     // (2) R tiles exchanged; every wave has read the slabs, Q, factors, V
+    if (chain) {
+      // ---- A2 (chain): U = T' R for row tile j
+      const bf16x8 rh = pack8(s_rx[0][0][lane], s_rx[1][0][lane]);
+      const bf16x8 rl = pack8(s_rx[0][1][lane], s_rx[1][1][lane]);
+      bf16x8 rh1 = pack8(s_rx[2][0][lane], s_rx[3][0][lane]);
+      bf16x8 rl1 = pack8(s_rx[2][1][lane], s_rx[3][1][lane]);
+      asm volatile("" : "+v"(rh1), "+v"(rl1));   // keeps the reads out of the branch below
+      f32x4 ua = mma(cur.th[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 ub = mma(cur.tl[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
+      ua = mma(cur.th[0], rl, ua);
+      if (j >= 2) {
+        ub = mma(cur.th[1], rh1, ub);
+        ua = mma(cur.tl[1], rh1, ua);
+        ub = mma(cur.th[1], rl1, ub);
+      }
+      const f32x4 U = ua + ub;
+      uint32_t uh0, ul0, uh1, ul1, wh0, wl0, wh1, wl1;
+      split2(U[0], U[1], uh0, ul0);
+      split2(U[2], U[3], uh1, ul1);
+      split2(c2.x * U[0], c2.y * U[1], wh0, wl0);
+      split2(c2.z * U[2], c2.w * U[3], wh1, wl1);
+      s_ux[j][0][lane] = make_uint2(uh0, uh1);
+      s_ux[j][1][lane] = make_uint2(ul0, ul1);
+      s_ux[j][2][lane] = make_uint2(wh0, wh1);
+      s_ux[j][3][lane] = make_uint2(wl0, wl1);
+    } else {
+      stage_qfv(na);
+    }
+    lds_barrier();     // (3) U tiles exchanged; every wave has read the R tiles
+    load_ops(na, nxt);   // chunk n+1's fragments of this wave's role
+
+    if (chain) {
+      // ---- B (chain): S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U for
+      // state rows 32 j .. 32 j + 31, K^T read transposed from this chunk's K rows
+      bf16x8 wh[2], wl[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        wh[m] = pack8(s_ux[2 * m][2][lane], s_ux[2 * m + 1][2][lane]);
+        wl[m] = pack8(s_ux[2 * m][3][lane], s_ux[2 * m + 1][3][lane]);
+      }
+      bf16x8 ak[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) ak[t][m] = frag_kt(kcur, 32 * j + 16 * t, 32 * m, lane);
+      f32x4 sb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) St[t][e] *= egl;
+        sb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          St[t] = mma(ak[t][m], wh[m], St[t]);
+          sb[t] = mma(ak[t][m], wl[m], sb[t]);
+        }
+      St[0] += sb[0];
+      St[1] += sb[1];
+      put_slab();
+    } else {
+      // ---- B (output): O = scale (Q S + P U) for row tile j, to the LDS output tile
+      const bf16x8 uh = pack8(s_ux[0][0][lane], s_ux[1][0][lane]);
+      const bf16x8 ul = pack8(s_ux[0][1][lane], s_ux[1][1][lane]);
+      bf16x8 uh1 = pack8(s_ux[2][0][lane], s_ux[3][0][lane]);
+      bf16x8 ul1 = pack8(s_ux[2][1][lane], s_ux[3][1][lane]);
+      asm volatile("" : "+v"(uh1), "+v"(ul1));   // keeps the reads out of the branch below
+      f32x4 pa = mma(cur.th[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 pb = mma(cur.tl[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
+      pa = mma(cur.th[0], ul, pa);
+      if (j >= 2) {
+        pb = mma(cur.th[1], uh1, pb);
+        pa = mma(cur.tl[1], uh1, pa);
+        pb = mma(cur.th[1], ul1, pb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s_ost[(16 * j + 4 * g4 + e) * O_STRIDE + c16] = f2bf(p.scale * (QS[e] + pa[e] + pb[e]));
+    }
+  };
+  for (int n = 0; n < ne; n += 2) {
+    chunk(n, oa, ob, std::integral_constant<int, 0>());
+    if (n + 1 < ne) chunk(n + 1, ob, oa, std::integral_constant<int, 1>());
+  }
+  wait_vmem();         // no copy is in flight when the workgroup ends
+  if (ne > 0) {
+    lds_barrier();     // the last chunk's output tile is complete
+    if (!chain) store_o(ne - 1);
+  }
+  if (chain && p.state_out) {
+    float* sp = p.state_out + ((int64_t)s * Hv + h) * DK * DV + col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp[(32 * j + 16 * t + 4 * g4 + e) * DV] = St[t][e];
+  }
+}
+
 template <int IO>
 static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   const int64_t cmax = ws_max_chunks(a.N, a.Ns);
@@ -2080,10 +2399,15 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   };
   const int64_t rb = ws_rec_bytes(four);
   if (rowsplit) {
+    // one round of workgroups: chain and output waves; two rounds: four waves per workgroup
     const int64_t groups = (int64_t)a.Ns * a.Hk;
     const dim3 grid((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * rs::NBLK));
-    hipLaunchKernelGGL(chunk_rowsplit_kernel, grid, dim3(rs::THR), 0, st, a, (const int32_t*)cmap,
-                       (const uint8_t*)recs);
+    if (pairs * rs::NBLK <= cus)
+      hipLaunchKernelGGL(chunk_rowsplit2_kernel, grid, dim3(rs2::THR), 0, st, a,
+                         (const int32_t*)cmap, (const uint8_t*)recs);
+    else
+      hipLaunchKernelGGL(chunk_rowsplit_kernel, grid, dim3(rs::THR), 0, st, a,
+                         (const int32_t*)cmap, (const uint8_t*)recs);
     return hipGetLastError();
   }
   SegArgs sg{G, 0, G, segs, rb};
