@@ -2191,6 +2191,9 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
       chunk_rows(na, ta, La);
       const uint8_t* kga = kg + ta * krow_bytes;
       const float4 cq = *reinterpret_cast<const float4*>(&s_f[CH + 16 * j + 4 * g4]);
+      // the copies go out first, so that the chain waves' LDS reads are served alone
+#pragma unroll
+      for (int jp = 0; jp < KJ; ++jp) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[jp], knext, j, jp);
       f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = qa;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -2199,10 +2202,7 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
         const bf16x8 aq = frag_rows(s_q, KS_STRIDE, 16 * j, 32 * m, lane);
         qa = mma(aq, sh, qa);
         qb = mma(aq, sl, qb);
-        if (m < KJ) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[m], knext, j, m);
       }
-#pragma unroll
-      for (int jp = 4; jp < KJ; ++jp) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[jp], knext, j, jp);
       const float cqv[4] = {cq.x, cq.y, cq.z, cq.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) QS[e] = cqv[e] * (qa[e] + qb[e]);
