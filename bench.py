@@ -356,7 +356,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(the mixer would shard by head groups or sequences with no exchange; "
               "see the design notes).", file=sys.stderr)
         sys.exit(2)
