@@ -1639,24 +1639,23 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 }
 
 // ============================================================================ 3b. row-split sweep
-// For few (sequence, head) chains (bf16 io): one 4-wave workgroup per (sequence, value
-// head, 16 dv columns).  Wave j keeps state rows 32 j .. 32 j + 31 of the 16 columns (two
-// accumulator tiles) and owns token row tile j (tokens 16 j .. 16 j + 15) of the chunk's
-// R, U and O, so each wave does a quarter of the column's products and hi/lo splits.
-// Per chunk, three barriers separate:
-//   A  (after barrier 1): K S and Q S for row tile j from the four waves' state slabs
-//      (exchanged as ready bf16 hi/lo fragments), R = V - diag(e^g/|k|) K S;
+// For few (sequence, head) chains (bf16 io): one workgroup per (sequence, value head, 16 dv
+// columns) with four row groups j.  Row group j keeps state rows 32 j .. 32 j + 31 of the
+// 16 columns (two accumulator tiles) and owns token row tile j (tokens 16 j .. 16 j + 15)
+// of the chunk's R, U and O, so it does a quarter of the column's products and hi/lo
+// splits.  Per chunk, three barriers separate:
+//   A  (after barrier 1): K S and Q S for row tile j from the four state slabs (exchanged
+//      as ready bf16 hi/lo fragments), R = V - diag(e^g/|k|) K S;  K S takes both parts of
+//      the state, and Q S too (o is small where Q S and P U cancel);
 //   A2 (after barrier 2): U = T' R for row tile j from the exchanged R tiles;
 //   B  (after barrier 3): O = scale (diag(e^g/|q|) Q S + P U) for row tile j and the
-//      update of the wave's state slab from the exchanged U tiles.
+//      update of the row group's state slab from the exchanged U tiles.
 // Operands: the K rows (double-buffered by chunk parity: they serve K S and, read
 // transposed, the state update), the Q rows, the factor rows and the V slice are copied
-// to LDS by DMA; each wave's T' and P fragments load from the fragment-native records
-// straight into registers, one chunk ahead.  Chunk n+1's K rows are copied in pieces
-// between chunk n's phase-A products, its Q rows, factors and V slice right after barrier
-// 2 (their chunk-n copies are read only in phase A).  Outputs leave through an LDS tile as
-// 16-byte rows after the next chunk's first barrier.  The LDS stays below half a CU's, so
-// two workgroups share a CU when the chains need it.
+// to LDS by DMA; T' and P fragments load from the fragment-native records straight into
+// registers, one chunk ahead.  Outputs leave through an LDS tile as 16-byte rows after the
+// next chunk's first barrier.  The LDS stays below half a CU's, so two workgroups share a
+// CU when the chains need it.
 // the row-split sweep is used while its workgroups fill the compute units at most this
 // many times over
 constexpr int ROWSPLIT_CU_ROUNDS = 2;
@@ -1688,323 +1687,20 @@ __device__ __forceinline__ void dma_row_piece(const uint8_t* base, uint32_t row_
   lds_dma16_sbase(base, __umul24(row, row_bytes) + (tab >> 8), (char*)dst + ins * 1024);
 }
 
-__global__ void __launch_bounds__(rs::THR, 2)
-chunk_rowsplit_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
-  typedef Io<IO_BF16> io;
-  typedef io::T T;
-  using namespace rs;
-  __shared__ __attribute__((aligned(16))) u16 s_k0[ROWS];     // K rows, even chunks
-  __shared__ __attribute__((aligned(16))) u16 s_k1[ROWS];     // K rows, odd chunks
-  __shared__ __attribute__((aligned(16))) u16 s_q[ROWS];      // Q rows
-  __shared__ __attribute__((aligned(16))) float s_f[FAC_ROWS * CH];    // factor rows
-  __shared__ __attribute__((aligned(16))) u16 s_v[CH * V_STRIDE];      // V slice
-  __shared__ __attribute__((aligned(16))) uint4 s_sx[4][2][64];        // state slabs: hi, lo fragments
-  __shared__ __attribute__((aligned(16))) uint2 s_rx[4][2][64];        // R tiles: hi, lo
-  __shared__ __attribute__((aligned(16))) uint2 s_ux[4][4][64];        // U tiles: U hi, U lo, Us hi, Us lo
-  __shared__ __attribute__((aligned(16))) u16 s_ost[CH * O_STRIDE];    // output tile
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int j = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave's row group
-  const int g4 = lane >> 4;
-  const int c16 = lane & 15;
-
-  // workgroups come in groups (sequence, key head) of r value heads x NBLK column blocks;
-  // a group's members get ids congruent mod 8, so they share one XCD's L2
-  const int Hv = p.Hv, r = Hv / p.Hk;
-  const int GS = r * NBLK;
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  const int member = slot % GS;
-  const int group = (slot / GS) * 8 + xcd;
-  if (group >= p.Ns * p.Hk) return;
-  const int blk = member % NBLK;
-  const int kh = group % p.Hk;
-  const int s = group / p.Hk;
-  const int h = kh * r + member / NBLK;
-  int64_t b0, b1;
-  seq_bounds(p.cu, p.N, s, b0, b1);
-  const int c0 = p.Ns == 1 ? 0 : cmap[s];   // (one sequence: no chunk map)
-  const int ne = (int)((b1 - b0 + CH - 1) / CH);
-  const int col = blk * DVB + c16;
-
-  const uint8_t* qg = (const uint8_t*)((const T*)p.q + (int64_t)kh * DK);
-  const uint8_t* kg = (const uint8_t*)((const T*)p.k + (int64_t)kh * DK);
-  const uint8_t* vg = (const uint8_t*)((const T*)p.v + (int64_t)h * DV + blk * DVB);
-  const uint32_t qrow_bytes = (uint32_t)(p.stride_q * (int64_t)sizeof(T));
-  const uint32_t krow_bytes = (uint32_t)(p.stride_k * (int64_t)sizeof(T));
-  const uint32_t vrow_bytes = (uint32_t)(p.stride_v * (int64_t)sizeof(T));
-  T* og0 = (T*)p.o + (int64_t)h * DV + blk * DVB;
-  const int64_t o_stride = (int64_t)Hv * DV;
-  uint32_t ktab[KJ], vtab[RowDma<VW, NW>::J];
-  rows_table<16, NW>(j, lane, ktab);
-  rows_table<VW, NW>(j, lane, vtab);
-
-  // ---- state slab: St[t] holds rows 32 j + 16 t + 4 g4 + e of column col
-  f32x4 St[2];
-  if (p.state_in) {
-    const float* sp = p.state_in + ((int64_t)s * Hv + h) * DK * DV + col;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) St[t][e] = sp[(32 * j + 16 * t + 4 * g4 + e) * DV];
-  } else {
-    St[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    St[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  auto put_slab = [&]() {
-    bf16x8 hi, lo;
-    frag_acc_split(St[0], St[1], hi, lo);
-    s_sx[j][0][lane] = __builtin_bit_cast(uint4, hi);
-    s_sx[j][1][lane] = __builtin_bit_cast(uint4, lo);
-  };
-  auto chunk_rows = [&](int n, int64_t& t0, int& L) {
-    t0 = b0 + (int64_t)n * CH;
-    L = (int)min((int64_t)CH, b1 - t0);
-  };
-  auto rec_of = [&](int n) { return recs + ((int64_t)(c0 + n) * Hv + h) * FR_REC_BYTES; };
-
-  // T' and P fragments of chunk n.  Token slab 1 is zero for row tiles 0 and 1, so only
-  // waves 2 and 3 load it, first: every load is consumed after the next chunk's wait for
-  // all loads, so the compiler's count of loads in flight never has to cover the branch.
-  auto load_ops = [&](int n, RsOps& o) {
-    const uint8_t* rec = rec_of(n);
-    if (j >= 2) {
-      o.th[1] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, 1, 0) + lane * 16);
-      o.tl[1] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, 1, 1) + lane * 16);
-      o.ph[1] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, 1, 0) + lane * 16);
-      o.pl[1] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, 1, 1) + lane * 16);
-    }
-    o.th[0] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, 0, 0) + lane * 16);
-    o.tl[0] = *reinterpret_cast<const bf16x8*>(rec + FR_T_OFF + fr_tp(j, 0, 1) + lane * 16);
-    o.ph[0] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, 0, 0) + lane * 16);
-    o.pl[0] = *reinterpret_cast<const bf16x8*>(rec + FR_P_OFF + fr_tp(j, 0, 1) + lane * 16);
-  };
-  // copies of chunk n's Q rows, factor rows and V slice (single LDS buffers)
-  auto stage_qfv = [&](int n) {
-    int64_t t0;
-    int L;
-    chunk_rows(n, t0, L);
-#pragma unroll
-    for (int jp = 0; jp < KJ; ++jp)
-      dma_row_piece<16, NW>(qg + t0 * qrow_bytes, qrow_bytes, L, ktab[jp], s_q, j, jp);
-    {   // the factor rows: two 1 KB copies (wave 2, 3 repeat the second)
-      const int ins = min(j, 1);
-      lds_dma16_sbase(rec_of(n) + FR_FAC_OFF, ins * 1024 + lane * 16, (char*)s_f + ins * 1024);
-    }
-#pragma unroll
-    for (int jp = 0; jp < RowDma<VW, NW>::J; ++jp)
-      dma_row_piece<VW, NW>(vg + t0 * vrow_bytes, vrow_bytes, L, vtab[jp], s_v, j, jp);
-  };
-  // rows of the output tile of chunk n to global memory (16-byte pieces)
-  auto store_o = [&](int n) {
-    int64_t t0;
-    int L;
-    chunk_rows(n, t0, L);
-    constexpr int WPR = DVB / 8;
-    if (tid < CH * WPR) {
-      const int row = tid / WPR, w = tid % WPR;
-      if (row < L)
-        *reinterpret_cast<uint4*>(og0 + (t0 + row) * o_stride + w * 8) =
-            *reinterpret_cast<const uint4*>(&s_ost[row * O_STRIDE + w * 8]);
-    }
-  };
-
-  RsOps oa, ob;
-  if (ne > 0) {
-    int64_t t0;
-    int L;
-    chunk_rows(0, t0, L);
-#pragma unroll
-    for (int jp = 0; jp < KJ; ++jp)
-      dma_row_piece<16, NW>(kg + t0 * krow_bytes, krow_bytes, L, ktab[jp], s_k0, j, jp);
-    stage_qfv(0);
-    load_ops(0, oa);
-  }
-  put_slab();
-
-  auto chunk = [&](int n, const RsOps& cur, RsOps& nxt, auto par) {
-    constexpr int PAR = decltype(par)::value;
-    const u16* const kcur = PAR ? s_k1 : s_k0;
-    u16* const knext = PAR ? s_k0 : s_k1;
-    const int na = n + 1 < ne ? n + 1 : n;   // the last chunk reloads its own (unused)
-    int64_t ta;
-    int La;
-    chunk_rows(na, ta, La);
-    const uint8_t* kga = kg + ta * krow_bytes;
-
-    wait_vmem();
-    lds_barrier();     // (1) chunk n's copies and the state slabs are in LDS
-    if (n > 0) store_o(n - 1);
-
-    // ---- A: K S and Q S for row tile j (hi and lo passes in separate accumulators); the
-    // copies of chunk n+1's K rows go out between the products
-    f32x4 QS, R;
-    float4 c2;
-    float egl;
-    {
-      // every factor and V are read here, before the products so that their latency
-      // hides under them (their next copies land from barrier 2 on).  V is read
-      // unconditionally: rows past the chunk end hold copies of its last row and are
-      // zeroed by a select, which keeps the four reads in one wait
-      const float4 ck = *reinterpret_cast<const float4*>(&s_f[16 * j + 4 * g4]);
-      const float4 cq = *reinterpret_cast<const float4*>(&s_f[CH + 16 * j + 4 * g4]);
-      c2 = *reinterpret_cast<const float4*>(&s_f[2 * CH + 16 * j + 4 * g4]);
-      egl = s_f[3 * CH];
-      u16 vraw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vraw[e] = s_v[(16 * j + 4 * g4 + e) * V_STRIDE + c16];
-      f32x4 ka = {0.f, 0.f, 0.f, 0.f}, kb = ka, qa = ka, qb = ka;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const bf16x8 sh = __builtin_bit_cast(bf16x8, s_sx[m][0][lane]);
-        const bf16x8 sl = __builtin_bit_cast(bf16x8, s_sx[m][1][lane]);
-        const bf16x8 ak = frag_rows(kcur, KS_STRIDE, 16 * j, 32 * m, lane);
-        const bf16x8 aq = frag_rows(s_q, KS_STRIDE, 16 * j, 32 * m, lane);
-        ka = mma(ak, sh, ka);
-        qa = mma(aq, sh, qa);
-        kb = mma(ak, sl, kb);
-        qb = mma(aq, sl, qb);
-        if (m < KJ) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[m], knext, j, m);
-      }
-#pragma unroll
-      for (int jp = 4; jp < KJ; ++jp) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[jp], knext, j, jp);
-      const float ckv[4] = {ck.x, ck.y, ck.z, ck.w};
-      const float cqv[4] = {cq.x, cq.y, cq.z, cq.w};
-      int64_t t0;
-      int L;
-      chunk_rows(n, t0, L);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * j + 4 * g4 + e;
-        const float vv = t < L ? bf2f(vraw[e]) : 0.f;
-        R[e] = vv - ckv[e] * (ka[e] + kb[e]);
-        QS[e] = cqv[e] * (qa[e] + qb[e]);
-      }
-      uint32_t rh0, rl0, rh1, rl1;
-      split2(R[0], R[1], rh0, rl0);
-      split2(R[2], R[3], rh1, rl1);
-      s_rx[j][0][lane] = make_uint2(rh0, rh1);
-      s_rx[j][1][lane] = make_uint2(rl0, rl1);
-    }
-    lds_barrier();     // (2) R tiles exchanged; every wave has read the slabs, Q, factors, V
-    stage_qfv(na);
-
-    // ---- A2: U = T' R for row tile j
-    {
-      // (all four R tiles are read by every wave, so that the reads share one wait)
-      const bf16x8 rh = pack8(s_rx[0][0][lane], s_rx[1][0][lane]);
-      const bf16x8 rl = pack8(s_rx[0][1][lane], s_rx[1][1][lane]);
-      bf16x8 rh1 = pack8(s_rx[2][0][lane], s_rx[3][0][lane]);
-      bf16x8 rl1 = pack8(s_rx[2][1][lane], s_rx[3][1][lane]);
-      asm volatile("" : "+v"(rh1), "+v"(rl1));   // keeps the reads out of the branch below
-      f32x4 ua = mma(cur.th[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 ub = mma(cur.tl[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
-      ua = mma(cur.th[0], rl, ua);
-      if (j >= 2) {
-        ub = mma(cur.th[1], rh1, ub);
-        ua = mma(cur.tl[1], rh1, ua);
-        ub = mma(cur.th[1], rl1, ub);
-      }
-      const f32x4 U = ua + ub;
-      uint32_t uh0, ul0, uh1, ul1, wh0, wl0, wh1, wl1;
-      split2(U[0], U[1], uh0, ul0);
-      split2(U[2], U[3], uh1, ul1);
-      split2(c2.x * U[0], c2.y * U[1], wh0, wl0);
-      split2(c2.z * U[2], c2.w * U[3], wh1, wl1);
-      s_ux[j][0][lane] = make_uint2(uh0, uh1);
-      s_ux[j][1][lane] = make_uint2(ul0, ul1);
-      s_ux[j][2][lane] = make_uint2(wh0, wh1);
-      s_ux[j][3][lane] = make_uint2(wl0, wl1);
-    }
-    lds_barrier();     // (3) U tiles exchanged; every wave has read the R tiles
-    load_ops(na, nxt);   // chunk n+1's T' and P fragments, away from the copies at the top
-
-    // ---- B: O = scale (Q S + P U) for row tile j, to the LDS output tile
-    {
-      const bf16x8 uh = pack8(s_ux[0][0][lane], s_ux[1][0][lane]);
-      const bf16x8 ul = pack8(s_ux[0][1][lane], s_ux[1][1][lane]);
-      bf16x8 uh1 = pack8(s_ux[2][0][lane], s_ux[3][0][lane]);
-      bf16x8 ul1 = pack8(s_ux[2][1][lane], s_ux[3][1][lane]);
-      asm volatile("" : "+v"(uh1), "+v"(ul1));   // keeps the reads out of the branch below
-      f32x4 pa = mma(cur.ph[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 pb = mma(cur.pl[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
-      pa = mma(cur.ph[0], ul, pa);
-      if (j >= 2) {
-        pb = mma(cur.ph[1], uh1, pb);
-        pa = mma(cur.pl[1], uh1, pa);
-        pb = mma(cur.ph[1], ul1, pb);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s_ost[(16 * j + 4 * g4 + e) * O_STRIDE + c16] = f2bf(p.scale * (QS[e] + pa[e] + pb[e]));
-    }
-    // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U for state rows 32 j ..
-    // 32 j + 31, K^T read transposed from this chunk's K rows
-    {
-      bf16x8 wh[2], wl[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        wh[m] = pack8(s_ux[2 * m][2][lane], s_ux[2 * m + 1][2][lane]);
-        wl[m] = pack8(s_ux[2 * m][3][lane], s_ux[2 * m + 1][3][lane]);
-      }
-      bf16x8 ak[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) ak[t][m] = frag_kt(kcur, 32 * j + 16 * t, 32 * m, lane);
-      f32x4 sb[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) St[t][e] *= egl;
-        sb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          St[t] = mma(ak[t][m], wh[m], St[t]);
-          sb[t] = mma(ak[t][m], wl[m], sb[t]);
-        }
-      St[0] += sb[0];
-      St[1] += sb[1];
-    }
-    put_slab();
-  };
-  for (int n = 0; n < ne; n += 2) {
-    chunk(n, oa, ob, std::integral_constant<int, 0>());
-    if (n + 1 < ne) chunk(n + 1, ob, oa, std::integral_constant<int, 1>());
-  }
-  wait_vmem();         // no copy is in flight when the workgroup ends
-  if (ne > 0) {
-    lds_barrier();     // the last chunk's output tile is complete
-    store_o(ne - 1);
-  }
-  if (p.state_out) {
-    float* sp = p.state_out + ((int64_t)s * Hv + h) * DK * DV + col;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sp[(32 * j + 16 * t + 4 * g4 + e) * DV] = St[t][e];
-  }
-}
-
-// ============================================================================ 3c. row-split sweep, chain and output waves
-// The row-split sweep with each workgroup's four waves doubled by role, for chains that
-// fit on the chip in one round of workgroups.  Chain waves j = 0..3 carry the recurrence:
-// K S for row tile j, R, U = T' R and the update of state rows 32 j .. 32 j + 31, at a
-// raised issue priority.  Output waves j = 0..3 form the chunk's output off that path:
-// Q S for row tile j in phase A and P U in phase B; they also issue every LDS copy and
-// store the output tiles.  The two roles of one row tile share a SIMD, so each fills the
-// other's waits; the per-chunk barriers and LDS buffers are those of the row-split sweep.
-// (Measured at 9B T=4096: 133 us against 138 us for the four-wave kernel; P U of the
-// previous chunk moved into phase A2, behind a second U buffer, was slower again.  With
-// two workgroups per CU the four-wave kernel is as fast, so it keeps that case.)
+// Each row group is two waves by role.  Chain waves j = 0..3 carry the recurrence: K S
+// for row tile j, R, U = T' R and the update of state rows 32 j .. 32 j + 31, at a raised
+// issue priority.  Output waves j = 0..3 form the chunk's output off that path: Q S for
+// row tile j in phase A and P U in phase B; they also issue every LDS copy (the next
+// chunk's K rows before their own LDS reads, so the chain waves' reads are served first)
+// and store the output tiles.  The two roles of a row group share a SIMD, so each fills
+// the other's waits.  (Measured at 9B T=4096: 130 us against 138 us with one wave per row
+// group; 397B T=32768, two workgroups per CU: 1.68 against 1.70 ms.)
 namespace rs2 {
 constexpr int THR = 2 * rs::THR;
 }
 
-__global__ void __launch_bounds__(rs2::THR, 2)
+// (four waves per SIMD: two workgroups per CU)
+__global__ void __launch_bounds__(rs2::THR, 4)
 chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
   typedef Io<IO_BF16> io;
   typedef io::T T;
@@ -2320,7 +2016,7 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   // records, or 8-wave ones, which form P themselves
   const int64_t pairs = (int64_t)a.Ns * a.Hv;
   const int64_t cus = a.cu_count > 0 ? a.cu_count : 256;
-  // bf16 io with few chains: the row-split sweep (eight 4-wave workgroups per chain)
+  // bf16 io with few chains: the row-split sweep (eight 8-wave workgroups per chain)
   const bool rowsplit = IO == IO_BF16 && pairs * rs::NBLK <= ROWSPLIT_CU_ROUNDS * cus;
   const int G = rowsplit ? 1 : seg_count(a.N, a.Ns, a.Hv, cus);
   const bool four = rowsplit || pairs * G * SweepSizes<IO, 4>::NBLK <= cus;
@@ -2399,15 +2095,10 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   };
   const int64_t rb = ws_rec_bytes(four);
   if (rowsplit) {
-    // one round of workgroups: chain and output waves; two rounds: four waves per workgroup
     const int64_t groups = (int64_t)a.Ns * a.Hk;
     const dim3 grid((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * rs::NBLK));
-    if (pairs * rs::NBLK <= cus)
-      hipLaunchKernelGGL(chunk_rowsplit2_kernel, grid, dim3(rs2::THR), 0, st, a,
-                         (const int32_t*)cmap, (const uint8_t*)recs);
-    else
-      hipLaunchKernelGGL(chunk_rowsplit_kernel, grid, dim3(rs::THR), 0, st, a,
-                         (const int32_t*)cmap, (const uint8_t*)recs);
+    hipLaunchKernelGGL(chunk_rowsplit2_kernel, grid, dim3(rs2::THR), 0, st, a,
+                       (const int32_t*)cmap, (const uint8_t*)recs);
     return hipGetLastError();
   }
   SegArgs sg{G, 0, G, segs, rb};
