@@ -1682,7 +1682,8 @@ template <int DW, int NW>
 __device__ __forceinline__ void dma_row_piece(const uint8_t* base, uint32_t row_bytes, int L,
                                               uint32_t tab, void* dst, int wave, int jp) {
   typedef RowDma<DW, NW> R;
-  const int ins = min(wave + NW * jp, R::INS - 1);
+  const int ins = wave + NW * jp;
+  if (ins >= R::INS) return;   // (wave-uniform) no copy left for this wave
   const uint32_t row = min(tab & 0xFFu, (uint32_t)(L - 1));
   lds_dma16_sbase(base, __umul24(row, row_bytes) + (tab >> 8), (char*)dst + ins * 1024);
 }
@@ -1795,10 +1796,8 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
 #pragma unroll
     for (int jp = 0; jp < KJ; ++jp)
       dma_row_piece<16, NW>(qg + t0 * qrow_bytes, qrow_bytes, L, ktab[jp], s_q, j, jp);
-    {
-      const int ins = min(j, 1);
-      lds_dma16_sbase(rec_of(n) + FR_FAC_OFF, ins * 1024 + lane * 16, (char*)s_f + ins * 1024);
-    }
+    if (j < 2)   // the factor rows: two 1 KB copies
+      lds_dma16_sbase(rec_of(n) + FR_FAC_OFF, j * 1024 + lane * 16, (char*)s_f + j * 1024);
 #pragma unroll
     for (int jp = 0; jp < RowDma<VW, NW>::J; ++jp)
       dma_row_piece<VW, NW>(vg + t0 * vrow_bytes, vrow_bytes, L, vtab[jp], s_v, j, jp);
