@@ -1709,7 +1709,7 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
   __shared__ __attribute__((aligned(16))) u16 s_k0[ROWS];     // K rows, even chunks
   __shared__ __attribute__((aligned(16))) u16 s_k1[ROWS];     // K rows, odd chunks
   __shared__ __attribute__((aligned(16))) u16 s_q[ROWS];      // Q rows
-  __shared__ __attribute__((aligned(16))) float s_f[FAC_ROWS * CH];    // factor rows
+  __shared__ __attribute__((aligned(16))) float s_f[4 * CH];    // factor rows 0 .. 3 (c_k, c_q, c_2, e^{gamma_L})
   __shared__ __attribute__((aligned(16))) u16 s_v[CH * V_STRIDE];      // V slice
   __shared__ __attribute__((aligned(16))) uint4 s_sx[4][2][64];        // state slabs: hi, lo fragments
   __shared__ __attribute__((aligned(16))) uint2 s_rx[4][2][64];        // R tiles: hi, lo
@@ -1796,8 +1796,8 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
 #pragma unroll
     for (int jp = 0; jp < KJ; ++jp)
       dma_row_piece<16, NW>(qg + t0 * qrow_bytes, qrow_bytes, L, ktab[jp], s_q, j, jp);
-    if (j < 2)   // the factor rows: two 1 KB copies
-      lds_dma16_sbase(rec_of(n) + FR_FAC_OFF, j * 1024 + lane * 16, (char*)s_f + j * 1024);
+    if (j == 0)   // factor rows 0 .. 3 (the rest serve the other sweeps)
+      lds_dma16_sbase(rec_of(n) + FR_FAC_OFF, lane * 16, (char*)s_f);
 #pragma unroll
     for (int jp = 0; jp < RowDma<VW, NW>::J; ++jp)
       dma_row_piece<VW, NW>(vg + t0 * vrow_bytes, vrow_bytes, L, vtab[jp], s_v, j, jp);
