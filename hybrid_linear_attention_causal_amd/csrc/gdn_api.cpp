@@ -203,9 +203,10 @@ gdn_status_t gdn_conv_chunk_prefill(const void* x, const float* conv_w, const vo
                       dt_bias, g_opt, beta_opt, state_in, state_out, o, cu_seqlens, Ns, N, Hk,
                       Hv, scale, use_qk_l2norm ? 1 : 0, 0, x, conv_w, conv_state_in,
                       conv_state_out, y, (int)cq,
-                      // one non-empty sequence (no chunk-less sequence to cover) and no
-                      // in-place state: the prep writes the final conv state itself
-                      (io == GDN_BF16 && conv_state_out && Ns == 1 && N > 0 &&
+                      // one sequence of all N > 0 tokens (no cu_seqlens, so no empty or
+                      // chunk-less sequence to cover) and no in-place state: the prep
+                      // writes the final conv state itself
+                      (io == GDN_BF16 && conv_state_out && Ns == 1 && N > 0 && !cu_seqlens &&
                        conv_state_out != conv_state_in) ? 1 : 0};
   return chunk_prefill_impl("conv_chunk_prefill", args, dk, dv, workspace, ws_bytes, io, stream);
 }

@@ -131,8 +131,9 @@ recurrent_step_kernel(StepArgs p) {
     }
   }
 
-  // the fused norm's z rows of the r heads (four values per thread) and its weights, loaded
-  // with the conv inputs (whose wait covers them) and parked in LDS
+  // the fused norm's z rows of the r heads (four values per thread; the first 256 HPP
+  // groups of four) and its weights, loaded with the conv inputs (whose wait covers them)
+  // and parked in LDS
   float zr[4] = {0.f, 0.f, 0.f, 0.f};
   float4 wr = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (NORM) {
@@ -169,6 +170,13 @@ recurrent_step_kernel(StepArgs p) {
     if (tid < r * 32) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) zsh[tid * 4 + c] = zr[c];
+    }
+    // more value heads than one z row per thread (r * 32 > threads): the rest of the
+    // rows, strided over the workgroup
+    for (int i = tid + nthr; i < r * 32; i += nthr) {
+      const T* zp = (const T*)p.z + ((int64_t)bseq * Hv + kh * r) * SD + i * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) zsh[i * 4 + c] = io::ld(zp, c);
     }
     if (tid < 32) *reinterpret_cast<float4*>(&wsh[tid * 4]) = wr;
   }

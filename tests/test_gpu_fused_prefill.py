@@ -160,3 +160,29 @@ def test_fused_single_sequence_final_conv_state(T, with_state):
         assert torch.equal(u, v), name
     ref = G.layer(inp)
     np.testing.assert_array_equal(host(outs[0][3]), ref["conv_state_out"])
+
+
+def test_fused_empty_sequence_passes_states_through():
+    """One sequence given by cu_seqlens = {0, 0} over a non-empty x: no token belongs to it,
+    so its final conv state is its initial conv state and its final recurrent state is its
+    initial state (the prep, which writes the conv state for one sequence without
+    cu_seqlens, has no chunk to do it from here)."""
+    io, hk, hv = "bf16", 1, 2
+    sh = synth.Shape("h1x2", hk=hk, hv=hv)
+    inp = synth.make(synth.custom(sh, io, 97, seqlens=[8], init_state=True))
+    x = to_dev(inp["x"], io)
+    w = f32_dev(inp["conv_w"])
+    a, b = to_dev(inp["a"], io), to_dev(inp["b"], io)
+    A_log, dt = f32_dev(inp["A_log"]), f32_dev(inp["dt_bias"])
+    cs_in = to_dev(inp["conv_state_in"], io)
+    s_in = f32_dev(inp["state_in"])
+    cu = torch.tensor([0, 0], dtype=torch.int32, device="cuda")
+    y = torch.empty_like(x)
+    o = torch.empty((8, hv, D), dtype=x.dtype, device="cuda")
+    s_out = torch.full((1, hv, D, D), 3.0, device="cuda")
+    cs_out = torch.full((1, 3, x.shape[1]), 7.0, dtype=x.dtype, device="cuda")
+    gdn.gdn_conv_chunk_prefill(x, w, y, a, b, A_log, dt, o, hk, hv, cu, cs_in, cs_out, s_in,
+                               s_out)
+    torch.cuda.synchronize()
+    assert torch.equal(cs_out, cs_in)
+    assert torch.equal(s_out, s_in)

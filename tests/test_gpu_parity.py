@@ -330,7 +330,11 @@ def test_recurrent_step_slots_parity(state_io):
 
 @pytest.mark.parametrize("io,state_io,hk,hv", [("bf16", "f32", 2, 4), ("bf16", "bf16", 2, 4),
                                               ("f32", "f32", 2, 4), ("bf16", "f32", 1, 3),
-                                              ("f32", "bf16", 1, 3)])
+                                              ("f32", "bf16", 1, 3),
+                                              # more value heads per key head than one z
+                                              # row per thread: one head per pass (9) and
+                                              # two per pass (18)
+                                              ("bf16", "f32", 1, 9), ("f32", "f32", 1, 18)])
 def test_recurrent_step_norm_parity(io, state_io, hk, hv):
     """The fused step + gated norm: y against the oracle's step -> norm, and o and the state
     bit for bit equal to the unfused step's (value heads two per pass, or one)."""
