@@ -287,18 +287,22 @@ def layer(inp, pairs=None):
     """Run conv -> core -> gated norm on a dict of inputs (see the input generator).
 
     Returns dict with y_conv, conv_state_out, o, state_out, y (all fp64 holding
-    io-rounded values where they cross a call boundary).
+    io-rounded values where they cross a call boundary), and y_conv_exact, o_exact,
+    y_exact: the same three call outputs before their own rounding (each computed from
+    the rounded outputs of the calls before it, as the next call receives them).
     """
     io = inp["io"]
     Hk, Hv, dk, dv = inp["Hk"], inp["Hv"], inp["dk"], inp["dv"]
-    y, cs_out = conv1d_fwd(inp["x"], inp["conv_w"], inp["cu_seqlens"], inp["conv_state_in"])
-    y = to_io(y, io)
+    y_exact, cs_out = conv1d_fwd(inp["x"], inp["conv_w"], inp["cu_seqlens"], inp["conv_state_in"])
+    y = to_io(y_exact, io)
     q = y[:, : Hk * dk]
     k = y[:, Hk * dk: 2 * Hk * dk]
     v = y[:, 2 * Hk * dk:]
-    o, s_out = prefill(q, k, v, inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], Hk, Hv,
-                       dk, dv, inp["state_in"], inp["cu_seqlens"], pairs=pairs)
-    o = to_io(o, io)
+    o_exact, s_out = prefill(q, k, v, inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], Hk, Hv,
+                             dk, dv, inp["state_in"], inp["cu_seqlens"], pairs=pairs)
+    o = to_io(o_exact, io)
     z = np.asarray(inp["z"], dtype=np.float64).reshape(o.shape)
-    yn = to_io(gated_rmsnorm(o, z, inp["norm_w"]), io)
-    return {"y_conv": y, "conv_state_out": cs_out, "o": o, "state_out": s_out, "y": yn}
+    yn_exact = gated_rmsnorm(o, z, inp["norm_w"])
+    return {"y_conv": y, "conv_state_out": cs_out, "o": o, "state_out": s_out,
+            "y": to_io(yn_exact, io), "y_conv_exact": y_exact, "o_exact": o_exact,
+            "y_exact": yn_exact}

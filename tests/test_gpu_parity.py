@@ -31,6 +31,9 @@ def _cu_dev(inp):
     return None if cu is None else torch.from_numpy(cu.astype(np.int32)).cuda()
 
 
+# (A decode step rounds its conv output to the io dtype inside the call, as the prefill
+# layer does at the conv call's boundary, so its o has one bf16 value upstream; see parity.)
+
 # ------------------------------------------------------------------------- conv
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("init_state", [False, True])
@@ -45,7 +48,7 @@ def test_conv1d_parity(io, init_state):
     gdn.gdn_conv1d_fwd(x, w, y, _cu_dev(inp), cs_in, cs_out)
     torch.cuda.synchronize()
     y_ref, cs_ref = G.conv1d_fwd(inp["x"], inp["conv_w"], inp["cu_seqlens"], inp["conv_state_in"])
-    assert_out(host(y), G.to_io(y_ref, io), io, "conv y")
+    assert_out(host(y), y_ref, io, "conv y")
     np.testing.assert_array_equal(host(cs_out), cs_ref)   # raw rows: bit-exact
 
 
@@ -59,7 +62,7 @@ def test_conv1d_state_in_place(io):
     gdn.gdn_conv1d_fwd(x, w, y, _cu_dev(inp), cs, cs)       # in == out
     torch.cuda.synchronize()
     y_ref, cs_ref = G.conv1d_fwd(inp["x"], inp["conv_w"], inp["cu_seqlens"], inp["conv_state_in"])
-    assert_out(host(y), G.to_io(y_ref, io), io, "conv y")
+    assert_out(host(y), y_ref, io, "conv y")
     np.testing.assert_array_equal(host(cs), cs_ref)
 
 
@@ -75,10 +78,10 @@ def test_gated_rmsnorm_parity(io):
     y = torch.empty_like(og)
     gdn.gdn_gated_rmsnorm(og, zg, f32_dev(w), y)
     torch.cuda.synchronize()
-    assert_out(host(y), G.to_io(G.gated_rmsnorm(o, z, w), io), io, "norm y")
+    assert_out(host(y), G.gated_rmsnorm(o, z, w), io, "norm y")
     gdn.gdn_gated_rmsnorm(og, zg, f32_dev(w), og)             # in place
     torch.cuda.synchronize()
-    assert_out(host(og), G.to_io(G.gated_rmsnorm(o, z, w), io), io, "norm y in place")
+    assert_out(host(og), G.gated_rmsnorm(o, z, w), io, "norm y in place")
 
 
 # ------------------------------------------------------------------------- prefill core
@@ -113,7 +116,7 @@ def test_chunk_prefill_parity_small(io, hk, hv):
     v = y[:, 2 * hk * D:]
     o_ref, s_ref = G.prefill(q, k, v, inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv,
                              D, D, inp["state_in"], inp["cu_seqlens"])
-    assert_out(o, G.to_io(o_ref, io), io, "prefill o")
+    assert_out(o, o_ref, io, "prefill o")
     assert_state(s, s_ref, "prefill state")
 
 
@@ -129,7 +132,7 @@ def test_chunk_prefill_parity_many_chains(io):
     o_ref, s_ref = G.prefill(y[:, :hk * D], y[:, hk * D:2 * hk * D], y[:, 2 * hk * D:],
                              inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv, D, D,
                              inp["state_in"], inp["cu_seqlens"])
-    assert_out(o, G.to_io(o_ref, io), io, "prefill o")
+    assert_out(o, o_ref, io, "prefill o")
     assert_state(s, s_ref, "prefill state")
 
 
@@ -145,7 +148,7 @@ def test_chunk_prefill_parity_rowsplit_two_rounds():
     o_ref, s_ref = G.prefill(y[:, :hk * D], y[:, hk * D:2 * hk * D], y[:, 2 * hk * D:],
                              inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv, D, D,
                              inp["state_in"], inp["cu_seqlens"])
-    assert_out(o, G.to_io(o_ref, io), io, "prefill o")
+    assert_out(o, o_ref, io, "prefill o")
     assert_state(s, s_ref, "prefill state")
 
 
@@ -163,7 +166,7 @@ def test_chunk_prefill_parity_segmented(io, lens):
     o_ref, s_ref = G.prefill(y[:, :hk * D], y[:, hk * D:2 * hk * D], y[:, 2 * hk * D:],
                              inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv, D, D,
                              inp["state_in"], inp["cu_seqlens"])
-    assert_out(o, G.to_io(o_ref, io), io, "prefill o")
+    assert_out(o, o_ref, io, "prefill o")
     assert_state(s, s_ref, "prefill state")
 
 
@@ -174,7 +177,7 @@ def test_chunk_prefill_zero_state_single_sequence(io):
     hk, hv = 2, 4
     o_ref, s_ref = G.prefill(y[:, :hk * D], y[:, hk * D:2 * hk * D], y[:, 2 * hk * D:],
                              inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv, D, D)
-    assert_out(o, G.to_io(o_ref, io), io, "prefill o")
+    assert_out(o, o_ref, io, "prefill o")
     assert_state(s, s_ref, "prefill state")
 
 
@@ -232,7 +235,7 @@ def test_recurrent_step_parity(io, hk, hv):
     o_ref, cs_ref, st_ref = G.recurrent_step(inp["x"], inp["conv_w"], inp["conv_state_in"],
                                              inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
                                              inp["state_in"], hk, hv, D, D, io=io)
-    assert_out(host(o), G.to_io(o_ref, io), io, "step o")
+    assert_out(host(o), o_ref, io, "step o", upstream_bf16=1)
     np.testing.assert_array_equal(host(cs), cs_ref)
     assert_state(host(st), st_ref, "step state")
 
@@ -256,7 +259,7 @@ def test_recurrent_step_bf16_state_parity(io, hk, hv):
     o_ref, cs_ref, st_ref = G.recurrent_step(inp["x"], inp["conv_w"], inp["conv_state_in"],
                                              inp["a"], inp["b"], inp["A_log"], inp["dt_bias"],
                                              s_bf, hk, hv, D, D, io=io, state_io="bf16")
-    assert_out(host(o), G.to_io(o_ref, io), io, "bf16-state step o")
+    assert_out(host(o), o_ref, io, "bf16-state step o", upstream_bf16=1)
     np.testing.assert_array_equal(host(cs), cs_ref)
     assert_bf16_state(host(st), st_ref, "bf16-state step state")
 
@@ -284,9 +287,9 @@ def test_recurrent_step_bf16_state_many_steps():
         os_gpu.append(o)
         o_r, cs_ref, s_ref = G.recurrent_step(xs[t], w, cs_ref, as_[t], bs[t], A_log, dt, s_ref,
                                               hk, hv, D, D, io=io, state_io="bf16")
-        os_ref.append(G.to_io(o_r, io))
+        os_ref.append(o_r)
     torch.cuda.synchronize()
-    assert_out(np.stack([host(o) for o in os_gpu]), np.stack(os_ref), io, "bf16-state steps o")
+    assert_out(np.stack([host(o) for o in os_gpu]), np.stack(os_ref), io, "bf16-state steps o", upstream_bf16=1)
     np.testing.assert_array_equal(host(cs), cs_ref)
     # One-ulp neighbours at one step carry into the next, so over many steps only the
     # Frobenius bound holds element-blind.
@@ -316,7 +319,7 @@ def test_recurrent_step_slots_parity(state_io):
         pool, slots, hk, hv, D, D, io=io, state_io="bf16" if state_io == "bf16" else "f64")
     og = host(o)
     assert np.all(og[[1, 3]] == 0.0)
-    assert_out(og, G.to_io(o_ref, io), io, "slot step o")
+    assert_out(og, o_ref, io, "slot step o", upstream_bf16=1)
     np.testing.assert_array_equal(host(cp), cp_ref)
     spg = host(sp)
     live = [7, 2, 4]
@@ -369,8 +372,8 @@ def test_recurrent_step_norm_parity(io, state_io, hk, hv):
                                    inp["b"], inp["A_log"], inp["dt_bias"], s0, hk, hv, D, D,
                                    io=io, state_io="bf16" if state_io == "bf16" else "f64")
     y_ref = G.gated_rmsnorm(G.to_io(o_ref, io), z, nw)
-    assert_out(host(o1), G.to_io(o_ref, io), io, "fused step o")
-    assert_out(host(y1), G.to_io(y_ref, io), io, "fused step y", upstream_bf16=1)
+    assert_out(host(o1), o_ref, io, "fused step o", upstream_bf16=1)
+    assert_out(host(y1), y_ref, io, "fused step y", upstream_bf16=2)
 
 
 def test_step_entry_points_accept_an_empty_batch():
@@ -413,6 +416,6 @@ def test_prefill_then_steps_equals_prefill():
                             z[t:t + 1], nw, hk, hv)
         ys.append(host(r["y"]))
     torch.cuda.synchronize()
-    assert_out(np.concatenate(ys), ref["y"], io, "layer y", upstream_bf16=1)
+    assert_out(np.concatenate(ys), ref["y_exact"], io, "layer y", upstream_bf16=2)
     assert_state(host(st), ref["state_out"], "final state")
     np.testing.assert_array_equal(host(cs), ref["conv_state_out"])

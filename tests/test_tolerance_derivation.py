@@ -25,3 +25,27 @@ def test_one_ulp_input_flips_need_the_downstream_slack():
     err1, _ = out_error(y_flip, y_ref, "bf16", upstream_bf16=1)
     assert err0 > bound          # a single-rounding slack would reject a correct kernel
     assert err1 < 0.5 * bound    # the downstream slack absorbs one-ulp input flips
+
+
+def test_a_call_output_is_compared_before_the_oracles_rounding():
+    """A GPU output is its fp32 value rounded once to bf16.  Against the oracle's fp64
+    value before rounding, that store moves it by at most half an ulp, inside the 2^-8
+    slack; against the oracle's value after its own rounding, values whose fp32 and fp64
+    forms straddle a rounding midpoint sit one full ulp apart, which exceeds the bound at
+    values of about ten times the RMS (the reading of the 2^-8 term: it is the GPU's store,
+    which the fp64 reference does not have)."""
+    rng = np.random.default_rng(1)
+    o64 = rng.standard_normal(200000) * 3e-3
+    # fp32 arithmetic: relative errors of a few ulp of fp32
+    o32 = o64 * (1 + 3e-7 * rng.standard_normal(o64.size))
+    # twenty values just above 2^-5 (about ten times the RMS), each next to a bf16 rounding
+    # midpoint, the fp64 value a few fp32 ulp (3.7e-9 here) below it and the fp32 value as
+    # far above
+    mid = 2.0 ** -5 * (1 + (np.arange(20) + 1.5) * 2.0 ** -7)
+    o64[:20] = mid - 1e-8
+    o32[:20] = mid + 1e-8
+    gpu = G.bf16_round(o32)
+    err_exact, bound = out_error(gpu, o64, "bf16")
+    err_rounded, _ = out_error(gpu, G.bf16_round(o64), "bf16")
+    assert err_exact < 0.05 * bound
+    assert err_rounded > bound
