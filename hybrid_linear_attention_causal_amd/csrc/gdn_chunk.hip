@@ -96,17 +96,18 @@ __host__ __device__ constexpr int64_t ws_krec_bytes(bool f32) {
   return f32 ? 4 * WS_ROWS_BYTES : 0;
 }
 
-// Intra-sequence scan: at most SEG_MAX segments per sequence, each of at least
+// Intra-sequence scan (fp32 io): at most SEG_MAX segments per sequence, each of at least
 // SEG_MIN_CHUNKS chunks on average, for at most SEG_MAX_CHAINS (sequence, head) chains;
 // the workspace reserves (SEG_MAX - 1) (A, B) pairs per chain when the chain count allows.
+// bf16 io never segments (few chains run the row-split sweep), so reserves nothing.
 constexpr int SEG_MAX = 8;
 constexpr int SEG_MIN_CHUNKS = 4;
 constexpr int64_t SEG_MAX_CHAINS = 64;
 constexpr int64_t SEG_PAIR_BYTES = 2LL * DK * DV * 4;   // A then B, fp32
 
-static int64_t ws_seg_bytes(int Ns, int Hv) {
+static int64_t ws_seg_bytes(int Ns, int Hv, bool f32) {
   const int64_t chains = (int64_t)Ns * Hv;
-  return chains <= SEG_MAX_CHAINS ? (SEG_MAX - 1) * chains * SEG_PAIR_BYTES : 0;
+  return f32 && chains <= SEG_MAX_CHAINS ? (SEG_MAX - 1) * chains * SEG_PAIR_BYTES : 0;
 }
 
 // Segments per sequence: enough to fill the compute units with the normal launch's two
@@ -124,7 +125,7 @@ static int seg_count(int64_t N, int Ns, int Hv, int64_t cus) {
 size_t chunk_workspace_bytes(int64_t N, int Ns, int Hk, int Hv, bool f32) {
   const int64_t cmax = ws_max_chunks(N, Ns);
   return (size_t)(ws_map_bytes(N, Ns) + cmax * Hv * ws_rec_bytes(true) + cmax * Hk * ws_krec_bytes(f32) +
-                  ws_seg_bytes(Ns, Hv));
+                  ws_seg_bytes(Ns, Hv, f32));
 }
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -2017,7 +2018,8 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   const int64_t cus = a.cu_count > 0 ? a.cu_count : 256;
   // bf16 io with few chains: the row-split sweep (eight 8-wave workgroups per chain)
   const bool rowsplit = IO == IO_BF16 && pairs * rs::NBLK <= ROWSPLIT_CU_ROUNDS * cus;
-  const int G = rowsplit ? 1 : seg_count(a.N, a.Ns, a.Hv, cus);
+  // (only fp32 io has segment scratch in its workspace)
+  const int G = (rowsplit || IO == IO_BF16) ? 1 : seg_count(a.N, a.Ns, a.Hv, cus);
   const bool four = rowsplit || pairs * G * SweepSizes<IO, 4>::NBLK <= cus;
   // the chunk map of packed sequences (one sequence needs none: its chunks are in order)
   hipError_t e = hipSuccess;

@@ -94,9 +94,10 @@ def test_prefill_rejects():
     # chunk offsets (int32 [Ns + 1]) and chunk table (int4 [cmax]), each padded to 256 B,
     # then cmax = ceil(N/64) + Ns chunks x (Hv x 38912 B + Hk x K record), K record 0 B
     # (bf16 io: K and Q are staged from the inputs) or 69632 B (fp32 io), then for at
-    # most 64 (sequence, head) chains 7 segment-transition pairs of 128 KB per chain
+    # most 64 (sequence, head) chains 7 segment-transition pairs of 128 KB per chain (fp32
+    # io only: bf16 io never segments)
     ws = _lib.lib().gdn_chunk_prefill_workspace_size
-    assert ws(4096, 1, 16, 32, 128, 1) == 256 + 1280 + 65 * (32 * 38912) + 7 * 32 * 131072
+    assert ws(4096, 1, 16, 32, 128, 1) == 256 + 1280 + 65 * (32 * 38912)
     assert ws(4096, 3, 16, 32, 128, 1) == 256 + 1280 + 67 * (32 * 38912)
     assert ws(100, 3, 1, 2, 128, 0) == 256 + 256 + 5 * (2 * 38912 + 1 * 69632) + 7 * 6 * 131072
     assert ws(-1, 1, 16, 32, 128, 1) == 0
