@@ -40,6 +40,7 @@ D = 128
 CHUNK = 64
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+FLUSH_BYTES = 512 << 20       # overwritten before each timed prefill (last-level cache 256 MB)
 
 
 CSRC = os.path.join(ROOT, "hybrid_linear_attention_causal_amd", "csrc")
@@ -116,6 +117,80 @@ def _cpu_chain(task):
     return G.to_io(G.gated_rmsnorm(o, z, norm_w), io).shape[0]
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def pool_procs(n_tasks: int):
+    """Worker processes for the CPU legs: the host cores this process may run on, at most
+    16 (the host's CPU share for one GPU); returns (procs, cores in the affinity mask)."""
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    return max(1, min(16, ncpu, n_tasks)), ncpu
+
+
+def _cpu_decode(task):
+    """Oracle decode step for a block of sequences (runs in a worker process)."""
+    from oracle import gdn_oracle as G
+    x, w, cs, a, b, A_log, dt_bias, st, hk, hv, io = task
+    o, _, _ = G.recurrent_step(x, w, cs, a, b, A_log, dt_bias, st, hk, hv, D, D, io=io)
+    return o.shape[0]
+
+
+def _single_threaded_blas():
+    keep = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                           "MKL_NUM_THREADS")}
+    for k in keep:
+        os.environ[k] = "1"
+    return keep
+
+
+def _restore_env(keep):
+    for k, v in keep.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+
+
+def cpu_baseline_decode(dec, reps=2):
+    """Time the fp64 oracle's decode step on the whole decode workload (all sequences, all
+    value heads), in a process pool over blocks of sequences, reps times over."""
+    import multiprocessing as mp
+
+    B = dec["N"]
+    procs, ncpu = pool_procs(B)
+    blocks = [list(range(i, B, procs)) for i in range(procs)]
+    tasks = [(dec["x"][bl], dec["conv_w"], dec["conv_state_in"][bl], dec["a"][bl], dec["b"][bl],
+              dec["A_log"], dec["dt_bias"], dec["state_in"][bl], dec["Hk"], dec["Hv"], dec["io"])
+             for bl in blocks]
+    keep = _single_threaded_blas()
+    try:
+        with mp.get_context("spawn").Pool(procs) as pool:
+            pool.map(_cpu_decode, [(t[0][:1], t[1], t[2][:1], t[3][:1], t[4][:1], t[5], t[6],
+                                    t[7][:1], t[8], t[9], t[10]) for t in tasks])   # warm
+            t0 = time.perf_counter()
+            done = sum(pool.map(_cpu_decode, tasks * reps, chunksize=1))
+            wall = time.perf_counter() - t0
+    finally:
+        _restore_env(keep)
+    assert done == reps * B
+    return {"value": reps * B / wall, "unit": "sequence-steps/s", "cores": procs,
+            "kind": "oracle", "wall_s": wall, "cpu_model": cpu_model(), "affinity_cores": ncpu,
+            "sample": (f"fp64 NumPy oracle decode step of the Qwen3.5-9B layer, all {B} "
+                       f"sequences x {dec['Hv']} value heads (conv + recurrence), run {reps} "
+                       f"times, {procs} worker processes")}
+
+
 def cpu_baseline(inp, budget_heads=None, reps=2):
     """Time the fp64 oracle on the prefill layer workload in a process pool over value
     heads (one BLAS thread per worker), the head list run reps times over (about 6 s of
@@ -135,15 +210,8 @@ def cpu_baseline(inp, budget_heads=None, reps=2):
         tasks.append((inp["x"][:, chans], inp["conv_w"][chans], inp["a"][:, h], inp["b"][:, h],
                       float(inp["A_log"][h]), float(inp["dt_bias"][h]),
                       inp["z"][:, h * D:(h + 1) * D], inp["norm_w"], inp["io"]))
-    try:
-        ncpu = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncpu = os.cpu_count() or 1
-    procs = max(1, min(16, ncpu, len(tasks)))
-    env_keep = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
-                                               "MKL_NUM_THREADS")}
-    for k in env_keep:
-        os.environ[k] = "1"
+    procs, ncpu = pool_procs(len(tasks))
+    keep = _single_threaded_blas()
     try:
         ctx = mp.get_context("spawn")
         with ctx.Pool(procs) as pool:
@@ -152,14 +220,10 @@ def cpu_baseline(inp, budget_heads=None, reps=2):
             pool.map(_cpu_chain, tasks * reps, chunksize=1)
             wall = time.perf_counter() - t0
     finally:
-        for k, v in env_keep.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+        _restore_env(keep)
     tokens_per_s = reps * N * (len(heads) / hv) / wall
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": procs, "kind": "oracle",
-            "wall_s": wall,
+            "wall_s": wall, "cpu_model": cpu_model(), "affinity_cores": ncpu,
             "sample": (f"fp64 NumPy oracle (token-by-token recurrence) of the Qwen3.5-9B prefill "
                        f"layer, T={N}, {len(heads)} of {hv} value heads (conv+core+norm per head) "
                        f"run {reps} times, {procs} worker processes; tokens/s scaled by heads/{hv}")}
@@ -238,9 +302,10 @@ def replay_leg(reps: int, warmup: int) -> dict:
 
 def prefill_configs_leg(reps: int) -> dict:
     """Beside the step: the chunked core (gdn_chunk_prefill) and the fused prefill layer
-    (gdn_conv_chunk_prefill -> gdn_gated_rmsnorm) on the two other prefill workloads, the
-    397B-A17B shape at T=32768 (one sequence) and the 9B shape over 64 packed sequences of
-    seeded lengths in [16, 2048] with carried recurrent and conv states.  Each call is timed
+    (gdn_conv_chunk_prefill -> gdn_gated_rmsnorm) on the three other prefill workloads: the
+    0.8B shape at T=256 with fp32 io, the 397B-A17B shape at T=32768 (one sequence) and the
+    9B shape over 64 packed sequences of seeded lengths in [16, 2048] with carried recurrent
+    and conv states.  Each call is timed
     with HIP events after a 512 MiB overwrite (inputs of these sizes would otherwise sit in
     the 256 MB last-level cache from the previous call); the median of `reps` is reported.
     The inputs are drawn on the device (torch's seeded Philox generator) with the
@@ -259,17 +324,18 @@ def prefill_configs_leg(reps: int) -> dict:
                                                          gdn_gated_rmsnorm)
     from hybrid_linear_attention_causal_amd.mixer import qkv_views
 
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     out = {}
-    for idx in (3, 4):
+    for idx in (0, 3, 4):
         wl = synth.workload(idx)
         sh = wl.shape
         seqlens = (synth.draw_lengths(np.random.default_rng(wl.seed)) if wl.lengths_from_rng
                    else list(wl.seqlens))
         N, Ns, hk, hv, cq = sum(seqlens), len(seqlens), sh.hk, sh.hv, sh.cq
         g = torch.Generator(device="cuda").manual_seed(wl.seed)
+        iodt = torch.float32 if wl.io == "f32" else torch.bfloat16
         bf = lambda *shape, s=1.0, o=0.0: (o + s * torch.randn(*shape, device="cuda", generator=g)
-                                           ).to(torch.bfloat16)
+                                           ).to(iodt)
         x = bf(N, cq)
         w = 0.25 * torch.randn(cq, 4, device="cuda", generator=g)
         a, b = bf(N, hv), bf(N, hv)
@@ -285,11 +351,11 @@ def prefill_configs_leg(reps: int) -> dict:
             s_in = 0.02 * torch.randn(Ns, hv, D, D, device="cuda", generator=g)
             cs_in = bf(Ns, 3, cq)
         y = torch.empty_like(x)
-        o = torch.empty(N, hv, D, dtype=torch.bfloat16, device="cuda")
+        o = torch.empty(N, hv, D, dtype=iodt, device="cuda")
         yn = torch.empty_like(o)
         s_out = torch.empty(Ns, hv, D, D, device="cuda")
-        cs_out = torch.empty(Ns, 3, cq, dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(gdn.gdn_chunk_prefill_workspace_size(N, Ns, hk, hv, io=torch.bfloat16),
+        cs_out = torch.empty(Ns, 3, cq, dtype=iodt, device="cuda")
+        ws = torch.empty(gdn.gdn_chunk_prefill_workspace_size(N, Ns, hk, hv, io=iodt),
                          dtype=torch.uint8, device="cuda")
         q, k, v = qkv_views(y, hk, hv)
 
@@ -322,10 +388,11 @@ def prefill_configs_leg(reps: int) -> dict:
         fused_ms, norm_ms, conv_ms, chunk_ms = med(fused), med(norm), med(conv), med(chunk)
         flops = chunk_core_flops(N, hk, hv, seqlens)
         tf = flops / (chunk_ms * 1e-3) / 1e12
-        name = ("Qwen3.5-397B-A17B GDN layer prefill T=32768 (B=1)" if idx == 3 else
-                f"Qwen3.5-9B GDN layer prefill, {Ns} sequences, {N} tokens, carried states")
+        name = {0: "Qwen3.5-0.8B GDN layer prefill T=256 (B=1), fp32 io",
+                3: "Qwen3.5-397B-A17B GDN layer prefill T=32768 (B=1)",
+                4: f"Qwen3.5-9B GDN layer prefill, {Ns} sequences, {N} tokens, carried states"}[idx]
         out[wl.name] = {
-            "workload": name, "tokens": N, "sequences": Ns, "Hk": hk, "Hv": hv,
+            "workload": name, "tokens": N, "sequences": Ns, "Hk": hk, "Hv": hv, "io": wl.io,
             "chunk_prefill_ms": chunk_ms, "chunk_prefill_tokens_per_s": N / (chunk_ms * 1e-3),
             "roofline_chunk_prefill": {"kernel": "gdn_chunk_prefill", "bound": "mfma",
                                        "achieved": tf, "peak": PEAK_BF16_FLOPS / 1e12,
@@ -455,13 +522,19 @@ def main():
             ev[3].record()
         decode(ev, 4)
 
+    # Before each step's prefill a 512 MiB overwrite evicts the 256 MB last-level cache,
+    # outside the kernel events (the 67 MB x and the workspace records would otherwise be
+    # read from it on the next step); the wall clock of the K steps includes it.
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     for _ in range(args.warmup):
+        flush.fill_(1)
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush.fill_(1)
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -470,9 +543,11 @@ def main():
 
     # Beside the step: the same step with the conv and the chunked core as two calls.
     for _ in range(args.warmup):
+        flush.fill_(1)
         step_unfused()
     evu = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for i in range(args.steps):
+        flush.fill_(1)
         step_unfused(evu[i])
     torch.cuda.synchronize()
     names_u = ["conv1d", "chunk_prefill", "prefill_norm", "recurrent_step", "decode_norm"]
@@ -555,9 +630,11 @@ def main():
         "replay": replay,
         "prefill_configs": configs,
         "cpu_baseline": None,
+        "cpu_baseline_decode": None,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pre, args.cpu_heads, args.cpu_reps)
+        res["cpu_baseline_decode"] = cpu_baseline_decode(dec, args.cpu_reps)
     print(json.dumps(res), flush=True)
 
 
