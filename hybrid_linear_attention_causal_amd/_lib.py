@@ -36,6 +36,9 @@ _SIGS = {
     "gdn_chunk_prefill": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                            _sz, _i32, _vp], _i32),
+    "gdn_chunk_prefill_noalloc": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32,
+                                   _f32, _i32, _i32, _vp], _i32),
     "gdn_conv_chunk_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                 _vp, _sz, _i32, _vp], _i32),
@@ -159,6 +162,24 @@ def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None,
         _p(dt_bias), _p(g_opt), _p(beta_opt), _p(state_in), _p(state_out), _p(o),
         _p(cu_seqlens), Ns, N, Hk, Hv, dk, dv, float(scale), int(bool(use_qk_l2norm)),
         _p(workspace), ws_bytes, _io(q), _stream(stream)))
+
+
+def gdn_chunk_prefill_noalloc(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None,
+                              state_in=None, state_out=None, g_opt=None, beta_opt=None, scale=0.0,
+                              use_qk_l2norm=True, stream=None, dk=128, dv=128):
+    """gdn_chunk_prefill on the library's fixed device workspace: allocates nothing.  Calls
+    that overlap on one device share that workspace and must not run concurrently."""
+    _dev(q, k, v, a, b, A_log, dt_bias, o, cu_seqlens, state_in, state_out, g_opt, beta_opt)
+    N = q.shape[0]
+    Ns = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    for t in (q, k, v):
+        if t.stride(-1) != 1:
+            raise ValueError("q, k, v rows must be contiguous")
+    _check("gdn_chunk_prefill_noalloc", lib().gdn_chunk_prefill_noalloc(
+        _p(q), _p(k), _p(v), q.stride(0), k.stride(0), v.stride(0), _p(a), _p(b), _p(A_log),
+        _p(dt_bias), _p(g_opt), _p(beta_opt), _p(state_in), _p(state_out), _p(o),
+        _p(cu_seqlens), Ns, N, Hk, Hv, dk, dv, float(scale), int(bool(use_qk_l2norm)), _io(q),
+        _stream(stream)))
 
 
 def gdn_conv_chunk_prefill(x, conv_w, y, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None,

@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_conv1d.hip", "gdn_chunk.hip", "gdn_step.hip", "gdn_norm.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_conv1d.hip", "gdn_chunk.hip", "gdn_step.hip", "gdn_norm.hip",
+           "gdn_noalloc.hip"]
 ARCH = "gfx950"
 
 

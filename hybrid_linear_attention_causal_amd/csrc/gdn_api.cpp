@@ -172,6 +172,36 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
   return chunk_prefill_impl("chunk_prefill", args, dk, dv, workspace, ws_bytes, io, stream);
 }
 
+static_assert(GDN_NOALLOC_SCRATCH_BYTES == gdn::NOALLOC_SCRATCH_BYTES, "one scratch size");
+
+gdn_status_t gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
+                                       int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                                       const void* a, const void* b, const float* A_log,
+                                       const float* dt_bias, const float* g_opt,
+                                       const float* beta_opt, const float* state_in,
+                                       float* state_out, void* o, const int32_t* cu_seqlens,
+                                       int Ns, int64_t N, int Hk, int Hv, int dk, int dv,
+                                       float scale, int use_qk_l2norm, gdn_dtype_t io,
+                                       void* stream) {
+  g_err[0] = 0;
+  const size_t need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk, io);
+  if (need > GDN_NOALLOC_SCRATCH_BYTES)
+    return fail(GDN_ERR_INVALID_ARG,
+                "chunk_prefill_noalloc: these sizes need a %zu-byte workspace, above the "
+                "fixed %zu bytes; use gdn_chunk_prefill with a caller workspace",
+                need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+  gdn_status_t st = check_device();
+  if (st != GDN_OK) return st;
+  void* ws = nullptr;
+  const hipError_t e = gdn::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "chunk_prefill_noalloc: scratch address");
+  gdn::ChunkArgs args{q, k, v, stride_q, stride_k, stride_v, a, b, A_log, dt_bias, g_opt,
+                      beta_opt, state_in, state_out, o, cu_seqlens, Ns, N, Hk, Hv, scale,
+                      use_qk_l2norm ? 1 : 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+  return chunk_prefill_impl("chunk_prefill_noalloc", args, dk, dv, ws, GDN_NOALLOC_SCRATCH_BYTES,
+                            io, stream);
+}
+
 gdn_status_t gdn_conv_chunk_prefill(const void* x, const float* conv_w, const void* conv_state_in,
                                     void* conv_state_out, void* y, const void* a, const void* b,
                                     const float* A_log, const float* dt_bias, const float* g_opt,

@@ -98,4 +98,9 @@ hipError_t launch_chunk_prefill(const ChunkArgs& a, void* ws, int io, hipStream_
 hipError_t launch_recurrent_step(const StepArgs& a, int io, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, int io, hipStream_t s);
 
+// the allocation-free prefill's fixed device workspace: its size, and its device address
+// on the current device (looked up once per device)
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)128 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace gdn

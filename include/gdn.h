@@ -160,6 +160,31 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
                                void* workspace, size_t ws_bytes, gdn_dtype_t io, void* stream);
 
 /*
+ * gdn_chunk_prefill_noalloc -- gdn_chunk_prefill without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The workspace is a fixed
+ * GDN_NOALLOC_SCRATCH_BYTES array in device memory that the library holds on each device
+ * it runs on until the process ends; the call allocates nothing.  Every call on one
+ * device shares that array, so calls that overlap on one device (concurrent streams or
+ * host threads) race and must be serialised by the caller.  Results are those of
+ * gdn_chunk_prefill (the same kernels run).
+ *
+ * Arguments and errors as for gdn_chunk_prefill, and INVALID_ARG when the workspace
+ * the sizes need (gdn_chunk_prefill_workspace_size) exceeds GDN_NOALLOC_SCRATCH_BYTES
+ * (about 4000 tokens of one sequence at 16 key / 32 value heads, bf16 io).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status_t gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
+                                       int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                                       const void* a, const void* b, const float* A_log,
+                                       const float* dt_bias, const float* g_opt,
+                                       const float* beta_opt, const float* state_in,
+                                       float* state_out, void* o, const int32_t* cu_seqlens,
+                                       int Ns, int64_t N, int Hk, int Hv, int dk, int dv,
+                                       float scale, int use_qk_l2norm, gdn_dtype_t io,
+                                       void* stream);
+
+/*
  * gdn_conv_chunk_prefill -- gdn_conv1d_fwd and gdn_chunk_prefill in one call: the conv
  * window + SiLU of the raw projection rows x is written to y and the chunked delta rule
  * runs on q, k, v read from y (q = y[:, 0 : Hk*dk], k = y[:, Hk*dk : 2*Hk*dk],

@@ -11,8 +11,9 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libgdn.so not built (run __graft_entry__.build())")
 
 EXPECTED = {"gdn_last_error", "gdn_version", "gdn_conv1d_fwd", "gdn_chunk_prefill_workspace_size",
-            "gdn_chunk_prefill", "gdn_conv_chunk_prefill", "gdn_recurrent_step", "gdn_recurrent_step_bf16_state",
-            "gdn_recurrent_step_slots", "gdn_recurrent_step_norm", "gdn_gated_rmsnorm"}
+            "gdn_chunk_prefill", "gdn_chunk_prefill_noalloc", "gdn_conv_chunk_prefill",
+            "gdn_recurrent_step", "gdn_recurrent_step_bf16_state", "gdn_recurrent_step_slots",
+            "gdn_recurrent_step_norm", "gdn_gated_rmsnorm"}
 
 
 def test_header_declares_the_calls():
@@ -203,3 +204,12 @@ def test_conv_chunk_prefill_rejects():
     assert _fused(Ns=2) == _lib.GDN_ERR_INVALID_ARG          # cu_seqlens NULL
     assert _fused(ws=None) == _lib.GDN_ERR_INVALID_ARG
     assert _fused(g=P) == _lib.GDN_ERR_INVALID_ARG           # g without beta
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_array_before_any_launch():
+    # 9B shape, 8192 tokens of one sequence: a 161 MB workspace against the fixed 128 MiB
+    L = _L()
+    args = [P, P, P, 4096, 4096, 4096, P, P, P, P, None, None, None, None, P, None, 1, 8192,
+            16, 32, 128, 128, 0.0, 1, 1, None]
+    assert L.gdn_chunk_prefill_noalloc(*args) == _lib.GDN_ERR_INVALID_ARG
+    assert "workspace" in _msg()
