@@ -442,23 +442,36 @@ __device__ __forceinline__ void conv_rows(const ChunkArgs& p, int s, int64_t t0,
                             : make_float4(0.f, 0.f, 0.f, 0.f);
       wt[0][j] = ww.x; wt[1][j] = ww.y; wt[2][j] = ww.z; wt[3][j] = ww.w;
     }
-#pragma unroll
+    // (the two halves run as a loop: unrolled, both windows' registers and row offsets
+    // are live at once and spill)
+#pragma unroll 1
     for (int half = 0; half < 2; ++half) {
       const int r0 = 16 * wave + 8 * half;
-      // rows r0 - 3 .. r0 + 7; rows past the chunk end feed only outputs past it
+      // rows r0 - 3 .. r0 + 7; rows past the chunk end feed only outputs past it.  The
+      // lane's pointer to its channels in the first row is formed once; row i is i Cq
+      // further (no per-row 64-bit scalar offsets to hold)
       uint4 raw[11];
+      const u16* xr = x + (t0 + r0 - 3) * (int64_t)Cq + ch;
+      if (t0 + r0 - 3 >= sb) {
+        // the whole window lies inside the sequence
 #pragma unroll
-      for (int i = 0; i < 11; ++i) {
-        const int row = r0 - 3 + i;
-        const int64_t tok = t0 + row;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (act && row < L) {
-          if (tok >= sb)
-            v = *reinterpret_cast<const uint4*>(x + tok * Cq + ch);
-          else if (cs)
-            v = *reinterpret_cast<const uint4*>(cs + ((int64_t)s * 3 + (tok - sb + 3)) * Cq + ch);
+        for (int i = 0; i < 11; ++i)
+          raw[i] = (act && r0 - 3 + i < L) ? *reinterpret_cast<const uint4*>(xr + i * Cq)
+                                          : make_uint4(0, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 11; ++i) {
+          const int row = r0 - 3 + i;
+          const int64_t tok = t0 + row;
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (act && row < L) {
+            if (tok >= sb)
+              v = *reinterpret_cast<const uint4*>(xr + i * Cq);
+            else if (cs)
+              v = *reinterpret_cast<const uint4*>(cs + ((int64_t)s * 3 + (tok - sb + 3)) * Cq + ch);
+          }
+          raw[i] = v;
         }
-        raw[i] = v;
       }
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -570,27 +583,29 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
 
-  // raw gate inputs of value head kh_ r + hb + wave for this lane's token
-  auto gate_in = [&](int hb, float& ga, float& gb, float& al, float& dt) {
+  // raw gate inputs of value head kh_ r + hb + wave for this lane's token: {a or g, b or
+  // beta, A_log, dt_bias} (returned by value: references into branches would leave the
+  // four values in scratch memory)
+  auto gate_in = [&](int hb) {
     const int jh = hb + wave;
-    ga = gb = al = dt = 0.f;
+    float4 gi = make_float4(0.f, 0.f, 0.f, 0.f);
     if (jh < r) {
       const int h = kh_ * r + jh;
       const int64_t idx = (t0 + (lane < L ? lane : L - 1)) * Hv + h;
       if (p.g_opt) {
-        ga = p.g_opt[idx];
-        gb = p.beta_opt[idx];
+        gi.x = p.g_opt[idx];
+        gi.y = p.beta_opt[idx];
       } else {
-        ga = io::ld((const T*)p.a, idx);
-        gb = io::ld((const T*)p.b, idx);
-        al = p.A_log[h];
-        dt = p.dt_bias[h];
+        gi.x = io::ld((const T*)p.a, idx);
+        gi.y = io::ld((const T*)p.b, idx);
+        gi.z = p.A_log[h];
+        gi.w = p.dt_bias[h];
       }
     }
+    return gi;
   };
   // the first batch's gate inputs go out before the rows, so their latency hides there
-  float ga0, gb0, al0, dt0;
-  gate_in(0, ga0, gb0, al0, dt0);
+  const float4 gin0 = gate_in(0);
 
   // ---- phase 0: K and Q rows to LDS, row norms (16 lanes of a DPP row share a row)
   if constexpr (CONV) {
@@ -762,15 +777,14 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
     // ---- gates of value heads hb .. hb+3 (wave w: head hb + w, lane: token)
     __syncthreads();     // K/Q rows (phase 0) or the previous heads' T are no longer read
     {
-      float ga = ga0, gb = gb0, al = al0, dt = dt0;
-      if (hb > 0) gate_in(hb, ga, gb, al, dt);
+      const float4 gin = hb > 0 ? gate_in(hb) : gin0;
       float g = 0.f, beta = 0.f;
       if (hb + wave < r && lane < L) {
         if (p.g_opt) {
-          g = ga;
-          beta = gb;
+          g = gin.x;
+          beta = gin.y;
         } else {
-          gate_pair(ga, gb, al, dt, g, beta);
+          gate_pair(gin.x, gin.y, gin.z, gin.w, g, beta);
         }
       }
       g = wave_prefix_sum(g);       // in-chunk cumulative log decay (padding adds 0)

@@ -171,7 +171,7 @@ gdn_status_t gdn_chunk_prefill(const void* q, const void* k, const void* v, int6
  *
  * Arguments and errors as for gdn_chunk_prefill, and INVALID_ARG when the workspace
  * the sizes need (gdn_chunk_prefill_workspace_size) exceeds GDN_NOALLOC_SCRATCH_BYTES
- * (about 4000 tokens of one sequence at 16 key / 32 value heads, bf16 io).
+ * (about 6,700 tokens of one sequence at 16 key / 32 value heads, bf16 io).
  */
 #define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 gdn_status_t gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
