@@ -301,8 +301,10 @@ def replay_leg(reps: int, warmup: int) -> dict:
 
 
 def prefill_configs_leg(reps: int) -> dict:
-    """Beside the step: the chunked core (gdn_chunk_prefill) and the fused prefill layer
-    (gdn_conv_chunk_prefill -> gdn_gated_rmsnorm) on the three other prefill workloads: the
+    """Beside the step: the chunked core (gdn_chunk_prefill) and the prefill layer in one call
+    (gdn_prefill_layer), in two (gdn_conv_chunk_prefill -> gdn_gated_rmsnorm) and in three
+    (gdn_conv1d_fwd -> gdn_chunk_prefill -> gdn_gated_rmsnorm) on the three other prefill
+    workloads: the
     0.8B shape at T=256 with fp32 io, the 397B-A17B shape at T=32768 (one sequence) and the
     9B shape over 64 packed sequences of seeded lengths in [16, 2048] with carried recurrent
     and conv states.  Each call is timed
@@ -321,7 +323,7 @@ def prefill_configs_leg(reps: int) -> dict:
     from hybrid_linear_attention_causal_amd import synth
     from hybrid_linear_attention_causal_amd._lib import (gdn_chunk_prefill, gdn_conv1d_fwd,
                                                          gdn_conv_chunk_prefill,
-                                                         gdn_gated_rmsnorm)
+                                                         gdn_gated_rmsnorm, gdn_prefill_layer)
     from hybrid_linear_attention_causal_amd.mixer import qkv_views
 
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
@@ -366,6 +368,10 @@ def prefill_configs_leg(reps: int) -> dict:
         def chunk():
             gdn_chunk_prefill(q, k, v, a, b, A_log, dt, o, hk, hv, cu, s_in, s_out, workspace=ws)
 
+        def layer():
+            gdn_prefill_layer(x, w, y, a, b, A_log, dt, o, z, nw, yn, hk, hv, cu, cs_in, cs_out,
+                              s_in, s_out, workspace=ws)
+
         def norm():
             gdn_gated_rmsnorm(o, z, nw, yn)
 
@@ -386,6 +392,7 @@ def prefill_configs_leg(reps: int) -> dict:
             return statistics.median(ts)
 
         fused_ms, norm_ms, conv_ms, chunk_ms = med(fused), med(norm), med(conv), med(chunk)
+        layer_ms = med(layer)
         flops = chunk_core_flops(N, hk, hv, seqlens)
         tf = flops / (chunk_ms * 1e-3) / 1e12
         name = {0: "Qwen3.5-0.8B GDN layer prefill T=256 (B=1), fp32 io",
@@ -399,7 +406,9 @@ def prefill_configs_leg(reps: int) -> dict:
                                        "unit": "TFLOP/s", "frac": tf * 1e12 / PEAK_BF16_FLOPS,
                                        "algorithmic_per_launch": flops},
             "conv_chunk_prefill_ms": fused_ms, "prefill_norm_ms": norm_ms,
-            "layer_tokens_per_s": N / ((fused_ms + norm_ms) * 1e-3),
+            "prefill_layer_ms": layer_ms,
+            "layer_tokens_per_s": N / (layer_ms * 1e-3),
+            "layer_two_calls_tokens_per_s": N / ((fused_ms + norm_ms) * 1e-3),
             "conv1d_ms": conv_ms,
             "layer_unfused_tokens_per_s": N / ((conv_ms + chunk_ms + norm_ms) * 1e-3)}
         del x, y, z, o, yn, ws, s_out, cs_out, s_in, cs_in, q, k, v

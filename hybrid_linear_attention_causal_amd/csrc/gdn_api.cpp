@@ -202,30 +202,45 @@ gdn_status_t gdn_chunk_prefill_noalloc(const void* q, const void* k, const void*
                             io, stream);
 }
 
-gdn_status_t gdn_conv_chunk_prefill(const void* x, const float* conv_w, const void* conv_state_in,
-                                    void* conv_state_out, void* y, const void* a, const void* b,
-                                    const float* A_log, const float* dt_bias, const float* g_opt,
-                                    const float* beta_opt, const float* state_in,
-                                    float* state_out, void* o, const int32_t* cu_seqlens, int Ns,
-                                    int64_t N, int Hk, int Hv, int dk, int dv, int K, float scale,
-                                    int use_qk_l2norm, void* workspace, size_t ws_bytes,
-                                    gdn_dtype_t io, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// validation and launch shared by gdn_conv_chunk_prefill and gdn_prefill_layer (z, norm_w,
+// y: the gated norm of the core output, or all NULL)
+gdn_status_t conv_chunk_impl(const char* name, const void* x, const float* conv_w,
+                             const void* conv_state_in, void* conv_state_out, void* y,
+                             const void* a, const void* b, const float* A_log,
+                             const float* dt_bias, const float* g_opt, const float* beta_opt,
+                             const float* state_in, float* state_out, void* o, const void* z,
+                             const float* norm_w, float eps, void* yn,
+                             const int32_t* cu_seqlens, int Ns, int64_t N, int Hk, int Hv, int dk,
+                             int dv, int K, float scale, int use_qk_l2norm, void* workspace,
+                             size_t ws_bytes, gdn_dtype_t io, void* stream) {
   g_err[0] = 0;
-  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: unknown io dtype %d", (int)io);
-  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "conv_chunk_prefill: kernel width %d (only 4)", K);
+  if (!io_ok(io)) return fail(GDN_ERR_INVALID_ARG, "%s: unknown io dtype %d", name, (int)io);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "%s: kernel width %d (only 4)", name, K);
   if (Hk < 1 || Hv < 1 || dk != 128 || dv != 128)
     return fail(dk != 128 || dv != 128 ? GDN_ERR_UNSUPPORTED : GDN_ERR_INVALID_ARG,
-                "conv_chunk_prefill: Hk=%d Hv=%d dk=%d dv=%d", Hk, Hv, dk, dv);
+                "%s: Hk=%d Hv=%d dk=%d dv=%d", name, Hk, Hv, dk, dv);
   const int64_t cq = 2LL * Hk * dk + (int64_t)Hv * dv;
   if (cq > GDN_MAX_ROW_STRIDE)
-    return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: %lld conv channels", (long long)cq);
+    return fail(GDN_ERR_INVALID_ARG, "%s: %lld conv channels", name, (long long)cq);
   if (N > 0 && (!x || !conv_w || !y))
-    return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: NULL x, conv_w or y");
+    return fail(GDN_ERR_INVALID_ARG, "%s: NULL x, conv_w or y", name);
   if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)) || (conv_w && !aligned(conv_w, 16)) ||
       (conv_state_in && !aligned(conv_state_in, 16)) ||
       (conv_state_out && !aligned(conv_state_out, 16)))
-    return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: pointers must be 16-byte aligned");
-  if (x && y && x == y) return fail(GDN_ERR_INVALID_ARG, "conv_chunk_prefill: y must not alias x");
+    return fail(GDN_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", name);
+  if (x && y && x == y) return fail(GDN_ERR_INVALID_ARG, "%s: y must not alias x", name);
+  if (yn) {
+    if (!(eps >= 0.f)) return fail(GDN_ERR_INVALID_ARG, "%s: eps=%g", name, (double)eps);
+    if (N > 0 && (!z || !norm_w))
+      return fail(GDN_ERR_INVALID_ARG, "%s: NULL z or norm_w", name);
+    if ((z && !aligned(z, 16)) || (norm_w && !aligned(norm_w, 16)) || !aligned(yn, 16))
+      return fail(GDN_ERR_INVALID_ARG, "%s: z, norm_w and the norm output must be 16-byte aligned",
+                  name);
+  }
   const size_t esz = io == GDN_BF16 ? 2 : 4;
   const char* yb = static_cast<const char*>(y);
   gdn::ChunkArgs args{yb, yb ? yb + (size_t)Hk * dk * esz : nullptr,
@@ -237,8 +252,45 @@ gdn_status_t gdn_conv_chunk_prefill(const void* x, const float* conv_w, const vo
                       // chunk-less sequence to cover) and no in-place state: the prep
                       // writes the final conv state itself
                       (io == GDN_BF16 && conv_state_out && Ns == 1 && N > 0 && !cu_seqlens &&
-                       conv_state_out != conv_state_in) ? 1 : 0};
-  return chunk_prefill_impl("conv_chunk_prefill", args, dk, dv, workspace, ws_bytes, io, stream);
+                       conv_state_out != conv_state_in) ? 1 : 0,
+                      z, norm_w, yn, eps};
+  return chunk_prefill_impl(name, args, dk, dv, workspace, ws_bytes, io, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_conv_chunk_prefill(const void* x, const float* conv_w, const void* conv_state_in,
+                                    void* conv_state_out, void* y, const void* a, const void* b,
+                                    const float* A_log, const float* dt_bias, const float* g_opt,
+                                    const float* beta_opt, const float* state_in,
+                                    float* state_out, void* o, const int32_t* cu_seqlens, int Ns,
+                                    int64_t N, int Hk, int Hv, int dk, int dv, int K, float scale,
+                                    int use_qk_l2norm, void* workspace, size_t ws_bytes,
+                                    gdn_dtype_t io, void* stream) {
+  return conv_chunk_impl("conv_chunk_prefill", x, conv_w, conv_state_in, conv_state_out, y, a, b,
+                         A_log, dt_bias, g_opt, beta_opt, state_in, state_out, o, nullptr,
+                         nullptr, 0.f, nullptr, cu_seqlens, Ns, N, Hk, Hv, dk, dv, K, scale,
+                         use_qk_l2norm, workspace, ws_bytes, io, stream);
+}
+
+gdn_status_t gdn_prefill_layer(const void* x, const float* conv_w, const void* conv_state_in,
+                               void* conv_state_out, void* y_conv, const void* a, const void* b,
+                               const float* A_log, const float* dt_bias, const float* g_opt,
+                               const float* beta_opt, const float* state_in, float* state_out,
+                               void* o, const void* z, const float* norm_w, float eps, void* y,
+                               const int32_t* cu_seqlens, int Ns, int64_t N, int Hk, int Hv,
+                               int dk, int dv, int K, float scale, int use_qk_l2norm,
+                               void* workspace, size_t ws_bytes, gdn_dtype_t io, void* stream) {
+  if (N > 0 && !y) {
+    g_err[0] = 0;
+    return fail(GDN_ERR_INVALID_ARG, "prefill_layer: NULL norm output y");
+  }
+  return conv_chunk_impl("prefill_layer", x, conv_w, conv_state_in, conv_state_out, y_conv, a, b,
+                         A_log, dt_bias, g_opt, beta_opt, state_in, state_out, o, z, norm_w, eps,
+                         y, cu_seqlens, Ns, N, Hk, Hv, dk, dv, K,
+                         scale, use_qk_l2norm, workspace, ws_bytes, io, stream);
 }
 
 namespace {

@@ -1388,11 +1388,14 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) asm volatile("" : "+v"(w[it]));
+    // (a wave-uniform base and a 32-bit element offset: no 64-bit addresses per lane)
+    T* const ob = og0 + t0 * o_stride;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int idx = tid + Z::THR * it;
       const int row = idx / WPR, c8 = idx % WPR;
-      if (row < L) *reinterpret_cast<u32x4*>(og0 + (t0 + row) * o_stride + c8 * 8) = w[it];
+      if (row < L)
+        *reinterpret_cast<u32x4*>(ob + (uint32_t)(row * (uint32_t)o_stride + c8 * 8)) = w[it];
     }
   };
 
@@ -1856,6 +1859,9 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
 
     wait_vmem();
     lds_barrier();     // (1) chunk n's copies and the state slabs are in LDS
+    // chunk n+1's fragments of this wave's role, a whole chunk ahead of the wait at the next
+    // barrier (1): the previous contents of nxt were last read in chunk n-1
+    load_ops(na, nxt);
     if (!chain && n > 0) store_o(n - 1);
 
     f32x4 QS;          // output waves: Q S of row tile j
@@ -1947,7 +1953,6 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
       stage_qfv(na);
     }
     lds_barrier();     // (3) U tiles exchanged; every wave has read the R tiles
-    load_ops(na, nxt);   // chunk n+1's fragments of this wave's role
 
     if (chain) {
       // ---- B (chain): S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U for
@@ -2137,7 +2142,12 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
 }
 
 hipError_t launch_chunk_prefill(const ChunkArgs& a, void* ws, int io, hipStream_t s) {
-  return io == IO_BF16 ? chunk_impl<IO_BF16>(a, ws, s) : chunk_impl<IO_F32>(a, ws, s);
+  hipError_t e = io == IO_BF16 ? chunk_impl<IO_BF16>(a, ws, s) : chunk_impl<IO_F32>(a, ws, s);
+  if (e != hipSuccess || a.yn == nullptr) return e;
+  // the gated norm of the stored core output, as its own kernel: fused into the output
+  // stores of the sweep it measured slower than this separate pass over o and z
+  const NormArgs na{a.o, a.z, a.norm_w, a.yn, a.N * a.Hv, a.eps};
+  return launch_gated_rmsnorm(na, io, s);
 }
 
 }  // namespace gdn

@@ -52,6 +52,13 @@ struct ChunkArgs {
   int Cq;
   int conv_state_in_prep;   // one non-empty sequence, conv_state_out not aliasing the input:
                             // the prep workgroup of the last chunk writes the final state
+  // gated norm of the core output (yn != NULL): yn = norm_w * o / sqrt(mean(o^2) + eps) *
+  // silu(z) per (token, value head) row, o taken as stored; z, yn [N, Hv, 128] io.  Formed by
+  // the norm kernel after the core, on the same stream.
+  const void* z;
+  const float* norm_w;
+  void* yn;
+  float eps;
 };
 
 struct StepArgs {

@@ -1,6 +1,6 @@
 """Thin helpers that allocate outputs with torch and chain the libgdn calls.
 
-prefill_layer:  conv1d+SiLU -> chunked delta rule (one call by default) -> z-gated RMSNorm
+prefill_layer:  conv1d+SiLU -> chunked delta rule -> z-gated RMSNorm (one call by default)
 decode_step:    recurrent step (conv + delta rule, in place) + z-gated RMSNorm, fused in one
                 launch by default
 DecodeGraph:    n decode steps captured once as a HIP graph, replayed as one launch
@@ -10,7 +10,7 @@ from __future__ import annotations
 import torch
 
 from ._lib import (gdn_chunk_prefill, gdn_chunk_prefill_workspace_size, gdn_conv1d_fwd,
-                   gdn_conv_chunk_prefill, gdn_gated_rmsnorm, gdn_recurrent_step,
+                   gdn_gated_rmsnorm, gdn_prefill_layer, gdn_recurrent_step,
                    gdn_recurrent_step_norm)
 
 D = 128
@@ -24,8 +24,8 @@ def qkv_views(y: torch.Tensor, Hk: int, Hv: int):
 def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens=None,
                   conv_state_in=None, state_in=None, eps=1e-6, want_states=True, bufs=None,
                   stream=None, fused=True):
-    """x [N, Cq] io; z [N, Hv*128] io.  Returns a dict of device tensors.  fused: the conv
-    and the chunked core in one call (gdn_conv_chunk_prefill), else two calls."""
+    """x [N, Cq] io; z [N, Hv*128] io.  Returns a dict of device tensors.  fused: the conv,
+    the chunked core and the gated norm in one call (gdn_prefill_layer), else three calls."""
     N, Cq = x.shape
     Ns = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
     dev, dt = x.device, x.dtype
@@ -48,18 +48,18 @@ def prefill_layer(x, conv_w, a, b, A_log, dt_bias, z, norm_w, Hk, Hv, cu_seqlens
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         bufs["workspace"] = ws
+    yn = bufs.get("y")
+    if yn is None:
+        yn = torch.empty_like(o)
     if fused:
-        gdn_conv_chunk_prefill(x, conv_w, y, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens,
-                               conv_state_in, cs_out, state_in, s_out, workspace=ws,
-                               stream=stream)
+        gdn_prefill_layer(x, conv_w, y, a, b, A_log, dt_bias, o, z, norm_w, yn, Hk, Hv,
+                          cu_seqlens, conv_state_in, cs_out, state_in, s_out, eps=eps,
+                          workspace=ws, stream=stream)
     else:
         gdn_conv1d_fwd(x, conv_w, y, cu_seqlens, conv_state_in, cs_out, stream=stream)
         gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens, state_in, s_out,
                           workspace=ws, stream=stream)
-    yn = bufs.get("y")
-    if yn is None:
-        yn = torch.empty_like(o)
-    gdn_gated_rmsnorm(o, z, norm_w, yn, eps, stream=stream)
+        gdn_gated_rmsnorm(o, z, norm_w, yn, eps, stream=stream)
     return {"y_conv": y, "o": o, "y": yn, "conv_state_out": cs_out, "state_out": s_out}
 
 

@@ -214,6 +214,34 @@ gdn_status_t gdn_conv_chunk_prefill(const void* x, const float* conv_w, const vo
                                     gdn_dtype_t io, void* stream);
 
 /*
+ * gdn_prefill_layer -- the whole prefill layer in one call: gdn_conv1d_fwd, the chunked
+ * delta rule and gdn_gated_rmsnorm, i.e. gdn_conv_chunk_prefill followed by
+ *   y[t, h, :] = norm_w * o[t, h, :] / sqrt(mean(o[t, h, :]^2) + eps) * silu(z[t, h, :])
+ * on the core output o as stored (rounded to io): the norm kernel runs after the core on the
+ * same stream, so y equals the result of the separate calls bit for bit.  (The
+ * conv, the delta rule and the z-gated norm are the steps of one linear-attention layer:
+ * llm-arch-viz Qwen3.5-9B page, module tree of Qwen3_5GatedDeltaNet, with
+ * Qwen3_5RMSNormGated 128.)
+ *
+ *   z                [N, Hv*dv]       io      gate input
+ *   norm_w           [dv]             fp32    norm weight (applied directly)
+ *   eps              >= 0 (the family's 1e-6)
+ *   y                [N, Hv, dv]      io      norm output (may alias o)
+ *   o                [N, Hv, dv]      io      core output, written
+ * All other arguments, the workspace (gdn_chunk_prefill_workspace_size) and the errors as
+ * for gdn_conv_chunk_prefill; also INVALID_ARG for NULL y, z or norm_w with N > 0, eps < 0,
+ * or z, norm_w, y not 16-byte aligned.
+ */
+gdn_status_t gdn_prefill_layer(const void* x, const float* conv_w, const void* conv_state_in,
+                               void* conv_state_out, void* y_conv, const void* a, const void* b,
+                               const float* A_log, const float* dt_bias, const float* g_opt,
+                               const float* beta_opt, const float* state_in, float* state_out,
+                               void* o, const void* z, const float* norm_w, float eps, void* y,
+                               const int32_t* cu_seqlens, int Ns, int64_t N, int Hk, int Hv,
+                               int dk, int dv, int K, float scale, int use_qk_l2norm,
+                               void* workspace, size_t ws_bytes, gdn_dtype_t io, void* stream);
+
+/*
  * gdn_recurrent_step -- one decode token for each of B independent sequences,
  * updating the conv state and the recurrent state IN PLACE.
  * (KerasFormers Qwen page, "Generation": decode carries the per-layer conv

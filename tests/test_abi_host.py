@@ -12,6 +12,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
 
 EXPECTED = {"gdn_last_error", "gdn_version", "gdn_conv1d_fwd", "gdn_chunk_prefill_workspace_size",
             "gdn_chunk_prefill", "gdn_chunk_prefill_noalloc", "gdn_conv_chunk_prefill",
+            "gdn_prefill_layer",
             "gdn_recurrent_step", "gdn_recurrent_step_bf16_state", "gdn_recurrent_step_slots",
             "gdn_recurrent_step_norm", "gdn_gated_rmsnorm"}
 
@@ -212,4 +213,26 @@ def test_noalloc_rejects_a_workspace_beyond_its_array_before_any_launch():
     args = [P, P, P, 4096, 4096, 4096, P, P, P, P, None, None, None, None, P, None, 1, 8192,
             16, 32, 128, 128, 0.0, 1, 1, None]
     assert L.gdn_chunk_prefill_noalloc(*args) == _lib.GDN_ERR_INVALID_ARG
+    assert "workspace" in _msg()
+
+
+def _layer(**kw):
+    args = dict(x=P, w=P, cs_in=None, cs_out=None, y=ctypes.c_void_p(32), a=P, b=P, A_log=P,
+                dt_bias=P, g=None, beta=None, s_in=None, s_out=None, o=ctypes.c_void_p(48),
+                z=P, nw=P, eps=1e-6, yn=ctypes.c_void_p(64), cu=None, Ns=1, N=64, Hk=16, Hv=32,
+                dk=128, dv=128, K=4, scale=0.0, l2=1, ws=None, ws_bytes=0, io=1)
+    args.update(kw)
+    return _L().gdn_prefill_layer(*args.values(), None)
+
+
+def test_prefill_layer_rejects():
+    assert _layer(yn=None) == _lib.GDN_ERR_INVALID_ARG
+    assert "norm output" in _msg()
+    assert _layer(z=None) == _lib.GDN_ERR_INVALID_ARG
+    assert "z or norm_w" in _msg()
+    assert _layer(eps=-1.0) == _lib.GDN_ERR_INVALID_ARG
+    assert _layer(yn=ctypes.c_void_p(24)) == _lib.GDN_ERR_INVALID_ARG
+    assert "aligned" in _msg()
+    assert _layer(K=3) == _lib.GDN_ERR_UNSUPPORTED
+    assert _layer() == _lib.GDN_ERR_INVALID_ARG     # no workspace
     assert "workspace" in _msg()

@@ -186,3 +186,44 @@ def test_fused_empty_sequence_passes_states_through():
     torch.cuda.synchronize()
     assert torch.equal(cs_out, cs_in)
     assert torch.equal(s_out, s_in)
+
+
+@pytest.mark.parametrize("hk,hv,lens", [
+    (2, 4, LENS),            # row-split sweep
+    (2, 4, LENS * 2),        # 4-wave sweep
+    (2, 4, LENS * 4),        # 8-wave sweep
+    (4, 8, LENS * 24),       # 288 sequences, 8-wave sweep
+])
+def test_prefill_layer_equals_conv_chunk_then_norm(hk, hv, lens):
+    """gdn_prefill_layer (conv + chunked core + gated norm in one call) against
+    gdn_conv_chunk_prefill followed by gdn_gated_rmsnorm: every output bit for bit, on each
+    sweep shape."""
+    io = "bf16"
+    inp, d = _inputs(hk, hv, io, 80 + len(lens), lens)
+    x = d["x"]
+    N = x.shape[0]
+    Ns = d["cu"].numel() - 1
+    z = to_dev(inp["z"], io).view(N, hv, D)
+    nw = f32_dev(inp["norm_w"])
+    outs = []
+    for one_call in (True, False):
+        y = torch.empty_like(x)
+        o = torch.empty((N, hv, D), dtype=x.dtype, device="cuda")
+        yn = torch.full_like(o, 3.0)
+        s_out = torch.empty((Ns, hv, D, D), device="cuda")
+        cs_out = torch.empty_like(d["conv_state_in"])
+        if one_call:
+            gdn.gdn_prefill_layer(x, d["conv_w"], y, d["a"], d["b"], d["A_log"], d["dt_bias"], o,
+                                  z, nw, yn, hk, hv, d["cu"], d["conv_state_in"], cs_out,
+                                  d["state_in"], s_out)
+        else:
+            gdn.gdn_conv_chunk_prefill(x, d["conv_w"], y, d["a"], d["b"], d["A_log"],
+                                       d["dt_bias"], o, hk, hv, d["cu"], d["conv_state_in"],
+                                       cs_out, d["state_in"], s_out)
+            gdn.gdn_gated_rmsnorm(o, z, nw, yn)
+        outs.append((y, o, yn, s_out, cs_out))
+    torch.cuda.synchronize()
+    for name, u, v in zip(("conv y", "o", "norm y", "state", "conv state"), *outs):
+        assert torch.equal(u, v), name
+    ref = G.layer(inp)
+    assert_out(host(outs[0][2]), ref["y_exact"], io, "layer y", upstream_bf16=2)
