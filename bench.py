@@ -50,15 +50,21 @@ KERNEL_SOURCES = {"gdn_chunk_prefill": ("gdn_chunk.hip", "gdn_common.hpp", "gdn_
                   "gdn_recurrent_step": ("gdn_step.hip", "gdn_common.hpp", "gdn_launch.hpp"),
                   "gdn_recurrent_step_bf16_state": ("gdn_step.hip", "gdn_common.hpp",
                                                     "gdn_launch.hpp")}
-# HBM bytes per launch on this workload from rocprofv3 PMC FETCH_SIZE and WRITE_SIZE,
-# each scaled by what the counter reads for a plain 256 MiB copy (the summary with the
-# commands is profiles/pmc_bytes_bench_qwen35_9b_prefill_T4096_decode_B256.txt).  Each
-# figure belongs to the kernel sources with the given digest and is not reported once
-# they change.
-MEASURED_TRAFFIC = {"gdn_chunk_prefill": ("80f8bcab896522b8", 255.1e6),
-                    "gdn_conv_chunk_prefill": ("7cef106a0a573938", 383.5e6),
-                    "gdn_recurrent_step": ("659bfa1d4d7b1d7e", 1105.8e6),
-                    "gdn_recurrent_step_bf16_state": ("659bfa1d4d7b1d7e", 568.8e6)}
+# HBM bytes per launch from rocprofv3 PMC FETCH_SIZE and WRITE_SIZE, each scaled by what
+# the counter reads for a plain 256 MiB copy (the summaries with the commands are
+# profiles/pmc_bench_qwen35_9b_prefill_T4096_decode_B256.txt and profiles/pmc_prefill_*.txt):
+# key -> (call whose sources the figure belongs to, their digest, bytes).  A figure is not
+# reported once those sources change.
+MEASURED_TRAFFIC = {
+    "gdn_chunk_prefill": ("gdn_chunk_prefill", "667153cc626d0e94", 247.9e6),
+    "gdn_conv_chunk_prefill": ("gdn_conv_chunk_prefill", "e1d80e521fefdb93", 373.4e6),
+    "gdn_recurrent_step": ("gdn_recurrent_step", "1b51b87b676685fb", 1105.9e6),
+    "gdn_recurrent_step_bf16_state": ("gdn_recurrent_step_bf16_state", "1b51b87b676685fb", 568.9e6),
+    # the chunk call on the prefill_configs workloads
+    "gdn_chunk_prefill@l0_qwen3.5-0.8b_T256_fp32": ("gdn_chunk_prefill", "667153cc626d0e94", 24.3e6),
+    "gdn_chunk_prefill@l3_qwen3.5-397b_T32768_bf16": ("gdn_chunk_prefill", "667153cc626d0e94", 3869.9e6),
+    "gdn_chunk_prefill@l4_qwen3.5-9b_varlen64_bf16": ("gdn_chunk_prefill", "667153cc626d0e94", 4447.7e6),
+}
 
 
 def source_digest(kernel: str) -> str:
@@ -70,8 +76,10 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    digest, nbytes = MEASURED_TRAFFIC[kernel]
+def measured_traffic(key: str):
+    if key not in MEASURED_TRAFFIC:
+        return None
+    kernel, digest, nbytes = MEASURED_TRAFFIC[key]
     return nbytes if source_digest(kernel) == digest else None
 
 
@@ -404,6 +412,7 @@ def prefill_configs_leg(reps: int) -> dict:
             "roofline_chunk_prefill": {"kernel": "gdn_chunk_prefill", "bound": "mfma",
                                        "achieved": tf, "peak": PEAK_BF16_FLOPS / 1e12,
                                        "unit": "TFLOP/s", "frac": tf * 1e12 / PEAK_BF16_FLOPS,
+                                       "traffic": measured_traffic(f"gdn_chunk_prefill@{wl.name}"),
                                        "algorithmic_per_launch": flops},
             "conv_chunk_prefill_ms": fused_ms, "prefill_norm_ms": norm_ms,
             "prefill_layer_ms": layer_ms,
