@@ -1126,17 +1126,6 @@ __device__ __forceinline__ void dma_rows(const uint8_t* base, uint32_t row_bytes
 // wait for all of this wave's outstanding vector-memory operations (incl. LDS DMA)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Workgroup barrier that orders LDS accesses only: this wave's LDS reads and writes have
-// completed (lgkmcnt 0) when it arrives, while its global loads and LDS DMA copies stay
-// in flight (a __syncthreads() would also wait for those).  The signal fences keep the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // LDS buffers of the sweep, one __shared__ object each so that the compiler can tell
 // the DMA destinations of one phase from the buffers the other phase reads.
 template <int IO, int NW>

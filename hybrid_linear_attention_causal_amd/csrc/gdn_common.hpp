@@ -130,6 +130,19 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------- barriers
+// Workgroup barrier that orders LDS accesses only: this wave's LDS reads and writes have
+// completed (lgkmcnt 0) when it arrives, while its global loads, stores and LDS DMA
+// copies stay in flight (a __syncthreads() also waits for those: vmcnt 0).  For kernels
+// whose barriers order no global memory between threads.  The signal fences keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------- reductions
 // sum over groups of W consecutive lanes (W a power of two <= 64)
 template <int W>

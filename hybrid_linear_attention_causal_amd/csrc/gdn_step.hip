@@ -11,6 +11,11 @@
 // every conv-state element is read and rewritten by exactly one thread, and it
 // runs the r value heads HPP (1 or 2) at a time with 256 threads per head.
 //
+// Barriers order LDS only (lds_barrier: no wait for global loads or stores), since no
+// thread reads global memory another thread of the workgroup writes: each conv-state
+// channel is read and rewritten by one thread, and every exchange goes through LDS.  So
+// the state stores drain while the output and the norm are formed.
+//
 // State traffic (the roofline): each head's 128 x 128 state (fp32, or bf16 in the
 // bf16-state variant: read, computed in fp32, rounded back) is read once and written
 // once, with nontemporal loads and stores (the state is touched once per step, so it
@@ -31,6 +36,36 @@ constexpr int SD = 128;  // head width (dk = dv)
 // bf16 variant holds half the registers).  Nontemporal: the state is touched once per step.
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 template <bool SBF> struct StateQuad;
+
+// An io value's bits in a 32-bit register (bf16: zero-extended, fp32: as is), its value,
+// and the io value of such bits
+template <int IO>
+__device__ __forceinline__ uint32_t raw_bits(const typename Io<IO>::T* p, int64_t i) {
+  if constexpr (IO == IO_BF16) return (uint32_t)p[i];
+  else return __float_as_uint(p[i]);
+}
+// the aligned 32-bit word holding element i (bf16: two elements; the row bases are
+// 16-byte aligned and the channel counts even), and element i's bits from it
+template <int IO>
+__device__ __forceinline__ uint32_t raw_word(const typename Io<IO>::T* p, int64_t i) {
+  if constexpr (IO == IO_BF16) return *reinterpret_cast<const uint32_t*>(p + (i & ~(int64_t)1));
+  else return __float_as_uint(p[i]);
+}
+template <int IO>
+__device__ __forceinline__ uint32_t word_bits(uint32_t w, int64_t i) {
+  if constexpr (IO == IO_BF16) return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+  else return w;
+}
+template <int IO>
+__device__ __forceinline__ float from_raw_bits(uint32_t w) {
+  if constexpr (IO == IO_BF16) return __uint_as_float(w << 16);
+  else return __uint_as_float(w);
+}
+template <int IO>
+__device__ __forceinline__ typename Io<IO>::T raw_to_io(uint32_t w) {
+  if constexpr (IO == IO_BF16) return (u16)w;
+  else return __uint_as_float(w);
+}
 template <> struct StateQuad<false> {
   typedef f32x4 Raw;
   static __device__ __forceinline__ Raw ld(const void* base, uint32_t i) {
@@ -103,73 +138,136 @@ recurrent_step_kernel(StepArgs p) {
       return;   // uniform over the workgroup
     }
   }
+  // (the byte offset is wave-uniform: kept in scalar registers)
   auto head_state = [&](int h) {
-    return (char*)p.state + (((int64_t)slot * Hv + h) * SD) * SD * (SBF ? 2 : 4);
+    const uint64_t off = (uint64_t)(((int64_t)slot * Hv + h) * SD) * SD * (SBF ? 2 : 4);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)off);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(off >> 32));
+    return (char*)p.state + (((uint64_t)hi << 32) | lo);
   };
 
-  // issue the first pass's state loads before the conv so HBM latency overlaps it
+  // Loads complete in issue order (one counter per wave), so everything the conv and the
+  // gates need is issued first and the first pass's state after it: the conv then waits
+  // for its own inputs only, while the state streams in behind them.
+  const T* xb = (const T*)p.x + (int64_t)bseq * Cq;
+  T* cs = (T*)p.conv_state + (int64_t)slot * 3 * Cq;
+  const int nch = 256 + r * SD;
+  auto conv_channel = [&](int i) {
+    if (i < SD) return kh * SD + i;                                   // q channel
+    if (i < 2 * SD) return Hk * SD + kh * SD + (i - SD);              // k channel
+    return 2 * Hk * SD + kh * r * SD + (i - 2 * SD);                  // v channels
+  };
+  // Every load before the state's is held as raw bits and read only after the state's
+  // loads are issued (the empty asm statements below): a value widened or used inside
+  // its branch would make the wave wait for its load there, one round trip at a time.
+  // The loads below that not every thread needs are issued by all threads at a clamped
+  // (in-bounds) index: a load under a branch gets its register copied where the branch
+  // joins, which waits for it.
+  // the conv inputs of this thread's first channel (i = tid: there are at least as many
+  // channels as threads)
+  float4 cw0;
+  uint32_t cv0[4];
+  {
+    const int c = conv_channel(min(tid, nch - 1));
+    cw0 = *reinterpret_cast<const float4*>(p.w + (int64_t)c * 4);
+    cv0[0] = raw_word<IO>(cs, c);
+    cv0[1] = raw_word<IO>(cs, Cq + c);
+    cv0[2] = raw_word<IO>(cs, 2 * Cq + c);
+    cv0[3] = raw_word<IO>(xb, c);
+  }
+
+  // the gate inputs of the r value heads (threads 64 .. 64 + r - 1)
+  uint32_t gr_a = 0u, gr_b = 0u, gr_al = 0u, gr_dt = 0u;
+  if (tid >= 64 && tid < 64 + r) {
+    const int h = kh * r + (tid - 64);
+    if (p.g_opt) {
+      gr_a = __float_as_uint(p.g_opt[(int64_t)bseq * Hv + h]);
+      gr_b = __float_as_uint(p.beta_opt[(int64_t)bseq * Hv + h]);
+    } else {
+      gr_a = raw_bits<IO>((const T*)p.a, (int64_t)bseq * Hv + h);
+      gr_b = raw_bits<IO>((const T*)p.b, (int64_t)bseq * Hv + h);
+      gr_al = __float_as_uint(p.A_log[h]);
+      gr_dt = __float_as_uint(p.dt_bias[h]);
+    }
+  }
+
+  // the fused norm's z rows of the r heads (four values per thread, as raw 8-byte words:
+  // the first 256 HPP groups of four) and its weights, parked in LDS after the conv
+  constexpr int ZW = IO == IO_BF16 ? 1 : 2;
+  uint2 zw[ZW];
+  float4 wr;
+  if constexpr (NORM) {
+    const uint2* zp = reinterpret_cast<const uint2*>(
+        (const T*)p.z + ((int64_t)bseq * Hv + kh * r) * SD + min(tid, r * 32 - 1) * 4);
+#pragma unroll
+    for (int w = 0; w < ZW; ++w) zw[w] = zp[w];
+    wr = *reinterpret_cast<const float4*>(p.norm_w + min(tid, 31) * 4);
+  }
+
+  // the first pass's state, behind the loads above
+  __builtin_amdgcn_sched_barrier(0);
   typename SQ::Raw Sv[16];
   {
     const char* sb = head_state(kh * r + hl);
 #pragma unroll
     for (int i = 0; i < 16; ++i) Sv[i] = SQ::ld(sb, toff + i * SD);
   }
-
-  // the gate inputs of the r value heads (threads 64 .. 64 + r - 1), also loaded before
-  // the conv so that their latency hides under it
-  float gin_a = 0.f, gin_b = 0.f, gin_al = 0.f, gin_dt = 0.f;
-  if (tid >= 64 && tid < 64 + r) {
-    const int h = kh * r + (tid - 64);
-    if (p.g_opt) {
-      gin_a = p.g_opt[(int64_t)bseq * Hv + h];
-      gin_b = p.beta_opt[(int64_t)bseq * Hv + h];
-    } else {
-      gin_a = io::ld((const T*)p.a, (int64_t)bseq * Hv + h);
-      gin_b = io::ld((const T*)p.b, (int64_t)bseq * Hv + h);
-      gin_al = p.A_log[h];
-      gin_dt = p.dt_bias[h];
-    }
-  }
-
-  // the fused norm's z rows of the r heads (four values per thread; the first 256 HPP
-  // groups of four) and its weights, loaded with the conv inputs (whose wait covers them)
-  // and parked in LDS
-  float zr[4] = {0.f, 0.f, 0.f, 0.f};
-  float4 wr = make_float4(0.f, 0.f, 0.f, 0.f);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" : "+v"(cw0.x), "+v"(cw0.y), "+v"(cw0.z), "+v"(cw0.w));
+  asm volatile("" : "+v"(cv0[0]), "+v"(cv0[1]), "+v"(cv0[2]), "+v"(cv0[3]));
+  asm volatile("" : "+v"(gr_a), "+v"(gr_b), "+v"(gr_al), "+v"(gr_dt));
   if constexpr (NORM) {
-    if (tid < r * 32) {
-      const T* zp = (const T*)p.z + ((int64_t)bseq * Hv + kh * r) * SD + tid * 4;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) zr[c] = io::ld(zp, c);
-    }
-    if (tid < 32) wr = *reinterpret_cast<const float4*>(p.norm_w + tid * 4);
+    for (int w = 0; w < ZW; ++w) asm volatile("" : "+v"(zw[w].x), "+v"(zw[w].y));
+    asm volatile("" : "+v"(wr.x), "+v"(wr.y), "+v"(wr.z), "+v"(wr.w));
   }
+  const float gin_a = p.g_opt ? __uint_as_float(gr_a) : from_raw_bits<IO>(gr_a);
+  const float gin_b = p.g_opt ? __uint_as_float(gr_b) : from_raw_bits<IO>(gr_b);
+  const float gin_al = __uint_as_float(gr_al), gin_dt = __uint_as_float(gr_dt);
 
   // ---- conv window + SiLU for this group's channels; shift the conv state
-  const T* xb = (const T*)p.x + (int64_t)bseq * Cq;
-  T* cs = (T*)p.conv_state + (int64_t)slot * 3 * Cq;
-  const int nch = 256 + r * SD;
   for (int i = tid; i < nch; i += nthr) {
-    int c;
-    if (i < SD) c = kh * SD + i;                                   // q channel
-    else if (i < 2 * SD) c = Hk * SD + kh * SD + (i - SD);         // k channel
-    else c = 2 * Hk * SD + kh * r * SD + (i - 2 * SD);             // v channels
-    const float4 w4 = *reinterpret_cast<const float4*>(p.w + (int64_t)c * 4);
-    const T c0 = cs[c], c1 = cs[Cq + c], c2 = cs[2 * Cq + c], xc = xb[c];
-    const float f0 = io::ld(&c0, 0), f1 = io::ld(&c1, 0), f2 = io::ld(&c2, 0), fx = io::ld(&xc, 0);
+    const int c = conv_channel(i);
+    float4 w4;
+    uint32_t c0, c1, c2, xc;
+    if (i == tid) {
+      w4 = cw0;
+      c0 = word_bits<IO>(cv0[0], c);
+      c1 = word_bits<IO>(cv0[1], c);
+      c2 = word_bits<IO>(cv0[2], c);
+      xc = word_bits<IO>(cv0[3], c);
+    } else {
+      w4 = *reinterpret_cast<const float4*>(p.w + (int64_t)c * 4);
+      c0 = raw_bits<IO>(cs, c);
+      c1 = raw_bits<IO>(cs, Cq + c);
+      c2 = raw_bits<IO>(cs, 2 * Cq + c);
+      xc = raw_bits<IO>(xb, c);
+    }
+    const float f0 = from_raw_bits<IO>(c0), f1 = from_raw_bits<IO>(c1);
+    const float f2 = from_raw_bits<IO>(c2), fx = from_raw_bits<IO>(xc);
     float acc = w4.x * f0;
     acc = fmaf(w4.y, f1, acc);
     acc = fmaf(w4.z, f2, acc);
     acc = fmaf(w4.w, fx, acc);
     yv[i] = io::round(silu(acc));  // the conv output crosses the io boundary
-    cs[c] = c1;
-    cs[Cq + c] = c2;
-    cs[2 * Cq + c] = xc;
+    cs[c] = raw_to_io<IO>(c1);
+    cs[Cq + c] = raw_to_io<IO>(c2);
+    cs[2 * Cq + c] = raw_to_io<IO>(xc);
   }
   if constexpr (NORM) {
     if (tid < r * 32) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) zsh[tid * 4 + c] = zr[c];
+      for (int c = 0; c < 4; ++c) {
+        uint32_t b;
+        if constexpr (IO == IO_BF16) {
+          const uint32_t w = (c >> 1) ? zw[0].y : zw[0].x;
+          b = (c & 1) ? (w >> 16) : (w & 0xFFFFu);
+        } else {
+          const uint2 w = zw[c >> 1];
+          b = (c & 1) ? w.y : w.x;
+        }
+        zsh[tid * 4 + c] = from_raw_bits<IO>(b);
+      }
     }
     // more value heads than one z row per thread (r * 32 > threads): the rest of the
     // rows, strided over the workgroup
@@ -180,7 +278,7 @@ recurrent_step_kernel(StepArgs p) {
     }
     if (tid < 32) *reinterpret_cast<float4*>(&wsh[tid * 4]) = wr;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- L2 norms of q and k, gates of the r value heads
   if (tid < 64) {
@@ -204,7 +302,7 @@ recurrent_step_kernel(StepArgs p) {
     gsh[j] = expf(g);
     bsh[j] = beta;
   }
-  __syncthreads();
+  lds_barrier();
 
   const float rq = nsh[0], rk = nsh[1];
 
@@ -234,7 +332,7 @@ recurrent_step_kernel(StepArgs p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) red1[(hl * 4 + wv) * SD + cg * 4 + c] = pk[c];
     }
-    __syncthreads();
+    lds_barrier();
     if constexpr (SBF) {
       // keep the bf16 state packed across the exchange: without this the compiler keeps
       // the values unpacked for the first product alive for the update (64 more registers)
@@ -274,7 +372,7 @@ recurrent_step_kernel(StepArgs p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) red2[(hl * 4 + wv) * SD + cg * 4 + c] = po[c];
     }
-    __syncthreads();
+    lds_barrier();
     if (t256 < 32) {
       float ov[4];
 #pragma unroll
@@ -303,7 +401,7 @@ recurrent_step_kernel(StepArgs p) {
           io::st((T*)p.y + ob, c, wsh[cg * 4 + c] * (ov[c] * inv) * silu(zsh[j * SD + cg * 4 + c]));
       }
     }
-    __syncthreads();  // red1/red2 are reused by the next pass
+    lds_barrier();  // red1/red2 are reused by the next pass
   }
 }
 
