@@ -308,6 +308,64 @@ def replay_leg(reps: int, warmup: int) -> dict:
             "decode_graph_state_GBps": state_bytes * n / (graph_ms * 1e-3) / 1e9}
 
 
+def segment_scan_leg(reps: int) -> dict:
+    """Beside the step: the chunked core where it runs the intra-sequence scan (bf16 io, few
+    long chains whose row-split launch would fill at most half the compute units): one
+    sequence of 32768 tokens at the 9B layer's share under 8-way head sharding (2 key, 4
+    value heads) and at the 0.8B shape (16 and 16).  Timed as in the prefill_configs leg
+    (median of `reps` HIP-event timings, each after a 512 MiB overwrite), on device-drawn
+    inputs with the recipe's distributions."""
+    import math
+    import statistics
+
+    import torch
+
+    import hybrid_linear_attention_causal_amd as gdn
+    from hybrid_linear_attention_causal_amd.mixer import qkv_views
+
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, hk, hv, N in (("qwen3.5-9b_shard8_T32768_bf16", 2, 4, 32768),
+                            ("qwen3.5-0.8b_T32768_bf16", 16, 16, 32768)):
+        g = torch.Generator(device="cuda").manual_seed(9)
+        cq = (2 * hk + hv) * D
+        y = torch.randn(N, cq, device="cuda", generator=g).to(torch.bfloat16)
+        a = torch.randn(N, hv, device="cuda", generator=g).to(torch.bfloat16)
+        b = torch.randn(N, hv, device="cuda", generator=g).to(torch.bfloat16)
+        A_log = torch.rand(hv, device="cuda", generator=g) * math.log(16.0)
+        dt = torch.log(torch.expm1(1e-3 + 0.099 * torch.rand(hv, device="cuda", generator=g)))
+        s_in = 0.02 * torch.randn(1, hv, D, D, device="cuda", generator=g)
+        o = torch.empty(N, hv, D, dtype=torch.bfloat16, device="cuda")
+        s_out = torch.empty_like(s_in)
+        ws = torch.empty(gdn.gdn_chunk_prefill_workspace_size(N, 1, hk, hv, io=torch.bfloat16),
+                         dtype=torch.uint8, device="cuda")
+        q, k, v = qkv_views(y, hk, hv)
+
+        def call():
+            gdn.gdn_chunk_prefill(q, k, v, a, b, A_log, dt, o, hk, hv, None, s_in, s_out,
+                                  workspace=ws)
+
+        call()
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = statistics.median(ts)
+        flops = chunk_core_flops(N, hk, hv)
+        out[name] = {"Hk": hk, "Hv": hv, "tokens": N, "chunk_prefill_ms": ms,
+                     "tokens_per_s": N / (ms * 1e-3),
+                     "core_TFLOPs": flops / (ms * 1e-3) / 1e12,
+                     "frac_bf16_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS}
+        del y, a, b, o, ws, s_in, s_out, q, k, v
+        torch.cuda.empty_cache()
+    return out
+
+
 def prefill_configs_leg(reps: int) -> dict:
     """Beside the step: the chunked core (gdn_chunk_prefill) and the prefill layer in one call
     (gdn_prefill_layer), in two (gdn_conv_chunk_prefill -> gdn_gated_rmsnorm) and in three
@@ -589,6 +647,7 @@ def main():
                                    for i in range(args.steps)]))
     replay = replay_leg(args.steps, args.warmup)
     configs = prefill_configs_leg(args.steps)
+    segscan = segment_scan_leg(args.steps)
     prefill_ms = ms["conv_chunk_prefill"] + ms["prefill_norm"]
     tokens_per_s = N / (prefill_ms * 1e-3)
     prefill_u_ms = ms_u["conv1d"] + ms_u["chunk_prefill"] + ms_u["prefill_norm"]
@@ -647,6 +706,7 @@ def main():
             "algorithmic_per_launch": dbytes_bf},
         "replay": replay,
         "prefill_configs": configs,
+        "segment_scan": segscan,
         "cpu_baseline": None,
         "cpu_baseline_decode": None,
     }

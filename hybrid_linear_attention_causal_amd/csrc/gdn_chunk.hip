@@ -96,18 +96,33 @@ __host__ __device__ constexpr int64_t ws_krec_bytes(bool f32) {
   return f32 ? 4 * WS_ROWS_BYTES : 0;
 }
 
-// Intra-sequence scan (fp32 io): at most SEG_MAX segments per sequence, each of at least
+// Intra-sequence scan: at most SEG_MAX segments per sequence, each of at least
 // SEG_MIN_CHUNKS chunks on average, for at most SEG_MAX_CHAINS (sequence, head) chains;
-// the workspace reserves (SEG_MAX - 1) (A, B) pairs per chain when the chain count allows.
-// bf16 io never segments (few chains run the row-split sweep), so reserves nothing.
+// the workspace reserves (SEG_MAX - 1) (A, B) pairs per chain when the scan may run.
+// fp32 io: whenever the chain count allows.  bf16 io: only for at most SEG_BF16_MAX_CHAINS
+// chains averaging at least SEG_BF16_MIN_CHUNKS chunks, where the row-split sweep would
+// leave most compute units idle for a long walk.  A transition pass costs as much as a
+// normal one over the same chunks, so the scan pays only there (measured on MI355X, B = 1,
+// bf16: 1 to 16 chains at 32768 tokens 16-22% faster than the row-split sweep, 5-11% at
+// 16384, 10-45% slower at 8192 and below, and 30% slower with 32 chains, which the
+// row-split sweep spreads over every compute unit).
 constexpr int SEG_MAX = 8;
 constexpr int SEG_MIN_CHUNKS = 4;
 constexpr int64_t SEG_MAX_CHAINS = 64;
+constexpr int64_t SEG_BF16_MAX_CHAINS = 16;
+constexpr int64_t SEG_BF16_MIN_CHUNKS = 256;
 constexpr int64_t SEG_PAIR_BYTES = 2LL * DK * DV * 4;   // A then B, fp32
 
-static int64_t ws_seg_bytes(int Ns, int Hv, bool f32) {
+// bf16 io: few, long chains (the shape condition; the launch also needs the compute units)
+static bool bf16_seg_shape(int64_t N, int Ns, int Hv) {
   const int64_t chains = (int64_t)Ns * Hv;
-  return f32 && chains <= SEG_MAX_CHAINS ? (SEG_MAX - 1) * chains * SEG_PAIR_BYTES : 0;
+  return chains <= SEG_BF16_MAX_CHAINS && Ns > 0 && (N + CH - 1) / CH / Ns >= SEG_BF16_MIN_CHUNKS;
+}
+
+static int64_t ws_seg_bytes(int64_t N, int Ns, int Hv, bool f32) {
+  const int64_t chains = (int64_t)Ns * Hv;
+  const bool may = f32 ? chains <= SEG_MAX_CHAINS : bf16_seg_shape(N, Ns, Hv);
+  return may ? (SEG_MAX - 1) * chains * SEG_PAIR_BYTES : 0;
 }
 
 // Segments per sequence: enough to fill the compute units with the normal launch's two
@@ -125,7 +140,7 @@ static int seg_count(int64_t N, int Ns, int Hv, int64_t cus) {
 size_t chunk_workspace_bytes(int64_t N, int Ns, int Hk, int Hv, bool f32) {
   const int64_t cmax = ws_max_chunks(N, Ns);
   return (size_t)(ws_map_bytes(N, Ns) + cmax * Hv * ws_rec_bytes(true) + cmax * Hk * ws_krec_bytes(f32) +
-                  ws_seg_bytes(Ns, Hv, f32));
+                  ws_seg_bytes(N, Ns, Hv, f32));
 }
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -583,29 +598,42 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, c16 = lane & 15;
 
-  // raw gate inputs of value head kh_ r + hb + wave for this lane's token: {a or g, b or
-  // beta, A_log, dt_bias} (returned by value: references into branches would leave the
-  // four values in scratch memory)
+  // gate inputs of value head kh_ r + hb + wave for this lane's token: {a or g, b or
+  // beta, A_log, dt_bias}, as raw bits (a and b in the io dtype, the rest fp32): widening
+  // a loaded value where it is loaded would make the wave wait for it there (returned by
+  // value: references into branches would leave the four values in scratch memory)
   auto gate_in = [&](int hb) {
     const int jh = hb + wave;
-    float4 gi = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint4 gi = make_uint4(0u, 0u, 0u, 0u);
     if (jh < r) {
       const int h = kh_ * r + jh;
       const int64_t idx = (t0 + (lane < L ? lane : L - 1)) * Hv + h;
       if (p.g_opt) {
-        gi.x = p.g_opt[idx];
-        gi.y = p.beta_opt[idx];
+        gi.x = __float_as_uint(p.g_opt[idx]);
+        gi.y = __float_as_uint(p.beta_opt[idx]);
       } else {
-        gi.x = io::ld((const T*)p.a, idx);
-        gi.y = io::ld((const T*)p.b, idx);
-        gi.z = p.A_log[h];
-        gi.w = p.dt_bias[h];
+        if constexpr (F32) {
+          gi.x = __float_as_uint(((const float*)p.a)[idx]);
+          gi.y = __float_as_uint(((const float*)p.b)[idx]);
+        } else {
+          gi.x = ((const u16*)p.a)[idx];
+          gi.y = ((const u16*)p.b)[idx];
+        }
+        gi.z = __float_as_uint(p.A_log[h]);
+        gi.w = __float_as_uint(p.dt_bias[h]);
       }
     }
     return gi;
   };
+  // the raw bits as values
+  auto gate_vals = [&](uint4 gi) {
+    const bool raw_io = !p.g_opt && !F32;   // a and b as bf16 bits
+    return make_float4(raw_io ? __uint_as_float(gi.x << 16) : __uint_as_float(gi.x),
+                       raw_io ? __uint_as_float(gi.y << 16) : __uint_as_float(gi.y),
+                       __uint_as_float(gi.z), __uint_as_float(gi.w));
+  };
   // the first batch's gate inputs go out before the rows, so their latency hides there
-  const float4 gin0 = gate_in(0);
+  const uint4 gin0 = gate_in(0);
 
   // ---- phase 0: K and Q rows to LDS, row norms (16 lanes of a DPP row share a row)
   if constexpr (CONV) {
@@ -777,7 +805,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
     // ---- gates of value heads hb .. hb+3 (wave w: head hb + w, lane: token)
     __syncthreads();     // K/Q rows (phase 0) or the previous heads' T are no longer read
     {
-      const float4 gin = hb > 0 ? gate_in(hb) : gin0;
+      const float4 gin = gate_vals(hb > 0 ? gate_in(hb) : gin0);
       float g = 0.f, beta = 0.f;
       if (hb + wave < r && lane < L) {
         if (p.g_opt) {
@@ -2024,10 +2052,14 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   // records, or 8-wave ones, which form P themselves
   const int64_t pairs = (int64_t)a.Ns * a.Hv;
   const int64_t cus = a.cu_count > 0 ? a.cu_count : 256;
-  // bf16 io with few chains: the row-split sweep (eight 8-wave workgroups per chain)
-  const bool rowsplit = IO == IO_BF16 && pairs * rs::NBLK <= ROWSPLIT_CU_ROUNDS * cus;
-  // (only fp32 io has segment scratch in its workspace)
-  const int G = (rowsplit || IO == IO_BF16) ? 1 : seg_count(a.N, a.Ns, a.Hv, cus);
+  // bf16 io with few, long chains whose row-split launch would fill at most half the
+  // compute units: the intra-sequence scan (see SEG_BF16_MAX_CHAINS)
+  const bool bf16_seg = IO == IO_BF16 && bf16_seg_shape(a.N, a.Ns, a.Hv) &&
+                        2 * pairs * rs::NBLK <= cus && seg_count(a.N, a.Ns, a.Hv, cus) >= 3;
+  // bf16 io with few chains otherwise: the row-split sweep (eight 8-wave workgroups per chain)
+  const bool rowsplit = IO == IO_BF16 && !bf16_seg && pairs * rs::NBLK <= ROWSPLIT_CU_ROUNDS * cus;
+  // (segment scratch is in the workspace for fp32 io with few chains and for the bf16 scan)
+  const int G = (IO == IO_F32 || bf16_seg) ? seg_count(a.N, a.Ns, a.Hv, cus) : 1;
   const bool four = rowsplit || pairs * G * SweepSizes<IO, 4>::NBLK <= cus;
   // the chunk map of packed sequences (one sequence needs none: its chunks are in order)
   hipError_t e = hipSuccess;

@@ -105,9 +105,11 @@ gdn_status_t gdn_conv1d_fwd(const void* x, const float* w, void* y, const int32_
  * The workspace holds the chunk map of the packed sequences; for at most
  * ceil(N/64) + Ns 64-token chunks, per (chunk, value head) a 38912-byte record (the
  * chunk's 64 x 64 T' and P matrices as bf16 hi/lo parts plus per-token factors) and,
- * for fp32 io only, per (chunk, key head) the bf16 hi/lo K and Q rows (69632 bytes)
- * and, when at most 64 (sequence, value head) pairs are given, 7 segment-transition
- * pairs of 128 KB per pair for the intra-sequence scan.  Returns 0 for invalid sizes.
+ * for fp32 io only, per (chunk, key head) the bf16 hi/lo K and Q rows (69632 bytes);
+ * and, where the intra-sequence scan may run, 7 segment-transition pairs of 128 KB per
+ * (sequence, value head) pair: fp32 io with at most 64 pairs, bf16 io with at most 16
+ * pairs and sequences of at least 256 chunks on average (ceil(N/64) / Ns >= 256).
+ * Returns 0 for invalid sizes.
  * (The io argument is one more than the five of the plain form (N, Ns, Hk, Hv, d): the
  * fp32 io records are larger, so the size depends on it.)
  */

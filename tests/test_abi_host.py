@@ -97,11 +97,16 @@ def test_prefill_rejects():
     # then cmax = ceil(N/64) + Ns chunks x (Hv x 38912 B + Hk x K record), K record 0 B
     # (bf16 io: K and Q are staged from the inputs) or 69632 B (fp32 io), then for at
     # most 64 (sequence, head) chains 7 segment-transition pairs of 128 KB per chain (fp32
-    # io only: bf16 io never segments)
+    # io; bf16 io only for at most 16 chains averaging at least 256 chunks)
     ws = _lib.lib().gdn_chunk_prefill_workspace_size
     assert ws(4096, 1, 16, 32, 128, 1) == 256 + 1280 + 65 * (32 * 38912)
     assert ws(4096, 3, 16, 32, 128, 1) == 256 + 1280 + 67 * (32 * 38912)
     assert ws(100, 3, 1, 2, 128, 0) == 256 + 256 + 5 * (2 * 38912 + 1 * 69632) + 7 * 6 * 131072
+    # bf16: 256 chunks of one sequence at 2 heads reserve the scan's pairs, 255 do not,
+    # nor do 32 chains
+    assert ws(16384, 1, 1, 2, 128, 1) == 256 + 4352 + 257 * (2 * 38912) + 7 * 2 * 131072
+    assert ws(16320, 1, 1, 2, 128, 1) == 256 + 4096 + 256 * (2 * 38912)
+    assert ws(32768, 1, 16, 32, 128, 1) == 256 + 8448 + 513 * (32 * 38912)
     assert ws(-1, 1, 16, 32, 128, 1) == 0
     assert ws(64, 1, 16, 32, 64, 1) == 0
 

@@ -66,6 +66,7 @@ def _both(d, hk, hv, in_place=False):
     # the prep inside the fused call
     ("bf16", 16, 32, [8192], False),        # 2064 prep workgroups, row-split sweep
     ("bf16", 4, 8, LENS * 24, True),        # 288 sequences, 8-wave sweep
+    ("bf16", 1, 2, [16500], False),         # 2 long chains: the intra-sequence scan
 ])
 def test_fused_equals_two_calls(io, hk, hv, lens, in_place):
     inp, d = _inputs(hk, hv, io, 70 + len(lens), lens)

@@ -170,6 +170,28 @@ def test_chunk_prefill_parity_segmented(io, lens):
     assert_state(s, s_ref, "prefill state")
 
 
+@pytest.mark.parametrize("lens", [[16500], [20000, 17000]], ids=["one", "varlen"])
+def test_chunk_prefill_parity_segmented_bf16(lens):
+    """bf16 with few, long chains: the intra-sequence scan instead of the row-split sweep
+    (2 or 4 chains, whose row-split launch would fill at most half the compute units, of
+    258 chunks with a ragged last one, or two sequences averaging 289 chunks), eight
+    segments per sequence, with carried states."""
+    io, hk, hv = "bf16", 1, 2
+    inp = _case(hk, hv, io, 71 + len(lens), seqlens=lens, init_state=True)
+    N, Ns = inp["N"], inp["Ns"]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert 2 * Ns * hv * 8 <= cus and -(-N // 64) // Ns >= 256   # the scan's launch shape
+    # the workspace holds the scan's segment pairs
+    ws = gdn.gdn_chunk_prefill_workspace_size(N, Ns, hk, hv, io=torch.bfloat16)
+    assert ws >= 7 * Ns * hv * 131072
+    y, o, s = _run_prefill(inp, io)
+    o_ref, s_ref = G.prefill(y[:, :hk * D], y[:, hk * D:2 * hk * D], y[:, 2 * hk * D:],
+                             inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv, D, D,
+                             inp["state_in"], inp["cu_seqlens"])
+    assert_out(o, o_ref, io, "prefill o")
+    assert_state(s, s_ref, "prefill state")
+
+
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_chunk_prefill_zero_state_single_sequence(io):
     inp = _case(2, 4, io, 31, seqlens=[257], init_state=False)
