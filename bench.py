@@ -52,18 +52,22 @@ KERNEL_SOURCES = {"gdn_chunk_prefill": ("gdn_chunk.hip", "gdn_common.hpp", "gdn_
                                                     "gdn_launch.hpp")}
 # HBM bytes per launch from rocprofv3 PMC FETCH_SIZE and WRITE_SIZE, each scaled by what
 # the counter reads for a plain 256 MiB copy (the summaries with the commands are
-# profiles/pmc_bench_qwen35_9b_prefill_T4096_decode_B256.txt and profiles/pmc_prefill_*.txt):
+# profiles/pmc_bench_qwen35_9b_prefill_T4096_decode_B256.txt and profiles/pmc_prefill_*.txt,
+# those of the segment_scan leg in profiles/pmc_prefill_segment_scan_*.txt):
 # key -> (call whose sources the figure belongs to, their digest, bytes).  A figure is not
 # reported once those sources change.
 MEASURED_TRAFFIC = {
-    "gdn_chunk_prefill": ("gdn_chunk_prefill", "667153cc626d0e94", 247.9e6),
-    "gdn_conv_chunk_prefill": ("gdn_conv_chunk_prefill", "e1d80e521fefdb93", 373.4e6),
-    "gdn_recurrent_step": ("gdn_recurrent_step", "1b51b87b676685fb", 1105.9e6),
-    "gdn_recurrent_step_bf16_state": ("gdn_recurrent_step_bf16_state", "1b51b87b676685fb", 568.9e6),
+    "gdn_chunk_prefill": ("gdn_chunk_prefill", "7e62f95a1a30b118", 248.4e6),
+    "gdn_conv_chunk_prefill": ("gdn_conv_chunk_prefill", "ee7b98346baef624", 373.4e6),
+    "gdn_recurrent_step": ("gdn_recurrent_step", "f9638a61dd1eac8d", 1105.9e6),
+    "gdn_recurrent_step_bf16_state": ("gdn_recurrent_step_bf16_state", "f9638a61dd1eac8d", 568.9e6),
     # the chunk call on the prefill_configs workloads
-    "gdn_chunk_prefill@l0_qwen3.5-0.8b_T256_fp32": ("gdn_chunk_prefill", "667153cc626d0e94", 24.3e6),
-    "gdn_chunk_prefill@l3_qwen3.5-397b_T32768_bf16": ("gdn_chunk_prefill", "667153cc626d0e94", 3869.9e6),
-    "gdn_chunk_prefill@l4_qwen3.5-9b_varlen64_bf16": ("gdn_chunk_prefill", "667153cc626d0e94", 4447.7e6),
+    "gdn_chunk_prefill@l0_qwen3.5-0.8b_T256_fp32": ("gdn_chunk_prefill", "7e62f95a1a30b118", 24.3e6),
+    "gdn_chunk_prefill@l3_qwen3.5-397b_T32768_bf16": ("gdn_chunk_prefill", "7e62f95a1a30b118", 3864.6e6),
+    "gdn_chunk_prefill@l4_qwen3.5-9b_varlen64_bf16": ("gdn_chunk_prefill", "7e62f95a1a30b118", 4447.6e6),
+    # and on the segment_scan workloads
+    "gdn_chunk_prefill@qwen3.5-9b_shard8_T32768_bf16": ("gdn_chunk_prefill", "7e62f95a1a30b118", 397.0e6),
+    "gdn_chunk_prefill@qwen3.5-0.8b_T32768_bf16": ("gdn_chunk_prefill", "7e62f95a1a30b118", 1942.3e6),
 }
 
 
@@ -360,7 +364,8 @@ def segment_scan_leg(reps: int) -> dict:
         out[name] = {"Hk": hk, "Hv": hv, "tokens": N, "chunk_prefill_ms": ms,
                      "tokens_per_s": N / (ms * 1e-3),
                      "core_TFLOPs": flops / (ms * 1e-3) / 1e12,
-                     "frac_bf16_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS}
+                     "frac_bf16_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
+                     "traffic": measured_traffic(f"gdn_chunk_prefill@{name}")}
         del y, a, b, o, ws, s_in, s_out, q, k, v
         torch.cuda.empty_cache()
     return out
