@@ -426,135 +426,159 @@ struct PrepSmem {
   alignas(16) float rnq[CH];
 };
 
-// Fused conv of the prep kernel (bf16 io): the conv window + SiLU of this key head's q, k
-// and v channels over the chunk's rows, rounded to bf16 as the conv call stores them
-// (the operation of gdn_conv1d_fwd: llm-arch-viz Qwen3.5-9B page, module tree, conv1d
-// 8192x1x4, depthwise, no bias).  The rows go to y, where the sweep reads q, k and v;
-// the q and k rows also go to LDS for the Gram products, with their row norms.  Per
-// pass, lane = a group of 8 channels (q 16, k 16, then 16 per value head) and wave w =
-// rows 16 w .. 16 w + 15 in two halves of 8; a half also reads the 3 rows before it
-// (from x, or before the sequence start from its conv state, or zeros).
-__device__ __forceinline__ void conv_rows(const ChunkArgs& p, int s, int64_t t0, int L, int kh,
-                                          int r, int wave, int lane, u16* k_rows, u16* q_rows,
-                                          float* rnk, float* rnq) {
-  const int Cq = p.Cq, Hk = p.Hk;
-  int64_t sb, se;
-  seq_bounds(p.cu, p.N, s, sb, se);
+// Fused conv of the prep kernel (bf16 io): the conv window + SiLU of this key head's
+// channels over the chunk's rows, rounded to bf16 as the conv call stores them (the
+// operation of gdn_conv1d_fwd: llm-arch-viz Qwen3.5-9B page, module tree, conv1d 8192x1x4,
+// depthwise, no bias).  The rows go to y, where the sweep reads them; the q and k rows
+// also go to LDS for the Gram products, with their row norms.  A lane handles a group of
+// 8 channels (q 16 groups, k 16, then 16 per value head) over 8 rows; its window adds the
+// 3 rows before them (from x, or before the sequence start from its conv state, or zeros).
+// Every global load is unconditional and in bounds (a load under a condition is waited for
+// where its branch joins), so a window's rows are waited for one by one as they are used.
+// gin (loaded before the call) is marked complete after the first row, whose wait covers
+// it (loads complete in order), so no later use of it waits for the y stores.
+
+// the 11 window rows r0 - 3 .. r0 + 7 of channels ch .. ch + 7 (rows at or past the chunk
+// end clamped to its last row: they feed only outputs that are not stored); inside:
+// the whole window lies inside the sequence
+__device__ __forceinline__ void conv_window(const ChunkArgs& p, int s, int64_t sb, int64_t t0,
+                                            int L, int r0, int ch, bool inside, uint4 (&raw)[11]) {
+  const int Cq = p.Cq;
   const u16* x = (const u16*)p.x;
   const u16* cs = (const u16*)p.conv_state_in;
+  if (inside) {
+    // one base pointer, row i is i Cq further (no per-row 64-bit offsets to hold)
+    const u16* xr = x + (t0 + r0 - 3) * (int64_t)Cq + ch;
+#pragma unroll
+    for (int i = 0; i < 11; ++i)
+      raw[i] = *reinterpret_cast<const uint4*>(xr + (min(r0 - 3 + i, L - 1) - (r0 - 3)) * Cq);
+  } else {
+    // rows before the sequence come from its conv state, or are zero without one (read
+    // from the sequence's first row and cleared)
+#pragma unroll
+    for (int i = 0; i < 11; ++i) {
+      const int64_t tok = t0 + min(r0 - 3 + i, L - 1);
+      const bool in_seq = tok >= sb;
+      const u16* src = in_seq ? x + tok * Cq + ch
+                     : cs    ? cs + ((int64_t)s * 3 + (tok - sb + 3)) * Cq + ch
+                             : x + sb * Cq + ch;
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      raw[i] = (in_seq || cs) ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// output row t (0 .. 7) of a window: 8 channels as packed bf16
+__device__ __forceinline__ uint4 conv_row8(const float4 (&wt)[8], const uint4 (&raw)[11], int t) {
+  const uint32_t w0[4] = {raw[t].x, raw[t].y, raw[t].z, raw[t].w};
+  const uint32_t w1[4] = {raw[t + 1].x, raw[t + 1].y, raw[t + 1].z, raw[t + 1].w};
+  const uint32_t w2[4] = {raw[t + 2].x, raw[t + 2].y, raw[t + 2].z, raw[t + 2].w};
+  const uint32_t w3[4] = {raw[t + 3].x, raw[t + 3].y, raw[t + 3].z, raw[t + 3].w};
+  float out[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      auto val = [&](uint32_t wd) { return __uint_as_float(hf ? (wd & 0xFFFF0000u) : (wd << 16)); };
+      out[2 * q + hf] = conv4_silu(wt[2 * q + hf], val(w0[q]), val(w1[q]), val(w2[q]), val(w3[q]));
+    }
+  }
+  return make_uint4(f2bf2(out[0], out[1]), f2bf2(out[2], out[3]), f2bf2(out[4], out[5]),
+                    f2bf2(out[6], out[7]));
+}
+
+// a q (group < 16) or k row of 8 channels to LDS (zero past the chunk end), with the
+// squared norm of the row over the 16 lanes of its DPP row
+__device__ __forceinline__ void qk_row_to_lds(const ChunkArgs& p, uint4 ow, int row, int L, int cg,
+                                              u16* k_rows, u16* q_rows, float* rnk, float* rnq) {
+  if (row >= L) ow = make_uint4(0, 0, 0, 0);
+  const uint32_t ox[4] = {ow.x, ow.y, ow.z, ow.w};
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float v0 = __uint_as_float(ox[q] << 16), v1 = __uint_as_float(ox[q] & 0xFFFF0000u);
+    ss = fmaf(v1, v1, fmaf(v0, v0, ss));
+  }
+  ss = row16_sum(ss);
+  const float rn = p.use_l2 ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.0f;
+  if (cg < 16) {
+    *reinterpret_cast<uint4*>(q_rows + row * KS_STRIDE + cg * 8) = ow;
+    if (cg == 0) rnq[row] = rn;
+  } else if (cg < 32) {
+    *reinterpret_cast<uint4*>(k_rows + row * KS_STRIDE + (cg - 16) * 8) = ow;
+    if (cg == 16) rnk[row] = rn;
+  }
+}
+
+// channel of group cg of key head kh (q 16 groups, k 16, then 16 per value head)
+__device__ __forceinline__ int conv_group_channel(int cg, int kh, int Hk, int r) {
+  return cg < 16 ? kh * DK + cg * 8
+       : cg < 32 ? Hk * DK + kh * DK + (cg - 16) * 8
+                 : 2 * Hk * DK + kh * r * DV + (cg - 32) * 8;
+}
+
+// the final conv state of every channel of this key head (the last 3 raw rows of the
+// sequence, from x or, for a sequence shorter than 3, from the conv state before it),
+// written by wave 0 of the workgroup whose chunk ends the sequence
+__device__ __forceinline__ void final_conv_state(const ChunkArgs& p, int s, int64_t sb, int64_t se,
+                                                 int kh, int r, int lane) {
+  const int Cq = p.Cq, G = 32 + 16 * r;
+  const u16* x = (const u16*)p.x;
+  const u16* cs = (const u16*)p.conv_state_in;
+  u16* cso = (u16*)p.conv_state_out;
+  for (int cg = lane; cg < G; cg += 64) {
+    const int ch = conv_group_channel(cg, kh, p.Hk, r);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int64_t tok = se - 3 + i;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (tok >= sb)
+        v = *reinterpret_cast<const uint4*>(x + tok * Cq + ch);
+      else if (cs)
+        v = *reinterpret_cast<const uint4*>(cs + ((int64_t)s * 3 + (tok - sb + 3)) * Cq + ch);
+      *reinterpret_cast<uint4*>(cso + ((int64_t)s * 3 + i) * Cq + ch) = v;
+    }
+  }
+}
+
+// every channel of the key head: per pass of 64 groups, wave w = rows 16 w .. 16 w + 15
+// in two halves of 8 (the halves and passes stay loops: unrolled, the windows' registers
+// and row offsets spill).  The weights are loaded again with each half's window (L1 hits):
+// loaded once before the halves' loop, the wave would wait for them before the window
+// loads could issue.
+__device__ __forceinline__ void conv_rows(const ChunkArgs& p, int s, int64_t t0, int L, int kh,
+                                          int r, int wave, int lane, u16* k_rows, u16* q_rows,
+                                          float* rnk, float* rnq, uint4& gin) {
+  const int Cq = p.Cq;
+  int64_t sb, se;
+  seq_bounds(p.cu, p.N, s, sb, se);
   u16* y = (u16*)p.y;
   const int G = 32 + 16 * r;
-  for (int pass = 0; pass * 64 < G; ++pass) {
-    const int cg = pass * 64 + lane;
-    const bool act = cg < G;
-    const int ch = cg < 16 ? kh * DK + cg * 8
-                 : cg < 32 ? Hk * DK + kh * DK + (cg - 16) * 8
-                           : 2 * Hk * DK + kh * r * DV + (cg - 32) * 8;
-    float wt[4][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 ww = act ? *reinterpret_cast<const float4*>(p.conv_w + (int64_t)(ch + j) * 4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-      wt[0][j] = ww.x; wt[1][j] = ww.y; wt[2][j] = ww.z; wt[3][j] = ww.w;
-    }
-    // (the two halves run as a loop: unrolled, both windows' registers and row offsets
-    // are live at once and spill)
+  // (a do-while: the first pass, which marks gin, runs on every path)
+  int pass = 0;
+  do {
+    // lanes past the last group repeat it: they compute and store the same bytes
+    const int cg = min(pass * 64 + lane, G - 1);
+    const int ch = conv_group_channel(cg, kh, p.Hk, r);
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
+      float4 wt[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wt[j] = *reinterpret_cast<const float4*>(p.conv_w + (int64_t)(ch + j) * 4);
       const int r0 = 16 * wave + 8 * half;
-      // rows r0 - 3 .. r0 + 7; rows past the chunk end feed only outputs past it.  The
-      // lane's pointer to its channels in the first row is formed once; row i is i Cq
-      // further (no per-row 64-bit scalar offsets to hold)
       uint4 raw[11];
-      const u16* xr = x + (t0 + r0 - 3) * (int64_t)Cq + ch;
-      if (t0 + r0 - 3 >= sb) {
-        // the whole window lies inside the sequence
-#pragma unroll
-        for (int i = 0; i < 11; ++i)
-          raw[i] = (act && r0 - 3 + i < L) ? *reinterpret_cast<const uint4*>(xr + i * Cq)
-                                          : make_uint4(0, 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 11; ++i) {
-          const int row = r0 - 3 + i;
-          const int64_t tok = t0 + row;
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (act && row < L) {
-            if (tok >= sb)
-              v = *reinterpret_cast<const uint4*>(xr + i * Cq);
-            else if (cs)
-              v = *reinterpret_cast<const uint4*>(cs + ((int64_t)s * 3 + (tok - sb + 3)) * Cq + ch);
-          }
-          raw[i] = v;
-        }
-      }
+      conv_window(p, s, sb, t0, L, r0, ch, t0 + r0 - 3 >= sb, raw);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int row = r0 + t;
-        float out[8];
-        {
-          const uint32_t w0[4] = {raw[t].x, raw[t].y, raw[t].z, raw[t].w};
-          const uint32_t w1[4] = {raw[t + 1].x, raw[t + 1].y, raw[t + 1].z, raw[t + 1].w};
-          const uint32_t w2[4] = {raw[t + 2].x, raw[t + 2].y, raw[t + 2].z, raw[t + 2].w};
-          const uint32_t w3[4] = {raw[t + 3].x, raw[t + 3].y, raw[t + 3].z, raw[t + 3].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              const int j = 2 * q + hf;
-              auto val = [&](uint32_t wd) {
-                return __uint_as_float(hf ? (wd & 0xFFFF0000u) : (wd << 16));
-              };
-              float acc = wt[0][j] * val(w0[q]);
-              acc = fmaf(wt[1][j], val(w1[q]), acc);
-              acc = fmaf(wt[2][j], val(w2[q]), acc);
-              acc = fmaf(wt[3][j], val(w3[q]), acc);
-              out[j] = silu(acc);
-            }
-          }
-        }
-        uint4 ow = make_uint4(f2bf2(out[0], out[1]), f2bf2(out[2], out[3]),
-                              f2bf2(out[4], out[5]), f2bf2(out[6], out[7]));
-        if (act && row < L) *reinterpret_cast<uint4*>(y + (t0 + row) * Cq + ch) = ow;
-        if (pass == 0) {
-          // q (lanes 0 .. 15) and k (lanes 16 .. 31) rows to LDS (zero past the chunk end)
-          // and their squared norms over the row's 16 lanes
-          if (row >= L) ow = make_uint4(0, 0, 0, 0);
-          const uint32_t ox[4] = {ow.x, ow.y, ow.z, ow.w};
-          float ss = 0.f;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float v0 = __uint_as_float(ox[q] << 16), v1 = __uint_as_float(ox[q] & 0xFFFF0000u);
-            ss = fmaf(v1, v1, fmaf(v0, v0, ss));
-          }
-          ss = row16_sum(ss);
-          const float rn = p.use_l2 ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.0f;
-          if (lane < 16) {
-            *reinterpret_cast<uint4*>(q_rows + row * KS_STRIDE + lane * 8) = ow;
-            if (lane == 0) rnq[row] = rn;
-          } else if (lane < 32) {
-            *reinterpret_cast<uint4*>(k_rows + row * KS_STRIDE + (lane - 16) * 8) = ow;
-            if (lane == 16) rnk[row] = rn;
-          }
-        }
+        const uint4 ow = conv_row8(wt, raw, t);
+        if (t == 0) asm volatile("" : "+v"(gin.x), "+v"(gin.y), "+v"(gin.z), "+v"(gin.w));
+        if (row < L) *reinterpret_cast<uint4*>(y + (t0 + row) * Cq + ch) = ow;
+        if (pass == 0) qk_row_to_lds(p, ow, row, L, cg, k_rows, q_rows, rnk, rnq);
       }
     }
-    // the final conv state (the last 3 raw rows of the sequence, from x or, for a
-    // sequence shorter than 3, from the conv state before it) when this chunk ends it
-    if (p.conv_state_in_prep && wave == 0 && act && t0 + L == se) {
-      u16* cso = (u16*)p.conv_state_out;
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int64_t tok = se - 3 + i;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (tok >= sb)
-          v = *reinterpret_cast<const uint4*>(x + tok * Cq + ch);
-        else if (cs)
-          v = *reinterpret_cast<const uint4*>(cs + ((int64_t)s * 3 + (tok - sb + 3)) * Cq + ch);
-        *reinterpret_cast<uint4*>(cso + ((int64_t)s * 3 + i) * Cq + ch) = v;
-      }
-    }
-  }
+  } while (++pass * 64 < G);
+  if (p.conv_state_in_prep && wave == 0 && t0 + L == se) final_conv_state(p, s, sb, se, kh, r, lane);
 }
 
 // waves per SIMD the prep kernel is built for (its workgroups resident per CU)
@@ -562,7 +586,9 @@ constexpr int prep_occupancy(int io, int mode) {
   return io == IO_BF16 ? (mode != PREP_ROWS_P ? 4 : 3) : 2;
 }
 
-template <int IO, int MODE, bool CONV = false>
+// fused conv of the prep: none, or every channel of the key head
+enum PrepConv { CONV_NONE = 0, CONV_ALL = 1 };
+template <int IO, int MODE, int CONV = CONV_NONE>
 __global__ void __launch_bounds__(NTHR, prep_occupancy(IO, MODE))
 chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restrict__ recs,
                   uint8_t* __restrict__ krecs) {
@@ -572,7 +598,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   constexpr bool WITHP = MODE != PREP_ROWS;
   constexpr bool FRAG = MODE == PREP_FRAG;
   static_assert(!(FRAG && F32), "fragment-native records are for bf16 io");
-  static_assert(!(CONV && F32), "the fused conv is for bf16 io");
+  static_assert(!(CONV != CONV_NONE && F32), "the fused conv is for bf16 io");
   constexpr int64_t REC = FRAG ? FR_REC_BYTES : ws_rec_bytes(WITHP);
   constexpr int64_t FAC_OFF = FRAG ? FR_FAC_OFF : WS_FAC_OFF;
   __shared__ PrepSmem<IO> sm;
@@ -633,11 +659,11 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
                        __uint_as_float(gi.z), __uint_as_float(gi.w));
   };
   // the first batch's gate inputs go out before the rows, so their latency hides there
-  const uint4 gin0 = gate_in(0);
+  uint4 gin0 = gate_in(0);
 
   // ---- phase 0: K and Q rows to LDS, row norms (16 lanes of a DPP row share a row)
-  if constexpr (CONV) {
-    conv_rows(p, ci.x, t0, L, kh_, r, wave, lane, sm.u.r.kh, sm.u.r.qh, sm.rnk, sm.rnq);
+  if constexpr (CONV != CONV_NONE) {
+    conv_rows(p, ci.x, t0, L, kh_, r, wave, lane, sm.u.r.kh, sm.u.r.qh, sm.rnk, sm.rnq, gin0);
   } else {
     RowBlock<IO> kb, qb;
     load_rows<IO>(kb, (const T*)p.k + (int64_t)kh_ * DK, p.stride_k, t0, L, tid);
@@ -805,7 +831,15 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
     // ---- gates of value heads hb .. hb+3 (wave w: head hb + w, lane: token)
     __syncthreads();     // K/Q rows (phase 0) or the previous heads' T are no longer read
     {
-      const float4 gin = gate_vals(hb > 0 ? gate_in(hb) : gin0);
+      // (a later batch's inputs are waited for in their own branch: merged with gin0
+      // while still in flight, they would be waited for after the join, behind every
+      // store issued since the conv)
+      uint4 graw = gin0;
+      if (hb > 0) {
+        graw = gate_in(hb);
+        asm volatile("" : "+v"(graw.x), "+v"(graw.y), "+v"(graw.z), "+v"(graw.w));
+      }
+      const float4 gin = gate_vals(graw);
       float g = 0.f, beta = 0.f;
       if (hb + wave < r && lane < L) {
         if (p.g_opt) {
@@ -2092,13 +2126,13 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
     if constexpr (IO == IO_BF16) {
       if (conv_in_prep) {
         if (rowsplit)
-          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG, true>), pgrid, dim3(NTHR), 0, st,
+          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
                              a, (const int4*)cinfo, recs, krecs);
         else if (four)
-          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS_P, true>), pgrid, dim3(NTHR), 0, st,
+          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS_P, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
                              a, (const int4*)cinfo, recs, krecs);
         else
-          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS, true>), pgrid, dim3(NTHR), 0, st,
+          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
                              a, (const int4*)cinfo, recs, krecs);
       } else if (rowsplit) {
         hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG>), pgrid, dim3(NTHR), 0, st, a,

@@ -80,6 +80,16 @@ template <> struct Io<IO_BF16> {
 __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
+// one output of the causal depthwise conv (width 4) + SiLU: taps w.x .. w.w applied to
+// the inputs at t-3 .. t, in this order of fp32 operations.  Every kernel that forms
+// conv outputs calls this, so that they agree bit for bit.
+__device__ __forceinline__ float conv4_silu(float4 w, float x0, float x1, float x2, float x3) {
+  float acc = w.x * x0;
+  acc = fmaf(w.y, x1, acc);
+  acc = fmaf(w.z, x2, acc);
+  acc = fmaf(w.w, x3, acc);
+  return silu(acc);
+}
 // 1 / (1 + e^{-x}) on the hardware exp2 and reciprocal (a few ulp)
 __device__ __forceinline__ float sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));

@@ -84,12 +84,9 @@ conv1d_silu_kernel(const typename Io<IO>::T* __restrict__ x, const float* __rest
   if (t0 >= N) return;
   const int64_t t1 = t0 + CONV_TT < N ? t0 + CONV_TT : N;
 
-  float wt[4][8];
+  float4 wt[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float4 ww = *reinterpret_cast<const float4*>(w + (int64_t)(c0 + j) * 4);
-    wt[0][j] = ww.x; wt[1][j] = ww.y; wt[2][j] = ww.z; wt[3][j] = ww.w;
-  }
+  for (int j = 0; j < 8; ++j) wt[j] = *reinterpret_cast<const float4*>(w + (int64_t)(c0 + j) * 4);
 
   int s = cu ? find_seq(cu, Ns, t0) : 0;
   int64_t sb = cu ? (int64_t)cu[s] : 0;
@@ -117,13 +114,7 @@ conv1d_silu_kernel(const typename Io<IO>::T* __restrict__ x, const float* __rest
       rows[t + 2].get(v2);
       rows[t + 3].get(v3);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float acc = wt[0][j] * v0[j];
-        acc = fmaf(wt[1][j], v1[j], acc);
-        acc = fmaf(wt[2][j], v2[j], acc);
-        acc = fmaf(wt[3][j], v3[j], acc);
-        out[j] = silu(acc);
-      }
+      for (int j = 0; j < 8; ++j) out[j] = conv4_silu(wt[j], v0[j], v1[j], v2[j], v3[j]);
       // nontemporal: y is written once here and read by the next call
       if constexpr (IO == IO_BF16) {
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -173,11 +164,7 @@ conv1d_silu_kernel(const typename Io<IO>::T* __restrict__ x, const float* __rest
     io::ld8(x, t * Cq + c0, xv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float acc = wt[0][j] * h[0][j];
-      acc = fmaf(wt[1][j], h[1][j], acc);
-      acc = fmaf(wt[2][j], h[2][j], acc);
-      acc = fmaf(wt[3][j], xv[j], acc);
-      out[j] = silu(acc);
+      out[j] = conv4_silu(wt[j], h[0][j], h[1][j], h[2][j], xv[j]);
       h[0][j] = h[1][j];
       h[1][j] = h[2][j];
       h[2][j] = xv[j];

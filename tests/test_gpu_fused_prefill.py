@@ -58,6 +58,7 @@ def _both(d, hk, hv, in_place=False):
 @pytest.mark.parametrize("io,hk,hv,lens,in_place", [
     ("bf16", 2, 4, LENS, False),            # 48 chains: row-split sweep, two rounds
     ("bf16", 1, 3, LENS[:7], True),         # 21 chains, three value heads per key head
+    ("bf16", 4, 4, [2, 130, 64, 0, 65], False),   # 20 chains, one value head per key head
     ("bf16", 2, 4, LENS * 2, False),        # 96 chains: 4-wave sweep
     ("bf16", 2, 4, LENS * 4, True),         # 192 chains: 8-wave sweep
     ("f32", 2, 4, LENS, False),             # fp32 io: conv then the chunk call
