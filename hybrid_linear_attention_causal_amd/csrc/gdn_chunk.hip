@@ -1731,13 +1731,20 @@ constexpr int ROWSPLIT_CU_ROUNDS = 2;
 namespace rs {
 constexpr int NW = 4;
 constexpr int THR = 64 * NW;
-constexpr int DVB = 16;                  // dv columns per workgroup
-constexpr int NBLK = DV / DVB;           // workgroups per chain
+constexpr int NBLK = DV / 16;            // workgroups per chain with one column tile
 constexpr int ROWS = CH * KS_STRIDE;
 constexpr int KJ = RowDma<16, NW>::J;    // K or Q row copies per wave
-constexpr int VW = DVB * 2 / 16;         // 16-byte words per V row slice
-constexpr int V_STRIDE = DVB + 8;        // u16 per staged V row
-constexpr int O_STRIDE = DVB + 8;        // u16 per staged output row
+// CT 16-column tiles of dv per workgroup: CT = 2 halves the workgroups per chain (and
+// reads each K, Q, T' and P fragment once for both tiles) where CT = 1 would need two
+// workgroups per CU
+template <int CT>
+struct Cols {
+  static constexpr int DVB = 16 * CT;           // dv columns per workgroup
+  static constexpr int NBLK = DV / DVB;         // workgroups per chain
+  static constexpr int VW = DVB * 2 / 16;       // 16-byte words per V row slice
+  static constexpr int V_STRIDE = DVB + 8;      // u16 per staged V row
+  static constexpr int O_STRIDE = DVB + 8;      // u16 per staged output row
+};
 }  // namespace rs
 
 // one chunk's register operands of wave j: T' and P of row tile j, token slabs 0, 1
@@ -1769,20 +1776,24 @@ namespace rs2 {
 constexpr int THR = 2 * rs::THR;
 }
 
-// (four waves per SIMD: two workgroups per CU)
-__global__ void __launch_bounds__(rs2::THR, 4)
+// (CT = 1: four waves per SIMD, two workgroups per CU; CT = 2: one workgroup per CU, so
+// two waves per SIMD and their registers)
+template <int CT>
+__global__ void __launch_bounds__(rs2::THR, CT == 1 ? 4 : 2)
 chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
   typedef Io<IO_BF16> io;
   typedef io::T T;
   using namespace rs;
+  typedef Cols<CT> C;
+  constexpr int DVB = C::DVB, NBLK = C::NBLK, VW = C::VW, V_STRIDE = C::V_STRIDE, O_STRIDE = C::O_STRIDE;
   __shared__ __attribute__((aligned(16))) u16 s_k0[ROWS];     // K rows, even chunks
   __shared__ __attribute__((aligned(16))) u16 s_k1[ROWS];     // K rows, odd chunks
   __shared__ __attribute__((aligned(16))) u16 s_q[ROWS];      // Q rows
   __shared__ __attribute__((aligned(16))) float s_f[4 * CH];    // factor rows 0 .. 3 (c_k, c_q, c_2, e^{gamma_L})
   __shared__ __attribute__((aligned(16))) u16 s_v[CH * V_STRIDE];      // V slice
-  __shared__ __attribute__((aligned(16))) uint4 s_sx[4][2][64];        // state slabs: hi, lo fragments
-  __shared__ __attribute__((aligned(16))) uint2 s_rx[4][2][64];        // R tiles: hi, lo
-  __shared__ __attribute__((aligned(16))) uint2 s_ux[4][4][64];        // U tiles: U hi, U lo, Us hi, Us lo
+  __shared__ __attribute__((aligned(16))) uint4 s_sx[CT][4][2][64];    // state slabs: hi, lo fragments
+  __shared__ __attribute__((aligned(16))) uint2 s_rx[CT][4][2][64];    // R tiles: hi, lo
+  __shared__ __attribute__((aligned(16))) uint2 s_ux[CT][4][4][64];    // U tiles: U hi, U lo, Us hi, Us lo
   __shared__ __attribute__((aligned(16))) u16 s_ost[CH * O_STRIDE];    // output tile
 
   const int tid = threadIdx.x;
@@ -1809,7 +1820,7 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
   seq_bounds(p.cu, p.N, s, b0, b1);
   const int c0 = p.Ns == 1 ? 0 : cmap[s];
   const int ne = (int)((b1 - b0 + CH - 1) / CH);
-  const int col = blk * DVB + c16;
+  const int col = blk * DVB + c16;   // column tile ct: col + 16 ct
 
   const uint8_t* qg = (const uint8_t*)((const T*)p.q + (int64_t)kh * DK);
   const uint8_t* kg = (const uint8_t*)((const T*)p.k + (int64_t)kh * DK);
@@ -1823,22 +1834,31 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
   rows_table<16, NW>(j, lane, ktab);
   rows_table<VW, NW>(j, lane, vtab);
 
-  // ---- state slab (chain waves): St[t] holds rows 32 j + 16 t + 4 g4 + e of column col
-  f32x4 St[2];
-  St[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  St[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---- state slab (chain waves): St[ct][t] holds rows 32 j + 16 t + 4 g4 + e of column
+  // col + 16 ct
+  f32x4 St[CT][2];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    St[ct][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    St[ct][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   if (chain && p.state_in) {
     const float* sp = p.state_in + ((int64_t)s * Hv + h) * DK * DV + col;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) St[t][e] = sp[(32 * j + 16 * t + 4 * g4 + e) * DV];
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) St[ct][t][e] = sp[(32 * j + 16 * t + 4 * g4 + e) * DV + 16 * ct];
   }
   auto put_slab = [&]() {
-    bf16x8 hi, lo;
-    frag_acc_split(St[0], St[1], hi, lo);
-    s_sx[j][0][lane] = __builtin_bit_cast(uint4, hi);
-    s_sx[j][1][lane] = __builtin_bit_cast(uint4, lo);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      bf16x8 hi, lo;
+      frag_acc_split(St[ct][0], St[ct][1], hi, lo);
+      s_sx[ct][j][0][lane] = __builtin_bit_cast(uint4, hi);
+      s_sx[ct][j][1][lane] = __builtin_bit_cast(uint4, lo);
+    }
   };
   auto chunk_rows = [&](int n, int64_t& t0, int& L) {
     t0 = b0 + (int64_t)n * CH;
@@ -1915,7 +1935,7 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
     load_ops(na, nxt);
     if (!chain && n > 0) store_o(n - 1);
 
-    f32x4 QS;          // output waves: Q S of row tile j
+    f32x4 QS[CT];      // output waves: Q S of row tile j
     float4 c2;         // chain waves: the update factors of row tile j
     float egl;
     if (chain) {
@@ -1923,34 +1943,47 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
       const float4 ck = *reinterpret_cast<const float4*>(&s_f[16 * j + 4 * g4]);
       c2 = *reinterpret_cast<const float4*>(&s_f[2 * CH + 16 * j + 4 * g4]);
       egl = s_f[3 * CH];
-      u16 vraw[4];
+      u16 vraw[CT][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vraw[e] = s_v[(16 * j + 4 * g4 + e) * V_STRIDE + c16];
-      f32x4 ka = {0.f, 0.f, 0.f, 0.f}, kb = ka;
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vraw[ct][e] = s_v[(16 * j + 4 * g4 + e) * V_STRIDE + 16 * ct + c16];
+      f32x4 ka[CT], kb[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        ka[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        kb[ct] = ka[ct];
+      }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const bf16x8 sh = __builtin_bit_cast(bf16x8, s_sx[m][0][lane]);
-        const bf16x8 sl = __builtin_bit_cast(bf16x8, s_sx[m][1][lane]);
         const bf16x8 ak = frag_rows(kcur, KS_STRIDE, 16 * j, 32 * m, lane);
-        ka = mma(ak, sh, ka);
-        kb = mma(ak, sl, kb);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const bf16x8 sh = __builtin_bit_cast(bf16x8, s_sx[ct][m][0][lane]);
+          const bf16x8 sl = __builtin_bit_cast(bf16x8, s_sx[ct][m][1][lane]);
+          ka[ct] = mma(ak, sh, ka[ct]);
+          kb[ct] = mma(ak, sl, kb[ct]);
+        }
       }
       const float ckv[4] = {ck.x, ck.y, ck.z, ck.w};
       int64_t t0;
       int L;
       chunk_rows(n, t0, L);
-      f32x4 R;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * j + 4 * g4 + e;
-        const float vv = t < L ? bf2f(vraw[e]) : 0.f;
-        R[e] = vv - ckv[e] * (ka[e] + kb[e]);
+      for (int ct = 0; ct < CT; ++ct) {
+        f32x4 R;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * j + 4 * g4 + e;
+          const float vv = t < L ? bf2f(vraw[ct][e]) : 0.f;
+          R[e] = vv - ckv[e] * (ka[ct][e] + kb[ct][e]);
+        }
+        uint32_t rh0, rl0, rh1, rl1;
+        split2(R[0], R[1], rh0, rl0);
+        split2(R[2], R[3], rh1, rl1);
+        s_rx[ct][j][0][lane] = make_uint2(rh0, rh1);
+        s_rx[ct][j][1][lane] = make_uint2(rl0, rl1);
       }
-      uint32_t rh0, rl0, rh1, rl1;
-      split2(R[0], R[1], rh0, rl0);
-      split2(R[2], R[3], rh1, rl1);
-      s_rx[j][0][lane] = make_uint2(rh0, rh1);
-      s_rx[j][1][lane] = make_uint2(rl0, rl1);
     } else {
       // ---- A (output): Q S for row tile j; chunk n+1's K rows copied between the products
       int64_t ta;
@@ -1961,45 +1994,58 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
       // the copies go out first, so that the chain waves' LDS reads are served alone
 #pragma unroll
       for (int jp = 0; jp < KJ; ++jp) dma_row_piece<16, NW>(kga, krow_bytes, La, ktab[jp], knext, j, jp);
-      f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = qa;
+      f32x4 qa[CT], qb[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        qa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        qb[ct] = qa[ct];
+      }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const bf16x8 sh = __builtin_bit_cast(bf16x8, s_sx[m][0][lane]);
-        const bf16x8 sl = __builtin_bit_cast(bf16x8, s_sx[m][1][lane]);
         const bf16x8 aq = frag_rows(s_q, KS_STRIDE, 16 * j, 32 * m, lane);
-        qa = mma(aq, sh, qa);
-        qb = mma(aq, sl, qb);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const bf16x8 sh = __builtin_bit_cast(bf16x8, s_sx[ct][m][0][lane]);
+          const bf16x8 sl = __builtin_bit_cast(bf16x8, s_sx[ct][m][1][lane]);
+          qa[ct] = mma(aq, sh, qa[ct]);
+          qb[ct] = mma(aq, sl, qb[ct]);
+        }
       }
       const float cqv[4] = {cq.x, cq.y, cq.z, cq.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) QS[e] = cqv[e] * (qa[e] + qb[e]);
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) QS[ct][e] = cqv[e] * (qa[ct][e] + qb[ct][e]);
     }
     lds_barrier();     // (2) R tiles exchanged; every wave has read the slabs, Q, factors, V
     if (chain) {
       // ---- A2 (chain): U = T' R for row tile j
-      const bf16x8 rh = pack8(s_rx[0][0][lane], s_rx[1][0][lane]);
-      const bf16x8 rl = pack8(s_rx[0][1][lane], s_rx[1][1][lane]);
-      bf16x8 rh1 = pack8(s_rx[2][0][lane], s_rx[3][0][lane]);
-      bf16x8 rl1 = pack8(s_rx[2][1][lane], s_rx[3][1][lane]);
-      asm volatile("" : "+v"(rh1), "+v"(rl1));   // keeps the reads out of the branch below
-      f32x4 ua = mma(cur.th[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 ub = mma(cur.tl[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
-      ua = mma(cur.th[0], rl, ua);
-      if (j >= 2) {
-        ub = mma(cur.th[1], rh1, ub);
-        ua = mma(cur.tl[1], rh1, ua);
-        ub = mma(cur.th[1], rl1, ub);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const bf16x8 rh = pack8(s_rx[ct][0][0][lane], s_rx[ct][1][0][lane]);
+        const bf16x8 rl = pack8(s_rx[ct][0][1][lane], s_rx[ct][1][1][lane]);
+        bf16x8 rh1 = pack8(s_rx[ct][2][0][lane], s_rx[ct][3][0][lane]);
+        bf16x8 rl1 = pack8(s_rx[ct][2][1][lane], s_rx[ct][3][1][lane]);
+        asm volatile("" : "+v"(rh1), "+v"(rl1));   // keeps the reads out of the branch below
+        f32x4 ua = mma(cur.th[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 ub = mma(cur.tl[0], rh, f32x4{0.f, 0.f, 0.f, 0.f});
+        ua = mma(cur.th[0], rl, ua);
+        if (j >= 2) {
+          ub = mma(cur.th[1], rh1, ub);
+          ua = mma(cur.tl[1], rh1, ua);
+          ub = mma(cur.th[1], rl1, ub);
+        }
+        const f32x4 U = ua + ub;
+        uint32_t uh0, ul0, uh1, ul1, wh0, wl0, wh1, wl1;
+        split2(U[0], U[1], uh0, ul0);
+        split2(U[2], U[3], uh1, ul1);
+        split2(c2.x * U[0], c2.y * U[1], wh0, wl0);
+        split2(c2.z * U[2], c2.w * U[3], wh1, wl1);
+        s_ux[ct][j][0][lane] = make_uint2(uh0, uh1);
+        s_ux[ct][j][1][lane] = make_uint2(ul0, ul1);
+        s_ux[ct][j][2][lane] = make_uint2(wh0, wh1);
+        s_ux[ct][j][3][lane] = make_uint2(wl0, wl1);
       }
-      const f32x4 U = ua + ub;
-      uint32_t uh0, ul0, uh1, ul1, wh0, wl0, wh1, wl1;
-      split2(U[0], U[1], uh0, ul0);
-      split2(U[2], U[3], uh1, ul1);
-      split2(c2.x * U[0], c2.y * U[1], wh0, wl0);
-      split2(c2.z * U[2], c2.w * U[3], wh1, wl1);
-      s_ux[j][0][lane] = make_uint2(uh0, uh1);
-      s_ux[j][1][lane] = make_uint2(ul0, ul1);
-      s_ux[j][2][lane] = make_uint2(wh0, wh1);
-      s_ux[j][3][lane] = make_uint2(wl0, wl1);
     } else {
       stage_qfv(na);
     }
@@ -2008,52 +2054,59 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
     if (chain) {
       // ---- B (chain): S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U for
       // state rows 32 j .. 32 j + 31, K^T read transposed from this chunk's K rows
-      bf16x8 wh[2], wl[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        wh[m] = pack8(s_ux[2 * m][2][lane], s_ux[2 * m + 1][2][lane]);
-        wl[m] = pack8(s_ux[2 * m][3][lane], s_ux[2 * m + 1][3][lane]);
-      }
       bf16x8 ak[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int m = 0; m < 2; ++m) ak[t][m] = frag_kt(kcur, 32 * j + 16 * t, 32 * m, lane);
-      f32x4 sb[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int ct = 0; ct < CT; ++ct) {
+        bf16x8 wh[2], wl[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) St[t][e] *= egl;
-        sb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m) {
+          wh[m] = pack8(s_ux[ct][2 * m][2][lane], s_ux[ct][2 * m + 1][2][lane]);
+          wl[m] = pack8(s_ux[ct][2 * m][3][lane], s_ux[ct][2 * m + 1][3][lane]);
+        }
+        f32x4 sb[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          St[t] = mma(ak[t][m], wh[m], St[t]);
-          sb[t] = mma(ak[t][m], wl[m], sb[t]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) St[ct][t][e] *= egl;
+          sb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-      St[0] += sb[0];
-      St[1] += sb[1];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            St[ct][t] = mma(ak[t][m], wh[m], St[ct][t]);
+            sb[t] = mma(ak[t][m], wl[m], sb[t]);
+          }
+        St[ct][0] += sb[0];
+        St[ct][1] += sb[1];
+      }
       put_slab();
     } else {
       // ---- B (output): O = scale (Q S + P U) for row tile j, to the LDS output tile
-      const bf16x8 uh = pack8(s_ux[0][0][lane], s_ux[1][0][lane]);
-      const bf16x8 ul = pack8(s_ux[0][1][lane], s_ux[1][1][lane]);
-      bf16x8 uh1 = pack8(s_ux[2][0][lane], s_ux[3][0][lane]);
-      bf16x8 ul1 = pack8(s_ux[2][1][lane], s_ux[3][1][lane]);
-      asm volatile("" : "+v"(uh1), "+v"(ul1));   // keeps the reads out of the branch below
-      f32x4 pa = mma(cur.th[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 pb = mma(cur.tl[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
-      pa = mma(cur.th[0], ul, pa);
-      if (j >= 2) {
-        pb = mma(cur.th[1], uh1, pb);
-        pa = mma(cur.tl[1], uh1, pa);
-        pb = mma(cur.th[1], ul1, pb);
-      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s_ost[(16 * j + 4 * g4 + e) * O_STRIDE + c16] = f2bf(p.scale * (QS[e] + pa[e] + pb[e]));
+      for (int ct = 0; ct < CT; ++ct) {
+        const bf16x8 uh = pack8(s_ux[ct][0][0][lane], s_ux[ct][1][0][lane]);
+        const bf16x8 ul = pack8(s_ux[ct][0][1][lane], s_ux[ct][1][1][lane]);
+        bf16x8 uh1 = pack8(s_ux[ct][2][0][lane], s_ux[ct][3][0][lane]);
+        bf16x8 ul1 = pack8(s_ux[ct][2][1][lane], s_ux[ct][3][1][lane]);
+        asm volatile("" : "+v"(uh1), "+v"(ul1));   // keeps the reads out of the branch below
+        f32x4 pa = mma(cur.th[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 pb = mma(cur.tl[0], uh, f32x4{0.f, 0.f, 0.f, 0.f});
+        pa = mma(cur.th[0], ul, pa);
+        if (j >= 2) {
+          pb = mma(cur.th[1], uh1, pb);
+          pa = mma(cur.tl[1], uh1, pa);
+          pb = mma(cur.th[1], ul1, pb);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s_ost[(16 * j + 4 * g4 + e) * O_STRIDE + 16 * ct + c16] =
+              f2bf(p.scale * (QS[ct][e] + pa[e] + pb[e]));
+      }
     }
   };
   for (int n = 0; n < ne; n += 2) {
@@ -2068,9 +2121,11 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
   if (chain && p.state_out) {
     float* sp = p.state_out + ((int64_t)s * Hv + h) * DK * DV + col;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sp[(32 * j + 16 * t + 4 * g4 + e) * DV] = St[t][e];
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp[(32 * j + 16 * t + 4 * g4 + e) * DV + 16 * ct] = St[ct][t][e];
   }
 }
 
@@ -2171,9 +2226,16 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   const int64_t rb = ws_rec_bytes(four);
   if (rowsplit) {
     const int64_t groups = (int64_t)a.Ns * a.Hk;
-    const dim3 grid((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * rs::NBLK));
-    hipLaunchKernelGGL(chunk_rowsplit2_kernel, grid, dim3(rs2::THR), 0, st, a,
-                       (const int32_t*)cmap, (const uint8_t*)recs);
+    // two column tiles per workgroup where one tile's workgroups would need two per CU
+    const bool ct2 = pairs * rs::NBLK > cus;
+    const int nblk = ct2 ? rs::Cols<2>::NBLK : rs::Cols<1>::NBLK;
+    const dim3 grid((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * nblk));
+    if (ct2)
+      hipLaunchKernelGGL(chunk_rowsplit2_kernel<2>, grid, dim3(rs2::THR), 0, st, a,
+                         (const int32_t*)cmap, (const uint8_t*)recs);
+    else
+      hipLaunchKernelGGL(chunk_rowsplit2_kernel<1>, grid, dim3(rs2::THR), 0, st, a,
+                         (const int32_t*)cmap, (const uint8_t*)recs);
     return hipGetLastError();
   }
   SegArgs sg{G, 0, G, segs, rb};
