@@ -68,6 +68,10 @@ def _both(d, hk, hv, in_place=False):
     ("bf16", 16, 32, [8192], False),        # 2064 prep workgroups, row-split sweep
     ("bf16", 4, 8, LENS * 24, True),        # 288 sequences, 8-wave sweep
     ("bf16", 1, 2, [16500], False),         # 2 long chains: the intra-sequence scan
+    # more than four value heads per key head: the prep stages gates in batches of four,
+    # and the fused conv takes two (112 channel groups) or three (160) passes
+    ("bf16", 1, 5, LENS[:7], False),        # 35 chains: row-split sweep, a partial batch
+    ("bf16", 2, 16, LENS * 4, True),        # 768 chains: 8-wave sweep, two full batches
 ])
 def test_fused_equals_two_calls(io, hk, hv, lens, in_place):
     inp, d = _inputs(hk, hv, io, 70 + len(lens), lens)

@@ -104,10 +104,12 @@ def _run_prefill(inp, io, use_l2=True, g=None, beta=None, with_state=True):
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-@pytest.mark.parametrize("hk,hv", [(2, 2), (1, 2), (1, 4)])
+@pytest.mark.parametrize("hk,hv", [(2, 2), (1, 2), (1, 4), (1, 5), (1, 8)])
 def test_chunk_prefill_parity_small(io, hk, hv):
-    """Ragged, empty and multi-chunk sequences with carried state; for bf16 the 16-32
-    chains' row-split workgroups fit the chip at once (the chain/output sweep)."""
+    """Ragged, empty and multi-chunk sequences with carried state; for bf16 the 16-64
+    chains' row-split workgroups fit the chip at once (the chain/output sweep).  More than
+    four value heads per key head take the prep's gates in batches of four: 5 ends on a
+    partial batch, 8 is two full ones."""
     lens = [1, 63, 64, 65, 200, 0, 3, 130]
     inp = _case(hk, hv, io, 20 + hv, seqlens=lens, init_state=True)
     y, o, s = _run_prefill(inp, io)
