@@ -2169,9 +2169,12 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   // the tokens fill; the grid's spare rows return at once)
   const int prep_mode = rowsplit ? PREP_FRAG : four ? PREP_ROWS_P : PREP_ROWS;
   const int64_t chunks = (a.N + CH - 1) / CH + a.Ns - 1;
-  const bool conv_in_prep = a.x != nullptr && IO == IO_BF16 &&
+  // the call includes the conv: x given, or (no tokens, x may then be NULL) a final conv
+  // state to write, which is then the initial one
+  const bool conv = a.x != nullptr || a.conv_state_out != nullptr;
+  const bool conv_in_prep = conv && IO == IO_BF16 &&
                             chunks * a.Hk <= (int64_t)prep_occupancy(IO, prep_mode) * cus;
-  if (a.x != nullptr && !conv_in_prep) {
+  if (conv && !conv_in_prep) {
     const ConvArgs ca{a.x, a.conv_w, a.y, a.cu, a.Ns, a.N, a.Cq, a.conv_state_in, a.conv_state_out};
     e = launch_conv1d(ca, IO, st);
     if (e != hipSuccess) return e;

@@ -420,6 +420,53 @@ def test_step_entry_points_accept_an_empty_batch():
     assert torch.count_nonzero(st) == 0
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("ns", [1, 3])
+def test_prefill_entry_points_accept_zero_tokens(io, ns):
+    """N = 0: every sequence is empty, so the final recurrent and conv states equal the
+    initial ones and nothing else is written (Ns = 1 without cu_seqlens, Ns = 3 with all
+    offsets zero)."""
+    hk, hv = 2, 4
+    C = (2 * hk + hv) * D
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.empty((0, C), dtype=dt, device="cuda")
+    y = torch.empty_like(x)
+    ab = torch.empty((0, hv), dtype=dt, device="cuda")
+    o = torch.empty((0, hv, D), dtype=dt, device="cuda")
+    z = torch.empty_like(o)
+    yn = torch.empty_like(o)
+    w = torch.randn(C, 4, device="cuda", generator=g)
+    hvf = torch.rand(hv, device="cuda", generator=g)
+    nw = torch.ones(D, device="cuda")
+    cu = None if ns == 1 else torch.zeros(ns + 1, dtype=torch.int32, device="cuda")
+    s_in = torch.randn(ns, hv, D, D, device="cuda", generator=g)
+    cs_in = torch.randn(ns, 3, C, device="cuda", generator=g).to(dt)
+    q, k, v = qkv_views(y, hk, hv)
+    calls = {
+        "conv": lambda so, co: gdn.gdn_conv1d_fwd(x, w, y, cu, cs_in, co),
+        "chunk": lambda so, co: gdn.gdn_chunk_prefill(q, k, v, ab, ab, hvf, hvf, o, hk, hv, cu,
+                                                      s_in, so),
+        "chunk_noalloc": lambda so, co: gdn.gdn_chunk_prefill_noalloc(
+            q, k, v, ab, ab, hvf, hvf, o, hk, hv, cu, s_in, so),
+        "conv_chunk": lambda so, co: gdn.gdn_conv_chunk_prefill(
+            x, w, y, ab, ab, hvf, hvf, o, hk, hv, cu, cs_in, co, s_in, so),
+        "layer": lambda so, co: gdn.gdn_prefill_layer(
+            x, w, y, ab, ab, hvf, hvf, o, z, nw, yn, hk, hv, cu, cs_in, co, s_in, so),
+    }
+    for name, call in calls.items():
+        s_out = torch.full_like(s_in, 7.0)
+        cs_out = torch.full_like(cs_in, 7.0)
+        call(s_out, cs_out)
+        torch.cuda.synchronize()
+        if name != "conv":
+            assert torch.equal(s_out, s_in), f"{name}: recurrent state"
+        if name not in ("chunk", "chunk_noalloc"):
+            assert torch.equal(cs_out, cs_in), f"{name}: conv state"
+    gdn.gdn_gated_rmsnorm(o, z, nw, yn)
+    torch.cuda.synchronize()
+
+
 def test_prefill_then_steps_equals_prefill():
     """Prefill of T1 tokens then T - T1 decode steps on carried state == prefill of T."""
     io = "bf16"
