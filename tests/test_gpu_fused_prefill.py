@@ -233,3 +233,41 @@ def test_prefill_layer_equals_conv_chunk_then_norm(hk, hv, lens):
         assert torch.equal(u, v), name
     ref = G.layer(inp)
     assert_out(host(outs[0][2]), ref["y_exact"], io, "layer y", upstream_bf16=2)
+
+
+@pytest.mark.parametrize("io,hk,hv,lens", [
+    ("bf16", 2, 4, LENS),          # row-split sweep, two column tiles per workgroup
+    ("bf16", 2, 4, LENS * 2),      # 4-wave sweep
+    ("bf16", 2, 4, LENS * 4),      # 8-wave sweep
+    ("f32", 2, 4, LENS),           # fp32 io
+    ("bf16", 1, 2, [16500]),       # the intra-sequence scan
+])
+def test_chunk_prefill_row_strides_and_no_state_out(io, hk, hv, lens):
+    """q, k and v in three separate buffers with padded rows (their own row strides, not
+    views into one conv output) give the same o and final state bit for bit; and a call
+    without state_out gives the same o."""
+    inp, d = _inputs(hk, hv, io, 110 + len(lens), lens)
+    x = d["x"]
+    N = x.shape[0]
+    Ns = d["cu"].numel() - 1
+    y = torch.empty_like(x)
+    gdn.gdn_conv1d_fwd(x, d["conv_w"], y, d["cu"], d["conv_state_in"], None)
+    q, k, v = qkv_views(y, hk, hv)
+    padded = []
+    for t, pad in ((q, 24), (k, 8), (v, 40)):
+        buf = torch.full((N, t.shape[1] + pad), float("nan"), dtype=t.dtype, device="cuda")
+        buf[:, : t.shape[1]] = t
+        padded.append(buf[:, : t.shape[1]])
+    outs = []
+    for qq, kk, vv, with_state in ((q, k, v, True), (*padded, True), (q, k, v, False)):
+        o = torch.empty((N, hv, D), dtype=x.dtype, device="cuda")
+        s_out = torch.empty((Ns, hv, D, D), device="cuda") if with_state else None
+        gdn.gdn_chunk_prefill(qq, kk, vv, d["a"], d["b"], d["A_log"], d["dt_bias"], o, hk, hv,
+                              d["cu"], d["state_in"], s_out)
+        outs.append((o, s_out))
+    torch.cuda.synchronize()
+    assert padded[0].stride(0) != q.stride(0)
+    assert torch.equal(outs[0][0], outs[1][0]), "o with padded rows"
+    assert torch.equal(outs[0][1], outs[1][1]), "state with padded rows"
+    assert torch.equal(outs[0][0], outs[2][0]), "o without state_out"
+    assert torch.isfinite(outs[0][0].float()).all()
