@@ -242,6 +242,46 @@ def test_chunk_prefill_orthonormal_recall():
     np.testing.assert_allclose(keys.astype(np.float64) @ S, vals, atol=2e-4)
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_explicit_output_scale(io):
+    """A caller-given output scale (0.3, not 1/sqrt(dk)) in the chunked core, on the
+    row-split sweep (bf16) and the 4-wave sweep (fp32), and in the decode step."""
+    hk, hv, scale = 1, 2, 0.3
+    inp = _case(hk, hv, io, 31, seqlens=[70, 5, 130], init_state=True)
+    y_ref, _ = G.conv1d_fwd(inp["x"], inp["conv_w"], inp["cu_seqlens"], inp["conv_state_in"])
+    y_io = G.to_io(y_ref, io).astype(np.float32)
+    yd = to_dev(y_io, io)
+    q, k, v = qkv_views(yd, hk, hv)
+    N = inp["N"]
+    o = torch.empty((N, hv, D), dtype=yd.dtype, device="cuda")
+    s_out = torch.empty((inp["Ns"], hv, D, D), device="cuda")
+    gdn.gdn_chunk_prefill(q, k, v, to_dev(inp["a"], io), to_dev(inp["b"], io),
+                          f32_dev(inp["A_log"]), f32_dev(inp["dt_bias"]), o, hk, hv, _cu_dev(inp),
+                          f32_dev(inp["state_in"]), s_out, scale=scale)
+    torch.cuda.synchronize()
+    y64 = y_io.astype(np.float64)
+    o_ref, s_ref = G.prefill(y64[:, : hk * D], y64[:, hk * D: 2 * hk * D], y64[:, 2 * hk * D:],
+                             inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv, D, D,
+                             inp["state_in"], inp["cu_seqlens"], scale=scale)
+    assert_out(host(o), o_ref, io, "prefill o, scale 0.3")
+    assert_state(host(s_out), s_ref, "prefill state, scale 0.3")
+
+    dec = _case(hk, hv, io, 32, batch=5, init_state=True, kind="decode")
+    x = to_dev(dec["x"], io)
+    cs = to_dev(dec["conv_state_in"], io)
+    st = f32_dev(dec["state_in"])
+    od = torch.empty((5, hv, D), dtype=x.dtype, device="cuda")
+    gdn.gdn_recurrent_step(x, f32_dev(dec["conv_w"]), cs, to_dev(dec["a"], io),
+                           to_dev(dec["b"], io), f32_dev(dec["A_log"]), f32_dev(dec["dt_bias"]),
+                           st, od, hk, hv, scale=scale)
+    torch.cuda.synchronize()
+    od_ref, _, st_ref = G.recurrent_step(dec["x"], dec["conv_w"], dec["conv_state_in"], dec["a"],
+                                         dec["b"], dec["A_log"], dec["dt_bias"], dec["state_in"],
+                                         hk, hv, D, D, scale=scale, io=io)
+    assert_out(host(od), od_ref, io, "step o, scale 0.3", upstream_bf16=1)
+    assert_state(host(st), st_ref, "step state, scale 0.3")
+
+
 # ------------------------------------------------------------------------- decode step
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("hk,hv", [(2, 4), (2, 2), (1, 4), (1, 3)])
