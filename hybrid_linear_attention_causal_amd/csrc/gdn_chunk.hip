@@ -28,7 +28,11 @@
 //      registers for the whole sequence and walks the chunks in order; per chunk
 //      the S-dependent products (K S, T' R, Q S + P U, K^T U) and the chunk's P
 //      (from the Q and K rows it stages) run on operands staged in LDS by DMA
-//      while the other phase's products run.
+//      while the other phase's products run.  With few chains (bf16, B = 1) the
+//      sweep instead spreads each chain over more compute units: the row-split
+//      sweep (16 columns per workgroup, its rows over four chain waves) while those
+//      workgroups fit the chip at once, else the column-chain sweep (two 16-column
+//      tiles per workgroup, one chain wave each).
 //
 // MFMA use: v_mfma_f32_16x16x32_bf16.  Operand fragments use a permuted
 // contraction index (lane group g, element e -> k = 4g + e for e < 4, 16 + 4g
@@ -1734,9 +1738,10 @@ constexpr int THR = 64 * NW;
 constexpr int NBLK = DV / 16;            // workgroups per chain with one column tile
 constexpr int ROWS = CH * KS_STRIDE;
 constexpr int KJ = RowDma<16, NW>::J;    // K or Q row copies per wave
-// CT 16-column tiles of dv per workgroup: CT = 2 halves the workgroups per chain (and
-// reads each K, Q, T' and P fragment once for both tiles) where CT = 1 would need two
-// workgroups per CU
+// CT 16-column tiles of dv per workgroup.  One tile is what runs: where one tile's
+// workgroups would need two per CU, two tiles per workgroup run on the column-chain sweep
+// instead (a CT = 2 instance of this kernel, which reads each K, Q, T' and P fragment once
+// for both tiles, measured 1-4% slower than that)
 template <int CT>
 struct Cols {
   static constexpr int DVB = 16 * CT;           // dv columns per workgroup
@@ -1776,8 +1781,8 @@ namespace rs2 {
 constexpr int THR = 2 * rs::THR;
 }
 
-// (CT = 1: four waves per SIMD, two workgroups per CU; CT = 2: one workgroup per CU, so
-// two waves per SIMD and their registers)
+// (CT = 1: four waves per SIMD, two workgroups per CU; CT = 2 would run one workgroup per
+// CU, so two waves per SIMD and their registers)
 template <int CT>
 __global__ void __launch_bounds__(rs2::THR, CT == 1 ? 4 : 2)
 chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
@@ -2129,6 +2134,376 @@ chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint
   }
 }
 
+// ============================================================================ 3c. column-chain sweep
+// bf16 io, one sequence-head chain's 128 dv columns over 128 / (16 CT) workgroups, one
+// workgroup per CU.  Each 16-column tile has two waves:
+//   chain wave: keeps the tile's whole 128 x 16 state slice in registers (eight accumulator
+//     tiles, tile t = state rows 16 t .. 16 t + 15) and walks the chunks: K S for the four
+//     token tiles, R = V - diag(c_k) K S, U = T' R, S <- e^{gamma_L} S + K^T diag(c_2) U.
+//     Every product's accumulator is the next one's B operand, so nothing is exchanged
+//     inside a chunk; the chunk's start state (as bf16 hi/lo fragments) and U (fp32) are
+//     left in LDS.
+//   output wave: forms chunk n-1's output O = scale (diag(c_q) Q S + P U) from what the
+//     chain wave left while that wave walks chunk n, storing it through an LDS tile as
+//     16-byte rows; the output waves also copy chunk n+1's K, V, factor and Q rows into LDS
+//     (the first one K, V and the factors, the last one Q).
+// The waves of a workgroup each run on their own SIMD, and the tiles of a workgroup share
+// the staged rows.  One barrier per chunk, where the chain waves end it.  K and V rows are
+// double-buffered by chunk parity; Q and factor rows, read one chunk later by the output
+// waves, by chunk mod 3; the handed-over state and U by parity.  T' (chain) and P (output)
+// fragments go straight from the fragment-native records to registers, a chunk ahead.
+namespace cc {
+constexpr int ROWS = CH * KS_STRIDE;      // u16 per staged K or Q chunk
+constexpr int KJ = RowDma<16, 1>::J;      // K or Q row copies per chunk
+constexpr int O_STRIDE = 16 + 8;          // u16 per staged output row of a tile
+// fragment index of (row tile j, token slab m) in the lower-triangular T' / P operands
+__device__ __forceinline__ constexpr int fi(int j, int m) { return j < 2 ? j : 2 * j - 2 + m; }
+template <int CT>
+struct Cfg {
+  static constexpr int THR = 128 * CT;          // CT chain waves, then CT output waves
+  static constexpr int DVB = 16 * CT;           // dv columns per workgroup
+  static constexpr int NBLK = DV / DVB;         // workgroups per chain
+  static constexpr int VW = DVB * 2 / 16;       // 16-byte words per V row slice
+  static constexpr int V_STRIDE = DVB + 8;      // u16 per staged V row (pad: one more word)
+  static constexpr int VJ = RowDma<VW, 1>::J;   // V row copies per chunk
+};
+}  // namespace cc
+
+template <int CT>
+__global__ void __launch_bounds__(cc::Cfg<CT>::THR, 1)
+chunk_colchain_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
+  typedef Io<IO_BF16>::T T;
+  using namespace cc;
+  typedef Cfg<CT> C;
+  constexpr int DVB = C::DVB, NBLK = C::NBLK, VW = C::VW, V_STRIDE = C::V_STRIDE, VJ = C::VJ;
+  __shared__ __attribute__((aligned(16))) u16 s_k[2][ROWS];             // K rows, by chunk parity
+  __shared__ __attribute__((aligned(16))) u16 s_q[3][ROWS];             // Q rows, by chunk mod 3
+  __shared__ __attribute__((aligned(16))) u16 s_v[2][CH * V_STRIDE];    // V slice, by parity
+  __shared__ __attribute__((aligned(16))) float s_f[3][4 * CH];         // c_k, c_q, c_2, e^{gamma_L}
+  __shared__ __attribute__((aligned(16))) uint4 s_sx[2][CT][4][2][64];  // start state: slab, hi/lo
+  __shared__ __attribute__((aligned(16))) float4 s_u[2][CT][4][64];     // U tiles (fp32)
+  __shared__ __attribute__((aligned(16))) u16 s_ost[CT][CH * O_STRIDE]; // output tiles
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool chain = wv < CT;          // wave-uniform role
+  const int ct = chain ? wv : wv - CT; // the wave's column tile
+  const int g4 = lane >> 4;
+  const int c16 = lane & 15;
+
+  // workgroup -> (sequence, value head, column block): the r * NBLK workgroups of a key
+  // head are consecutive in blockIdx / 8 (they read the same K and Q rows)
+  const int Hv = p.Hv, r = Hv / p.Hk;
+  const int GS = r * NBLK;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int member = slot % GS;
+  const int group = (slot / GS) * 8 + xcd;
+  if (group >= p.Ns * p.Hk) return;
+  const int blk = member % NBLK;
+  const int kh = group % p.Hk;
+  const int s = group / p.Hk;
+  const int h = kh * r + member / NBLK;
+  int64_t b0, b1;
+  seq_bounds(p.cu, p.N, s, b0, b1);
+  const int c0 = p.Ns == 1 ? 0 : cmap[s];
+  const int ne = (int)((b1 - b0 + CH - 1) / CH);
+  const int col = blk * DVB + 16 * ct + c16;
+
+  auto chunk_rows = [&](int n, int64_t& t0, int& L) {
+    t0 = b0 + (int64_t)n * CH;
+    L = (int)min((int64_t)CH, b1 - t0);
+  };
+  auto rec_of = [&](int n) { return recs + ((int64_t)(c0 + n) * Hv + h) * FR_REC_BYTES; };
+  // chunk n's six lower-triangular fragments (hi, lo) of T' (chain wave) or P (output wave)
+  auto load_frags = [&](int n, bf16x8 (&fh)[6], bf16x8 (&fl)[6]) {
+    const uint8_t* rec = rec_of(n) + (chain ? FR_T_OFF : FR_P_OFF) + lane * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int m = 0; m < (j < 2 ? 1 : 2); ++m) {
+        fh[fi(j, m)] = *reinterpret_cast<const bf16x8*>(rec + fr_tp(j, m, 0));
+        fl[fi(j, m)] = *reinterpret_cast<const bf16x8*>(rec + fr_tp(j, m, 1));
+      }
+  };
+  // Y = M X for a lower-triangular M given by its fragments and X by the B operands of its
+  // two token slabs (hi, lo): three passes (Mh Xh, Ml Xh, Mh Xl)
+  auto tri = [&](const bf16x8 (&mh)[6], const bf16x8 (&ml)[6], const bf16x8 (&xh)[2],
+                 const bf16x8 (&xl)[2], f32x4 (&y)[4]) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 y2[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = mma(mh[fi(j, 0)], xh[0], z);
+#pragma unroll
+    for (int j = 2; j < 4; ++j) y2[j - 2] = mma(mh[fi(j, 1)], xh[1], z);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = mma(ml[fi(j, 0)], xh[0], y[j]);
+#pragma unroll
+    for (int j = 2; j < 4; ++j) y2[j - 2] = mma(ml[fi(j, 1)], xh[1], y2[j - 2]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = mma(mh[fi(j, 0)], xl[0], y[j]);
+#pragma unroll
+    for (int j = 2; j < 4; ++j) y2[j - 2] = mma(mh[fi(j, 1)], xl[1], y2[j - 2]);
+    y[2] += y2[0];
+    y[3] += y2[1];
+  };
+
+  if (chain) {
+    // ------------------------------------------------------------------ chain wave
+    f32x4 St[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) St[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.state_in) {
+      const float* sp = p.state_in + ((int64_t)s * Hv + h) * DK * DV + col;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) St[t][e] = sp[(16 * t + 4 * g4 + e) * DV];
+    }
+    bf16x8 th[6], tl[6];
+    if (ne > 0) load_frags(0, th, tl);
+    bf16x8 sh[4], sl[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) frag_acc_split(St[2 * m], St[2 * m + 1], sh[m], sl[m]);
+    lds_barrier();   // chunk 0's rows are in LDS
+
+    auto chunk = [&](int n, auto par) {
+      constexpr int PAR = decltype(par)::value;
+      const u16* kc = s_k[PAR];
+      const float* f = s_f[n % 3];
+      // the chunk's start state for the output wave
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        s_sx[PAR][ct][m][0][lane] = __builtin_bit_cast(uint4, sh[m]);
+        s_sx[PAR][ct][m][1][lane] = __builtin_bit_cast(uint4, sl[m]);
+      }
+      // K S for token tiles 0 .. 3; every K fragment, the V slice and the factors are read
+      // up front (no read sits under a condition, which would wait for it in place)
+      bf16x8 ak[4][4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ak[m][i] = frag_rows(kc, KS_STRIDE, 16 * i, 32 * m, lane);
+      u16 vraw[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vraw[i][e] = s_v[PAR][(16 * i + 4 * g4 + e) * V_STRIDE + 16 * ct + c16];
+      float4 ck[4], c2[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ck[i] = *reinterpret_cast<const float4*>(&f[16 * i + 4 * g4]);
+        c2[i] = *reinterpret_cast<const float4*>(&f[2 * CH + 16 * i + 4 * g4]);
+      }
+      const float egl = f[3 * CH];
+      f32x4 ks[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ks[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ks[i] = mma(ak[m][i], sh[m], ks[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ks[i] = mma(ak[m][i], sl[m], ks[i]);
+      }
+      // the update's K^T fragments, read while R and U are formed
+      bf16x8 kt[2][8];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) kt[m][t] = frag_kt(kc, 16 * t, 32 * m, lane);
+      // R = V - diag(e^gamma / |k|) K S (rows past the chunk end are zero)
+      int64_t t0;
+      int L;
+      chunk_rows(n, t0, L);
+      f32x4 R[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ckv[4] = {ck[i].x, ck[i].y, ck[i].z, ck[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * i + 4 * g4 + e;
+          const float vv = t < L ? bf2f(vraw[i][e]) : 0.f;
+          R[i][e] = vv - ckv[e] * ks[i][e];
+        }
+      }
+      bf16x8 rh[2], rl[2];
+      frag_acc_split(R[0], R[1], rh[0], rl[0]);
+      frag_acc_split(R[2], R[3], rh[1], rl[1]);
+      // U = T' R
+      f32x4 U[4];
+      tri(th, tl, rh, rl, U);
+      // the next chunk's T' (this chunk's is dead), a chunk ahead of its use; the last
+      // chunk reloads its own
+      load_frags(n + 1 < ne ? n + 1 : n, th, tl);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_u[PAR][ct][i][lane] = __builtin_bit_cast(float4, U[i]);
+      // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma} / |k|) U
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        U[i][0] *= c2[i].x;
+        U[i][1] *= c2[i].y;
+        U[i][2] *= c2[i].z;
+        U[i][3] *= c2[i].w;
+      }
+      bf16x8 wh[2], wl[2];
+      frag_acc_split(U[0], U[1], wh[0], wl[0]);
+      frag_acc_split(U[2], U[3], wh[1], wl[1]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) St[t][e] *= egl;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) St[t] = mma(kt[m][t], wh[m], St[t]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) St[t] = mma(kt[m][t], wl[m], St[t]);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) frag_acc_split(St[2 * m], St[2 * m + 1], sh[m], sl[m]);
+      lds_barrier();   // this chunk's hand-over is in LDS; the next chunk's rows are too
+    };
+    for (int n = 0; n < ne; n += 2) {
+      chunk(n, std::integral_constant<int, 0>());
+      if (n + 1 < ne) chunk(n + 1, std::integral_constant<int, 1>());
+    }
+    if (p.state_out) {
+      float* sp = p.state_out + ((int64_t)s * Hv + h) * DK * DV + col;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp[(16 * t + 4 * g4 + e) * DV] = St[t][e];
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------------- output wave
+  const uint8_t* qg = (const uint8_t*)((const T*)p.q + (int64_t)kh * DK);
+  const uint8_t* kg = (const uint8_t*)((const T*)p.k + (int64_t)kh * DK);
+  const uint8_t* vg = (const uint8_t*)((const T*)p.v + (int64_t)h * DV + blk * DVB);
+  const uint32_t qrow_bytes = (uint32_t)(p.stride_q * (int64_t)sizeof(T));
+  const uint32_t krow_bytes = (uint32_t)(p.stride_k * (int64_t)sizeof(T));
+  const uint32_t vrow_bytes = (uint32_t)(p.stride_v * (int64_t)sizeof(T));
+  T* og0 = (T*)p.o + (int64_t)h * DV + blk * DVB + 16 * ct;
+  const int64_t o_stride = (int64_t)Hv * DV;
+  uint32_t ktab[KJ], vtab[VJ];
+  rows_table<16, 1>(0, lane, ktab);
+  rows_table<VW, 1>(0, lane, vtab);
+
+  // chunk n's rows into LDS (PAR = n & 1): K, V and the factors by the first output wave,
+  // Q by the last
+  auto stage = [&](int n, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    int64_t t0;
+    int L;
+    chunk_rows(n, t0, L);
+    if (ct == 0) {
+#pragma unroll
+      for (int jp = 0; jp < KJ; ++jp)
+        dma_row_piece<16, 1>(kg + t0 * krow_bytes, krow_bytes, L, ktab[jp], s_k[PAR], 0, jp);
+#pragma unroll
+      for (int jp = 0; jp < VJ; ++jp)
+        dma_row_piece<VW, 1>(vg + t0 * vrow_bytes, vrow_bytes, L, vtab[jp], s_v[PAR], 0, jp);
+      lds_dma16_sbase(rec_of(n) + FR_FAC_OFF, lane * 16, (char*)s_f[n % 3]);
+    }
+    if (ct == CT - 1) {
+#pragma unroll
+      for (int jp = 0; jp < KJ; ++jp)
+        dma_row_piece<16, 1>(qg + t0 * qrow_bytes, qrow_bytes, L, ktab[jp], s_q[n % 3], 0, jp);
+    }
+  };
+  // chunk n's output from the chain wave's hand-over (PAR = n & 1) and P
+  auto output = [&](int n, auto par, const bf16x8 (&ph)[6], const bf16x8 (&pl)[6]) {
+    constexpr int PAR = decltype(par)::value;
+    const u16* qc = s_q[n % 3];
+    const float* f = s_f[n % 3];
+    u16* ost = s_ost[ct];
+    bf16x8 sh[4], sl[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      sh[m] = __builtin_bit_cast(bf16x8, s_sx[PAR][ct][m][0][lane]);
+      sl[m] = __builtin_bit_cast(bf16x8, s_sx[PAR][ct][m][1][lane]);
+    }
+    f32x4 qs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qs[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      bf16x8 aq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) aq[i] = frag_rows(qc, KS_STRIDE, 16 * i, 32 * m, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qs[i] = mma(aq[i], sh[m], qs[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qs[i] = mma(aq[i], sl[m], qs[i]);
+    }
+    f32x4 U[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) U[i] = __builtin_bit_cast(f32x4, s_u[PAR][ct][i][lane]);
+    bf16x8 uh[2], ul[2];
+    frag_acc_split(U[0], U[1], uh[0], ul[0]);
+    frag_acc_split(U[2], U[3], uh[1], ul[1]);
+    f32x4 pu[4];
+    tri(ph, pl, uh, ul, pu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 cq = *reinterpret_cast<const float4*>(&f[CH + 16 * i + 4 * g4]);
+      const float cqv[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ost[(16 * i + 4 * g4 + e) * O_STRIDE + c16] = f2bf(p.scale * (cqv[e] * qs[i][e] + pu[i][e]));
+    }
+    int64_t t0;
+    int L;
+    chunk_rows(n, t0, L);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int sl2 = lane + 64 * k, row = sl2 >> 1, w = sl2 & 1;
+      const uint4 ov = *reinterpret_cast<const uint4*>(&ost[row * O_STRIDE + 8 * w]);
+      if (row < L) *reinterpret_cast<uint4*>(og0 + (t0 + row) * o_stride + 8 * w) = ov;
+    }
+  };
+
+  bf16x8 pah[6], pal[6], pbh[6], pbl[6];   // P of even and odd chunks
+  if (ne > 0) {
+    stage(0, std::integral_constant<int, 0>());
+    load_frags(0, pah, pal);
+  }
+  wait_vmem();
+  lds_barrier();
+  // interval n (between the chain waves' barriers n-1 and n): stage chunk n+1, load P of
+  // chunk n, form chunk n-1's output
+  auto interval = [&](int n, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    if (n + 1 < ne) stage(n + 1, std::integral_constant<int, 1 - PAR>());
+    if constexpr (PAR == 0) {
+      if (n > 0) load_frags(n, pah, pal);
+      if (n > 0) output(n - 1, std::integral_constant<int, 1>(), pbh, pbl);
+    } else {
+      load_frags(n, pbh, pbl);
+      output(n - 1, std::integral_constant<int, 0>(), pah, pal);
+    }
+    wait_vmem();
+    // every P load is complete here; redefining the registers tells the compiler so (it
+    // does not count the copies above, and would otherwise wait for them when P is used)
+#pragma unroll
+    for (int i = 0; i < 6; ++i) asm volatile("" : "+v"(pah[i]), "+v"(pal[i]), "+v"(pbh[i]), "+v"(pbl[i]));
+    lds_barrier();
+  };
+  for (int n = 0; n < ne; n += 2) {
+    interval(n, std::integral_constant<int, 0>());
+    if (n + 1 < ne) interval(n + 1, std::integral_constant<int, 1>());
+  }
+  if (ne > 0) {
+    if ((ne - 1) & 1)
+      output(ne - 1, std::integral_constant<int, 1>(), pbh, pbl);
+    else
+      output(ne - 1, std::integral_constant<int, 0>(), pah, pal);
+  }
+}
+
 template <int IO>
 static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   const int64_t cmax = ws_max_chunks(a.N, a.Ns);
@@ -2229,12 +2604,13 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   const int64_t rb = ws_rec_bytes(four);
   if (rowsplit) {
     const int64_t groups = (int64_t)a.Ns * a.Hk;
-    // two column tiles per workgroup where one tile's workgroups would need two per CU
+    // two column tiles per workgroup (the column-chain sweep) where one tile's row-split
+    // workgroups would need two per CU
     const bool ct2 = pairs * rs::NBLK > cus;
-    const int nblk = ct2 ? rs::Cols<2>::NBLK : rs::Cols<1>::NBLK;
+    const int nblk = ct2 ? cc::Cfg<2>::NBLK : rs::NBLK;
     const dim3 grid((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * nblk));
     if (ct2)
-      hipLaunchKernelGGL(chunk_rowsplit2_kernel<2>, grid, dim3(rs2::THR), 0, st, a,
+      hipLaunchKernelGGL(chunk_colchain_kernel<2>, grid, dim3(cc::Cfg<2>::THR), 0, st, a,
                          (const int32_t*)cmap, (const uint8_t*)recs);
     else
       hipLaunchKernelGGL(chunk_rowsplit2_kernel<1>, grid, dim3(rs2::THR), 0, st, a,
