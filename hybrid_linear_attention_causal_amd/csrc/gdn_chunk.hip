@@ -2271,12 +2271,6 @@ chunk_colchain_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
       constexpr int PAR = decltype(par)::value;
       const u16* kc = s_k[PAR];
       const float* f = s_f[n % 3];
-      // the chunk's start state for the output wave
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        s_sx[PAR][ct][m][0][lane] = __builtin_bit_cast(uint4, sh[m]);
-        s_sx[PAR][ct][m][1][lane] = __builtin_bit_cast(uint4, sl[m]);
-      }
       // K S for token tiles 0 .. 3; every K fragment, the V slice and the factors are read
       // up front (no read sits under a condition, which would wait for it in place)
       bf16x8 ak[4][4];
@@ -2306,6 +2300,13 @@ chunk_colchain_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8
         for (int i = 0; i < 4; ++i) ks[i] = mma(ak[m][i], sh[m], ks[i]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ks[i] = mma(ak[m][i], sl[m], ks[i]);
+      }
+      // the chunk's start state for the output wave, written once the K S reads are out
+      // (the output wave reads it after this chunk's barrier)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        s_sx[PAR][ct][m][0][lane] = __builtin_bit_cast(uint4, sh[m]);
+        s_sx[PAR][ct][m][1][lane] = __builtin_bit_cast(uint4, sl[m]);
       }
       // the update's K^T fragments, read while R and U are formed
       bf16x8 kt[2][8];
