@@ -27,7 +27,14 @@ Tolerances (stated once, used everywhere):
 * a bf16-stored state: the same Frobenius bound, and element by element
   |a - b| <= 2^-8 (|a| + |b|) + 1e-5 RMS (each side's bf16 store moves a value by
   half an ulp; 1e-5 RMS covers the fp32 arithmetic before it), with a != b on at
-  most 1% of the elements.
+  most 1% of the elements.  A decode step rounds its conv output to bf16 inside the
+  call, so the core's k and v carry one bf16 value upstream: where the fp32 and fp64
+  conv values straddle a rounding boundary, v_j differs by one ulp and column j of the
+  updated state by beta k_i times that ulp (k_c, likewise, moves row c), which is not a
+  rounding of the state element itself (measured with the oracle alone, an fp32 conv
+  feeding it: 1.0e-4 past that bound at a state RMS of 0.03).  Such a state has the
+  element bound on all but 1% of its elements, and the rest within the io outputs'
+  3e-2 RMS(ref).
 * conv state: bit-exact (it is a copy of input rows).
 """
 from __future__ import annotations
@@ -116,21 +123,31 @@ def assert_state(gpu, ref, what=""):
     return worst
 
 
-def assert_bf16_state(gpu, ref, what="", max_flip=0.01):
+def assert_bf16_state(gpu, ref, what="", max_flip=0.01, upstream_bf16=0):
     """gpu, ref: bf16-valued states; equal up to rounding neighbours on few elements.
 
     Before the bf16 store the two sides differ by the fp32 arithmetic error e of the
     step (taken as 1e-5 RMS(ref), about ten times a 128-term fp32 dot product's); each
     store then moves a value by at most half an ulp, 2^-8 |x|.  So element by element
-    |a - b| <= 2^-8 (|a| + |b|) + e, and a and b differ on at most max_flip of them."""
+    |a - b| <= 2^-8 (|a| + |b|) + e, and a and b differ on at most max_flip of them.
+    upstream_bf16 > 0: the step's k and v were themselves rounded to bf16 (a decode step's
+    conv output), and a one-ulp difference there moves a whole row or column of the
+    update; then at most max_flip of the elements may pass that bound, each by no more
+    than the io outputs' BF16_RMS_TOL RMS(ref)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert_state(gpu, ref, what)
     d = np.abs(gpu - ref)
-    e = 1e-5 * float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    excess = d - (BF16_HALF_ULP * (np.abs(gpu) + np.abs(ref)) + e)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    excess = d - (BF16_HALF_ULP * (np.abs(gpu) + np.abs(ref)) + 1e-5 * rms)
     worst = float(excess.max(initial=-1.0))
-    assert worst <= 0, f"{what}: a bf16 state element exceeds the rounding bound by {worst:.3e}"
+    if upstream_bf16:
+        over = float(np.mean(excess > 0)) if d.size else 0.0
+        assert over <= max_flip, f"{what}: {over:.2%} of the bf16 state elements exceed the rounding bound"
+        assert worst <= BF16_RMS_TOL * rms, \
+            f"{what}: a bf16 state element exceeds the rounding bound by {worst:.3e} > {BF16_RMS_TOL} RMS"
+    else:
+        assert worst <= 0, f"{what}: a bf16 state element exceeds the rounding bound by {worst:.3e}"
     flips = float(np.mean(d > 0)) if d.size else 0.0
     assert flips <= max_flip, f"{what}: {flips:.2%} of the bf16 state elements differ"
     return flips

@@ -325,7 +325,7 @@ def test_recurrent_step_bf16_state_parity(io, hk, hv):
                                              s_bf, hk, hv, D, D, io=io, state_io="bf16")
     assert_out(host(o), o_ref, io, "bf16-state step o", upstream_bf16=1)
     np.testing.assert_array_equal(host(cs), cs_ref)
-    assert_bf16_state(host(st), st_ref, "bf16-state step state")
+    assert_bf16_state(host(st), st_ref, "bf16-state step state", upstream_bf16=1)
 
 
 def test_recurrent_step_bf16_state_many_steps():
@@ -390,7 +390,7 @@ def test_recurrent_step_slots_parity(state_io):
     for s in sorted(set(range(n)) - set(live)):
         np.testing.assert_array_equal(spg[s], pool[s])
     if state_io == "bf16":
-        assert_bf16_state(spg[live], sp_ref[live], "slot step bf16 state")
+        assert_bf16_state(spg[live], sp_ref[live], "slot step bf16 state", upstream_bf16=1)
     else:
         assert_state(spg[live], sp_ref[live], "slot step state")
 
