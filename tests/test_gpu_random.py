@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import hybrid_linear_attention_causal_amd as gdn
 from hybrid_linear_attention_causal_amd import synth
 from hybrid_linear_attention_causal_amd.mixer import decode_step, prefill_layer
 from oracle import gdn_oracle as G
@@ -103,3 +104,70 @@ def test_random_decode_step(c):
         assert_bf16_state(host(st), st_ref, "bf16 state", upstream_bf16=1)
     else:
         assert_state(host(st), st_ref, "state")
+
+
+def _chunk_case(seed):
+    rng = np.random.default_rng(7000 + seed)
+    hk = int(rng.choice([1, 2, 4]))
+    hv = hk * int(rng.integers(1, 9))
+    while True:
+        ns = int(rng.integers(1, 13))
+        lens = [0 if rng.random() < 0.15 else int(rng.integers(1, 301)) for _ in range(ns)]
+        if sum(lens) * hv <= TOKEN_HEADS:
+            break
+    return dict(hk=hk, hv=hv, io=str(rng.choice(["bf16", "bf16", "f32"])), lens=lens,
+                gates=bool(rng.random() < 0.4), l2=bool(rng.random() < 0.7),
+                scale=float(rng.choice([0.0, round(float(rng.uniform(0.05, 0.5)), 3)])),
+                init_state=bool(rng.random() < 0.7))
+
+
+CHUNK = [_chunk_case(s) for s in range(16)]
+
+
+@pytest.mark.parametrize("c", CHUNK, ids=[_id(c) for c in CHUNK])
+def test_random_chunk_prefill(c):
+    """The chunked core alone on q, k, v in separate buffers with padded rows, with given
+    gates or the gate formula, the L2 norm on or off and a given or default output scale;
+    the no-allocation entry point equals it bit for bit."""
+    hk, hv, io = c["hk"], c["hv"], c["io"]
+    sh = synth.Shape(f"h{hk}x{hv}", hk=hk, hv=hv)
+    inp = synth.make(synth.custom(sh, io, 7000 + sum(c["lens"]), seqlens=c["lens"],
+                                  init_state=c["init_state"]))
+    N = inp["N"]
+    rng = np.random.default_rng(7100 + N)
+    # unnormalised keys of norm ~1 keep beta |k|^2 < 2, so the recurrence stays bounded
+    ks = 1.0 if c["l2"] else 0.09
+    q = G.to_io(rng.standard_normal((N, hk * D)), io)
+    k = G.to_io(ks * rng.standard_normal((N, hk * D)), io)
+    v = G.to_io(rng.standard_normal((N, hv * D)), io)
+    g = beta = None
+    if c["gates"]:
+        g = -rng.uniform(0.0, 0.5, (N, hv))
+        beta = rng.uniform(0.0, 1.0, (N, hv))
+    padded = []
+    for arr, pad in ((q, 16), (k, 40), (v, 8)):
+        buf = torch.full((N, arr.shape[1] + pad), float("nan"), device="cuda",
+                         dtype=torch.bfloat16 if io == "bf16" else torch.float32)
+        buf[:, : arr.shape[1]] = to_dev(arr, io)
+        padded.append(buf[:, : arr.shape[1]])
+    cu = torch.from_numpy(inp["cu_seqlens"].astype(np.int32)).cuda()
+    s_in = f32_dev(inp["state_in"]) if c["init_state"] else None
+    gate_args = [to_dev(inp["a"], io), to_dev(inp["b"], io), f32_dev(inp["A_log"]),
+                 f32_dev(inp["dt_bias"])]
+    kw = dict(g_opt=f32_dev(g), beta_opt=f32_dev(beta), scale=c["scale"],
+              use_qk_l2norm=c["l2"])
+    Ns = len(c["lens"])
+    outs = []
+    for fn in (gdn.gdn_chunk_prefill, gdn.gdn_chunk_prefill_noalloc):
+        o = torch.empty((N, hv, D), dtype=padded[0].dtype, device="cuda")
+        s_out = torch.empty((Ns, hv, D, D), device="cuda")
+        fn(*padded, *gate_args, o, hk, hv, cu, s_in, s_out, **kw)
+        outs.append((o, s_out))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]), "no-allocation o"
+    assert torch.equal(outs[0][1], outs[1][1]), "no-allocation state"
+    o_ref, s_ref = G.prefill(q, k, v, inp["a"], inp["b"], inp["A_log"], inp["dt_bias"], hk, hv,
+                             D, D, inp["state_in"], inp["cu_seqlens"], scale=c["scale"],
+                             use_qk_l2norm=c["l2"], g=g, beta=beta)
+    assert_out(host(outs[0][0]), o_ref, io, "chunk o")
+    assert_state(host(outs[0][1]), s_ref, "chunk state")
