@@ -1727,10 +1727,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
 // transposed, the state update), the Q rows, the factor rows and the V slice are copied
 // to LDS by DMA; T' and P fragments load from the fragment-native records straight into
 // registers, one chunk ahead.  Outputs leave through an LDS tile as 16-byte rows after the
-// next chunk's first barrier.  The LDS stays below half a CU's, so two workgroups share a
-// CU when the chains need it.
-// the row-split sweep is used while its workgroups fill the compute units at most this
-// many times over
+// next chunk's first barrier.  It runs where its workgroups fit the compute units once (one
+// per CU); more chains, up to a second round, go to the column-chain sweep below.
+// the row-split family (this sweep, or the column-chain sweep past one round) is used while
+// its one-tile workgroups would fill the compute units at most this many times over
 constexpr int ROWSPLIT_CU_ROUNDS = 2;
 namespace rs {
 constexpr int NW = 4;
@@ -1776,13 +1776,14 @@ __device__ __forceinline__ void dma_row_piece(const uint8_t* base, uint32_t row_
 // chunk's K rows before their own LDS reads, so the chain waves' reads are served first)
 // and store the output tiles.  The two roles of a row group share a SIMD, so each fills
 // the other's waits.  (Measured at 9B T=4096: 130 us against 138 us with one wave per row
-// group; 397B T=32768, two workgroups per CU: 1.68 against 1.70 ms.)
+// group; 397B T=32768, when it still ran there at two workgroups per CU: 1.68 against
+// 1.70 ms.)
 namespace rs2 {
 constexpr int THR = 2 * rs::THR;
 }
 
-// (CT = 1: four waves per SIMD, two workgroups per CU; CT = 2 would run one workgroup per
-// CU, so two waves per SIMD and their registers)
+// (CT = 1 is built for four waves per SIMD, which would let two workgroups share a CU; CT = 2
+// would run one workgroup per CU, so two waves per SIMD and their registers)
 template <int CT>
 __global__ void __launch_bounds__(rs2::THR, CT == 1 ? 4 : 2)
 chunk_rowsplit2_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t* __restrict__ recs) {
