@@ -545,43 +545,58 @@ __device__ __forceinline__ void final_conv_state(const ChunkArgs& p, int s, int6
   }
 }
 
-// every channel of the key head: per pass of 64 groups, wave w = rows 16 w .. 16 w + 15
-// in two halves of 8 (the halves and passes stay loops: unrolled, the windows' registers
-// and row offsets spill).  The weights are loaded again with each half's window (L1 hits):
-// loaded once before the halves' loop, the wave would wait for them before the window
-// loads could issue.
-__device__ __forceinline__ void conv_rows(const ChunkArgs& p, int s, int64_t t0, int L, int kh,
-                                          int r, int wave, int lane, u16* k_rows, u16* q_rows,
-                                          float* rnk, float* rnq, uint4& gin) {
+// one pass over 32 channel groups from group g0: lane l takes group g0 + (l & 31) (lanes
+// past the last group repeat it: they compute and store the same bytes) over rows
+// 16 w + 8 (l >> 5) .. + 7 of wave w.  The weights are loaded with the window (L1 hits).
+// The first row is opaque to the compiler: the rows do not depend on the pass, and their
+// 64-bit offsets, hoisted out of the v passes' loop, would stay live across it and spill.
+// QK: groups 0 .. 31 (q, then k), whose rows also go to LDS with their norms (each DPP row
+// of 16 lanes then holds the 16 groups of one head's q or k for the same rows); gin is
+// marked complete after the first row, whose wait covers it (loads complete in order).
+template <bool QK>
+__device__ __forceinline__ void conv_pass(const ChunkArgs& p, int s, int64_t sb, int64_t t0, int L,
+                                          int kh, int r, int wave, int lane, int g0, u16* k_rows,
+                                          u16* q_rows, float* rnk, float* rnq, uint4& gin) {
   const int Cq = p.Cq;
+  u16* y = (u16*)p.y;
+  const int cg = min(g0 + (lane & 31), 32 + 16 * r - 1);
+  const int ch = conv_group_channel(cg, kh, p.Hk, r);
+  float4 wt[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wt[j] = *reinterpret_cast<const float4*>(p.conv_w + (int64_t)(ch + j) * 4);
+  int r0 = 16 * wave + 8 * (lane >> 5);
+  asm volatile("" : "+v"(r0));
+  uint4 raw[11];
+  conv_window(p, s, sb, t0, L, r0, ch, t0 + r0 - 3 >= sb, raw);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int row = r0 + t;
+    const uint4 ow = conv_row8(wt, raw, t);
+    if (QK && t == 0) asm volatile("" : "+v"(gin.x), "+v"(gin.y), "+v"(gin.z), "+v"(gin.w));
+    if (row < L) *reinterpret_cast<uint4*>(y + (t0 + row) * Cq + ch) = ow;
+    if constexpr (QK) qk_row_to_lds(p, ow, row, L, cg, k_rows, q_rows, rnk, rnq);
+  }
+}
+
+// the q and k channels of the key head: rows to y, and to LDS for the Gram products
+__device__ __forceinline__ void conv_qk(const ChunkArgs& p, int s, int64_t t0, int L, int kh, int r,
+                                        int wave, int lane, u16* k_rows, u16* q_rows, float* rnk,
+                                        float* rnq, uint4& gin) {
   int64_t sb, se;
   seq_bounds(p.cu, p.N, s, sb, se);
-  u16* y = (u16*)p.y;
-  const int G = 32 + 16 * r;
-  // (a do-while: the first pass, which marks gin, runs on every path)
-  int pass = 0;
-  do {
-    // lanes past the last group repeat it: they compute and store the same bytes
-    const int cg = min(pass * 64 + lane, G - 1);
-    const int ch = conv_group_channel(cg, kh, p.Hk, r);
+  conv_pass<true>(p, s, sb, t0, L, kh, r, wave, lane, 0, k_rows, q_rows, rnk, rnq, gin);
+}
+
+// the v channels of the key head's r value heads (rows to y only, for the sweep), and the
+// final conv state of every channel of the key head
+__device__ __forceinline__ void conv_v(const ChunkArgs& p, int s, int64_t t0, int L, int kh, int r,
+                                       int wave, int lane) {
+  int64_t sb, se;
+  seq_bounds(p.cu, p.N, s, sb, se);
+  uint4 none = make_uint4(0, 0, 0, 0);
 #pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-      float4 wt[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wt[j] = *reinterpret_cast<const float4*>(p.conv_w + (int64_t)(ch + j) * 4);
-      const int r0 = 16 * wave + 8 * half;
-      uint4 raw[11];
-      conv_window(p, s, sb, t0, L, r0, ch, t0 + r0 - 3 >= sb, raw);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int row = r0 + t;
-        const uint4 ow = conv_row8(wt, raw, t);
-        if (t == 0) asm volatile("" : "+v"(gin.x), "+v"(gin.y), "+v"(gin.z), "+v"(gin.w));
-        if (row < L) *reinterpret_cast<uint4*>(y + (t0 + row) * Cq + ch) = ow;
-        if (pass == 0) qk_row_to_lds(p, ow, row, L, cg, k_rows, q_rows, rnk, rnq);
-      }
-    }
-  } while (++pass * 64 < G);
+  for (int g0 = 32; g0 < 32 + 16 * r; g0 += 32)
+    conv_pass<false>(p, s, sb, t0, L, kh, r, wave, lane, g0, nullptr, nullptr, nullptr, nullptr, none);
   if (p.conv_state_in_prep && wave == 0 && t0 + L == se) final_conv_state(p, s, sb, se, kh, r, lane);
 }
 
@@ -667,7 +682,8 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
 
   // ---- phase 0: K and Q rows to LDS, row norms (16 lanes of a DPP row share a row)
   if constexpr (CONV != CONV_NONE) {
-    conv_rows(p, ci.x, t0, L, kh_, r, wave, lane, sm.u.r.kh, sm.u.r.qh, sm.rnk, sm.rnq, gin0);
+    conv_qk(p, ci.x, t0, L, kh_, r, wave, lane, sm.u.r.kh, sm.u.r.qh, sm.rnk, sm.rnq, gin0);
+    conv_v(p, ci.x, t0, L, kh_, r, wave, lane);
   } else {
     RowBlock<IO> kb, qb;
     load_rows<IO>(kb, (const T*)p.k + (int64_t)kh_ * DK, p.stride_k, t0, L, tid);
