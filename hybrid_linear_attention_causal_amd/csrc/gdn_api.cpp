@@ -94,7 +94,16 @@ gdn_status_t gdn_conv1d_fwd(const void* x, const float* w, void* y, const int32_
 }
 
 size_t gdn_chunk_prefill_workspace_size(int64_t N, int Ns, int Hk, int Hv, int d, gdn_dtype_t io) {
-  if (N < 0 || Ns < 1 || Hk < 1 || Hv < 1 || d != 128 || !io_ok(io)) return 0;
+  if (N < 0 || Ns < 1 || Hk < 1 || Hv < 1 || Hv % Hk != 0 || d != 128 || !io_ok(io)) return 0;
+  // the chunk and (sequence, head) counts the prefill calls accept
+  if ((N + 63) / 64 + Ns > 0x7fffffffLL || ((int64_t)Ns * Hk + 8) * (Hv / Hk) * 2 > 0x7fffffffLL)
+    return 0;
+  // an upper bound of the byte count, in 128-bit arithmetic: at most 128 KiB per chunk and
+  // head (record, K/Q rows, map entry) and 2 MiB per (sequence, value head) of segment
+  // scratch.  Below 2^62 the size's own 64-bit arithmetic cannot overflow.
+  const __int128 chunks = (__int128)((N + 63) / 64 + Ns);
+  const __int128 bound = chunks * (Hv + Hk) * (128 << 10) + (__int128)Ns * Hv * (2 << 20);
+  if (bound > ((__int128)1 << 62)) return 0;
   return gdn::chunk_workspace_bytes(N, Ns, Hk, Hv, io == GDN_F32);
 }
 
@@ -138,11 +147,12 @@ gdn_status_t chunk_prefill_impl(const char* name, gdn::ChunkArgs args, int dk, i
         !aligned(args.o, 16))
       return fail(GDN_ERR_INVALID_ARG, "%s: q, k, v, o must be 16-byte aligned", name);
   }
+  if ((N + 63) / 64 + Ns > 0x7fffffffLL) return fail(GDN_ERR_INVALID_ARG, "%s: too many chunks", name);
   const size_t need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk, io);
+  if (need == 0) return fail(GDN_ERR_INVALID_ARG, "%s: sizes beyond the workspace bound", name);
   if (!workspace || ws_bytes < need || !aligned(workspace, 256))
     return fail(GDN_ERR_INVALID_ARG,
                 "%s: workspace must be a 256-byte aligned buffer of >= %zu bytes", name, need);
-  if ((N + 63) / 64 + Ns > 0x7fffffffLL) return fail(GDN_ERR_INVALID_ARG, "%s: too many chunks", name);
   if (args.scale <= 0.f) args.scale = 1.0f / sqrtf((float)dk);
   int cus = 0;
   gdn_status_t st = check_device(&cus);

@@ -109,7 +109,9 @@ gdn_status_t gdn_conv1d_fwd(const void* x, const float* w, void* y, const int32_
  * and, where the intra-sequence scan may run, 7 segment-transition pairs of 128 KB per
  * (sequence, value head) pair: fp32 io with at most 64 pairs, bf16 io with at most 16
  * pairs and sequences of at least 256 chunks on average (ceil(N/64) / Ns >= 256).
- * Returns 0 for invalid sizes.
+ * Returns 0 for invalid sizes: those gdn_chunk_prefill rejects (Hv not a multiple of
+ * Hk, more than 2^31 - 1 chunks or too many (sequence, head) pairs), and any whose byte
+ * count could pass 2^62.
  * (The io argument is one more than the five of the plain form (N, Ns, Hk, Hv, d): the
  * fp32 io records are larger, so the size depends on it.)
  */

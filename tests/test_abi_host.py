@@ -109,6 +109,20 @@ def test_prefill_rejects():
     assert ws(32768, 1, 16, 32, 128, 1) == 256 + 8448 + 513 * (32 * 38912)
     assert ws(-1, 1, 16, 32, 128, 1) == 0
     assert ws(64, 1, 16, 32, 64, 1) == 0
+    assert ws(64, 1, 16, 24, 128, 1) == 0            # Hv not a multiple of Hk
+    # sizes beyond what the calls accept, or whose byte count would pass 2^62: 0, not a
+    # wrapped-around 64-bit product
+    assert ws(1 << 50, 1, 16, 64, 128, 1) == 0       # more than 2^31 chunks
+    assert ws(1 << 36, 1, 1, 1 << 20, 128, 1) == 0   # 2^30 chunks x 2^20 heads
+    assert ws((1 << 36) - 64, 1, 16, 64, 128, 1) > 0
+    # and a call with such sizes is refused before the workspace is compared or a device used
+    assert _prefill(N=1 << 50, ws=P, ws_bytes=1024) == _lib.GDN_ERR_INVALID_ARG
+    assert "chunks" in _msg()
+    # (row strides of at most 2^20 elements cap Hv at 8192, so through the call the size
+    # stays below the bound, and is compared unwrapped with the workspace given)
+    assert _prefill(N=1 << 36, Hk=1, Hv=8192, sv=1 << 20, ws=P, ws_bytes=1024) == \
+        _lib.GDN_ERR_INVALID_ARG
+    assert "workspace" in _msg()
 
 
 def _step(fn="gdn_recurrent_step", **kw):
