@@ -422,6 +422,9 @@ gdn_status_t gdn_gated_rmsnorm(const void* o, const void* z, const float* w, voi
   if (D != 128) return fail(GDN_ERR_UNSUPPORTED, "gated_rmsnorm: row width %d (only 128)", D);
   if (rows < 0 || !(eps >= 0.f))
     return fail(GDN_ERR_INVALID_ARG, "gated_rmsnorm: rows=%lld eps=%g", (long long)rows, (double)eps);
+  // 16 rows per block and at most 2^31 - 1 blocks
+  if (rows > 0x7fffffffLL * 16)
+    return fail(GDN_ERR_INVALID_ARG, "gated_rmsnorm: %lld rows (at most 2^35 - 16)", (long long)rows);
   if (rows > 0) {
     if (!o || !z || !w || !y) return fail(GDN_ERR_INVALID_ARG, "gated_rmsnorm: NULL pointer");
     if (!aligned(o, 16) || !aligned(z, 16) || !aligned(w, 16) || !aligned(y, 16))

@@ -160,6 +160,10 @@ def test_norm_rejects():
     assert L.gdn_gated_rmsnorm(P, P, P, P, -1, 128, 1e-6, 1, None) == _lib.GDN_ERR_INVALID_ARG
     assert L.gdn_gated_rmsnorm(P, None, P, P, 10, 128, 1e-6, 1, None) == _lib.GDN_ERR_INVALID_ARG
     assert L.gdn_gated_rmsnorm(P, P, P, P, 10, 128, -1.0, 1, None) == _lib.GDN_ERR_INVALID_ARG
+    # more rows than 2^31 - 1 blocks of 16 hold: refused, not a truncated grid
+    assert L.gdn_gated_rmsnorm(P, P, P, P, (1 << 36) + 16, 128, 1e-6, 1, None) == \
+        _lib.GDN_ERR_INVALID_ARG
+    assert "rows" in _msg()
 
 
 def _slots(**kw):
