@@ -68,7 +68,9 @@ constexpr int F_STRIDE = CH + 4;       // floats per A/T row
 //     planes, then 8 x 64 fp32 per-token rows e^gamma/|k|, e^gamma/|q|,
 //     e^{gamma_L - gamma}/|k|, e^{gamma_L}, gamma, 1/|k|, 1/|q| (and one of padding),
 //     then, for the 4-wave sweep, P hi, P lo planes (38912 bytes; 20480 without P:
-//     the 8-wave sweep forms P from the Q and K rows it stages anyway);
+//     the fp32 8-wave sweep forms P from the Q and K rows it stages anyway); bf16 io
+//     writes fragment-native records instead (below: with P for the row-split and
+//     column-chain sweeps, T' only for the 8-wave sweep);
 //   fp32 io only, per (global chunk c, key head kh): K hi, K lo, Q hi, Q lo rows
 //     (64 x 136 bf16 each); bf16 io stages K and Q straight from the input rows.
 constexpr int64_t WS_PL_BYTES = (int64_t)CH * T_STRIDE * 2;          // 9216 per plane
@@ -90,6 +92,19 @@ constexpr int64_t FR_P_OFF = 16 * 1024;
 constexpr int64_t FR_FAC_OFF = 32 * 1024;
 constexpr int64_t FR_REC_BYTES = FR_FAC_OFF + FAC_ROWS * CH * 4;     // 34816
 __host__ __device__ constexpr int fr_tp(int j, int m, int plane) { return ((j * 2 + m) * 2 + plane) * 1024; }
+// Fragment-native records without P (the 8-wave sweep of bf16 io, which forms P itself):
+// the T' fragments as above, then the factor rows
+constexpr int64_t FRT_FAC_OFF = 16 * 1024;
+constexpr int64_t FRT_REC_BYTES = FRT_FAC_OFF + FAC_ROWS * CH * 4;   // 18432
+// u16 offset of element (i, j) of a 64 x 64 operand held as A-operand fragments in LDS
+// (fragment (i / 16, j / 32, plane) of 512 u16 at the fr_tp place; lane (g, r) holds row
+// r and the permuted contraction index 4 g + e, e < 4, and 16 + 4 g + e - 4, e >= 4)
+__device__ __forceinline__ int frag_off(int i, int j, int plane) {
+  const int kk = j & 31;
+  const int lane = ((kk & 15) >> 2) * 16 + (i & 15);
+  const int e = (kk & 3) + ((kk >> 4) << 2);
+  return (((i >> 4) * 2 + (j >> 5)) * 2 + plane) * 512 + lane * 8 + e;
+}
 
 static int64_t ws_max_chunks(int64_t N, int Ns) { return (N + CH - 1) / CH + Ns; }
 static int64_t ws_cmap_bytes(int Ns) { return (((int64_t)Ns + 1) * 4 + 255) / 256 * 256; }
@@ -257,6 +272,41 @@ __device__ __forceinline__ void tri_apply(const u16* mp, const bf16x8 (&xh)[2], 
   tri_apply(mp, xh, xl, y, lane, []() {});
 }
 
+// tri_apply for M held as A-operand fragments in LDS (fr_tp order, 512 u16 each): one
+// 16-byte lane-linear read per fragment
+template <typename F>
+__device__ __forceinline__ void tri_apply_frag(const u16* mp, const bf16x8 (&xh)[2], const bf16x8 (&xl)[2],
+                                               f32x4 (&y)[4], int lane, F mid) {
+  auto fr = [&](int I, int m, int pl) {
+    return *reinterpret_cast<const bf16x8*>(mp + fr_tp(I, m, pl) / 2 + lane * 8);
+  };
+  bf16x8 ah[4], al[4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    ah[I] = fr(I, 0, 0);
+    al[I] = fr(I, 0, 1);
+  }
+#pragma unroll
+  for (int I = 0; I < 4; ++I) y[I] = mma(ah[I], xh[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+  for (int I = 0; I < 4; ++I) y[I] = mma(al[I], xh[0], y[I]);
+#pragma unroll
+  for (int I = 0; I < 4; ++I) y[I] = mma(ah[I], xl[0], y[I]);
+  mid();
+  bf16x8 bh[2], bl[2];
+#pragma unroll
+  for (int I = 0; I < 2; ++I) {
+    bh[I] = fr(I + 2, 1, 0);
+    bl[I] = fr(I + 2, 1, 1);
+  }
+#pragma unroll
+  for (int I = 0; I < 2; ++I) y[I + 2] = mma(bh[I], xh[1], y[I + 2]);
+#pragma unroll
+  for (int I = 0; I < 2; ++I) y[I + 2] = mma(bl[I], xh[1], y[I + 2]);
+#pragma unroll
+  for (int I = 0; I < 2; ++I) y[I + 2] = mma(bh[I], xl[1], y[I + 2]);
+}
+
 // lower-triangle tile list of a 4 x 4 grid of 16 x 16 tiles
 __device__ __forceinline__ void tri_tile(int n, int& I, int& J) {
   I = (n >= 6) ? 3 : (n >= 3) ? 2 : (n >= 1) ? 1 : 0;
@@ -398,9 +448,10 @@ __global__ void __launch_bounds__(256) chunk_map_kernel(const int32_t* cu, int N
 // (K^ K^T and Q^ K^T with the 1/|k|, 1/|q| factors) are formed once; then, per value
 // head, its decay and write strength scale the tiles into A and P, I + A is inverted,
 // and the head's record is written.
-// record layouts the prep kernel writes: rows without P (8-wave sweep), rows with P
-// (4-wave sweep), fragment-native with P and K^T (row-split sweep)
-enum PrepMode { PREP_ROWS = 0, PREP_ROWS_P = 1, PREP_FRAG = 2 };
+// record layouts the prep kernel writes: rows without P (8-wave sweep, fp32 io), rows with
+// P (4-wave sweep), fragment-native with P (row-split sweep), fragment-native T' without P
+// (8-wave sweep, bf16 io)
+enum PrepMode { PREP_ROWS = 0, PREP_ROWS_P = 1, PREP_FRAG = 2, PREP_FRAG_T = 3 };
 constexpr int PREP_RB = 4;                // value heads whose gates are staged at once
 static_assert(PREP_RB == NTHR / 64, "one wave stages the gates of one value head");
 
@@ -614,12 +665,12 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   typedef Io<IO> io;
   typedef typename io::T T;
   constexpr bool F32 = (IO == IO_F32);
-  constexpr bool WITHP = MODE != PREP_ROWS;
-  constexpr bool FRAG = MODE == PREP_FRAG;
+  constexpr bool WITHP = MODE == PREP_ROWS_P || MODE == PREP_FRAG;
+  constexpr bool FRAG = MODE == PREP_FRAG || MODE == PREP_FRAG_T;
   static_assert(!(FRAG && F32), "fragment-native records are for bf16 io");
   static_assert(!(CONV != CONV_NONE && F32), "the fused conv is for bf16 io");
-  constexpr int64_t REC = FRAG ? FR_REC_BYTES : ws_rec_bytes(WITHP);
-  constexpr int64_t FAC_OFF = FRAG ? FR_FAC_OFF : WS_FAC_OFF;
+  constexpr int64_t REC = FRAG ? (WITHP ? FR_REC_BYTES : FRT_REC_BYTES) : ws_rec_bytes(WITHP);
+  constexpr int64_t FAC_OFF = FRAG ? (WITHP ? FR_FAC_OFF : FRT_FAC_OFF) : WS_FAC_OFF;
   __shared__ PrepSmem<IO> sm;
 
   const int c = blockIdx.x;               // global chunk
@@ -747,15 +798,17 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
   if constexpr (FRAG) {
     // J runs downwards, so block ia is read (as kj) before the tiles J < ia need it (as ka)
     bf16x8 ka[4], qw[4];
+    if constexpr (WITHP) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) qw[m] = frag_rows(sm.u.r.qh, KS_STRIDE, 16 * wave, 32 * m, lane);
+      for (int m = 0; m < 4; ++m) qw[m] = frag_rows(sm.u.r.qh, KS_STRIDE, 16 * wave, 32 * m, lane);
+    }
     const float4 ki4 = *reinterpret_cast<const float4*>(&sm.rnk[16 * ia + 4 * g4]);
     const float qi = sm.rnq[16 * wave + c16];
 #pragma unroll
     for (int J = 3; J >= 0; --J) {
       gk[J] = f32x4{0.f, 0.f, 0.f, 0.f};
       pq[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (J <= ia || J <= wave) {
+      if (J <= ia || (WITHP && J <= wave)) {
         bf16x8 kj[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) kj[m] = frag_rows(sm.u.r.kh, KS_STRIDE, 16 * J, 32 * m, lane);
@@ -772,7 +825,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
           gk[J][2] *= ki4.z * rkj;
           gk[J][3] *= ki4.w * rkj;
         }
-        if (J <= wave) {
+        if (WITHP && J <= wave) {
           // (K Q^T) tile (J, w): accumulators hold rnq_i rnk_j (q_i . k_j) at
           // i = 16 w + c16, j = 16 J + 4 g4 + e; tiles J = 2m, 2m+1 together are the
           // layout of P's A-operand fragment [row tile w][token slab m]
@@ -956,7 +1009,7 @@ chunk_prep_kernel(ChunkArgs p, const int4* __restrict__ cinfo, uint8_t* __restri
           }
         }
       }
-      if constexpr (FRAG) {
+      if constexpr (FRAG && WITHP) {
         // P fragments of row tile w straight from the transposed tiles:
         // P_ij = e^{gamma_i - gamma_j} rnq_i rnk_j (q_i . k_j) for j <= i < L
         const int i = 16 * wave + c16;
@@ -1251,6 +1304,9 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   // P: copied from the record by the 4-wave (latency-bound) shape, formed in the sweep
   // from the staged Q and K rows by the 8-wave (throughput-bound) shape
   constexpr bool PREC = (NW == 4);
+  // bf16 io, 8 waves, normal launch: T' comes as fragment-native records (no P) and P is
+  // formed in fragment order, so both are read as one 16-byte lane-linear word per fragment
+  constexpr bool FT = !F32 && NW == 8 && !TRANS;
   typedef SweepSizes<IO, NW> Z;
   constexpr int DVB = Z::DVB, NBLK = Z::NBLK, O_STRIDE = Z::O_STRIDE, V_STRIDE = Z::V_STRIDE;
   // K rows are double-buffered by chunk parity: chunk n's rows serve its K S products
@@ -1409,8 +1465,20 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
         dma_rows<16, NW>((const uint8_t*)qg + t0 * qrow_bytes, qrow_bytes, L, ktab, s_qh, wave_u);
       }
     } else if (part == 2) {
-      dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec, s_tp, wave_u, lane);
-      dma_linear<FAC_ROWS * CH * 4 / 16, NW>(rec + WS_FAC_OFF, s_fac, wave_u, lane);
+      if constexpr (FT) {
+        // the 12 non-zero T' fragments (row tiles 0 and 1 have no token slab 1), one
+        // 1 KB copy each, then the factor rows
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int ins = min(wave_u + NW * jj, 11);
+          const int f = ins < 2 ? ins : ins < 4 ? ins + 2 : ins + 4;
+          lds_dma16<false>(rec + FR_T_OFF + f * 1024 + lane * 16, (char*)s_tp + f * 1024);
+        }
+        dma_linear<FAC_ROWS * CH * 4 / 16, NW>(rec + FRT_FAC_OFF, s_fac, wave_u, lane);
+      } else {
+        dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec, s_tp, wave_u, lane);
+        dma_linear<FAC_ROWS * CH * 4 / 16, NW>(rec + WS_FAC_OFF, s_fac, wave_u, lane);
+      }
     } else if (!TRANS || half == 0) {
       const uint8_t* vb = vg0 + t0 * vrow_bytes;
       if constexpr (F32) {
@@ -1481,7 +1549,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
     for (int idx = tid; idx < 1024; idx += Z::THR) {
       const int t = (idx >> 8) & 1, e = idx & 255;
       const int i = 32 * t + (e >> 4), j = 32 * t + 16 + (e & 15);
-      s_pp[(idx >> 9) * CH * T_STRIDE + i * T_STRIDE + j] = 0;
+      if constexpr (FT)
+        s_pp[frag_off(i, j, idx >> 9)] = 0;
+      else
+        s_pp[(idx >> 9) * CH * T_STRIDE + i * T_STRIDE + j] = 0;
     }
   }
   if (ne > nb) {
@@ -1602,8 +1673,13 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
           const float v = (i >= j && i < L) ? __expf(gam[i] - gj) * rnq[i] * rkj * acc[e] : 0.f;
           uint32_t ph, pl;
           split2(v, 0.f, ph, pl);
-          s_pp[i * T_STRIDE + j] = (u16)ph;
-          s_pp[CH * T_STRIDE + i * T_STRIDE + j] = (u16)pl;
+          if constexpr (FT) {
+            s_pp[frag_off(i, j, 0)] = (u16)ph;
+            s_pp[frag_off(i, j, 1)] = (u16)pl;
+          } else {
+            s_pp[i * T_STRIDE + j] = (u16)ph;
+            s_pp[CH * T_STRIDE + i * T_STRIDE + j] = (u16)pl;
+          }
         }
       }
     }
@@ -1615,7 +1691,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
       bf16x8 rh[2], rl[2];
       frag_acc_split(R[0], R[1], rh[0], rl[0]);
       frag_acc_split(R[2], R[3], rh[1], rl[1]);
-      tri_apply(s_tp, rh, rl, U, lane);
+      if constexpr (FT)
+        tri_apply_frag(s_tp, rh, rl, U, lane, []() {});
+      else
+        tri_apply(s_tp, rh, rl, U, lane);
     }
     // the state update's right operand diag(e^{gamma_L - gamma} / |k|) U, and e^{gamma_L}:
     // every factor is read in phase A, since the next chunk's factors land in phase B
@@ -1651,7 +1730,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
       frag_acc_split(U[0], U[1], uh[0], ul[0]);
       frag_acc_split(U[2], U[3], uh[1], ul[1]);
       f32x4 pu[4];
-      tri_apply(s_pp, uh, ul, pu, lane, [&]() { stage_a(na, 1, knext, knl); });
+      if constexpr (FT)
+        tri_apply_frag(s_pp, uh, ul, pu, lane, [&]() { stage_a(na, 1, knext, knl); });
+      else
+        tri_apply(s_pp, uh, ul, pu, lane, [&]() { stage_a(na, 1, knext, knl); });
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         float ov[4];
@@ -2560,7 +2642,7 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   // kernel first.
   // (the prep's working workgroups: at most one chunk more per sequence boundary than
   // the tokens fill; the grid's spare rows return at once)
-  const int prep_mode = rowsplit ? PREP_FRAG : four ? PREP_ROWS_P : PREP_ROWS;
+  const int prep_mode = rowsplit ? PREP_FRAG : four ? PREP_ROWS_P : IO == IO_BF16 ? PREP_FRAG_T : PREP_ROWS;
   const int64_t chunks = (a.N + CH - 1) / CH + a.Ns - 1;
   // the call includes the conv: x given, or (no tokens, x may then be NULL) a final conv
   // state to write, which is then the initial one
@@ -2583,17 +2665,20 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
           hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS_P, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
                              a, (const int4*)cinfo, recs, krecs);
         else
-          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
+          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG_T, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
                              a, (const int4*)cinfo, recs, krecs);
       } else if (rowsplit) {
         hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG>), pgrid, dim3(NTHR), 0, st, a,
+                           (const int4*)cinfo, recs, krecs);
+      } else if (!four) {
+        hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG_T>), pgrid, dim3(NTHR), 0, st, a,
                            (const int4*)cinfo, recs, krecs);
       }
     }
     if (!conv_in_prep && !rowsplit && four)
       hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS_P>), pgrid, dim3(NTHR), 0, st, a,
                          (const int4*)cinfo, recs, krecs);
-    else if (!conv_in_prep && !rowsplit)
+    else if (!conv_in_prep && !rowsplit && IO == IO_F32)
       hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS>), pgrid, dim3(NTHR), 0, st, a,
                          (const int4*)cinfo, recs, krecs);
     e = hipGetLastError();
@@ -2619,7 +2704,9 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
     const int64_t groups = (int64_t)a.Ns * a.Hk * segs_in_launch;
     return dim3((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * nb));
   };
-  const int64_t rb = ws_rec_bytes(four);
+  // record stride of the sweep: with P (4-wave), fragment-native T' (bf16 8-wave), rows
+  // (fp32 8-wave)
+  const int64_t rb = four ? ws_rec_bytes(true) : IO == IO_BF16 ? FRT_REC_BYTES : ws_rec_bytes(false);
   if (rowsplit) {
     const int64_t groups = (int64_t)a.Ns * a.Hk;
     // two column tiles per workgroup (the column-chain sweep) where one tile's row-split
