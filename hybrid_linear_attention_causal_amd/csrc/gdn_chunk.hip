@@ -1304,9 +1304,12 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   // P: copied from the record by the 4-wave (latency-bound) shape, formed in the sweep
   // from the staged Q and K rows by the 8-wave (throughput-bound) shape
   constexpr bool PREC = (NW == 4);
-  // bf16 io, 8 waves, normal launch: T' comes as fragment-native records (no P) and P is
-  // formed in fragment order, so both are read as one 16-byte lane-linear word per fragment
-  constexpr bool FT = !F32 && NW == 8 && !TRANS;
+  // bf16 io: T' (and, for the 4-wave shape, P) comes as fragment-native records, and the
+  // 8-wave shape forms P in fragment order, so every T' and P fragment is one 16-byte
+  // lane-linear read (records with P for the 4-wave and transition launches, which share
+  // them, without P for the 8-wave normal launch)
+  constexpr bool FT = !F32;
+  constexpr int64_t TFAC_OFF = (TRANS || PREC) ? FR_FAC_OFF : FRT_FAC_OFF;
   typedef SweepSizes<IO, NW> Z;
   constexpr int DVB = Z::DVB, NBLK = Z::NBLK, O_STRIDE = Z::O_STRIDE, V_STRIDE = Z::V_STRIDE;
   // K rows are double-buffered by chunk parity: chunk n's rows serve its K S products
@@ -1442,6 +1445,16 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   T vraw[4][4];   // fp32 io: the V slice goes through registers
   // (sched_barrier keeps the instruction scheduler from sinking a piece past the
   // products it is meant to overlap)
+  // the 12 non-zero fragments of a fragment-native T' or P (row tiles 0 and 1 have no
+  // token slab 1), one 1 KB copy each, the waves taking turns
+  auto frag_copy = [&](const uint8_t* src, u16* dst) {
+#pragma unroll
+    for (int jj = 0; jj < (12 + NW - 1) / NW; ++jj) {
+      const int ins = min(wave_u + NW * jj, 11);
+      const int f = ins < 2 ? ins : ins < 4 ? ins + 2 : ins + 4;
+      lds_dma16<false>(src + f * 1024 + lane * 16, (char*)dst + f * 1024);
+    }
+  };
   auto stage_a = [&](int n, int part, u16* kdst, u16* kldst) {
     __builtin_amdgcn_sched_barrier(0);
     const int64_t t0 = b0 + (int64_t)n * CH;
@@ -1468,13 +1481,8 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
       if constexpr (FT) {
         // the 12 non-zero T' fragments (row tiles 0 and 1 have no token slab 1), one
         // 1 KB copy each, then the factor rows
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int ins = min(wave_u + NW * jj, 11);
-          const int f = ins < 2 ? ins : ins < 4 ? ins + 2 : ins + 4;
-          lds_dma16<false>(rec + FR_T_OFF + f * 1024 + lane * 16, (char*)s_tp + f * 1024);
-        }
-        dma_linear<FAC_ROWS * CH * 4 / 16, NW>(rec + FRT_FAC_OFF, s_fac, wave_u, lane);
+        frag_copy(rec + FR_T_OFF, s_tp);
+        dma_linear<FAC_ROWS * CH * 4 / 16, NW>(rec + TFAC_OFF, s_fac, wave_u, lane);
       } else {
         dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec, s_tp, wave_u, lane);
         dma_linear<FAC_ROWS * CH * 4 / 16, NW>(rec + WS_FAC_OFF, s_fac, wave_u, lane);
@@ -1541,7 +1549,10 @@ chunk_sweep_kernel(ChunkArgs p, const int32_t* __restrict__ cmap, const uint8_t*
   auto stage_p = [&](int n) {     // phase-B operand of chunk n: the P planes of its record
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* rec = recs + ((int64_t)(c0 + n) * Hv + h) * sg.rec_bytes;
-    dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec + WS_P_OFF, s_pp, wave_u, lane);
+    if constexpr (FT)
+      frag_copy(rec + FR_P_OFF, s_pp);
+    else
+      dma_linear<(2 * WS_PL_BYTES) / 16, NW>(rec + WS_P_OFF, s_pp, wave_u, lane);
     __builtin_amdgcn_sched_barrier(0);
   };
   if constexpr (!TRANS && !PREC) {
@@ -2642,7 +2653,9 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   // kernel first.
   // (the prep's working workgroups: at most one chunk more per sequence boundary than
   // the tokens fill; the grid's spare rows return at once)
-  const int prep_mode = rowsplit ? PREP_FRAG : four ? PREP_ROWS_P : IO == IO_BF16 ? PREP_FRAG_T : PREP_ROWS;
+  // (bf16 io: fragment-native records, with P where the sweep reads P from them)
+  const int prep_mode = IO == IO_BF16 ? ((rowsplit || four) ? PREP_FRAG : PREP_FRAG_T)
+                                      : (four ? PREP_ROWS_P : PREP_ROWS);
   const int64_t chunks = (a.N + CH - 1) / CH + a.Ns - 1;
   // the call includes the conv: x given, or (no tokens, x may then be NULL) a final conv
   // state to write, which is then the initial one
@@ -2657,30 +2670,25 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
   if (a.N > 0) {
     const dim3 pgrid((unsigned)cmax, (unsigned)a.Hk);
     if constexpr (IO == IO_BF16) {
-      if (conv_in_prep) {
-        if (rowsplit)
-          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
-                             a, (const int4*)cinfo, recs, krecs);
-        else if (four)
-          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS_P, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
-                             a, (const int4*)cinfo, recs, krecs);
-        else
-          hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG_T, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
-                             a, (const int4*)cinfo, recs, krecs);
-      } else if (rowsplit) {
+      if (conv_in_prep && prep_mode == PREP_FRAG)
+        hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
+                           a, (const int4*)cinfo, recs, krecs);
+      else if (conv_in_prep)
+        hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG_T, CONV_ALL>), pgrid, dim3(NTHR), 0, st,
+                           a, (const int4*)cinfo, recs, krecs);
+      else if (prep_mode == PREP_FRAG)
         hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG>), pgrid, dim3(NTHR), 0, st, a,
                            (const int4*)cinfo, recs, krecs);
-      } else if (!four) {
+      else
         hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_FRAG_T>), pgrid, dim3(NTHR), 0, st, a,
                            (const int4*)cinfo, recs, krecs);
-      }
-    }
-    if (!conv_in_prep && !rowsplit && four)
+    } else if (four) {
       hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS_P>), pgrid, dim3(NTHR), 0, st, a,
                          (const int4*)cinfo, recs, krecs);
-    else if (!conv_in_prep && !rowsplit && IO == IO_F32)
+    } else {
       hipLaunchKernelGGL((chunk_prep_kernel<IO, PREP_ROWS>), pgrid, dim3(NTHR), 0, st, a,
                          (const int4*)cinfo, recs, krecs);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2704,9 +2712,9 @@ static hipError_t chunk_impl(const ChunkArgs& a, void* ws, hipStream_t st) {
     const int64_t groups = (int64_t)a.Ns * a.Hk * segs_in_launch;
     return dim3((unsigned)((groups + 7) / 8 * 8 * (a.Hv / a.Hk) * nb));
   };
-  // record stride of the sweep: with P (4-wave), fragment-native T' (bf16 8-wave), rows
-  // (fp32 8-wave)
-  const int64_t rb = four ? ws_rec_bytes(true) : IO == IO_BF16 ? FRT_REC_BYTES : ws_rec_bytes(false);
+  // record stride of the sweep launches: bf16 io fragment-native with P (4-wave and
+  // transition launches) or without (8-wave), fp32 rows with P (4-wave) or without
+  const int64_t rb = IO == IO_BF16 ? (four ? FR_REC_BYTES : FRT_REC_BYTES) : ws_rec_bytes(four);
   if (rowsplit) {
     const int64_t groups = (int64_t)a.Ns * a.Hk;
     // two column tiles per workgroup (the column-chain sweep) where one tile's row-split
