@@ -123,6 +123,19 @@ def _dev(*ts):
             raise ValueError("libgdn takes device (GPU) tensors only")
 
 
+def _row_stride(t: torch.Tensor) -> int:
+    """Row stride (elements) of a [N, width] view with contiguous rows.  With at most one
+    row no stride is ever applied, and torch reports arbitrary strides for such tensors
+    (an empty array from NumPy has strides (0, 0)): the width is passed then."""
+    if t.shape[0] <= 1:
+        if t.numel() > 1 and t.stride(-1) != 1:
+            raise ValueError("q, k, v rows must be contiguous")
+        return t.shape[-1]
+    if t.stride(-1) != 1:
+        raise ValueError("q, k, v rows must be contiguous")
+    return t.stride(0)
+
+
 def version() -> str:
     return lib().gdn_version().decode()
 
@@ -153,15 +166,13 @@ def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqlens=None,
          workspace)
     N = q.shape[0]
     Ns = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
-    for t in (q, k, v):
-        if t.stride(-1) != 1:
-            raise ValueError("q, k, v rows must be contiguous")
+    sq, sk, sv = (_row_stride(t) for t in (q, k, v))
     if workspace is None:
         need = gdn_chunk_prefill_workspace_size(N, Ns, Hk, Hv, dk, _io(q))
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("gdn_chunk_prefill", lib().gdn_chunk_prefill(
-        _p(q), _p(k), _p(v), q.stride(0), k.stride(0), v.stride(0), _p(a), _p(b), _p(A_log),
+        _p(q), _p(k), _p(v), sq, sk, sv, _p(a), _p(b), _p(A_log),
         _p(dt_bias), _p(g_opt), _p(beta_opt), _p(state_in), _p(state_out), _p(o),
         _p(cu_seqlens), Ns, N, Hk, Hv, dk, dv, float(scale), int(bool(use_qk_l2norm)),
         _p(workspace), ws_bytes, _io(q), _stream(stream)))
@@ -175,11 +186,9 @@ def gdn_chunk_prefill_noalloc(q, k, v, a, b, A_log, dt_bias, o, Hk, Hv, cu_seqle
     _dev(q, k, v, a, b, A_log, dt_bias, o, cu_seqlens, state_in, state_out, g_opt, beta_opt)
     N = q.shape[0]
     Ns = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
-    for t in (q, k, v):
-        if t.stride(-1) != 1:
-            raise ValueError("q, k, v rows must be contiguous")
+    sq, sk, sv = (_row_stride(t) for t in (q, k, v))
     _check("gdn_chunk_prefill_noalloc", lib().gdn_chunk_prefill_noalloc(
-        _p(q), _p(k), _p(v), q.stride(0), k.stride(0), v.stride(0), _p(a), _p(b), _p(A_log),
+        _p(q), _p(k), _p(v), sq, sk, sv, _p(a), _p(b), _p(A_log),
         _p(dt_bias), _p(g_opt), _p(beta_opt), _p(state_in), _p(state_out), _p(o),
         _p(cu_seqlens), Ns, N, Hk, Hv, dk, dv, float(scale), int(bool(use_qk_l2norm)), _io(q),
         _stream(stream)))

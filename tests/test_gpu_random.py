@@ -46,7 +46,13 @@ def _decode_case(seed):
                 fused=bool(rng.random() < 0.6))
 
 
-PREFILL = [_prefill_case(s) for s in range(24)]
+PREFILL = [_prefill_case(s) for s in range(24)] + [
+    # inputs of at most one row built from NumPy (an empty array has strides (0, 0)) through
+    # the separate calls, whose binding passes the q, k, v row strides
+    dict(hk=2, hv=14, io="bf16", lens=[0], init_state=False, fused=False),
+    dict(hk=2, hv=4, io="bf16", lens=[0, 0], init_state=True, fused=False),
+    dict(hk=1, hv=2, io="f32", lens=[1], init_state=True, fused=False),
+]
 DECODE = [_decode_case(s) for s in range(16)]
 
 
