@@ -21,8 +21,9 @@
 //      raw K and Q rows in LDS, forms K K^T and Q K^T on MFMA once for the value
 //      heads sharing the key head, then per value head inverts I + A (blocked:
 //      fp32 forward substitution on the diagonal blocks, fp32 MFMA products off
-//      it) and writes T' = T diag(beta) as bf16 hi/lo planes plus the per-token
-//      factors to the workspace.
+//      it) and writes T' = T diag(beta) as bf16 hi/lo parts (MFMA A-operand
+//      fragments for bf16 io, row-major planes for fp32 io), P where the sweep
+//      reads it, and the per-token factors to the workspace.
 //   3. sweep: one workgroup per (sequence, value head, block of dv columns; 4 or 8
 //      waves of 16 columns).  Each wave keeps a 128 x 16 slice of the fp32 state in
 //      registers for the whole sequence and walks the chunks in order; per chunk
