@@ -114,8 +114,7 @@ recurrent_step_kernel(StepArgs p) {
   float* red2 = red1 + HPP * 4 * SD;         // HPP * 4 * 128
   float* gsh = red2 + HPP * 4 * SD;          // r: decay e^g
   float* bsh = gsh + r;                      // r: beta
-  float* nsh = bsh + r;                      // 2: 1/|q|, 1/|k|
-  float* zsh = nsh + 2;                      // NORM: r * 128 gate values z
+  float* zsh = bsh + r + 2;                  // NORM: r * 128 gate values z (after 2 spare)
   float* wsh = zsh + (NORM ? r * SD : 0);    // NORM: 128 norm weights
 
   const int hl = __builtin_amdgcn_readfirstlane(tid >> 8);   // head slot inside a pass
@@ -280,17 +279,21 @@ recurrent_step_kernel(StepArgs p) {
   }
   lds_barrier();
 
-  // ---- L2 norms of q and k, gates of the r value heads
-  if (tid < 64) {
-    const float q0 = yv[tid], q1 = yv[tid + 64], k0 = yv[SD + tid], k1 = yv[SD + tid + 64];
-    float sq = group_sum<64>(q0 * q0 + q1 * q1);
-    float sk = group_sum<64>(k0 * k0 + k1 * k1);
-    if (tid == 0) {
-      // hardware reciprocal square root (about 1 ulp)
-      nsh[0] = p.use_l2 ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.0f;
-      nsh[1] = p.use_l2 ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 1.0f;
-    }
-  } else if (tid >= 64 && tid < 64 + r) {
+  // ---- L2 norms of q and k: every wave forms them from the staged conv outputs and keeps
+  // them in registers (the same lanes and shuffle order in every wave, so the same values),
+  // which saves a barrier; gates of the r value heads, read after the first exchange
+  // barrier of the head loop
+  float rq, rk;
+  {
+    const int l = tid & 63;
+    const float q0 = yv[l], q1 = yv[l + 64], k0 = yv[SD + l], k1 = yv[SD + l + 64];
+    const float sq = group_sum<64>(q0 * q0 + q1 * q1);
+    const float sk = group_sum<64>(k0 * k0 + k1 * k1);
+    // hardware reciprocal square root (about 1 ulp)
+    rq = p.use_l2 ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.0f;
+    rk = p.use_l2 ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 1.0f;
+  }
+  if (tid >= 64 && tid < 64 + r) {
     const int j = tid - 64;
     float g, beta;
     if (p.g_opt) {
@@ -302,9 +305,6 @@ recurrent_step_kernel(StepArgs p) {
     gsh[j] = expf(g);
     bsh[j] = beta;
   }
-  lds_barrier();
-
-  const float rq = nsh[0], rk = nsh[1];
 
   for (int h0 = 0; h0 < r; h0 += HPP) {
     const int j = h0 + hl;        // value head inside the group
