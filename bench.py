@@ -57,17 +57,17 @@ KERNEL_SOURCES = {"gdn_chunk_prefill": ("gdn_chunk.hip", "gdn_common.hpp", "gdn_
 # key -> (call whose sources the figure belongs to, their digest, bytes).  A figure is not
 # reported once those sources change.
 MEASURED_TRAFFIC = {
-    "gdn_chunk_prefill": ("gdn_chunk_prefill", "c27019f1065ebd34", 248.6e6),
-    "gdn_conv_chunk_prefill": ("gdn_conv_chunk_prefill", "ce4bfadd5fd04439", 355.8e6),
+    "gdn_chunk_prefill": ("gdn_chunk_prefill", "6d1b9ac6e5ec6db2", 248.6e6),
+    "gdn_conv_chunk_prefill": ("gdn_conv_chunk_prefill", "224f272e80008db9", 355.8e6),
     "gdn_recurrent_step": ("gdn_recurrent_step", "d9d1bfb2ad95a136", 1105.8e6),
     "gdn_recurrent_step_bf16_state": ("gdn_recurrent_step_bf16_state", "d9d1bfb2ad95a136", 568.8e6),
     # the chunk call on the prefill_configs workloads
-    "gdn_chunk_prefill@l0_qwen3.5-0.8b_T256_fp32": ("gdn_chunk_prefill", "c27019f1065ebd34", 24.3e6),
-    "gdn_chunk_prefill@l3_qwen3.5-397b_T32768_bf16": ("gdn_chunk_prefill", "c27019f1065ebd34", 3461.9e6),
-    "gdn_chunk_prefill@l4_qwen3.5-9b_varlen64_bf16": ("gdn_chunk_prefill", "c27019f1065ebd34", 3970.7e6),
+    "gdn_chunk_prefill@l0_qwen3.5-0.8b_T256_fp32": ("gdn_chunk_prefill", "6d1b9ac6e5ec6db2", 24.3e6),
+    "gdn_chunk_prefill@l3_qwen3.5-397b_T32768_bf16": ("gdn_chunk_prefill", "6d1b9ac6e5ec6db2", 3461.9e6),
+    "gdn_chunk_prefill@l4_qwen3.5-9b_varlen64_bf16": ("gdn_chunk_prefill", "6d1b9ac6e5ec6db2", 3970.7e6),
     # and on the segment_scan workloads
-    "gdn_chunk_prefill@qwen3.5-9b_shard8_T32768_bf16": ("gdn_chunk_prefill", "c27019f1065ebd34", 335.6e6),
-    "gdn_chunk_prefill@qwen3.5-0.8b_T32768_bf16": ("gdn_chunk_prefill", "c27019f1065ebd34", 1701.3e6),
+    "gdn_chunk_prefill@qwen3.5-9b_shard8_T32768_bf16": ("gdn_chunk_prefill", "6d1b9ac6e5ec6db2", 335.6e6),
+    "gdn_chunk_prefill@qwen3.5-0.8b_T32768_bf16": ("gdn_chunk_prefill", "6d1b9ac6e5ec6db2", 1701.3e6),
 }
 
 

@@ -70,8 +70,9 @@ constexpr int F_STRIDE = CH + 4;       // floats per A/T row
 //     e^{gamma_L - gamma}/|k|, e^{gamma_L}, gamma, 1/|k|, 1/|q| (and one of padding),
 //     then, for the 4-wave sweep, P hi, P lo planes (38912 bytes; 20480 without P:
 //     the fp32 8-wave sweep forms P from the Q and K rows it stages anyway); bf16 io
-//     writes fragment-native records instead (below: with P for the row-split and
-//     column-chain sweeps, T' only for the 8-wave sweep);
+//     writes fragment-native records instead (below: with P for the row-split,
+//     column-chain and 4-wave sweeps and the transition launches, T' only for the 8-wave
+//     sweep);
 //   fp32 io only, per (global chunk c, key head kh): K hi, K lo, Q hi, Q lo rows
 //     (64 x 136 bf16 each); bf16 io stages K and Q straight from the input rows.
 constexpr int64_t WS_PL_BYTES = (int64_t)CH * T_STRIDE * 2;          // 9216 per plane
@@ -449,9 +450,9 @@ __global__ void __launch_bounds__(256) chunk_map_kernel(const int32_t* cu, int N
 // (K^ K^T and Q^ K^T with the 1/|k|, 1/|q| factors) are formed once; then, per value
 // head, its decay and write strength scale the tiles into A and P, I + A is inverted,
 // and the head's record is written.
-// record layouts the prep kernel writes: rows without P (8-wave sweep, fp32 io), rows with
-// P (4-wave sweep), fragment-native with P (row-split sweep), fragment-native T' without P
-// (8-wave sweep, bf16 io)
+// record layouts the prep kernel writes: rows without P (8-wave sweep) and rows with P
+// (4-wave sweep) for fp32 io; for bf16 io fragment-native with P (row-split, column-chain
+// and 4-wave sweeps, transition launches) and fragment-native T' without P (8-wave sweep)
 enum PrepMode { PREP_ROWS = 0, PREP_ROWS_P = 1, PREP_FRAG = 2, PREP_FRAG_T = 3 };
 constexpr int PREP_RB = 4;                // value heads whose gates are staged at once
 static_assert(PREP_RB == NTHR / 64, "one wave stages the gates of one value head");
