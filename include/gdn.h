@@ -104,7 +104,9 @@ gdn_status_t gdn_conv1d_fwd(const void* x, const float* w, void* y, const int32_
  * sequences with Hk key heads, Hv value heads, head width d (128) and io dtype io.
  * The workspace holds the chunk map of the packed sequences; for at most
  * ceil(N/64) + Ns 64-token chunks, per (chunk, value head) a 38912-byte record (the
- * chunk's 64 x 64 T' and P matrices as bf16 hi/lo parts plus per-token factors) and,
+ * chunk's 64 x 64 T' and P matrices as bf16 hi/lo parts plus per-token factors; bf16 io
+ * lays them out as MFMA operand fragments in the first 34816 bytes, or 18432 without
+ * P, for the sweep shapes that form P themselves) and,
  * for fp32 io only, per (chunk, key head) the bf16 hi/lo K and Q rows (69632 bytes);
  * and, where the intra-sequence scan may run, 7 segment-transition pairs of 128 KB per
  * (sequence, value head) pair: fp32 io with at most 64 pairs, bf16 io with at most 16
