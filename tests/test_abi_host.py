@@ -259,3 +259,23 @@ def test_prefill_layer_rejects():
     assert _layer(K=3) == _lib.GDN_ERR_UNSUPPORTED
     assert _layer() == _lib.GDN_ERR_INVALID_ARG     # no workspace
     assert "workspace" in _msg()
+
+
+def test_binding_row_strides():
+    """The binding passes q, k, v row strides: a view's stride(0) when it has rows to step
+    over, its width when it has at most one (torch reports arbitrary strides for those: an
+    empty array from NumPy has strides (0, 0)), and it refuses rows that are not contiguous."""
+    import numpy as np
+    import torch
+
+    y = torch.zeros(5, 1536)
+    assert _lib._row_stride(y[:, 256:512]) == 1536
+    empty = torch.from_numpy(np.zeros((0, 1536), dtype=np.float32))
+    assert empty.stride() == (0, 0)
+    assert _lib._row_stride(empty[:, :256]) == 256
+    one = torch.zeros(1, 1536).as_strided((1, 256), (1, 1))
+    assert _lib._row_stride(one) == 256
+    with pytest.raises(ValueError):
+        _lib._row_stride(y.t()[:, :3])
+    with pytest.raises(ValueError):
+        _lib._row_stride(torch.zeros(1, 512)[:, ::2])
